@@ -1,0 +1,155 @@
+"""Seeded synthetic workloads for D = A.B + C.
+
+This module only draws numbers: it holds none of the operation's arithmetic and
+imports neither the HIP binding nor the oracle.  Both sides take their inputs
+from here.
+
+Draw recipe (the same for every workload):
+
+* ``numpy.random.default_rng(seed)`` (PCG64); draw order A (M x K, row-major),
+  B (its N x K storage order), C (M x N), then SFA, SFB.
+* Floating values are drawn in float32 and rounded to the element type with
+  torch's CPU casts (round to nearest even): bf16, fp16, float8_e4m3fn.
+* "N(0, s)": s is the standard deviation.
+* Integer variants: A, B, C uniform integers in [-4, 4]; for the block-scaled
+  form the e4m3 elements are integers in [-4, 4] and the scale exponents lie
+  in {0, 1, 2}, so every partial sum stays an integer below 2^24.
+* e8m0 scales: exponent e uniform in {-4..4}, stored code 127 + e.
+
+Each workload keeps its operands as raw element codes (uint16 for bf16/fp16,
+uint8 for e4m3/e8m0) plus float32 C, laid out packed (lda = ldb = K,
+ldc = N).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    M: int
+    N: int
+    K: int
+    in_type: str            # "bf16" | "fp16" | "e4m3"
+    out_type: str           # "f32" | "bf16"
+    dist_a: tuple
+    dist_b: tuple
+    dist_c: tuple | None    # None: C absent (C = 0, passed as NULL)
+    seed: int
+    scaled: bool = False    # block-scaled e4m3 with e8m0 scales per 32 K
+    note: str = ""
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M * self.N * self.K
+
+
+U11 = ("uniform", -1.0, 1.0)
+
+WORKLOADS = {
+    "square256_bf16": Workload("square256_bf16", 256, 256, 256, "bf16", "f32", U11, U11, U11, 0,
+                               note="M=N=K=256 bf16, C and D fp32"),
+    "square4096_bf16": Workload("square4096_bf16", 4096, 4096, 4096, "bf16", "f32", U11, U11, U11, 1,
+                                note="M=N=K=4096 bf16, C and D fp32"),
+    "ragged_fp16": Workload("ragged_fp16", 4000, 3000, 4100, "fp16", "f32",
+                            ("normal", 1.0), ("normal", 1.0), None, 2,
+                            note="M=4000 N=3000 K=4100 fp16, C=0, fp32 out"),
+    "llm_proj_bf16": Workload("llm_proj_bf16", 16384, 14336, 4096, "bf16", "bf16",
+                              ("normal", 1.0), ("normal", 0.02), None, 3,
+                              note="M=16384 N=14336 K=4096 bf16, C=0, bf16 out"),
+    "mxfp8_8192": Workload("mxfp8_8192", 8192, 8192, 8192, "e4m3", "f32", U11, U11, None, 4,
+                           scaled=True, note="M=N=K=8192 e4m3 + e8m0 per 32 K, C=0, fp32 out"),
+}
+
+
+def _draw(rng, dist, shape):
+    kind = dist[0]
+    if kind == "uniform":
+        lo, hi = dist[1], dist[2]
+        return rng.uniform(lo, hi, size=shape).astype(np.float32)
+    if kind == "normal":
+        x = rng.standard_normal(size=shape, dtype=np.float32)
+        return x * np.float32(dist[1])
+    raise ValueError(kind)
+
+
+def to_codes(x_f32: np.ndarray, in_type: str) -> np.ndarray:
+    """float32 -> raw element codes by torch's RNE casts (generation only)."""
+    t = torch.from_numpy(np.ascontiguousarray(x_f32, dtype=np.float32))
+    if in_type == "bf16":
+        return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    if in_type == "fp16":
+        return t.to(torch.float16).view(torch.int16).numpy().view(np.uint16)
+    if in_type == "e4m3":
+        return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    raise ValueError(in_type)
+
+
+def generate(w: Workload, integer: bool = False, M=None, N=None, K=None, seed=None):
+    """Draw a workload's operands.  Sizes and seed may be overridden (for
+    reduced-size parity cases of the same recipe).
+
+    Returns a dict with ``A`` (M x K codes), ``B`` (N x K codes), ``C`` (M x N
+    float32 or None), ``SFA``/``SFB`` (uint8 e8m0 codes or None) and the sizes.
+    """
+    M = w.M if M is None else M
+    N = w.N if N is None else N
+    K = w.K if K is None else K
+    seed = w.seed if seed is None else seed
+    rng = np.random.default_rng(seed)
+    if integer:
+        A = to_codes(rng.integers(-4, 5, size=(M, K)).astype(np.float32), w.in_type)
+        B = to_codes(rng.integers(-4, 5, size=(N, K)).astype(np.float32), w.in_type)
+        C = rng.integers(-4, 5, size=(M, N)).astype(np.float32) if w.dist_c is not None else None
+    else:
+        A = to_codes(_draw(rng, w.dist_a, (M, K)), w.in_type)
+        B = to_codes(_draw(rng, w.dist_b, (N, K)), w.in_type)
+        C = _draw(rng, w.dist_c, (M, N)) if w.dist_c is not None else None
+    SFA = SFB = None
+    if w.scaled:
+        nkb = -(-K // 32)
+        if integer:
+            SFA = (127 + rng.integers(0, 3, size=(M, nkb))).astype(np.uint8)
+            SFB = (127 + rng.integers(0, 3, size=(N, nkb))).astype(np.uint8)
+        else:
+            SFA = (127 + rng.integers(-4, 5, size=(M, nkb))).astype(np.uint8)
+            SFB = (127 + rng.integers(-4, 5, size=(N, nkb))).astype(np.uint8)
+    return {"A": A, "B": B, "C": C, "SFA": SFA, "SFB": SFB, "M": M, "N": N, "K": K,
+            "in_type": w.in_type, "out_type": w.out_type}
+
+
+def random_codes(rng, in_type, shape, integer=False, dist=U11):
+    """Free-standing operand draw (parity sweeps of odd shapes)."""
+    if integer:
+        return to_codes(rng.integers(-4, 5, size=shape).astype(np.float32), in_type)
+    return to_codes(_draw(rng, dist, shape), in_type)
+
+
+def sample_indices(M: int, N: int, seed: int, count: int = 4096):
+    """Output elements to check on large outputs.
+
+    ``(random, forced)`` flat indices ``m*N + n``: ``count`` distinct elements
+    from ``default_rng(seed + 7919)``, and a forced set: the four corners, 64
+    elements in the last 256 rows, 64 in the last 256 columns, and the
+    crossings of rows and columns on both sides of the 128/256 boundaries.
+    """
+    total = M * N
+    rng = np.random.default_rng(seed + 7919)
+    count = min(count, total)
+    rand = rng.choice(total, size=count, replace=False).astype(np.int64)
+    forced = {(0, 0), (0, N - 1), (M - 1, 0), (M - 1, N - 1)}
+    r_lo, c_lo = max(0, M - 256), max(0, N - 256)
+    for _ in range(64):
+        forced.add((int(rng.integers(r_lo, M)), int(rng.integers(0, N))))
+        forced.add((int(rng.integers(0, M)), int(rng.integers(c_lo, N))))
+    edges_r = [r for r in (127, 128, 255, 256, M - 2) if 0 <= r < M]
+    edges_c = [c for c in (127, 128, 255, 256, N - 2) if 0 <= c < N]
+    for r in edges_r:
+        for c in edges_c:
+            forced.add((r, c))
+    forced_idx = np.array(sorted(m * N + n for m, n in forced), dtype=np.int64)
+    return rand, forced_idx

@@ -1,0 +1,150 @@
+"""Benchmark of D = A.B + C on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+One step is one D = A.B + C call on the workload, inputs already resident in
+HBM.  W untimed steps, then exactly K timed steps bracketed by device
+synchronisation; the GEMM kernel's average duration is taken with HIP events
+recorded on the stream the kernel is launched on (torch's current stream).
+Prints one JSON line.  The default workload is the 4096^3 bf16 GEMM with fp32
+C and D.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GEMM TFLOP/s and % of MI355X MFMA peak (bf16 4096³; mxfp8 8192³)"
+# MI355X published dense peaks (256 CUs at 2.4 GHz), TFLOP/s
+PEAK_TFLOPS = {"bf16": 2516.6, "fp16": 2516.6, "e4m3": 5033.2}
+
+
+def algorithmic_bytes(w):
+    """Bytes the operation must move at least once: A, B, (C), D, (scales)."""
+    es = 1 if w.in_type == "e4m3" else 2
+    os_ = 4 if w.out_type == "f32" else 2
+    b = (w.M * w.K + w.N * w.K) * es + w.M * w.N * os_
+    if w.dist_c is not None:
+        b += w.M * w.N * os_
+    if w.scaled:
+        b += (w.M + w.N) * (w.K // 32)
+    return b
+
+
+def device_inputs(w, x, torch):
+    dev = torch.device("cuda:0")
+    if w.in_type == "e4m3":
+        A = torch.from_numpy(x["A"]).to(dev)
+        B = torch.from_numpy(x["B"]).to(dev)
+        extra = (torch.from_numpy(x["SFA"]).to(dev), torch.from_numpy(x["SFB"]).to(dev))
+    else:
+        import numpy as np
+        dt = torch.bfloat16 if w.in_type == "bf16" else torch.float16
+        A = torch.from_numpy(x["A"].view(np.int16)).view(dt).to(dev)
+        B = torch.from_numpy(x["B"].view(np.int16)).view(dt).to(dev)
+        extra = None
+    C = torch.from_numpy(x["C"]).to(dev) if x["C"] is not None else None
+    return A, B, C, extra
+
+
+def cpu_baseline(w, x, target_rows):
+    """Time the oracle on the first `target_rows` full rows of D (every column)."""
+    import numpy as np
+    import oracle
+    rows = min(target_rows, w.M)
+    idx = np.arange(rows * w.N, dtype=np.int64)
+    oracle.gemm_ref(w.in_type, x["A"][:1], x["B"][:1], C=None, idx=np.zeros(1, np.int64))  # load, warm
+    t0 = time.perf_counter()
+    oracle.gemm_ref(w.in_type, x["A"], x["B"], C=x["C"], SFA=x["SFA"], SFB=x["SFB"], idx=idx)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * w.N * w.K
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "first %d rows x all %d columns of D (%d elements, each a full K=%d fp64 dot product); "
+                      "%.1f s" % (rows, w.N, rows * w.N, w.K, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="square4096_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=192)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (got --gpus %d)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import tiled_dense_gemm_tile_amd as tg
+    from tiled_dense_gemm_tile_amd import inputs
+
+    w = inputs.WORKLOADS[args.workload]
+    x = inputs.generate(w)
+    A, B, C, extra = device_inputs(w, x, torch)
+    out_dtype = torch.float32 if w.out_type == "f32" else torch.bfloat16
+    D = torch.empty((w.M, w.N), dtype=out_dtype, device="cuda:0")
+
+    if w.in_type == "bf16":
+        step = lambda: tg.gemm_bf16(A, B, C, out_dtype=out_dtype, D=D)
+    elif w.in_type == "fp16":
+        step = lambda: tg.gemm_fp16(A, B, C, out_dtype=out_dtype, D=D)
+    else:
+        SFA, SFB = extra
+        step = lambda: tg.gemm_mxfp8(A, SFA, B, SFB, C, out_dtype=out_dtype, D=D)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kernel_ms = ev0.elapsed_time(ev1) / args.steps     # one kernel launch per step
+    ms_per_step = wall * 1e3 / args.steps
+
+    tflops = w.flops / (kernel_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.in_type]
+    res = {
+        "metric": METRIC,
+        "value": round(w.flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.in_type,
+        "data": "synthetic",
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "in": w.in_type, "out": w.out_type,
+                   "C": "fp32 U[-1,1]" if w.dist_c else "none", "layout": "A row-major, B column-major (N x K)",
+                   "seed": w.seed, "note": w.note},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(tflops / peak, 4), "traffic": None,
+                     "kernel_ms": round(kernel_ms, 5),
+                     "algorithmic_bytes": algorithmic_bytes(w)},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, x, args.cpu_rows)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,134 @@
+/*
+ * tilegemm.h -- C ABI of the tiled matrix multiply-accumulate D = A.B + C
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (page "Tensor Core 数据布局的演进" / Evolution of Tensor Core
+ * data layouts, section 概览, the equation D = AB + C; section
+ * 一个具体的 fragment 映射 for the operand convention):
+ *
+ *     D[m][n] = C[m][n] + sum_{k<K} a(m,k) * b(k,n)     0 <= m < M, 0 <= n < N
+ *
+ * Layouts (all sizes and leading dimensions in ELEMENTS, not bytes):
+ *   A  M x K row-major:                      a(m,k) = A[m*lda + k]
+ *   B  K x N column-major, i.e. stored as N rows of K elements:
+ *                                            b(k,n) = B[n*ldb + k]
+ *   C  M x N row-major, element type = the output type, or NULL (C = 0)
+ *   D  M x N row-major, element type given by out_type
+ * Products are formed exactly and accumulated in fp32.  Summation order
+ * inside the library is unspecified; integer-valued inputs whose partial sums
+ * stay below 2^24 in magnitude give exact results.
+ *
+ * Calling convention shared by every entry point:
+ *   - The caller owns every buffer (device memory) and the stream.  The
+ *     library allocates nothing, keeps no per-call state and is re-entrant.
+ *   - Calls are asynchronous: the work is enqueued on `stream` (NULL = the
+ *     default stream) and the call returns without synchronising.
+ *   - Arguments are validated before anything is enqueued.  On any status
+ *     other than GEMM_OK nothing was enqueued and D is untouched.
+ *   - M == 0 or N == 0: GEMM_OK, nothing is launched.  K == 0: D = C (or 0).
+ *   - Leading dimensions: lda >= K, ldb >= K, ldc >= N, ldd >= N, else
+ *     GEMM_ERR_BAD_LD.  Any such ld is accepted; the load width follows the
+ *     alignment of pointers, leading dimensions and K (16-byte vectors when
+ *     everything is a multiple of 16 bytes, narrower otherwise).  The
+ *     remainder of M, N and K that does not fill a tile is predicated (page
+ *     "（二）CUTLASS —— 掌握 TMA", section on remainder tiles: out-of-range
+ *     elements are never read or written); unlike the TMA rule on that page,
+ *     leading dimensions need no 16-byte padding.
+ *   - Pointers: A and B must be non-NULL when M*N*K > 0, D when M*N > 0
+ *     (GEMM_ERR_NULL_POINTER); each must be aligned to its element size
+ *     (GEMM_ERR_MISALIGNED).
+ *   - Size limits: M, N, K < 2^31 and each operand's rows may span at most
+ *     2^31 / 256 bytes of leading dimension (lda*esize, ldb*esize,
+ *     ldc*osize, ldd*osize < 8 MiB); larger values give
+ *     GEMM_ERR_UNSUPPORTED.
+ *   - Aliasing: C == D with ldc == ldd is allowed (in-place D += A.B).  Any
+ *     other overlap of C with D is GEMM_ERR_UNSUPPORTED; A or B overlapping
+ *     D is undefined behaviour.
+ *   - A failed launch returns GEMM_ERR_HIP; gemm_last_hip_error() then gives
+ *     the hipError_t of the calling thread's last failure.
+ */
+#ifndef TILEGEMM_H
+#define TILEGEMM_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GEMM_OK = 0,
+    GEMM_ERR_INVALID_SIZE = 1,   /* M, N or K negative */
+    GEMM_ERR_NULL_POINTER = 2,   /* a required pointer is NULL */
+    GEMM_ERR_BAD_LD = 3,         /* a leading dimension is too small */
+    GEMM_ERR_MISALIGNED = 4,     /* a pointer is not aligned to its element size */
+    GEMM_ERR_UNSUPPORTED = 5,    /* valid but outside this library's limits */
+    GEMM_ERR_HIP = 6             /* the HIP runtime reported an error */
+} gemm_status;
+
+typedef enum {
+    GEMM_OUT_F32 = 0,            /* D (and C) are fp32 */
+    GEMM_OUT_BF16 = 1            /* D (and C) are bf16; fp32 sums rounded to nearest even */
+} gemm_out_type;
+
+/*
+ * gemm_bf16 -- D = A.B + C with bf16 A and B, fp32 accumulation.
+ * Source: "Tensor Core 数据布局的演进", section 一个具体的 fragment 映射
+ * (A row-major, B column-major, 16-bit inputs, fp32 accumulator).
+ *   A: bf16, M x K row-major, lda     B: bf16, N x K (column-major K x N), ldb
+ *   C: out_type, M x N row-major, ldc, or NULL
+ *   D: out_type, M x N row-major, ldd
+ *   out_type: GEMM_OUT_F32 or GEMM_OUT_BF16 (else GEMM_ERR_UNSUPPORTED)
+ */
+gemm_status gemm_bf16(int64_t M, int64_t N, int64_t K,
+                      const void *A, int64_t lda,
+                      const void *B, int64_t ldb,
+                      const void *C, int64_t ldc,
+                      void *D, int64_t ldd,
+                      int out_type, hipStream_t stream);
+
+/*
+ * gemm_fp16 -- as gemm_bf16 with IEEE binary16 A and B (same page and
+ * section: the fragment mapping is stated for fp16 or bf16 inputs).
+ */
+gemm_status gemm_fp16(int64_t M, int64_t N, int64_t K,
+                      const void *A, int64_t lda,
+                      const void *B, int64_t ldb,
+                      const void *C, int64_t ldc,
+                      void *D, int64_t ldd,
+                      int out_type, hipStream_t stream);
+
+/*
+ * gemm_mxfp8 -- block-scaled fp8: D = A.B + C with
+ *     a(m,k) = e4m3(A[m*lda + k]) * 2^(SFA[m*ldsfa + k/32] - 127)
+ *     b(k,n) = e4m3(B[n*ldb + k]) * 2^(SFB[n*ldsfb + k/32] - 127)
+ * Source: "Tensor Core 数据布局的演进", section Block-Scaled MMA 的 Scale
+ * Factors: SFA(M, SFK) scales K block sfk of row m of A, SFB(N, SFK) scales
+ * column n of B, one scale shared by all K elements of its block.  Here a
+ * block is 32 contiguous K elements and a scale is an e8m0 code.
+ *   A: OCP e4m3 (fn) bytes, M x K row-major       SFA: e8m0 bytes, M x K/32, ldsfa
+ *   B: e4m3 bytes, N x K (column-major K x N)     SFB: e8m0 bytes, N x K/32, ldsfb
+ *   C, D, out_type: as gemm_bf16
+ * K must be a multiple of 32 (else GEMM_ERR_UNSUPPORTED); ldsfa, ldsfb >=
+ * K/32 (else GEMM_ERR_BAD_LD); SFA and SFB non-NULL when M*N*K > 0.  Scale
+ * code 0xFF (NaN) and e4m3 NaN inputs give NaN in the affected outputs.
+ */
+gemm_status gemm_mxfp8(int64_t M, int64_t N, int64_t K,
+                       const void *A, int64_t lda, const void *SFA, int64_t ldsfa,
+                       const void *B, int64_t ldb, const void *SFB, int64_t ldsfb,
+                       const void *C, int64_t ldc,
+                       void *D, int64_t ldd,
+                       int out_type, hipStream_t stream);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char *gemm_status_string(int status);
+
+/* hipError_t of the calling thread's last GEMM_ERR_HIP (0 if none). */
+int gemm_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TILEGEMM_H */

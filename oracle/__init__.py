@@ -85,6 +85,8 @@ def lib():
                 f.argtypes = [arg]
             L.orc_rne_bf16.restype = ctypes.c_uint16
             L.orc_rne_bf16.argtypes = [ctypes.c_double]
+            L.orc_rne_bf16_f32_array.restype = None
+            L.orc_rne_bf16_f32_array.argtypes = [vp, vp, i64]
             L.oracle_num_threads.restype = ctypes.c_int
             L.oracle_num_threads.argtypes = []
             _lib = L
@@ -201,6 +203,14 @@ def rne_bf16(x) -> np.ndarray:
     x = np.asarray(x, dtype=np.float64)
     out = np.fromiter((f(float(v)) for v in x.ravel()), dtype=np.uint16, count=x.size)
     return out.reshape(x.shape)
+
+
+def rne_bf16_f32(x) -> np.ndarray:
+    """Round a float32 array to bf16 bits, nearest-even (C loop, OpenMP)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint16)
+    lib().orc_rne_bf16_f32_array(x.ctypes.data, out.ctypes.data, x.size)
+    return out
 
 
 def num_threads() -> int:

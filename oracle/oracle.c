@@ -171,6 +171,14 @@ uint16_t orc_rne_bf16(double x)
     return (uint16_t)(sign | (eb << 7) | f);
 }
 
+/* Element-wise orc_rne_bf16 over an fp32 array (each value widened exactly). */
+void orc_rne_bf16_f32_array(const float *x, uint16_t *out, int64_t n)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = orc_rne_bf16((double)x[i]);
+}
+
 /* ---- the operation ---------------------------------------------------- */
 
 static double dec_elem(int type, const void *base, int64_t i)

@@ -1,0 +1,98 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments before touching the GPU (CPU only: no compute call is made)."""
+import os
+import re
+import subprocess
+
+import pytest
+
+import tiled_dense_gemm_tile_amd as tg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tilegemm.h")
+
+OK, INVALID_SIZE, NULL_POINTER, BAD_LD, MISALIGNED, UNSUPPORTED = 0, 1, 2, 3, 4, 5
+F32, BF16 = 0, 1
+P = 0x10000000  # a fake, aligned device address: never dereferenced by these calls
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == ["gemm_bf16", "gemm_fp16", "gemm_last_hip_error", "gemm_mxfp8",
+                                    "gemm_status_string"]
+
+
+def test_library_exports_every_declared_symbol():
+    path = tg.library_path()
+    assert os.path.exists(path), "build the library first"
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(tg.raw, name) is not None
+
+
+def test_status_strings():
+    for s in range(7):
+        assert tg.raw.status_string(s).startswith(tg.STATUS[s])
+    assert "unknown" in tg.raw.status_string(99)
+    assert tg.raw.gemm_last_hip_error() == 0
+
+
+def call16(fn="gemm_bf16", M=64, N=64, K=64, A=P, lda=64, B=P, ldb=64, C=None, ldc=0, D=P + (1 << 24),
+           ldd=64, out=F32):
+    return getattr(tg.raw, fn)(M, N, K, A, lda, B, ldb, C, ldc, D, ldd, out, None)
+
+
+@pytest.mark.parametrize("fn", ["gemm_bf16", "gemm_fp16"])
+def test_validation_16bit(fn):
+    assert call16(fn, M=-1) == INVALID_SIZE
+    assert call16(fn, N=-5) == INVALID_SIZE
+    assert call16(fn, K=-1) == INVALID_SIZE
+    assert call16(fn, M=0) == OK                       # nothing to do, nothing launched
+    assert call16(fn, N=0, D=None, A=None) == OK
+    assert call16(fn, M=1 << 31) == UNSUPPORTED
+    assert call16(fn, out=7) == UNSUPPORTED
+    assert call16(fn, lda=63) == BAD_LD
+    assert call16(fn, ldb=10) == BAD_LD
+    assert call16(fn, ldd=63) == BAD_LD
+    assert call16(fn, C=P + (1 << 26), ldc=32) == BAD_LD
+    assert call16(fn, D=None) == NULL_POINTER
+    assert call16(fn, A=None) == NULL_POINTER
+    assert call16(fn, B=None) == NULL_POINTER
+    assert call16(fn, A=P + 1) == MISALIGNED
+    assert call16(fn, D=P + (1 << 24) + 2) == MISALIGNED
+    assert call16(fn, D=P + (1 << 24) + 2, out=BF16, C=P + 3, ldc=64) == MISALIGNED
+    assert call16(fn, lda=4 << 20, K=64) == UNSUPPORTED     # 8 MiB rows
+    D = P + (1 << 24)
+    assert call16(fn, C=D + 4, ldc=64, D=D) == UNSUPPORTED  # partial overlap of C and D
+    assert call16(fn, C=D, ldc=128, D=D, ldd=64) == UNSUPPORTED
+
+
+def call8(M=64, N=64, K=64, A=P, lda=64, SFA=P + 4096, ldsfa=2, B=P, ldb=64, SFB=P + 8192, ldsfb=2,
+          C=None, ldc=0, D=P + (1 << 24), ldd=64, out=F32):
+    return tg.raw.gemm_mxfp8(M, N, K, A, lda, SFA, ldsfa, B, ldb, SFB, ldsfb, C, ldc, D, ldd, out, None)
+
+
+def test_validation_mxfp8():
+    assert call8(M=-1) == INVALID_SIZE
+    assert call8(M=0) == OK
+    assert call8(K=48, lda=64, ldb=64) == UNSUPPORTED       # K not a multiple of 32
+    assert call8(ldsfa=1) == BAD_LD
+    assert call8(ldsfb=1) == BAD_LD
+    assert call8(SFA=None) == NULL_POINTER
+    assert call8(SFB=None) == NULL_POINTER
+    assert call8(lda=32) == BAD_LD
+    assert call8(D=None) == NULL_POINTER
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(tg, "_LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(tg, "_lib", None)
+    with pytest.raises(tg.LibraryMissing):
+        tg.raw.gemm_bf16

@@ -1,0 +1,259 @@
+"""Parity of the HIP path (bf16 / fp16 inputs) against the oracle on an MI355X.
+
+Bar: bit-exact on integer-valued inputs; otherwise
+|D - D_ref| <= 2^-12 * sum_k |a*b| + 1e-6 per element (and D finite); bf16
+output equals the nearest-even rounding of the same call's fp32 result.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import check
+from tiled_dense_gemm_tile_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from gpuutil import DEV, bf16_bits, dev16, run16, say, to_f64
+
+
+def _full_check(in_type, x, Dg, integer, C=None):
+    Dr, S = oracle.gemm_ref_full(in_type, x["A"], x["B"], C=C)
+    if integer:
+        bad = np.argwhere(Dg != Dr)
+        assert bad.size == 0, "first mismatches %s" % bad[:5].tolist()
+    else:
+        rep = check.report(Dg, Dr, S)
+        assert rep["fail"] == 0, rep
+
+
+def _case(in_type, M, N, K, seed, integer, with_c=True):
+    rng = np.random.default_rng(seed)
+    x = {"A": inputs.random_codes(rng, in_type, (M, K), integer=integer),
+         "B": inputs.random_codes(rng, in_type, (N, K), integer=integer)}
+    C = None
+    if with_c:
+        C = (rng.integers(-4, 5, size=(M, N)) if integer else rng.uniform(-1, 1, size=(M, N))).astype(np.float32)
+    return x, C
+
+
+# ---- the small workload, every element ------------------------------------------
+
+@pytest.mark.parametrize("integer", [False, True])
+def test_square256_every_element(integer):
+    w = inputs.WORKLOADS["square256_bf16"]
+    x = inputs.generate(w, integer=integer)
+    say("square256 bf16 integer=%s" % integer)
+    D = run16("bf16", dev16(x["A"], "bf16"), dev16(x["B"], "bf16"), torch.from_numpy(x["C"]).to(DEV))
+    torch.cuda.synchronize()
+    Dg = to_f64(D)
+    Dr, S = oracle.gemm_ref("bf16", x["A"], x["B"], C=x["C"])   # naive loop, every element
+    if integer:
+        assert np.array_equal(Dg, Dr)
+    else:
+        rep = check.report(Dg, Dr, S)
+        assert rep["fail"] == 0, rep
+
+
+# ---- ragged shapes -------------------------------------------------------------------
+
+RAGGED = [(1, 1, 1), (1, 17, 3), (7, 5, 9), (17, 13, 65), (63, 64, 65), (64, 64, 64), (65, 63, 127),
+          (130, 70, 8), (255, 257, 256), (257, 255, 300), (129, 200, 4100), (300, 40, 1000),
+          (70, 70, 1), (70, 70, 15), (70, 70, 16), (70, 70, 17), (70, 70, 63), (70, 70, 129)]
+
+
+@pytest.mark.parametrize("in_type", ["bf16", "fp16"])
+@pytest.mark.parametrize("shape", RAGGED)
+def test_ragged(in_type, shape):
+    M, N, K = shape
+    for integer in (True, False):
+        x, C = _case(in_type, M, N, K, seed=M * 7 + N * 3 + K, integer=integer)
+        say("ragged %s %dx%dx%d integer=%s" % (in_type, M, N, K, integer))
+        D = run16(in_type, dev16(x["A"], in_type), dev16(x["B"], in_type), torch.from_numpy(C).to(DEV))
+        torch.cuda.synchronize()
+        _full_check(in_type, x, to_f64(D), integer, C)
+
+
+# ---- leading dimensions and misaligned bases -------------------------------------------
+
+@pytest.mark.parametrize("pad_a,pad_b,off", [(0, 0, 0), (2, 0, 0), (4, 6, 0), (1, 3, 0), (0, 0, 1), (8, 8, 2),
+                                             (6, 2, 4), (0, 1, 3)])
+def test_leading_dims_and_offsets(pad_a, pad_b, off):
+    M, N, K = 300, 260, 200
+    in_type = "bf16"
+    x, C = _case(in_type, M, N, K, seed=99 + pad_a + pad_b + off, integer=True)
+    lda, ldb = K + pad_a, K + pad_b
+    rng = np.random.default_rng(1)
+    Abuf = inputs.random_codes(rng, in_type, (M * lda + off,), integer=True)
+    Bbuf = inputs.random_codes(rng, in_type, (N * ldb + off,), integer=True)
+    Abuf[off:].reshape(M, lda)[:, :K] = x["A"]
+    Bbuf[off:].reshape(N, ldb)[:, :K] = x["B"]
+    Ad = dev16(Abuf, in_type)[off:].view(M, lda)[:, :K]
+    Bd = dev16(Bbuf, in_type)[off:].view(N, ldb)[:, :K]
+    say("ld lda=%d ldb=%d off=%d" % (lda, ldb, off))
+    D = run16(in_type, Ad, Bd, torch.from_numpy(C).to(DEV))
+    torch.cuda.synchronize()
+    _full_check(in_type, x, to_f64(D), True, C)
+
+
+# ---- C handling, in-place, K = 0, empty outputs, canaries --------------------------------
+
+def test_c_null_equals_zero_buffer_and_in_place():
+    M, N, K = 333, 280, 190
+    x, C = _case("bf16", M, N, K, seed=5, integer=False)
+    A, B = dev16(x["A"], "bf16"), dev16(x["B"], "bf16")
+    say("C null / zero / in-place")
+    D0 = run16("bf16", A, B, None)
+    Dz = run16("bf16", A, B, torch.zeros(M, N, device=DEV))
+    Cd = torch.from_numpy(C).to(DEV)
+    Dc = run16("bf16", A, B, Cd)
+    inplace = Cd.clone()
+    run16("bf16", A, B, inplace, D=inplace)
+    torch.cuda.synchronize()
+    assert torch.equal(D0, Dz)
+    assert torch.equal(Dc, inplace)
+    _full_check("bf16", x, to_f64(Dc), False, C)
+
+
+def test_k_zero_gives_c():
+    M, N = 100, 77
+    C = torch.randn(M, N, device=DEV)
+    A = torch.empty(M, 0, dtype=torch.bfloat16, device=DEV)
+    B = torch.empty(N, 0, dtype=torch.bfloat16, device=DEV)
+    say("K=0")
+    D = run16("bf16", A, B, C)
+    D0 = run16("bf16", A, B, None)
+    torch.cuda.synchronize()
+    assert torch.equal(D, C) and not D0.any()
+
+
+def test_empty_outputs_do_nothing():
+    D = torch.full((4, 4), 7.0, device=DEV)
+    A = torch.ones(0, 8, dtype=torch.bfloat16, device=DEV)
+    B = torch.ones(4, 8, dtype=torch.bfloat16, device=DEV)
+    run16("bf16", A, B, None, D=D[:0])
+    run16("bf16", B, A, None, D=D[:, :0])
+    torch.cuda.synchronize()
+    assert torch.all(D == 7.0)
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(200, 136, 328), (1000, 1000, 64), (513, 1030, 96)])
+def test_guard_band_untouched(out, shape):
+    M, N, K = shape
+    x, _ = _case("bf16", M, N, K, seed=3, integer=True, with_c=False)
+    ldd = N + 5
+    dt = torch.float32 if out == "f32" else torch.bfloat16
+    buf = torch.full((M + 2, ldd), float("nan"), dtype=dt, device=DEV)
+    D = buf[1:M + 1, :N]
+    say("guard %s %s" % (out, shape))
+    run16("bf16", dev16(x["A"], "bf16"), dev16(x["B"], "bf16"), None, out=out, D=D)
+    torch.cuda.synchronize()
+    assert torch.isnan(buf[0]).all() and torch.isnan(buf[M + 1]).all() and torch.isnan(buf[:, N:]).all()
+    assert not torch.isnan(D).any()
+    Dr, _ = oracle.gemm_ref_full("bf16", x["A"], x["B"])
+    if out == "f32":
+        assert np.array_equal(to_f64(D), Dr)
+    else:   # the exact integer sum, rounded once to bf16
+        assert np.array_equal(bf16_bits(D), oracle.rne_bf16_f32(Dr.astype(np.float32)))
+
+
+def test_deterministic():
+    x, C = _case("bf16", 1024, 768, 1000, seed=8, integer=False)
+    A, B, Cd = dev16(x["A"], "bf16"), dev16(x["B"], "bf16"), torch.from_numpy(C).to(DEV)
+    say("determinism")
+    D1 = run16("bf16", A, B, Cd)
+    D2 = run16("bf16", A, B, Cd)
+    torch.cuda.synchronize()
+    assert torch.equal(D1.view(torch.int32), D2.view(torch.int32))
+
+
+@pytest.mark.parametrize("shape", [(300, 200, 500), (2048, 2048, 256)])
+def test_bf16_output_is_rne_of_fp32(shape):
+    M, N, K = shape
+    x, C = _case("bf16", M, N, K, seed=21, integer=False, with_c=False)
+    A, B = dev16(x["A"], "bf16"), dev16(x["B"], "bf16")
+    say("bf16 out %s" % (shape,))
+    D32 = run16("bf16", A, B, None, out="f32")
+    D16 = run16("bf16", A, B, None, out="bf16")
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_bits(D16), oracle.rne_bf16_f32(D32.cpu().numpy()))
+    _full_check("bf16", x, to_f64(D32), False)
+
+
+# ---- the large workloads --------------------------------------------------------------------
+
+def _sampled(w, x, Dg_flat, extra_rel=0.0):
+    rand, forced = inputs.sample_indices(x["M"], x["N"], w.seed)
+    for name, idx in (("random", rand), ("forced", forced)):
+        Dr, S = oracle.gemm_ref(w.in_type, x["A"], x["B"], C=x["C"], idx=idx)
+        rep = check.report(Dg_flat[idx], Dr, S, extra_rel=extra_rel)
+        say("  %s: %s" % (name, rep))
+        assert rep["fail"] == 0, (name, rep)
+
+
+def test_square4096():
+    w = inputs.WORKLOADS["square4096_bf16"]
+    x = inputs.generate(w)
+    say("square4096 bf16")
+    D = run16("bf16", dev16(x["A"], "bf16"), dev16(x["B"], "bf16"), torch.from_numpy(x["C"]).to(DEV))
+    torch.cuda.synchronize()
+    Dg = D.cpu().numpy()
+    _sampled(w, x, Dg.ravel().astype(np.float64))
+    a, b = oracle.operands_f64("bf16", x["A"], x["B"])
+    ok, ratio = check.freivalds_blocks(Dg, a, b, x["C"], block=64)
+    say("  freivalds worst ratio %.3g" % ratio)
+    assert ok
+
+
+def test_square4096_integer():
+    w = inputs.WORKLOADS["square4096_bf16"]
+    x = inputs.generate(w, integer=True)
+    say("square4096 bf16 integer")
+    D = run16("bf16", dev16(x["A"], "bf16"), dev16(x["B"], "bf16"), torch.from_numpy(x["C"]).to(DEV))
+    torch.cuda.synchronize()
+    Dg = D.cpu().numpy()
+    a, b = oracle.operands_f64("bf16", x["A"], x["B"])
+    ok, _ = check.freivalds_blocks(Dg, a, b, x["C"], integer=True)
+    assert ok
+    rand, forced = inputs.sample_indices(4096, 4096, w.seed)
+    idx = np.concatenate([rand, forced])
+    Dr, _ = oracle.gemm_ref("bf16", x["A"], x["B"], C=x["C"], idx=idx)
+    assert np.array_equal(Dg.ravel()[idx].astype(np.float64), Dr)
+
+
+def test_ragged_fp16_every_element():
+    w = inputs.WORKLOADS["ragged_fp16"]
+    x = inputs.generate(w)
+    say("ragged fp16 4000x3000x4100")
+    D = run16("fp16", dev16(x["A"], "fp16"), dev16(x["B"], "fp16"), None)
+    torch.cuda.synchronize()
+    Dg = to_f64(D)
+    _sampled(w, x, Dg.ravel())
+    Dr, S = oracle.gemm_ref_full("fp16", x["A"], x["B"])
+    rep = check.report(Dg, Dr, S)
+    say("  full: %s" % rep)
+    assert rep["fail"] == 0
+
+
+def test_llm_projection_bf16_out():
+    w = inputs.WORKLOADS["llm_proj_bf16"]
+    x = inputs.generate(w)
+    say("llm projection 16384x14336x4096 bf16 out")
+    A, B = dev16(x["A"], "bf16"), dev16(x["B"], "bf16")
+    D16 = run16("bf16", A, B, None, out="bf16")
+    D32 = run16("bf16", A, B, None, out="f32")
+    torch.cuda.synchronize()
+    d32 = D32.cpu().numpy()
+    del D32
+    # (ii) bf16 result is the nearest-even rounding of the same kernel's fp32 result, every element
+    assert np.array_equal(bf16_bits(D16), oracle.rne_bf16_f32(d32))
+    # (i) the fp32 result meets the tolerance on the samples and the block-Freivalds check
+    _sampled(w, x, d32.ravel().astype(np.float64))
+    # (iii) the bf16 result against the oracle with the bf16 half-ulp added
+    _sampled(w, x, to_f64(D16).ravel(), extra_rel=2.0 ** -8)
+    a, b = oracle.operands_f64("bf16", x["A"], x["B"])
+    ok, ratio = check.freivalds_blocks(d32, a, b, None, block=64)
+    say("  freivalds worst ratio %.3g" % ratio)
+    assert ok

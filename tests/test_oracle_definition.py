@@ -259,6 +259,7 @@ def test_rne_bf16_matches_torch():
     ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     got = oracle.rne_bf16(x.astype(np.float64))
     assert np.array_equal(got, ref)
+    assert np.array_equal(oracle.rne_bf16_f32(x), ref)
 
 
 # ---- block scales -----------------------------------------------------------

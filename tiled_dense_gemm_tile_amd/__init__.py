@@ -1,0 +1,169 @@
+"""tiled_dense_gemm_tile_amd -- D = A.B + C on MI355X (gfx950).
+
+Thin Python binding of ``libtilegemm.so`` (the C ABI in ``include/tilegemm.h``).
+It only marshals arguments: every step of the operation runs in the HIP
+kernels.  PyTorch supplies device memory and the stream.  When the library is
+not built the calls raise :class:`LibraryMissing`; there is no fallback.
+
+Tensor conventions (same as the C ABI):
+  A: (M, K) row-major;  B: (N, K), i.e. the K x N operand stored column by
+  column;  C, D: (M, N) row-major.  The last stride of every tensor must be 1;
+  the first stride is passed as the leading dimension.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+__all__ = ["gemm_bf16", "gemm_fp16", "gemm_mxfp8", "raw", "GemmError", "LibraryMissing",
+           "library_path", "STATUS"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libtilegemm.so")
+
+STATUS = {0: "GEMM_OK", 1: "GEMM_ERR_INVALID_SIZE", 2: "GEMM_ERR_NULL_POINTER", 3: "GEMM_ERR_BAD_LD",
+          4: "GEMM_ERR_MISALIGNED", 5: "GEMM_ERR_UNSUPPORTED", 6: "GEMM_ERR_HIP"}
+OUT_F32, OUT_BF16 = 0, 1
+
+
+class LibraryMissing(RuntimeError):
+    pass
+
+
+class GemmError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH):
+                raise LibraryMissing("libtilegemm.so is not built (run __graft_entry__.build()); "
+                                     "there is no fallback path")
+            L = ctypes.CDLL(_LIB_PATH)
+            i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+            sig16 = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp, i64, ci, vp]
+            for name in ("gemm_bf16", "gemm_fp16"):
+                f = getattr(L, name)
+                f.restype, f.argtypes = ci, sig16
+            L.gemm_mxfp8.restype = ci
+            L.gemm_mxfp8.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp, i64, ci, vp]
+            L.gemm_status_string.restype = ctypes.c_char_p
+            L.gemm_status_string.argtypes = [ci]
+            L.gemm_last_hip_error.restype = ci
+            L.gemm_last_hip_error.argtypes = []
+            _lib = L
+    return _lib
+
+
+class _Raw:
+    """Direct C-ABI calls with integer pointers; each returns the gemm_status."""
+
+    def __getattr__(self, name):
+        return getattr(_load(), name)
+
+    def status_string(self, s: int) -> str:
+        return _load().gemm_status_string(int(s)).decode()
+
+
+raw = _Raw()
+
+
+def _check(status: int):
+    if status != 0:
+        L = _load()
+        msg = L.gemm_status_string(status).decode()
+        if status == 6:
+            msg += " (hipError_t %d)" % L.gemm_last_hip_error()
+        raise GemmError(status, msg)
+
+
+def _ld(t, cols):
+    if t.dim() != 2:
+        raise ValueError("expected a 2-D tensor")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError("the last stride must be 1")
+    if t.shape[0] <= 1:
+        return max(cols, t.stride(0) if t.shape[0] == 1 else 0)
+    return t.stride(0)
+
+
+def _prep(A, B, C, D, out_dtype, in_dtypes):
+    import torch
+    if A.dtype not in in_dtypes or B.dtype not in in_dtypes:
+        raise TypeError("A and B must be %s" % (in_dtypes,))
+    if not (A.is_cuda and B.is_cuda):
+        raise ValueError("A and B must be device tensors")
+    M, K = A.shape
+    N = B.shape[0]
+    if B.shape[1] != K:
+        raise ValueError("B must be (N, K) with K = A.shape[1]")
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out_dtype must be float32 or bfloat16")
+    if D is None:
+        D = torch.empty((M, N), dtype=out_dtype, device=A.device)
+    if D.dtype != out_dtype or tuple(D.shape) != (M, N):
+        raise ValueError("D must be (M, N) of out_dtype")
+    if C is not None and (C.dtype != out_dtype or tuple(C.shape) != (M, N)):
+        raise ValueError("C must be (M, N) of out_dtype")
+    stream = torch.cuda.current_stream(A.device).cuda_stream
+    out = OUT_BF16 if out_dtype == torch.bfloat16 else OUT_F32
+    return M, N, K, D, stream, out
+
+
+def _call16(name, A, B, C, out_dtype, D, dtype):
+    M, N, K, D, stream, out = _prep(A, B, C, D, out_dtype, (dtype,))
+    lda = _ld(A, K) if K else 0
+    ldb = _ld(B, K) if K else 0
+    fn = getattr(_load(), name)
+    st = fn(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb,
+            C.data_ptr() if C is not None else None, _ld(C, N) if C is not None else 0,
+            D.data_ptr(), _ld(D, N), out, stream)
+    _check(st)
+    return D
+
+
+def gemm_bf16(A, B, C=None, out_dtype=None, D=None):
+    """D = A @ B.T + C for bf16 A (M, K) and B (N, K); fp32 accumulation.
+
+    ``out_dtype`` float32 (default) or bfloat16; C (optional) has out_dtype;
+    D is allocated unless given.  Enqueued on torch's current stream.
+    """
+    import torch
+    return _call16("gemm_bf16", A, B, C, torch.float32 if out_dtype is None else out_dtype, D, torch.bfloat16)
+
+
+def gemm_fp16(A, B, C=None, out_dtype=None, D=None):
+    """As :func:`gemm_bf16` with float16 A and B."""
+    import torch
+    return _call16("gemm_fp16", A, B, C, torch.float32 if out_dtype is None else out_dtype, D, torch.float16)
+
+
+def gemm_mxfp8(A, SFA, B, SFB, C=None, out_dtype=None, D=None):
+    """Block-scaled fp8: A (M, K), B (N, K) e4m3 (float8_e4m3fn or uint8 codes);
+    SFA (M, K/32), SFB (N, K/32) e8m0 codes (uint8 or float8_e8m0fnu)."""
+    import torch
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    M, N, K, D, stream, out = _prep(A, B, C, D, out_dtype, (torch.float8_e4m3fn, torch.uint8))
+    for s, rows in ((SFA, M), (SFB, N)):
+        if s.dtype not in (torch.uint8, torch.float8_e8m0fnu) or not s.is_cuda or s.shape[0] != rows:
+            raise ValueError("scale arrays must be uint8/e8m0 device tensors of shape (rows, K/32)")
+    nkb = K // 32
+    st = _load().gemm_mxfp8(M, N, K, A.data_ptr(), _ld(A, K) if K else 0, SFA.data_ptr(), _ld(SFA, nkb) if K else 0,
+                            B.data_ptr(), _ld(B, K) if K else 0, SFB.data_ptr(), _ld(SFB, nkb) if K else 0,
+                            C.data_ptr() if C is not None else None, _ld(C, N) if C is not None else 0,
+                            D.data_ptr(), _ld(D, N), out, stream)
+    _check(st)
+    return D

@@ -257,3 +257,28 @@ def test_llm_projection_bf16_out():
     ok, ratio = check.freivalds_blocks(d32, a, b, None, block=64)
     say("  freivalds worst ratio %.3g" % ratio)
     assert ok
+
+
+# ---- every kernel configuration ------------------------------------------------------------
+
+N_DMA_CFGS = 8
+
+
+@pytest.mark.parametrize("cfg", list(range(N_DMA_CFGS)))
+def test_every_config(cfg, monkeypatch):
+    """Each direct-to-LDS configuration, forced through the tuning override:
+    bit-exact on integers over ragged shapes, within tolerance on random data."""
+    monkeypatch.setenv("TILEGEMM_F16_CONFIG", str(cfg))
+    for (M, N, K) in [(300, 520, 200), (777, 513, 1000), (64, 64, 64)]:
+        for integer in (True, False):
+            x, C = _case("bf16", M, N, K, seed=cfg * 31 + M, integer=integer)
+            say("cfg %d %dx%dx%d integer=%s" % (cfg, M, N, K, integer))
+            D = run16("bf16", dev16(x["A"], "bf16"), dev16(x["B"], "bf16"), torch.from_numpy(C).to(DEV))
+            torch.cuda.synchronize()
+            _full_check("bf16", x, to_f64(D), integer, C)
+    x, _ = _case("fp16", 513, 300, 4160, seed=cfg, integer=True, with_c=False)
+    D16 = run16("fp16", dev16(x["A"], "fp16"), dev16(x["B"], "fp16"), None, out="bf16")
+    D32 = run16("fp16", dev16(x["A"], "fp16"), dev16(x["B"], "fp16"), None, out="f32")
+    torch.cuda.synchronize()
+    _full_check("fp16", x, to_f64(D32), True)
+    assert np.array_equal(bf16_bits(D16), oracle.rne_bf16_f32(D32.cpu().numpy()))

@@ -39,6 +39,14 @@ __device__ __forceinline__ uint32_t span_bytes(int rows_left, int cols, int64_t 
     return b >= (int64_t)kOOB ? kOOB - 1 : (uint32_t)b;
 }
 
+// fp32 -> bf16, round to nearest even (finite inputs; NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
+    uint32_t u = __builtin_bit_cast(uint32_t, x);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
 // ---- LDS layout --------------------------------------------------------
 // A tile of R rows x BK 16-bit elements is stored row after row, each row
 // BK*2 bytes split into 16-byte chunks.  Logical chunk c of row r sits at

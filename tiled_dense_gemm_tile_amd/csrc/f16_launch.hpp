@@ -1,0 +1,80 @@
+// Kernel configurations of the 16-bit-input GEMM and their launchers.
+// Each (input type, output type) pair is instantiated in its own
+// translation unit (f16_<in>_<out>.hip) so they compile in parallel.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "gemm_f16.hpp"
+#include "gemm_f16_dma.hpp"
+
+namespace tg {
+
+// Direct-to-LDS configurations: id, BM, BN, BK, waves along M, waves along N,
+// LDS slots for A, LDS slots for B.
+#define TG_F16_DMA_CONFIGS(X)           \
+    X(0, 256, 256, 64, 2, 2, 2, 2)      \
+    X(1, 256, 256, 64, 2, 2, 3, 2)      \
+    X(2, 256, 256, 64, 2, 4, 2, 2)      \
+    X(3, 256, 256, 64, 2, 4, 3, 2)      \
+    X(4, 256, 128, 64, 2, 2, 3, 2)      \
+    X(5, 128, 128, 64, 2, 2, 2, 2)      \
+    X(6, 128, 128, 64, 2, 2, 3, 2)      \
+    X(7, 64, 64, 64, 2, 2, 2, 2)
+
+struct F16CfgInfo {
+    int bm, bn, bk, wm, wn, na, nb;
+};
+
+#define TG_F16_INFO(id, bm, bn, bk, wm, wn, na, nb) {bm, bn, bk, wm, wn, na, nb},
+constexpr F16CfgInfo kF16DmaCfgs[] = {TG_F16_DMA_CONFIGS(TG_F16_INFO)};
+#undef TG_F16_INFO
+constexpr int kNumF16DmaCfgs = sizeof(kF16DmaCfgs) / sizeof(kF16DmaCfgs[0]);
+
+// Register-staged fallback (any alignment): 128 x 128 x 64 tiles, 4 waves.
+using StagedCfg = TileCfg<128, 128, 64, 2, 2>;
+
+template <bool FP16, bool OUT_BF16>
+hipError_t launch_f16_dma(int cfg, unsigned grid, hipStream_t s, const F16Args &p, const F16Epi &e);
+
+template <bool FP16, bool OUT_BF16>
+hipError_t launch_f16_staged(int vec, unsigned grid, hipStream_t s, const F16Args &p);
+
+}  // namespace tg
+
+// Body of one instance translation unit: define TG_FP16 and TG_OUT_BF16,
+// then include this header with TG_F16_INSTANCE defined.
+#ifdef TG_F16_INSTANCE
+namespace tg {
+
+template <>
+hipError_t launch_f16_dma<TG_FP16, TG_OUT_BF16>(int cfg, unsigned grid, hipStream_t s, const F16Args &p,
+                                                const F16Epi &e) {
+    switch (cfg) {
+#define TG_F16_CASE(id, bm, bn, bk, wm, wn, na, nb)                                                            \
+    case id:                                                                                                   \
+        hipLaunchKernelGGL((gemm_f16_dma_kernel<DmaCfg<bm, bn, bk, wm, wn, na, nb>, TG_FP16, TG_OUT_BF16>), \
+                           dim3(grid), dim3(wm * wn * 64), 0, s, p, e);                                     \
+        break;
+        TG_F16_DMA_CONFIGS(TG_F16_CASE)
+#undef TG_F16_CASE
+    default:
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <>
+hipError_t launch_f16_staged<TG_FP16, TG_OUT_BF16>(int vec, unsigned grid, hipStream_t s, const F16Args &p) {
+    switch (vec) {
+    case 8: hipLaunchKernelGGL((gemm_f16_kernel<StagedCfg, 8, TG_FP16, TG_OUT_BF16>), dim3(grid), dim3(StagedCfg::NT), 0, s, p); break;
+    case 4: hipLaunchKernelGGL((gemm_f16_kernel<StagedCfg, 4, TG_FP16, TG_OUT_BF16>), dim3(grid), dim3(StagedCfg::NT), 0, s, p); break;
+    case 2: hipLaunchKernelGGL((gemm_f16_kernel<StagedCfg, 2, TG_FP16, TG_OUT_BF16>), dim3(grid), dim3(StagedCfg::NT), 0, s, p); break;
+    case 1: hipLaunchKernelGGL((gemm_f16_kernel<StagedCfg, 1, TG_FP16, TG_OUT_BF16>), dim3(grid), dim3(StagedCfg::NT), 0, s, p); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace tg
+#endif

@@ -72,14 +72,6 @@ template <> struct GVec<1> {
     }
 };
 
-// fp32 -> bf16, round to nearest even (finite inputs; NaN stays NaN).
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
-    uint32_t u = __builtin_bit_cast(uint32_t, x);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
-
 template <class Cfg, int VEC, bool FP16, bool OUT_BF16>
 __global__ void __launch_bounds__(Cfg::NT) gemm_f16_kernel(F16Args p) {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK;

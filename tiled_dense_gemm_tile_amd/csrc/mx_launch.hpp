@@ -1,0 +1,52 @@
+// Kernel configurations of the block-scaled fp8 GEMM and their launchers;
+// one instance translation unit per output type (mx_<out>.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "gemm_mxfp8.hpp"
+
+namespace tg {
+
+// id, BM, BN, waves along M, waves along N
+#define TG_MX_CONFIGS(X)     \
+    X(0, 256, 256, 2, 4)     \
+    X(1, 256, 256, 2, 2)     \
+    X(2, 128, 128, 2, 2)     \
+    X(3, 64, 64, 2, 2)
+
+struct MxCfgInfo {
+    int bm, bn, wm, wn;
+};
+
+#define TG_MX_INFO(id, bm, bn, wm, wn) {bm, bn, wm, wn},
+constexpr MxCfgInfo kMxCfgs[] = {TG_MX_CONFIGS(TG_MX_INFO)};
+#undef TG_MX_INFO
+constexpr int kNumMxCfgs = sizeof(kMxCfgs) / sizeof(kMxCfgs[0]);
+
+template <bool OUT_BF16>
+hipError_t launch_mx(int cfg, unsigned grid, hipStream_t s, const MxArgs &q, const F16Epi &e);
+
+}  // namespace tg
+
+#ifdef TG_MX_INSTANCE
+namespace tg {
+
+template <>
+hipError_t launch_mx<TG_OUT_BF16>(int cfg, unsigned grid, hipStream_t s, const MxArgs &q, const F16Epi &e) {
+    switch (cfg) {
+#define TG_MX_CASE(id, bm, bn, wm, wn)                                                                  \
+    case id:                                                                                            \
+        hipLaunchKernelGGL((gemm_mxfp8_kernel<MxCfg<bm, bn, wm, wn>, TG_OUT_BF16>), dim3(grid),         \
+                           dim3(wm * wn * 64), 0, s, q, e);                                              \
+        break;
+        TG_MX_CONFIGS(TG_MX_CASE)
+#undef TG_MX_CASE
+    default:
+        return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace tg
+#endif

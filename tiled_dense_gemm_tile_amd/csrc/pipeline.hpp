@@ -1,0 +1,136 @@
+// Pieces shared by the direct-to-LDS GEMM kernels: explicit waits, the
+// workgroup barrier, scheduling masks and the LDS-staged epilogue.
+#pragma once
+
+#include "common.hpp"
+
+namespace tg {
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt low bits [3:0], high bits [15:14]; expcnt and lgkmcnt left at max).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Workgroup barrier that also stops the compiler from moving memory
+// accesses across it (the waits before it are issued explicitly).
+__device__ __forceinline__ void barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Scheduling masks of __builtin_amdgcn_sched_group_barrier.
+constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100, kSchedVmemRead = 0x020;
+
+struct F16Epi {
+    bool vec_c, vec_d;   // C / D rows allow full-width vector access
+};
+
+// LDS bytes the staged epilogue needs: 32 rows of every wave's tile columns.
+constexpr int epilogue_lds_bytes(int nwaves, int wtn) { return nwaves * 32 * (wtn + 8) * 4; }
+
+// D = acc + C for one wave's WTM x WTN block of a tile whose 32x32 MFMA
+// accumulators are acc[i][j] (lane l, register r holds row
+// 8*(r/4) + 4*(l/32) + r%4 and column l%32 of block (i, j)).  Each pass
+// stages 32 rows in this wave's private LDS area (pitch WTN + 8 floats,
+// so the two half-waves write disjoint banks) and reads them back as
+// 16-byte row segments: C is read and D written with whole-vector accesses
+// where the row and alignment allow, element-wise at the right edge.
+// The caller guarantees every wave is done with the LDS it reuses.
+template <bool OUT_BF16, int TM, int TN, int WTM, int WTN>
+__device__ __forceinline__ void epilogue_lds(const f32x16 (&acc)[TM][TN], char *smem, int wave, int lane, int wm,
+                                             int wn, int m0, int n0, int M, int N, const void *C, int64_t ldc,
+                                             void *D, int64_t ldd, F16Epi e) {
+    constexpr int OS = OUT_BF16 ? 2 : 4;
+    constexpr int EP = WTN + 8;
+    const int fr = lane & 31, fh = lane >> 5;
+    float *ep = (float *)smem + wave * 32 * EP;
+    const __amdgpu_buffer_rsrc_t rD =
+        make_rsrc((char *)D + (int64_t)m0 * ldd * OS, span_bytes(M - m0, N, ldd, OS));
+    const bool hasC = C != nullptr;
+    const __amdgpu_buffer_rsrc_t rC =
+        make_rsrc(hasC ? (const char *)C + (int64_t)m0 * ldc * OS : (const char *)D,
+                  hasC ? span_bytes(M - m0, N, ldc, OS) : 0u);
+    constexpr int LPR = WTN / 4;                       // lanes per staged row (4 floats each)
+    constexpr int RPS = 64 / LPR;                      // rows per read instruction
+    const int erow = lane / LPR, ecol = (lane % LPR) * 4;
+    const int gcol = n0 + wn * WTN + ecol;             // first output column of this lane
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                ep[(8 * (r >> 2) + 4 * fh + (r & 3)) * EP + j * 32 + fr] = acc[i][j][r];
+        wait_lgkmcnt0();
+#pragma unroll
+        for (int q = 0; q < 32 / RPS; ++q) {
+            const int lr = q * RPS + erow;             // row inside the 32-row pass
+            const f32x4 v = *(const f32x4 *)(ep + lr * EP + ecol);
+            const int row = wm * WTM + i * 32 + lr;    // tile-relative row
+            const bool rin = m0 + row < M;
+            const bool full = rin && gcol + 4 <= N;
+            float o[4] = {v[0], v[1], v[2], v[3]};
+            if (hasC) {
+                if (full && e.vec_c) {
+                    const uint32_t coff = (uint32_t)(row * ldc + gcol) * OS;
+                    if constexpr (OUT_BF16) {
+                        const u32x2 cb = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rC, coff, 0, 0));
+                        o[0] += __builtin_bit_cast(float, cb[0] << 16);
+                        o[1] += __builtin_bit_cast(float, cb[0] & 0xffff0000u);
+                        o[2] += __builtin_bit_cast(float, cb[1] << 16);
+                        o[3] += __builtin_bit_cast(float, cb[1] & 0xffff0000u);
+                    } else {
+                        const f32x4 c4 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rC, coff, 0, 0));
+                        o[0] += c4[0];
+                        o[1] += c4[1];
+                        o[2] += c4[2];
+                        o[3] += c4[3];
+                    }
+                } else {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const uint32_t coff = (rin && gcol + u < N) ? (uint32_t)(row * ldc + gcol + u) * OS : kOOB;
+                        if constexpr (OUT_BF16)
+                            o[u] += __builtin_bit_cast(float, (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rC, coff, 0, 0) << 16);
+                        else
+                            o[u] += __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rC, coff, 0, 0));
+                    }
+                }
+            }
+            if (full && e.vec_d) {
+                const uint32_t doff = (uint32_t)(row * ldd + gcol) * OS;
+                if constexpr (OUT_BF16) {
+                    u32x2 pk;
+                    pk[0] = (uint32_t)f32_to_bf16_rne(o[0]) | ((uint32_t)f32_to_bf16_rne(o[1]) << 16);
+                    pk[1] = (uint32_t)f32_to_bf16_rne(o[2]) | ((uint32_t)f32_to_bf16_rne(o[3]) << 16);
+                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, pk), rD, doff, 0, 0);
+                } else {
+                    u32x4 pk;
+                    pk[0] = __builtin_bit_cast(uint32_t, o[0]);
+                    pk[1] = __builtin_bit_cast(uint32_t, o[1]);
+                    pk[2] = __builtin_bit_cast(uint32_t, o[2]);
+                    pk[3] = __builtin_bit_cast(uint32_t, o[3]);
+                    __builtin_amdgcn_raw_buffer_store_b128(pk, rD, doff, 0, 0);
+                }
+            } else {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const uint32_t doff = (rin && gcol + u < N) ? (uint32_t)(row * ldd + gcol + u) * OS : kOOB;
+                    if constexpr (OUT_BF16)
+                        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(o[u]), rD, doff, 0, 0);
+                    else
+                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o[u]), rD, doff, 0, 0);
+                }
+            }
+        }
+        wait_lgkmcnt0();   // reads of this pass done before the next pass overwrites the stage
+    }
+}
+
+}  // namespace tg

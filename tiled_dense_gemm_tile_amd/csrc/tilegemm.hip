@@ -6,7 +6,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "gemm_f16.hpp"
+#include <stdlib.h>
+
+#include "f16_launch.hpp"
+#include "mx_launch.hpp"
 
 namespace {
 
@@ -73,12 +76,38 @@ gemm_status launched(hipError_t e) {
 
 // ---- 16-bit inputs ------------------------------------------------------
 
-using CfgBig = tg::TileCfg<256, 256, 64, 2, 2>;
-using CfgMid = tg::TileCfg<128, 128, 64, 2, 2>;
-using CfgSmall = tg::TileCfg<64, 64, 64, 2, 2>;
+// Widest vector (in elements) that every row start and K boundary allows.
+int pick_vec(const Common &a) {
+    for (int v = 8; v > 1; v >>= 1) {
+        const uintptr_t bytes = (uintptr_t)v * 2;
+        if (((uintptr_t)a.A % bytes) == 0 && ((uintptr_t)a.B % bytes) == 0 && a.lda % v == 0 &&
+            a.ldb % v == 0 && a.K % v == 0)
+            return v;
+    }
+    return 1;
+}
 
-template <class Cfg, int VEC, bool FP16, bool OUT_BF16>
-gemm_status launch_f16(const Common &a, hipStream_t s) {
+int64_t tiles_of(const Common &a, int bm, int bn) { return ((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn); }
+
+// Tuning override: TILEGEMM_F16_CONFIG=<id> forces one direct-to-LDS
+// configuration (read at every call; ignored when out of range).
+int forced_f16_cfg() {
+    const char *e = getenv("TILEGEMM_F16_CONFIG");
+    if (!e || !*e) return -1;
+    const int id = atoi(e);
+    return (id >= 0 && id < tg::kNumF16DmaCfgs) ? id : -1;
+}
+
+int pick_f16_cfg(const Common &a) {
+    const int forced = forced_f16_cfg();
+    if (forced >= 0) return forced;
+    if (tiles_of(a, 256, 256) >= 240) return 3;
+    if (tiles_of(a, 128, 128) >= 240) return 6;
+    return 7;
+}
+
+template <bool FP16, bool OUT_BF16>
+gemm_status dispatch_f16(const Common &a, hipStream_t s) {
     tg::F16Args p;
     p.A = a.A;
     p.B = a.B;
@@ -91,42 +120,27 @@ gemm_status launch_f16(const Common &a, hipStream_t s) {
     p.M = (int)a.M;
     p.N = (int)a.N;
     p.K = (int)a.K;
-    p.tiles_m = (int)((a.M + Cfg::BM - 1) / Cfg::BM);
-    p.tiles_n = (int)((a.N + Cfg::BN - 1) / Cfg::BN);
     p.group_m = 4;
+    const int vec = pick_vec(a);
+    int bm = tg::StagedCfg::BM, bn = tg::StagedCfg::BN, cfg = -1;
+    if (vec == 8) {
+        cfg = pick_f16_cfg(a);
+        bm = tg::kF16DmaCfgs[cfg].bm;
+        bn = tg::kF16DmaCfgs[cfg].bn;
+    }
+    p.tiles_m = (int)((a.M + bm - 1) / bm);
+    p.tiles_n = (int)((a.N + bn - 1) / bn);
     const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
     if (tiles >= kMaxDim) return GEMM_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL((tg::gemm_f16_kernel<Cfg, VEC, FP16, OUT_BF16>), dim3((unsigned)tiles), dim3(Cfg::NT),
-                       0, s, p);
-    return launched(hipGetLastError());
-}
-
-// Widest vector (in elements) that every row start and K boundary allows.
-int pick_vec(const Common &a) {
-    for (int v = 8; v > 1; v >>= 1) {
-        const uintptr_t bytes = (uintptr_t)v * 2;
-        if (((uintptr_t)a.A % bytes) == 0 && ((uintptr_t)a.B % bytes) == 0 && a.lda % v == 0 &&
-            a.ldb % v == 0 && a.K % v == 0)
-            return v;
+    if (cfg >= 0) {
+        const int os = OUT_BF16 ? 2 : 4;
+        const uintptr_t vb = (uintptr_t)os * 4;
+        tg::F16Epi e;
+        e.vec_d = ((uintptr_t)a.D % vb) == 0 && a.ldd % 4 == 0;
+        e.vec_c = a.C && ((uintptr_t)a.C % vb) == 0 && a.ldc % 4 == 0;
+        return launched(tg::launch_f16_dma<FP16, OUT_BF16>(cfg, (unsigned)tiles, s, p, e));
     }
-    return 1;
-}
-
-template <bool FP16, bool OUT_BF16>
-gemm_status dispatch_f16(const Common &a, hipStream_t s) {
-    const int vec = pick_vec(a);
-    const int64_t big_tiles = ((a.M + 255) / 256) * ((a.N + 255) / 256);
-    const int64_t mid_tiles = ((a.M + 127) / 128) * ((a.N + 127) / 128);
-    if (vec == 8) {
-        if (big_tiles >= 256) return launch_f16<CfgBig, 8, FP16, OUT_BF16>(a, s);
-        if (mid_tiles >= 256) return launch_f16<CfgMid, 8, FP16, OUT_BF16>(a, s);
-        return launch_f16<CfgSmall, 8, FP16, OUT_BF16>(a, s);
-    }
-    switch (vec) {
-    case 4: return launch_f16<CfgMid, 4, FP16, OUT_BF16>(a, s);
-    case 2: return launch_f16<CfgMid, 2, FP16, OUT_BF16>(a, s);
-    default: return launch_f16<CfgMid, 1, FP16, OUT_BF16>(a, s);
-    }
+    return launched(tg::launch_f16_staged<FP16, OUT_BF16>(vec, (unsigned)tiles, s, p));
 }
 
 gemm_status run_f16(bool fp16, const Common &a, hipStream_t s) {
@@ -136,6 +150,56 @@ gemm_status run_f16(bool fp16, const Common &a, hipStream_t s) {
     if (fp16)
         return a.out_type == GEMM_OUT_BF16 ? dispatch_f16<true, true>(a, s) : dispatch_f16<true, false>(a, s);
     return a.out_type == GEMM_OUT_BF16 ? dispatch_f16<false, true>(a, s) : dispatch_f16<false, false>(a, s);
+}
+
+// ---- block-scaled fp8 ------------------------------------------------------
+
+int forced_mx_cfg() {
+    const char *e = getenv("TILEGEMM_MX_CONFIG");
+    if (!e || !*e) return -1;
+    const int id = atoi(e);
+    return (id >= 0 && id < tg::kNumMxCfgs) ? id : -1;
+}
+
+gemm_status dispatch_mx(const Common &a, const void *SFA, int64_t ldsfa, const void *SFB, int64_t ldsfb,
+                        hipStream_t s) {
+    // The kernel streams 16-byte A/B chunks and 4-byte scale words per K tile of 128.
+    const bool fast = a.K % 128 == 0 && (uintptr_t)a.A % 16 == 0 && (uintptr_t)a.B % 16 == 0 && a.lda % 16 == 0 &&
+                      a.ldb % 16 == 0 && (uintptr_t)SFA % 4 == 0 && (uintptr_t)SFB % 4 == 0 && ldsfa % 4 == 0 &&
+                      ldsfb % 4 == 0;
+    if (!fast && a.K > 0) return GEMM_ERR_UNSUPPORTED;
+    int cfg = forced_mx_cfg();
+    if (cfg < 0) cfg = tiles_of(a, 256, 256) >= 240 ? 1 : (tiles_of(a, 128, 128) >= 240 ? 2 : 3);
+    tg::MxArgs q;
+    q.g.A = a.A;
+    q.g.B = a.B;
+    q.g.C = a.C;
+    q.g.D = a.D;
+    q.g.lda = a.lda;
+    q.g.ldb = a.ldb;
+    q.g.ldc = a.ldc;
+    q.g.ldd = a.ldd;
+    q.g.M = (int)a.M;
+    q.g.N = (int)a.N;
+    q.g.K = (int)a.K;
+    q.g.group_m = 4;
+    q.g.tiles_m = (int)((a.M + tg::kMxCfgs[cfg].bm - 1) / tg::kMxCfgs[cfg].bm);
+    q.g.tiles_n = (int)((a.N + tg::kMxCfgs[cfg].bn - 1) / tg::kMxCfgs[cfg].bn);
+    // K == 0 reads no scales: any valid address stands in for NULL ones
+    q.SFA = SFA ? SFA : a.D;
+    q.SFB = SFB ? SFB : a.D;
+    q.ldsfa = ldsfa;
+    q.ldsfb = ldsfb;
+    const int64_t tiles = (int64_t)q.g.tiles_m * q.g.tiles_n;
+    if (tiles >= kMaxDim) return GEMM_ERR_UNSUPPORTED;
+    const bool bf16 = a.out_type == GEMM_OUT_BF16;
+    const int os = bf16 ? 2 : 4;
+    const uintptr_t vb = (uintptr_t)os * 4;
+    tg::F16Epi e;
+    e.vec_d = ((uintptr_t)a.D % vb) == 0 && a.ldd % 4 == 0;
+    e.vec_c = a.C && ((uintptr_t)a.C % vb) == 0 && a.ldc % 4 == 0;
+    return launched(bf16 ? tg::launch_mx<true>(cfg, (unsigned)tiles, s, q, e)
+                         : tg::launch_mx<false>(cfg, (unsigned)tiles, s, q, e));
 }
 
 }  // namespace
@@ -167,8 +231,7 @@ gemm_status gemm_mxfp8(int64_t M, int64_t N, int64_t K, const void *A, int64_t l
     }
     if (K % 32 != 0) return GEMM_ERR_UNSUPPORTED;
     if (ldsfa >= kMaxLdBytes || ldsfb >= kMaxLdBytes) return GEMM_ERR_UNSUPPORTED;
-    (void)stream;
-    return GEMM_ERR_UNSUPPORTED;
+    return dispatch_mx(a, SFA, ldsfa, SFB, ldsfb, stream);
 }
 
 const char *gemm_status_string(int s) {

@@ -38,6 +38,20 @@ def algorithmic_bytes(w):
     return b
 
 
+def measured_traffic(w):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary, or None when there is none or the kernels changed since."""
+    from rocprof_summary import PROFILES, kernel_source_hash
+    path = os.path.join(PROFILES, "%s_traffic.json" % w.name)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        doc = json.load(f)
+    if doc.get("kernel_sources") != kernel_source_hash():
+        return None
+    return int(round(doc["traffic_bytes_per_launch"]))
+
+
 def device_inputs(w, x, torch):
     dev = torch.device("cuda:0")
     if w.in_type == "e4m3":
@@ -77,7 +91,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="square4096_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=768)
+    ap.add_argument("--cpu-rows", type=int, default=0,
+                    help="rows of D the CPU baseline evaluates (default: about 1.3e10 multiply-adds)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -149,12 +164,13 @@ def main():
                    "C": "fp32 U[-1,1]" if w.dist_c else "none", "layout": "A row-major, B column-major (N x K)",
                    "seed": w.seed, "note": w.note},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
-                     "frac": round(tflops / peak, 4), "traffic": None,
+                     "frac": round(tflops / peak, 4), "traffic": measured_traffic(w),
                      "kernel_ms": round(kernel_ms, 5),
                      "algorithmic_bytes": algorithmic_bytes(w)},
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, x, args.cpu_rows)
+        rows = args.cpu_rows or max(1, int(1.3e10 // (w.N * w.K)))
+        res["cpu_baseline"] = cpu_baseline(w, x, rows)
     print(json.dumps(res), flush=True)
 
 

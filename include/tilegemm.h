@@ -110,9 +110,12 @@ gemm_status gemm_fp16(int64_t M, int64_t N, int64_t K,
  *   A: OCP e4m3 (fn) bytes, M x K row-major       SFA: e8m0 bytes, M x K/32, ldsfa
  *   B: e4m3 bytes, N x K (column-major K x N)     SFB: e8m0 bytes, N x K/32, ldsfb
  *   C, D, out_type: as gemm_bf16
- * K must be a multiple of 32 (else GEMM_ERR_UNSUPPORTED); ldsfa, ldsfb >=
- * K/32 (else GEMM_ERR_BAD_LD); SFA and SFB non-NULL when M*N*K > 0.  Scale
- * code 0xFF (NaN) and e4m3 NaN inputs give NaN in the affected outputs.
+ * ldsfa, ldsfb >= K/32 (else GEMM_ERR_BAD_LD); SFA and SFB non-NULL when
+ * M*N*K > 0 (else GEMM_ERR_NULL_POINTER).  K must be a multiple of 32; this
+ * version also needs K % 128 == 0, A, B and lda, ldb 16-byte aligned and
+ * SFA, SFB and ldsfa, ldsfb 4-byte aligned, and returns
+ * GEMM_ERR_UNSUPPORTED otherwise.  Scale code 0xFF (NaN) and e4m3 NaN
+ * inputs give NaN in the affected outputs.
  */
 gemm_status gemm_mxfp8(int64_t M, int64_t N, int64_t K,
                        const void *A, int64_t lda, const void *SFA, int64_t ldsfa,

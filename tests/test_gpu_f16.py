@@ -282,3 +282,52 @@ def test_every_config(cfg, monkeypatch):
     torch.cuda.synchronize()
     _full_check("fp16", x, to_f64(D32), True)
     assert np.array_equal(bf16_bits(D16), oracle.rne_bf16_f32(D32.cpu().numpy()))
+
+
+@pytest.mark.parametrize("cfg", [3, 6, 7])
+@pytest.mark.parametrize("pad", [2, 4])
+def test_lane4_configs(cfg, pad, monkeypatch):
+    """Rows only 4- or 8-byte aligned (leading dimension K + pad) take the
+    4-byte-lane direct-to-LDS kernels; every such configuration, forced."""
+    monkeypatch.setenv("TILEGEMM_F16_CONFIG", str(cfg))
+    for in_type in ("bf16", "fp16"):
+        for integer in (True, False):
+            M, N, K = 520, 300, 4100
+            x, C = _case(in_type, M, N, K, seed=cfg + pad, integer=integer)
+            lda = K + pad
+            Ab = np.zeros((M, lda), np.uint16); Ab[:, :K] = x["A"]
+            Bb = np.zeros((N, lda), np.uint16); Bb[:, :K] = x["B"]
+            say("lane4 cfg %d pad %d %s integer=%s" % (cfg, pad, in_type, integer))
+            D = run16(in_type, dev16(Ab, in_type)[:, :K], dev16(Bb, in_type)[:, :K], torch.from_numpy(C).to(DEV))
+            torch.cuda.synchronize()
+            _full_check(in_type, x, to_f64(D), integer, C)
+
+
+@pytest.mark.parametrize("cfg", [1, 3, 6])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_c_streamed_in_k_loop(cfg, out, monkeypatch):
+    """K long enough (>= 34 tiles of 64) that C is added during the K loop
+    instead of in the epilogue: ragged M/N, both output types, and C == D."""
+    monkeypatch.setenv("TILEGEMM_F16_CONFIG", str(cfg))
+    M, N, K = 300, 520, 2304
+    for integer in (True, False):
+        x, C = _case("bf16", M, N, K, seed=cfg * 7 + (out == "bf16"), integer=integer)
+        A, B = dev16(x["A"], "bf16"), dev16(x["B"], "bf16")
+        if out == "bf16":
+            Cb = torch.from_numpy(C).to(DEV).to(torch.bfloat16)
+            Cref = Cb.float().cpu().numpy()
+            say("c-loop cfg %d bf16 out integer=%s" % (cfg, integer))
+            D16 = run16("bf16", A, B, Cb, out="bf16")
+            D32 = run16("bf16", A, B, torch.from_numpy(Cref).to(DEV), out="f32")
+            torch.cuda.synchronize()
+            _full_check("bf16", x, to_f64(D32), integer, Cref)
+            assert np.array_equal(bf16_bits(D16), oracle.rne_bf16_f32(D32.cpu().numpy()))
+        else:
+            Cd = torch.from_numpy(C).to(DEV)
+            say("c-loop cfg %d f32 out integer=%s" % (cfg, integer))
+            D = run16("bf16", A, B, Cd)
+            inplace = Cd.clone()
+            run16("bf16", A, B, inplace, D=inplace)
+            torch.cuda.synchronize()
+            _full_check("bf16", x, to_f64(D), integer, C)
+            assert torch.equal(D, inplace)

@@ -22,6 +22,10 @@ namespace tg {
     X(6, 128, 128, 64, 2, 2, 3, 2)      \
     X(7, 64, 64, 64, 2, 2, 2, 2)
 
+// Configurations also built with 4-byte global->LDS lanes (for rows that are
+// only 4-byte aligned).
+constexpr bool f16_has_lane4(int id) { return id == 3 || id == 6 || id == 7; }
+
 struct F16CfgInfo {
     int bm, bn, bk, wm, wn, na, nb;
 };
@@ -34,8 +38,10 @@ constexpr int kNumF16DmaCfgs = sizeof(kF16DmaCfgs) / sizeof(kF16DmaCfgs[0]);
 // Register-staged fallback (any alignment): 128 x 128 x 64 tiles, 4 waves.
 using StagedCfg = TileCfg<128, 128, 64, 2, 2>;
 
+// lane_bytes: 16 or 4 (4 only for ids with f16_has_lane4).
 template <bool FP16, bool OUT_BF16>
-hipError_t launch_f16_dma(int cfg, unsigned grid, hipStream_t s, const F16Args &p, const F16Epi &e);
+hipError_t launch_f16_dma(int cfg, int lane_bytes, unsigned grid, hipStream_t s, const F16Args &p,
+                          const F16Epi &e);
 
 template <bool FP16, bool OUT_BF16>
 hipError_t launch_f16_staged(int vec, unsigned grid, hipStream_t s, const F16Args &p);
@@ -48,13 +54,23 @@ hipError_t launch_f16_staged(int vec, unsigned grid, hipStream_t s, const F16Arg
 namespace tg {
 
 template <>
-hipError_t launch_f16_dma<TG_FP16, TG_OUT_BF16>(int cfg, unsigned grid, hipStream_t s, const F16Args &p,
-                                                const F16Epi &e) {
+hipError_t launch_f16_dma<TG_FP16, TG_OUT_BF16>(int cfg, int lane_bytes, unsigned grid, hipStream_t s,
+                                                const F16Args &p, const F16Epi &e) {
     switch (cfg) {
-#define TG_F16_CASE(id, bm, bn, bk, wm, wn, na, nb)                                                            \
-    case id:                                                                                                   \
-        hipLaunchKernelGGL((gemm_f16_dma_kernel<DmaCfg<bm, bn, bk, wm, wn, na, nb>, TG_FP16, TG_OUT_BF16>), \
-                           dim3(grid), dim3(wm * wn * 64), 0, s, p, e);                                     \
+#define TG_F16_CASE(id, bm, bn, bk, wm, wn, na, nb)                                                        \
+    case id:                                                                                               \
+        if (lane_bytes == 16) {                                                                            \
+            hipLaunchKernelGGL(                                                                            \
+                (gemm_f16_dma_kernel<DmaCfg<bm, bn, bk, wm, wn, na, nb>, TG_FP16, TG_OUT_BF16, 16>),       \
+                dim3(grid), dim3(wm * wn * 64), 0, s, p, e);                                               \
+        } else {                                                                                           \
+            if constexpr (f16_has_lane4(id))                                                               \
+                hipLaunchKernelGGL(                                                                        \
+                    (gemm_f16_dma_kernel<DmaCfg<bm, bn, bk, wm, wn, na, nb>, TG_FP16, TG_OUT_BF16, 4>),    \
+                    dim3(grid), dim3(wm * wn * 64), 0, s, p, e);                                           \
+            else                                                                                           \
+                return hipErrorInvalidValue;                                                               \
+        }                                                                                                  \
         break;
         TG_F16_DMA_CONFIGS(TG_F16_CASE)
 #undef TG_F16_CASE

@@ -26,13 +26,40 @@
 
 namespace tg {
 
+// acc[i][j][r0 .. r0 + QR) += cq for part q = Q of a TM x TN block grid
+// (16 / QR parts per block), selected at run time among the static indices.
+template <int TN, int QR, int Q, int NQ, class Acc>
+__device__ __forceinline__ void add_part(Acc &acc, const float *cq, int q) {
+    if constexpr (Q < NQ) {
+        if (q == Q) {
+            constexpr int blk = Q / (16 / QR), r0 = (Q % (16 / QR)) * QR;
+#pragma unroll
+            for (int u = 0; u < QR; ++u) acc[blk / TN][blk % TN][r0 + u] += cq[u];
+            return;
+        }
+        add_part<TN, QR, Q + 1, NQ>(acc, cq, q);
+    }
+}
+
+// One direct global->LDS load: each lane moves LB bytes from `off` in the
+// resource to LDS at lds + lane * LB.
+template <int LB>
+__device__ __forceinline__ void dma_load(__amdgpu_buffer_rsrc_t r, char *lds, uint32_t off) {
+    if constexpr (LB == 16)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, off, 0, 0, 0);
+    else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 4, off, 0, 0, 0);
+}
+
 template <int BM_, int BN_, int BK_, int WM_, int WN_, int NA_, int NB_>
 struct DmaCfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, NA = NA_, NB = NB_;
     static constexpr int NT = WM * WN * 64;
 };
 
-template <class Cfg, bool FP16, bool OUT_BF16>
+// LB: bytes each lane moves per global->LDS instruction: 16 (rows 16-byte
+// aligned) or 4 (rows only 4-byte aligned; K even).
+template <class Cfg, bool FP16, bool OUT_BF16, int LB>
 __global__ void __launch_bounds__(Cfg::NT) gemm_f16_dma_kernel(F16Args p, F16Epi e) {
     constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, NA = Cfg::NA, NB = Cfg::NB;
     constexpr int WM = Cfg::WM, WN = Cfg::WN, NW = WM * WN;
@@ -41,9 +68,10 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_f16_dma_kernel(F16Args p, F16Epi
     constexpr int KK = BK / 16;                        // MFMA K steps per tile
     constexpr int ROWB = BK * 2, CPR = ROWB / 16;
     constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB;
-    constexpr int RPI = 1024 / ROWB;                   // rows one load instruction fills
-    constexpr int A_INST = A_BYTES / 1024 / NW;        // load instructions per wave per tile
-    constexpr int B_INST = B_BYTES / 1024 / NW;
+    constexpr int IB = 64 * LB;                        // LDS bytes one load instruction fills
+    constexpr int RPI = IB / ROWB;                     // rows one load instruction fills
+    constexpr int A_INST = A_BYTES / IB / NW;          // load instructions per wave per tile
+    constexpr int B_INST = B_BYTES / IB / NW;
     constexpr int LPW = A_INST + B_INST;
     constexpr int SA = NA - 1, SB = NB - 1;            // prefetch distances
     constexpr int WAIT_N = (SA - SB) * A_INST;         // loads still in flight at a tile barrier
@@ -51,7 +79,8 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_f16_dma_kernel(F16Args p, F16Epi
     constexpr int RING_BYTES = NA * A_BYTES + NB * B_BYTES;
     constexpr int EPI_BYTES = epilogue_lds_bytes(NW, WTN);
     constexpr int LDS_BYTES = RING_BYTES > EPI_BYTES ? RING_BYTES : EPI_BYTES;
-    static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "load tiling");
+    static_assert(LB == 16 || LB == 4, "lane bytes");
+    static_assert(A_BYTES % (IB * NW) == 0 && B_BYTES % (IB * NW) == 0 && RPI >= 1, "load tiling");
     static_assert(SB == 1 && (SA == 1 || SA == 2), "ring depths");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS capacity");
     static_assert(KK % 2 == 0, "fragment double buffer parity");
@@ -70,36 +99,50 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_f16_dma_kernel(F16Args p, F16Epi
     const __amdgpu_buffer_rsrc_t rB =
         make_rsrc((const char *)p.B + (int64_t)n0 * p.ldb * 2, span_bytes(N - n0, K, p.ldb, 2));
 
-    // Per-lane global offsets (without the K offset) and the first K element
-    // of each lane's chunk, for every load instruction of this wave.
-    uint32_t a_goff[A_INST], b_goff[B_INST];
-    int a_kel[A_INST], b_kel[B_INST];
-    {
-        const int lrow = lane / CPR, lchunk = lane % CPR;
+    // Lane L of a load instruction fills LDS bytes [L*LB, L*LB + LB) of the
+    // instruction's IB bytes: row L*LB / ROWB, physical chunk p, byte q of
+    // the chunk; it fetches the same bytes of logical chunk p ^ swz(row).
+    // Global offsets exclude the K offset; kel is the first K element.
+    const int lrow = (lane * LB) / ROWB, lp = ((lane * LB) % ROWB) / 16, lq = (lane * LB) % 16;
+    auto chunk_of = [&](int j) {
+        const int row = (j * NW + wave) * RPI + lrow;
+        return lp ^ swz<CPR>(row);
+    };
+    constexpr int NOFF = LB == 16 ? (A_INST > B_INST ? A_INST : B_INST) : 1;
+    uint32_t a_goff[NOFF], b_goff[NOFF];
+    int kel[NOFF];
+    if constexpr (LB == 16) {
 #pragma unroll
-        for (int j = 0; j < A_INST; ++j) {
+        for (int j = 0; j < NOFF; ++j) {
             const int row = (j * NW + wave) * RPI + lrow;
-            const int c = lchunk ^ swz<CPR>(row);
+            const int c = chunk_of(j);
             a_goff[j] = (uint32_t)(row * p.lda * 2) + c * 16;
-            a_kel[j] = c * 8;
-        }
-#pragma unroll
-        for (int j = 0; j < B_INST; ++j) {
-            const int row = (j * NW + wave) * RPI + lrow;
-            const int c = lchunk ^ swz<CPR>(row);
             b_goff[j] = (uint32_t)(row * p.ldb * 2) + c * 16;
-            b_kel[j] = c * 8;
+            kel[j] = c * 8;
         }
+    } else {
+        a_goff[0] = (uint32_t)((wave * RPI + lrow) * p.lda * 2) + lq;
+        b_goff[0] = (uint32_t)((wave * RPI + lrow) * p.ldb * 2) + lq;
     }
+    // offset of instruction j (K element k0 onward) or kOOB past K
+    auto goff = [&](const uint32_t *base, int64_t ld, int j, int k0) -> uint32_t {
+        if constexpr (LB == 16) {
+            return (k0 + kel[j] < K) ? base[j] + (uint32_t)k0 * 2 : kOOB;
+        } else {
+            const int c = chunk_of(j);
+            const int k = k0 + c * 8 + lq / 2;
+            const uint32_t o = base[0] + (uint32_t)(j * NW * RPI * ld * 2) + c * 16 + (uint32_t)k0 * 2;
+            return k < K ? o : kOOB;
+        }
+    };
 
     auto fetchA = [&](int t) {
         const int k0 = t * BK;
         char *sA = smem + (t % NA) * A_BYTES;
 #pragma unroll
         for (int j = 0; j < A_INST; ++j) {
-            const uint32_t off = (k0 + a_kel[j] < K) ? a_goff[j] + (uint32_t)k0 * 2 : kOOB;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rA, (__attribute__((address_space(3))) void *)(sA + (j * NW + wave) * 1024), 16, off, 0, 0, 0);
+            const uint32_t off = goff(a_goff, p.lda, j, k0);
+            dma_load<LB>(rA, sA + (j * NW + wave) * IB, off);
         }
     };
     auto fetchB = [&](int t) {
@@ -107,9 +150,8 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_f16_dma_kernel(F16Args p, F16Epi
         char *sB = smem + B_BASE + (t % NB) * B_BYTES;
 #pragma unroll
         for (int j = 0; j < B_INST; ++j) {
-            const uint32_t off = (k0 + b_kel[j] < K) ? b_goff[j] + (uint32_t)k0 * 2 : kOOB;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rB, (__attribute__((address_space(3))) void *)(sB + (j * NW + wave) * 1024), 16, off, 0, 0, 0);
+            const uint32_t off = goff(b_goff, p.ldb, j, k0);
+            dma_load<LB>(rB, sB + (j * NW + wave) * IB, off);
         }
     };
 
@@ -181,12 +223,48 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_f16_dma_kernel(F16Args p, F16Epi
         }
     };
 
+    // C is streamed into the accumulators during the K loop so the epilogue
+    // only writes D: C "part" q (QR accumulator registers of one 32x32 block
+    // per lane) is loaded at the transition into tile q + 1, ahead of that
+    // transition's B fetch, so the next barrier's wait covers it, and added
+    // right after that wait.  With fewer than NQ + 2 tiles the epilogue adds C.
+    constexpr int QR = (TM * TN * 16 / 32) > 4 ? (TM * TN * 16 / 32) : 4;
+    constexpr int NQ = TM * TN * 16 / QR;
+    constexpr int OS = OUT_BF16 ? 2 : 4;
+    const int nk = (K + BK - 1) / BK;
+    const bool hasC = p.C != nullptr;
+    const bool c_loop = hasC && nk >= NQ + 2;
+    const __amdgpu_buffer_rsrc_t rC =
+        make_rsrc(hasC ? (const char *)p.C + (int64_t)m0 * p.ldc * OS : (const char *)p.D,
+                  hasC ? span_bytes(M - m0, N, p.ldc, OS) : 0u);
+    float cq[QR];
+    auto load_c_part = [&](int q) {                    // inactive parts read nothing (zeros)
+        const bool act = c_loop && q < NQ;
+        const int qq = act ? q : 0;
+        const int blk = qq / (16 / QR), r0 = (qq % (16 / QR)) * QR;
+        const int i = blk / TN, j = blk % TN;
+        const int col = n0 + wn * WTN + j * 32 + fr;
+#pragma unroll
+        for (int u = 0; u < QR; ++u) {
+            const int r = r0 + u;
+            const int row = wm * WTM + i * 32 + 8 * (r >> 2) + 4 * fh + (r & 3);
+            const uint32_t off = (act && col < N) ? (uint32_t)(row * p.ldc + col) * OS : kOOB;
+            if constexpr (OUT_BF16)
+                cq[u] = __builtin_bit_cast(float, (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rC, off, 0, 0) << 16);
+            else
+                cq[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rC, off, 0, 0));
+        }
+    };
+    auto add_c_part = [&](int q) {
+        if (c_loop && q >= 0 && q < NQ) add_part<TN, QR, 0, NQ>(acc, cq, q);
+    };
+
     // The rings always fetch once per tile; fetches of tiles past the end
     // read nothing (every chunk is out of range), write zeros into a slot no
     // later tile uses, and keep the loads in flight at every tile barrier at
-    // exactly WAIT_N: the B fetch of the next tile is the newest one that
-    // must have landed, and only the A fetch issued after it may still run.
-    const int nk = (K + BK - 1) / BK;
+    // exactly WAIT_N: the B fetch of the next tile (with the C part before
+    // it) is the newest load that must have landed, and only the A fetch
+    // issued after it may still run.
     if (nk > 0) {
         fetchB(0);
         fetchA(0);
@@ -201,7 +279,9 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_f16_dma_kernel(F16Args p, F16Epi
             tile_steps(t);
             wait_vmcnt<WAIT_N>();
             wait_lgkmcnt0();
+            add_c_part(t - 1);
             barrier();
+            load_c_part(t);
             fetchB(t + 1 + SB);
             fetchA(t + 1 + SA);
             load_frags(0, t + 1, 0);
@@ -216,7 +296,8 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_f16_dma_kernel(F16Args p, F16Epi
     wait_vmcnt<0>();                                   // no fetch still writing a slot
     wait_lgkmcnt0();
     barrier();                                         // every wave is done with the tile slots
-    epilogue_lds<OUT_BF16, TM, TN, WTM, WTN>(acc, smem, wave, lane, wm, wn, m0, n0, M, N, p.C, p.ldc, p.D, p.ldd, e);
+    epilogue_lds<OUT_BF16, TM, TN, WTM, WTN>(acc, smem, wave, lane, wm, wn, m0, n0, M, N, c_loop ? nullptr : p.C,
+                                             p.ldc, p.D, p.ldd, e);
 }
 
 }  // namespace tg

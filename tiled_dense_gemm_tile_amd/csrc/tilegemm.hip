@@ -98,9 +98,10 @@ int forced_f16_cfg() {
     return (id >= 0 && id < tg::kNumF16DmaCfgs) ? id : -1;
 }
 
-int pick_f16_cfg(const Common &a) {
+// lane_bytes 4 is only built for the configurations f16_has_lane4 names.
+int pick_f16_cfg(const Common &a, int lane_bytes) {
     const int forced = forced_f16_cfg();
-    if (forced >= 0) return forced;
+    if (forced >= 0 && (lane_bytes == 16 || tg::f16_has_lane4(forced))) return forced;
     if (tiles_of(a, 256, 256) >= 240) return 3;
     if (tiles_of(a, 128, 128) >= 240) return 6;
     return 7;
@@ -121,10 +122,13 @@ gemm_status dispatch_f16(const Common &a, hipStream_t s) {
     p.N = (int)a.N;
     p.K = (int)a.K;
     p.group_m = 4;
+    // 16-byte rows: 16-byte direct-to-LDS lanes; 4- or 8-byte rows: 4-byte
+    // lanes; 2-byte rows (odd K or leading dimension): register staging.
     const int vec = pick_vec(a);
+    const int lane_bytes = vec == 8 ? 16 : 4;
     int bm = tg::StagedCfg::BM, bn = tg::StagedCfg::BN, cfg = -1;
-    if (vec == 8) {
-        cfg = pick_f16_cfg(a);
+    if (vec >= 2) {
+        cfg = pick_f16_cfg(a, lane_bytes);
         bm = tg::kF16DmaCfgs[cfg].bm;
         bn = tg::kF16DmaCfgs[cfg].bn;
     }
@@ -138,7 +142,7 @@ gemm_status dispatch_f16(const Common &a, hipStream_t s) {
         tg::F16Epi e;
         e.vec_d = ((uintptr_t)a.D % vb) == 0 && a.ldd % 4 == 0;
         e.vec_c = a.C && ((uintptr_t)a.C % vb) == 0 && a.ldc % 4 == 0;
-        return launched(tg::launch_f16_dma<FP16, OUT_BF16>(cfg, (unsigned)tiles, s, p, e));
+        return launched(tg::launch_f16_dma<FP16, OUT_BF16>(cfg, lane_bytes, (unsigned)tiles, s, p, e));
     }
     return launched(tg::launch_f16_staged<FP16, OUT_BF16>(vec, (unsigned)tiles, s, p));
 }

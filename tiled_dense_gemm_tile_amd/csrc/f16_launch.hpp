@@ -7,6 +7,8 @@
 
 #include "gemm_f16.hpp"
 #include "gemm_f16_dma.hpp"
+#include "gemm_f16_pp.hpp"
+#include "gemm_f16_w4.hpp"
 
 namespace tg {
 
@@ -31,9 +33,22 @@ struct F16CfgInfo {
 };
 
 #define TG_F16_INFO(id, bm, bn, bk, wm, wn, na, nb) {bm, bn, bk, wm, wn, na, nb},
-constexpr F16CfgInfo kF16DmaCfgs[] = {TG_F16_DMA_CONFIGS(TG_F16_INFO)};
+// Then the ping-pong kernels (256 x 256 x 64, 8 waves in two alternating
+// groups) with 32x32 and 16x16 MFMA blocks, and the four-wave kernels
+// (256 x 256, 128 x 128 per wave) with 32-wide K slabs in rings of 5 or 4
+// and with 64-wide K tiles in rings of 2 (A) and 2 or 3 (B); all of these
+// take 16-byte lanes only.
+constexpr F16CfgInfo kF16DmaCfgs[] = {TG_F16_DMA_CONFIGS(TG_F16_INFO){256, 256, 64, 2, 4, 0, 0},
+                                      {256, 256, 64, 2, 4, 0, 0},
+                                      {256, 256, 32, 2, 2, 5, 5},
+                                      {256, 256, 32, 2, 2, 4, 4},
+                                      {256, 256, 64, 2, 2, 2, 2},
+                                      {256, 256, 64, 2, 2, 2, 3}};
 #undef TG_F16_INFO
 constexpr int kNumF16DmaCfgs = sizeof(kF16DmaCfgs) / sizeof(kF16DmaCfgs[0]);
+constexpr int kF16PingPong32 = kNumF16DmaCfgs - 6, kF16PingPong16 = kNumF16DmaCfgs - 5;
+constexpr int kF16FourWave5 = kNumF16DmaCfgs - 4, kF16FourWave4 = kNumF16DmaCfgs - 3;
+constexpr int kF16FourWaveT22 = kNumF16DmaCfgs - 2, kF16FourWaveT23 = kNumF16DmaCfgs - 1;
 
 // Register-staged fallback (any alignment): 128 x 128 x 64 tiles, 4 waves.
 using StagedCfg = TileCfg<128, 128, 64, 2, 2>;
@@ -56,6 +71,30 @@ namespace tg {
 template <>
 hipError_t launch_f16_dma<TG_FP16, TG_OUT_BF16>(int cfg, int lane_bytes, unsigned grid, hipStream_t s,
                                                 const F16Args &p, const F16Epi &e) {
+    if (cfg == kF16PingPong32 || cfg == kF16PingPong16) {
+        if (lane_bytes != 16) return hipErrorInvalidValue;
+        if (cfg == kF16PingPong32)
+            hipLaunchKernelGGL((gemm_f16_pp_kernel<32, TG_FP16, TG_OUT_BF16>), dim3(grid), dim3(512), 0, s, p, e);
+        else
+            hipLaunchKernelGGL((gemm_f16_pp_kernel<16, TG_FP16, TG_OUT_BF16>), dim3(grid), dim3(512), 0, s, p, e);
+        return hipGetLastError();
+    }
+    if (cfg == kF16FourWave5 || cfg == kF16FourWave4) {
+        if (lane_bytes != 16) return hipErrorInvalidValue;
+        if (cfg == kF16FourWave5)
+            hipLaunchKernelGGL((gemm_f16_w4_kernel<5, TG_FP16, TG_OUT_BF16>), dim3(grid), dim3(256), 0, s, p, e);
+        else
+            hipLaunchKernelGGL((gemm_f16_w4_kernel<4, TG_FP16, TG_OUT_BF16>), dim3(grid), dim3(256), 0, s, p, e);
+        return hipGetLastError();
+    }
+    if (cfg == kF16FourWaveT22 || cfg == kF16FourWaveT23) {
+        if (lane_bytes != 16) return hipErrorInvalidValue;
+        if (cfg == kF16FourWaveT22)
+            hipLaunchKernelGGL((gemm_f16_w4t_kernel<2, 2, TG_FP16, TG_OUT_BF16>), dim3(grid), dim3(256), 0, s, p, e);
+        else
+            hipLaunchKernelGGL((gemm_f16_w4t_kernel<2, 3, TG_FP16, TG_OUT_BF16>), dim3(grid), dim3(256), 0, s, p, e);
+        return hipGetLastError();
+    }
     switch (cfg) {
 #define TG_F16_CASE(id, bm, bn, bk, wm, wn, na, nb)                                                        \
     case id:                                                                                               \

@@ -45,6 +45,19 @@ __device__ __forceinline__ f32x16 mfma_32x32x16(u32x4 a, u32x4 b, f32x16 c) {
                                                        __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// One 16x16x32 MFMA: lane l holds row (A) / column (B) l % 16 and K
+// elements 8*(l/16) .. 8*(l/16)+7; accumulator register r of lane l is
+// row 4*(l/16) + r, column l % 16 of the 16x16 block.
+template <bool FP16>
+__device__ __forceinline__ f32x4 mfma_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+    if constexpr (FP16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
 // A global vector of VEC 16-bit elements.
 template <int VEC> struct GVec;
 template <> struct GVec<8> {

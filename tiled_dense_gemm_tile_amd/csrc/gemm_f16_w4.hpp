@@ -1,0 +1,446 @@
+// Four-wave schedule for D = A.B + C with 16-bit inputs whose rows are
+// 16-byte aligned (K a multiple of 8), gfx950.
+//
+// The workgroup computes a 256 x 256 output tile with 4 waves, one per SIMD,
+// each owning a 128 x 128 quadrant as 8 x 8 blocks of 16 x 16 accumulators
+// (v_mfma_f32_16x16x32: 256 accumulator registers per lane).  Large wave
+// tiles keep LDS traffic low: per 32-wide K slab each wave reads 16 KiB of
+// fragments (64 KiB for the workgroup) against 32 KiB of tile data written
+// by the direct global->LDS loads, and the 16x16 MFMA form draws less power
+// per flop than 32x32, so the clock holds higher under load.
+//
+// K advances in slabs of 32 (one MFMA step).  A and B each have a ring of NS
+// LDS slots of 256 rows x 64 bytes.  In iteration s a wave
+//   - issues the 64 MFMAs of slab s from fragments already in registers,
+//   - reads slab s + 1's fragments into the other register buffer,
+//   - issues its quarter of the global->LDS loads of slab s + NS into the
+//     slot slab s used (every wave finished reading it before the barrier
+//     that opened iteration s),
+// then waits until its own loads of slab s + 2 have landed and joins the
+// barrier that opens iteration s + 1.  A slab's loads thus have NS - 1
+// iterations to land.  Loads past K read nothing (out-of-range offsets give
+// zeros) so the wait counts stay fixed to the end.
+#pragma once
+
+#include <type_traits>
+
+#include "common.hpp"
+#include "gemm_f16.hpp"
+#include "pipeline.hpp"
+
+namespace tg {
+
+// In-place MFMA on an AGPR accumulator block: acc = A.B + acc.
+template <bool FP16>
+__device__ __forceinline__ void mfma16_acc_asm(f32x4 &acc, const u32x4 &a, const u32x4 &b) {
+    if constexpr (FP16)
+        asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+    else
+        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+// acc = A.B (C operand the inline constant 0).
+template <bool FP16>
+__device__ __forceinline__ void mfma16_zero_asm(f32x4 &acc, const u32x4 &a, const u32x4 &b) {
+    if constexpr (FP16)
+        asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, 0" : "=a"(acc) : "v"(a), "v"(b));
+    else
+        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=a"(acc) : "v"(a), "v"(b));
+}
+
+// Wait states between the last MFMA writing the accumulators and any other
+// instruction touching them (far more than the dependent-read hazard of a
+// 16x16x32 MFMA needs).  Every accumulator passes through one of these
+// statements, which issue in order, so no use can be scheduled before the
+// s_nops.
+template <int TM, int TN>
+__device__ __forceinline__ void mfma_result_fence(f32x4 (&acc)[TM][TN]) {
+    static_assert(TN == 8, "eight blocks per statement");
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        if (i == 0)
+            asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 3"
+                         : "+a"(acc[i][0]), "+a"(acc[i][1]), "+a"(acc[i][2]), "+a"(acc[i][3]), "+a"(acc[i][4]),
+                           "+a"(acc[i][5]), "+a"(acc[i][6]), "+a"(acc[i][7]));
+        else
+            asm volatile(""
+                         : "+a"(acc[i][0]), "+a"(acc[i][1]), "+a"(acc[i][2]), "+a"(acc[i][3]), "+a"(acc[i][4]),
+                           "+a"(acc[i][5]), "+a"(acc[i][6]), "+a"(acc[i][7]));
+    }
+}
+
+// 64-byte LDS rows (four 16-byte chunks): logical chunk c of row r sits at
+// physical chunk c ^ ((r >> 2) & 3).  A 16x16x32 fragment read has each
+// group of 16 lanes read one chunk of 16 consecutive rows; rows r and r + 4
+// share banks, and the swizzle gives those four rows four different chunks,
+// so every 16-lane (and 8-lane) group hits distinct banks.
+__device__ __forceinline__ int swz64(int r) { return (r >> 2) & 3; }
+
+template <int NS, bool FP16, bool OUT_BF16>
+__global__ void __launch_bounds__(256) gemm_f16_w4_kernel(F16Args p, F16Epi e) {
+    constexpr int BM = 256, BN = 256, KS = 32;         // tile and K slab
+    constexpr int WTM = 128, WTN = 128, TM = 8, TN = 8;
+    constexpr int ROWB = KS * 2;                       // 64-byte LDS rows
+    constexpr int SLOT = 256 * ROWB;                   // 16 KiB per operand slot
+    constexpr int B_BASE = NS * SLOT;
+    constexpr int RING_BYTES = 2 * NS * SLOT;
+    constexpr int EPI_BYTES = 4 * 32 * (WTN + 8) * 4;
+    constexpr int LDS_BYTES = RING_BYTES > EPI_BYTES ? RING_BYTES : EPI_BYTES;
+    constexpr int IB = 1024;                           // one load instruction: 16 rows
+    constexpr int LPS = 4;                             // load instructions per wave per operand per slab
+    constexpr int WAIT_N = (NS - 2) * 2 * LPS;         // loads still in flight at a barrier
+    static_assert(NS >= 3 && LDS_BYTES <= 160 * 1024 && WAIT_N < 64, "ring");
+
+    __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    int tmi, tni;
+    tile_order(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, tmi, tni);
+    const int m0 = tmi * BM, n0 = tni * BN;
+    const int M = p.M, N = p.N, K = p.K;
+
+    const __amdgpu_buffer_rsrc_t rA =
+        make_rsrc((const char *)p.A + (int64_t)m0 * p.lda * 2, span_bytes(M - m0, K, p.lda, 2));
+    const __amdgpu_buffer_rsrc_t rB =
+        make_rsrc((const char *)p.B + (int64_t)n0 * p.ldb * 2, span_bytes(N - n0, K, p.ldb, 2));
+
+    // Load instruction j of a wave fills slot rows (4 j + wave) * 16 + lane / 4:
+    // lane L writes physical chunk L % 4 and fetches logical chunk
+    // (L % 4) ^ swz64(row) = (L % 4) ^ ((L / 16) % 4), the same for every j.
+    const int chunk = (lane & 3) ^ ((lane >> 4) & 3);
+    const int kel = chunk * 8;
+    uint32_t a_off[LPS], b_off[LPS];
+#pragma unroll
+    for (int j = 0; j < LPS; ++j) {
+        const int row = (4 * j + wave) * 16 + (lane >> 2);
+        a_off[j] = (uint32_t)(row * p.lda * 2) + chunk * 16;
+        b_off[j] = (uint32_t)(row * p.ldb * 2) + chunk * 16;
+    }
+    // Load k (0..7) of this wave for slab sl: k < 4 is A instruction k, else B.
+    auto dma = [&](int sl, int k) {
+        const int k0 = sl * KS;
+        const uint32_t oob = (uint32_t)(k0 + kel >= K) << 31;   // offsets stay below 2^31
+        char *d = smem + (sl % NS) * SLOT + (k >= LPS ? B_BASE : 0) + ((k % LPS) * 4 + wave) * IB;
+        const uint32_t off = ((k < LPS ? a_off[k % LPS] : b_off[k % LPS]) + (uint32_t)k0 * 2) | oob;
+        dma_load<16>(k < LPS ? rA : rB, d, off);
+    };
+
+    // Fragment reads: lane l reads row l % 16 of each block, chunk l / 16.
+    const int fr = lane & 15, fq = lane >> 4;
+    const int coff = (fq ^ swz64(fr)) << 4;            // the same for every block (16 rows apart)
+    const int a_read = (wm * WTM + fr) * ROWB + coff;
+    const int b_read = B_BASE + (wn * WTN + fr) * ROWB + coff;
+
+    // The accumulators live in AGPRs and every MFMA updates its block in
+    // place (tied asm operand), so the register allocator never moves them.
+    // The asm is volatile and a scheduling barrier follows each MFMA, so
+    // MFMAs, LDS reads, global->LDS loads and their address arithmetic issue
+    // in source order: nothing is hoisted in front of a slab's first MFMA.
+    f32x4 acc[TM][TN];
+    u32x4 fa[2][TM], fb[2][TN];
+    auto read_frag = [&](int buf, int sl, int k) {     // k < 8: A block k, else B block k - 8
+        const char *s0 = smem + (sl % NS) * SLOT;
+        if (k < TM)
+            fa[buf][k] = *(const u32x4 *)(s0 + a_read + k * 16 * ROWB);
+        else
+            fb[buf][k - TM] = *(const u32x4 *)(s0 + b_read + (k - TM) * 16 * ROWB);
+    };
+    auto slab_end = [&]() {
+        wait_vmcnt<WAIT_N>();
+        wait_lgkmcnt0();
+        barrier();
+    };
+    // Slab sl: its 64 MFMAs on fragment buffer buf; after every second of the
+    // first 32 MFMAs one fragment read of slab sl + 1 into buf ^ 1, and after
+    // every fourth of MFMAs 28..56 one load of slab sl + NS.  FIRST: the
+    // accumulators start from zero (the MFMA's C operand is the constant 0).
+    auto iteration = [&](auto first, int buf, int sl) {
+#pragma unroll
+        for (int q = 0; q < TM * TN; ++q) {
+            const int i = q / TN, j = q % TN;
+            if constexpr (decltype(first)::value)
+                mfma16_zero_asm<FP16>(acc[i][j], fa[buf][i], fb[buf][j]);
+            else
+                mfma16_acc_asm<FP16>(acc[i][j], fa[buf][i], fb[buf][j]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (q % 2 == 1 && q / 2 < TM + TN) read_frag(buf ^ 1, sl + 1, q / 2);
+            if (q >= 28 && q % 4 == 0 && (q - 28) / 4 < 2 * LPS) dma(sl + NS, (q - 28) / 4);
+        }
+        slab_end();
+    };
+
+    const int ns = (K + KS - 1) / KS;
+    if (ns > 0) {
+#pragma unroll
+        for (int q = 0; q < NS; ++q)                   // slabs 0 .. NS-1
+#pragma unroll
+            for (int k = 0; k < 2 * LPS; ++k) dma(q, k);
+        wait_vmcnt<(NS - 1) * 2 * LPS>();              // slab 0 landed
+        barrier();
+#pragma unroll
+        for (int k = 0; k < TM + TN; ++k) read_frag(0, 0, k);
+        slab_end();                                    // slab 1 landed, slab 0 fragments in registers
+        iteration(std::true_type(), 0, 0);
+        // Slabs in pairs: with ns even the last pass multiplies the all-zero
+        // slab ns (loaded out of range) and adds nothing.
+        for (int s = 1; s < ns; s += 2) {
+            iteration(std::false_type(), 1, s);
+            iteration(std::false_type(), 0, s + 1);
+        }
+        // The epilogue reads the accumulators with VALU instructions; the
+        // compiler cannot see that they were last written by MFMAs, so wait
+        // out that hazard here, ahead of every accumulator use.
+        mfma_result_fence<TM, TN>(acc);
+    } else {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+
+    wait_vmcnt<0>();
+    wait_lgkmcnt0();
+    barrier();
+    epilogue_lds16<OUT_BF16, TM, TN, WTM, WTN>(acc, smem, wave, lane, wm, wn, m0, n0, M, N, p.C, p.ldc, p.D, p.ldd, e);
+}
+
+
+// The same four-wave, 128 x 128-per-wave layout with 64-wide K tiles:
+// 128-byte LDS rows, so every global->LDS load instruction moves whole
+// 128-byte lines (8 rows of a tile), and rings of NA slots for A and NB for
+// B (32 KiB a slot).  Per tile a wave issues 128 MFMAs in two K steps of
+// 32.  Half of the second step's MFMAs are issued after the barrier that
+// opens the next tile, while that tile's first fragments are read, so the
+// matrix pipe does not drain at the barrier:
+//   after barrier t:  MFMAs of tile t-1 step 1 (blocks i = 4..7)
+//                     + fragment reads of tile t step 0 + loads of A(t+NA-1)
+//                     MFMAs of tile t step 0
+//                     + fragment reads of tile t step 1 + loads of B(t+NB-1)
+//                     MFMAs of tile t step 1 (blocks i = 0..3)
+//                     wait for A(t+1), B(t+1); barrier t+1
+// A tile's slots are read only between its own two barriers, so the loads
+// of A(t+NA-1) and B(t+NB-1) go to slots freed at barrier t; A has one
+// tile of time to land, B (with NB = NA + 1) two.
+//
+// With C given and at least 17 K tiles, C is streamed into the accumulators
+// during the first 17 tiles and the epilogue only writes D.  Those tiles are
+// unrolled so the accumulator blocks they update have fixed register names:
+// tile c + 1 adds C part c -- the four blocks 4c .. 4c+3, loaded during tile
+// c into register set c % 2 -- at a point where no MFMA on those blocks is
+// in flight and many MFMAs separate the add from the block's previous and
+// next update (blocks of rows 0..63 early in the tile, rows 64..127 in its
+// second phase).  C thus arrives over 16 tiles instead of all at the end.
+template <int NA, int NB, bool FP16, bool OUT_BF16>
+__global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) {
+    constexpr int BM = 256, BN = 256, KT = 64;         // tile
+    constexpr int WTM = 128, WTN = 128, TM = 8, TN = 8;
+    constexpr int ROWB = KT * 2, CPR = ROWB / 16;      // 128-byte LDS rows
+    constexpr int SLOT = 256 * ROWB;                   // 32 KiB per operand slot
+    constexpr int B_BASE = NA * SLOT;
+    constexpr int RING_BYTES = (NA + NB) * SLOT;
+    constexpr int EPI_BYTES = 4 * 32 * (WTN + 8) * 4;
+    constexpr int LDS_BYTES = RING_BYTES > EPI_BYTES ? RING_BYTES : EPI_BYTES;
+    constexpr int IB = 1024;                           // one load instruction: 8 rows
+    constexpr int LPT = 8;                             // load instructions per wave per operand per tile
+    constexpr int WAIT_N = (NB - NA) * LPT;            // B loads still in flight at a barrier
+    static_assert(NA == 2 && (NB == 2 || NB == 3) && LDS_BYTES <= 160 * 1024, "ring");
+
+    __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    int tmi, tni;
+    tile_order(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, tmi, tni);
+    const int m0 = tmi * BM, n0 = tni * BN;
+    const int M = p.M, N = p.N, K = p.K;
+
+    const __amdgpu_buffer_rsrc_t rA =
+        make_rsrc((const char *)p.A + (int64_t)m0 * p.lda * 2, span_bytes(M - m0, K, p.lda, 2));
+    const __amdgpu_buffer_rsrc_t rB =
+        make_rsrc((const char *)p.B + (int64_t)n0 * p.ldb * 2, span_bytes(N - n0, K, p.ldb, 2));
+
+    // Load instruction j of a wave fills slot rows (4 j + wave) * 8 + lane / 8:
+    // lane L writes physical chunk L % 8 and fetches logical chunk
+    // (L % 8) ^ swz(row) = (L % 8) ^ (L / 8) ^ (wave % 2), the same for every j.
+    const int chunk = (lane & 7) ^ (lane >> 3) ^ (wave & 1);
+    const int kel = chunk * 8;
+    uint32_t a_off[LPT], b_off[LPT];
+#pragma unroll
+    for (int j = 0; j < LPT; ++j) {
+        const int row = (4 * j + wave) * 8 + (lane >> 3);
+        a_off[j] = (uint32_t)(row * p.lda * 2) + chunk * 16;
+        b_off[j] = (uint32_t)(row * p.ldb * 2) + chunk * 16;
+    }
+    auto dma_a = [&](int t, int j) __attribute__((always_inline)) {
+        const int k0 = t * KT;
+        const uint32_t oob = (uint32_t)(k0 + kel >= K) << 31;   // offsets stay below 2^31
+        char *d = smem + (t % NA) * SLOT + (j * 4 + wave) * IB;
+        const uint32_t off = (a_off[j] + (uint32_t)k0 * 2) | oob;
+        dma_load<16>(rA, d, off);
+    };
+    auto dma_b = [&](int t, int j) __attribute__((always_inline)) {
+        const int k0 = t * KT;
+        const uint32_t oob = (uint32_t)(k0 + kel >= K) << 31;
+        char *d = smem + B_BASE + (t % NB) * SLOT + (j * 4 + wave) * IB;
+        const uint32_t off = (b_off[j] + (uint32_t)k0 * 2) | oob;
+        dma_load<16>(rB, d, off);
+    };
+
+    // Fragment reads: lane l reads row l % 16 of each block and chunk
+    // 4 step + l / 16 of that row.
+    const int fr = lane & 15, fq = lane >> 4;
+    const int fswz = swz<CPR>(fr);                     // the same for every block (16 rows apart)
+    const int a_read = (wm * WTM + fr) * ROWB;
+    const int b_read = (wn * WTN + fr) * ROWB;
+
+    // Accumulators in AGPRs, updated in place by volatile asm MFMAs; a
+    // scheduling barrier after each keeps the issue order of the source.
+    f32x4 acc[TM][TN];
+    u32x4 fa[2][TM], fb[2][TN];                        // [K step][block]
+
+    // C streamed into the accumulators (see above).
+    constexpr int OS = OUT_BF16 ? 2 : 4;
+    constexpr int CPARTS = TM * TN / 4;                // 16 parts of 4 blocks
+    const int nt = (K + KT - 1) / KT;
+    const bool c_loop = p.C != nullptr && nt >= CPARTS + 1;
+    const __amdgpu_buffer_rsrc_t rC =
+        make_rsrc(c_loop ? (const char *)p.C + (int64_t)m0 * p.ldc * OS : (const char *)p.D,
+                  c_loop ? span_bytes(M - m0, N, p.ldc, OS) : 0u);
+    float cv[2][4][4];                                 // [set][block of the part][row]
+    auto load_c = [&](int part, int u) __attribute__((always_inline)) {               // block u of a part: 4 loads
+        const int b = 4 * part + u;
+        const int col = n0 + wn * WTN + (b % TN) * 16 + fr;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = wm * WTM + (b / TN) * 16 + 4 * fq + r;   // rows past M lie past the resource
+            const uint32_t off = col < N ? (uint32_t)(row * p.ldc + col) * OS : kOOB;
+            if constexpr (OUT_BF16)
+                cv[part % 2][u][r] =
+                    __builtin_bit_cast(float, (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rC, off, 0, 0) << 16);
+            else
+                cv[part % 2][u][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rC, off, 0, 0));
+        }
+    };
+    // Block u of a part += its C.  The empty tied statements pin where the
+    // accumulators are read and written back: the compiler cannot see that
+    // the asm MFMAs around them read and write these registers, so without
+    // them it may move the write-back right in front of the next MFMA on the
+    // block and break the required distance between the two.
+    auto add_c = [&](int part, int u) __attribute__((always_inline)) {
+        const int b = 4 * part + u;
+        f32x4 &a = acc[b / TN][b % TN];
+        asm volatile("" : "+a"(a));
+        f32x4 t = a;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) t[r] += cv[part % 2][u][r];
+        asm volatile("" : "+a"(t));
+        a = t;
+    };
+
+    // Fragment read k of K step st of tile t: k = 0 is A block 0, k = 1..8
+    // B blocks 0..7, k = 9..15 A blocks 1..7 -- the order the MFMAs use them.
+    auto read_frag = [&](int t, int st, int k) __attribute__((always_inline)) {
+        const int coff = ((4 * st + fq) ^ fswz) << 4;
+        if (k == 0 || k >= 9) {
+            const int i = k == 0 ? 0 : k - 8;
+            fa[st][i] = *(const u32x4 *)(smem + (t % NA) * SLOT + a_read + i * 16 * ROWB + coff);
+        } else {
+            const int j = k - 1;
+            fb[st][j] = *(const u32x4 *)(smem + B_BASE + (t % NB) * SLOT + b_read + j * 16 * ROWB + coff);
+        }
+    };
+    auto mfma = [&](auto zero, int st, int i, int j) __attribute__((always_inline)) {
+        if constexpr (decltype(zero)::value)
+            mfma16_zero_asm<FP16>(acc[i][j], fa[st][i], fb[st][j]);
+        else
+            mfma16_acc_asm<FP16>(acc[i][j], fa[st][i], fb[st][j]);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // One tile; FIRST: no previous tile (no deferred MFMAs, accumulators
+    // start from zero).  CP: the C part this tile adds (-1: none, but load
+    // part 0; -2: no C at all); it loads part CP + 1 when that exists.
+    auto tile = [&](auto first, auto cp, int t) __attribute__((always_inline)) {
+        constexpr int CP = decltype(cp)::value;
+        constexpr bool LOAD = CP >= -1 && CP + 1 < CPARTS;
+        // step 1 of tile t-1, blocks i = 4..7, with tile t step 0 reads and A loads
+#pragma unroll
+        for (int q = 0; q < 32; ++q) {
+            if constexpr (!decltype(first)::value) mfma(std::false_type(), 1, 4 + q / TN, q % TN);
+            if (q % 2 == 0) read_frag(t, 0, q / 2);
+            if (q % 4 == 1) dma_a(t + NA - 1, q / 4);
+            if constexpr (LOAD) {
+                if (q >= 2 && q < 6) load_c(CP + 1, q - 2);      // ahead of the last A load
+            }
+            if constexpr (CP >= 0 && CP < CPARTS / 2) {
+                if (q >= 16 && q < 20) add_c(CP, q - 16);       // blocks of rows 0..63
+            }
+        }
+        // step 0 of tile t, with step 1 reads (first half) and B loads (second half)
+#pragma unroll
+        for (int q = 0; q < 64; ++q) {
+            mfma(first, 0, q / TN, q % TN);
+            if (q % 2 == 1 && q < 32) read_frag(t, 1, q / 2);
+            if (q % 4 == 1 && q >= 32) dma_b(t + NB - 1, (q - 32) / 4);
+            if constexpr (CP >= CPARTS / 2) {
+                if (q >= 16 && q < 20) add_c(CP, q - 16);       // blocks of rows 64..127
+            }
+        }
+        // step 1 of tile t, blocks i = 0..3
+#pragma unroll
+        for (int q = 0; q < 32; ++q) mfma(std::false_type(), 1, q / TN, q % TN);
+        wait_vmcnt<WAIT_N>();                          // A(t+1), B(t+1) (and C part CP + 1) landed
+        wait_lgkmcnt0();
+        barrier();
+    };
+    // tiles 0 .. CPARTS with C parts streamed in, unrolled
+    auto c_tiles = [&](auto self, auto cp) __attribute__((always_inline)) {
+        constexpr int CP = decltype(cp)::value;
+        if constexpr (CP < CPARTS) {
+            tile(std::false_type(), std::integral_constant<int, CP>(), CP + 1);
+            self(self, std::integral_constant<int, CP + 1>());
+        }
+    };
+
+    if (nt > 0) {
+        // A(0); B(0) .. B(NB-2): the loads the first tiles' iterations do not issue
+#pragma unroll
+        for (int j = 0; j < LPT; ++j) dma_a(0, j);
+#pragma unroll
+        for (int b = 0; b < NB - 1; ++b)
+#pragma unroll
+            for (int j = 0; j < LPT; ++j) dma_b(b, j);
+        wait_vmcnt<(NB - 2) * LPT>();                  // A(0), B(0) landed
+        barrier();
+        int t0 = 1;
+        if (c_loop) {
+            tile(std::true_type(), std::integral_constant<int, -1>(), 0);   // loads C part 0
+            c_tiles(c_tiles, std::integral_constant<int, 0>());             // tiles 1 .. CPARTS
+            t0 = CPARTS + 1;
+        } else {
+            tile(std::true_type(), std::integral_constant<int, -2>(), 0);
+        }
+        for (int t = t0; t < nt; ++t) tile(std::false_type(), std::integral_constant<int, -2>(), t);
+        // the deferred half of the last tile's step 1
+#pragma unroll
+        for (int q = 0; q < 32; ++q) mfma(std::false_type(), 1, 4 + q / TN, q % TN);
+        mfma_result_fence<TM, TN>(acc);
+    } else {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+
+    wait_vmcnt<0>();
+    wait_lgkmcnt0();
+    barrier();
+    epilogue_lds16<OUT_BF16, TM, TN, WTM, WTN>(acc, smem, wave, lane, wm, wn, m0, n0, M, N, c_loop ? nullptr : p.C,
+                                               p.ldc, p.D, p.ldd, e);
+}
+
+}  // namespace tg

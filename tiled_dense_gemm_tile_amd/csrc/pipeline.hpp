@@ -34,21 +34,22 @@ struct F16Epi {
 // LDS bytes the staged epilogue needs: 32 rows of every wave's tile columns.
 constexpr int epilogue_lds_bytes(int nwaves, int wtn) { return nwaves * 32 * (wtn + 8) * 4; }
 
-// D = acc + C for one wave's WTM x WTN block of a tile whose 32x32 MFMA
-// accumulators are acc[i][j] (lane l, register r holds row
-// 8*(r/4) + 4*(l/32) + r%4 and column l%32 of block (i, j)).  Each pass
-// stages 32 rows in this wave's private LDS area (pitch WTN + 8 floats,
-// so the two half-waves write disjoint banks) and reads them back as
-// 16-byte row segments: C is read and D written with whole-vector accesses
-// where the row and alignment allow, element-wise at the right edge.
+// D = acc + C for one wave's WTM x WTN block of a tile, in WTM / 32 passes
+// of 32 rows.  stage(pass, ep) writes the accumulators of rows
+// [32 pass, 32 pass + 32) of the wave block into this wave's private LDS
+// area ep (row-major, pitch WTN + PAD floats, PAD chosen by the stager so
+// its writes hit disjoint banks); the pass then reads them back as 16-byte
+// row segments:
+// C is read and D written with whole-vector accesses where the row and
+// alignment allow, element-wise at the right edge.
 // The caller guarantees every wave is done with the LDS it reuses.
-template <bool OUT_BF16, int TM, int TN, int WTM, int WTN>
-__device__ __forceinline__ void epilogue_lds(const f32x16 (&acc)[TM][TN], char *smem, int wave, int lane, int wm,
-                                             int wn, int m0, int n0, int M, int N, const void *C, int64_t ldc,
-                                             void *D, int64_t ldd, F16Epi e) {
+template <bool OUT_BF16, int WTM, int WTN, int PAD, class Stage>
+__device__ __forceinline__ void epilogue_lds_passes(Stage &&stage, char *smem, int wave, int lane, int wm, int wn,
+                                                    int m0, int n0, int M, int N, const void *C, int64_t ldc,
+                                                    void *D, int64_t ldd, F16Epi e) {
+    static_assert(PAD <= 8, "stage area");
     constexpr int OS = OUT_BF16 ? 2 : 4;
-    constexpr int EP = WTN + 8;
-    const int fr = lane & 31, fh = lane >> 5;
+    constexpr int EP = WTN + PAD;
     float *ep = (float *)smem + wave * 32 * EP;
     const __amdgpu_buffer_rsrc_t rD =
         make_rsrc((char *)D + (int64_t)m0 * ldd * OS, span_bytes(M - m0, N, ldd, OS));
@@ -61,12 +62,8 @@ __device__ __forceinline__ void epilogue_lds(const f32x16 (&acc)[TM][TN], char *
     const int erow = lane / LPR, ecol = (lane % LPR) * 4;
     const int gcol = n0 + wn * WTN + ecol;             // first output column of this lane
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                ep[(8 * (r >> 2) + 4 * fh + (r & 3)) * EP + j * 32 + fr] = acc[i][j][r];
+    for (int i = 0; i < WTM / 32; ++i) {
+        stage(i, ep);
         wait_lgkmcnt0();
 #pragma unroll
         for (int q = 0; q < 32 / RPS; ++q) {
@@ -131,6 +128,45 @@ __device__ __forceinline__ void epilogue_lds(const f32x16 (&acc)[TM][TN], char *
         }
         wait_lgkmcnt0();   // reads of this pass done before the next pass overwrites the stage
     }
+}
+
+// Epilogue for 32x32 MFMA accumulators acc[i][j] (lane l, register r holds
+// row 8*(r/4) + 4*(l/32) + r%4 and column l%32 of block (i, j)).
+template <bool OUT_BF16, int TM, int TN, int WTM, int WTN>
+__device__ __forceinline__ void epilogue_lds(const f32x16 (&acc)[TM][TN], char *smem, int wave, int lane, int wm,
+                                             int wn, int m0, int n0, int M, int N, const void *C, int64_t ldc,
+                                             void *D, int64_t ldd, F16Epi e) {
+    static_assert(TM * 32 == WTM && TN * 32 == WTN, "32x32 blocks");
+    constexpr int EP = WTN + 8;                        // half-waves 4 rows apart: 32 banks apart
+    const int fr = lane & 31, fh = lane >> 5;
+    auto stage = [&](int i, float *ep) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                ep[(8 * (r >> 2) + 4 * fh + (r & 3)) * EP + j * 32 + fr] = acc[i][j][r];
+    };
+    epilogue_lds_passes<OUT_BF16, WTM, WTN, 8>(stage, smem, wave, lane, wm, wn, m0, n0, M, N, C, ldc, D, ldd, e);
+}
+
+// Epilogue for 16x16 MFMA accumulators acc[i][j] (lane l, register r holds
+// row 4*(l/16) + r and column l%16 of block (i, j)); a pass stages two block rows.
+template <bool OUT_BF16, int TM, int TN, int WTM, int WTN>
+__device__ __forceinline__ void epilogue_lds16(const f32x4 (&acc)[TM][TN], char *smem, int wave, int lane, int wm,
+                                               int wn, int m0, int n0, int M, int N, const void *C, int64_t ldc,
+                                               void *D, int64_t ldd, F16Epi e) {
+    static_assert(TM * 16 == WTM && TN * 16 == WTN && TM % 2 == 0, "16x16 blocks");
+    constexpr int EP = WTN + 4;                        // lane quarters 4 rows apart: 16 banks apart
+    const int fc = lane & 15, fq = lane >> 4;
+    auto stage = [&](int p, float *ep) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) ep[(16 * h + 4 * fq + r) * EP + j * 16 + fc] = acc[2 * p + h][j][r];
+    };
+    epilogue_lds_passes<OUT_BF16, WTM, WTN, 4>(stage, smem, wave, lane, wm, wn, m0, n0, M, N, C, ldc, D, ldd, e);
 }
 
 }  // namespace tg

@@ -91,6 +91,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="square4096_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--settle", type=float, default=0.3, metavar="SECONDS",
+                    help="untimed run of the same step before the warmup steps, so the timed steps "
+                         "see the clocks the GPU holds under sustained load (0 disables)")
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="rows of D the CPU baseline evaluates (default: about 1.3e10 multiply-adds)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -129,6 +132,14 @@ def main():
         SFA, SFB = extra
         step = lambda: tg.gemm_mxfp8(A, SFA, B, SFB, C, out_dtype=out_dtype, D=D)
 
+    # The GPU raises its clocks over the first milliseconds of sustained
+    # work; a few warmup launches of a ~0.1 ms kernel end before that, so
+    # the same step first runs untimed for about --settle seconds.
+    t_settle = time.perf_counter() + args.settle
+    while time.perf_counter() < t_settle:
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()

@@ -39,13 +39,14 @@ __device__ __forceinline__ uint32_t span_bytes(int rows_left, int cols, int64_t 
     return b >= (int64_t)kOOB ? kOOB - 1 : (uint32_t)b;
 }
 
-// fp32 -> bf16, round to nearest even (finite inputs; NaN stays NaN).
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
-    uint32_t u = __builtin_bit_cast(uint32_t, x);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+// fp32 -> bf16, round to nearest even (NaN stays NaN), two at a time with
+// gfx950's packed conversion (v_cvt_pk_bf16_f32): lo in bits 0..15.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{lo, hi}), bf16x2_t));
 }
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) { return (uint16_t)pack_bf16x2(x, 0.0f); }
 
 // ---- LDS layout --------------------------------------------------------
 // A tile of R rows x BK 16-bit elements is stored row after row, each row
@@ -64,6 +65,12 @@ __device__ __forceinline__ int swz(int r) {
         return 0;
     }
 }
+
+// Swizzle of 128-byte rows for 16x16x32 fragment reads (each quarter-wave
+// reads one chunk of 16 consecutive rows): logical chunk c of row r sits at
+// physical chunk c ^ (r & 7).  Measured free of bank conflicts for that
+// pattern on gfx950, where swz<8> (tuned for the 32x32 pattern) is not.
+__device__ __forceinline__ int swz16(int r) { return r & 7; }
 
 // ---- tile order ---------------------------------------------------------
 // Workgroup w is dispatched to XCD (w mod 8).  Renumber so each XCD owns a

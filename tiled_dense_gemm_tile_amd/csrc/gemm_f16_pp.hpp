@@ -90,7 +90,9 @@ __global__ void __launch_bounds__(512) gemm_f16_pp_kernel(F16Args p, F16Epi e) {
     // ring slot: lane L writes physical chunk L % 8 of row L / 8 and fetches
     // logical chunk (L % 8) ^ swz(row), which is the same for every j.
     const int lrow = lane >> 3;
-    const int chunk = (lane & 7) ^ swz<CPR>(s * 8 + lrow);
+    // 32x32 fragment reads use swz<8>, 16x16 ones swz16 (bank-conflict free
+    // for each read pattern); rows (4 j + s) * 8 + lrow give the same chunk for every j.
+    const int chunk = (lane & 7) ^ (MS == 32 ? swz<CPR>(s * 8 + lrow) : swz16(lrow));
     const int kel = chunk * 8;                          // first K element of this lane's chunk
     const int a_row0 = g == 0 ? 128 : 0;                // group 0 loads half 1, group 1 half 0
     uint32_t a_off[4], b_off[8];
@@ -125,7 +127,7 @@ __global__ void __launch_bounds__(512) gemm_f16_pp_kernel(F16Args p, F16Epi e) {
     // Fragment reads: lane l reads row l % MS of each block and 16-byte chunk
     // KK-step * (KS / 8) + l / MS of that row (its 8 K elements).
     const int fr = lane % MS, fq = lane / MS;
-    const int fswz = swz<CPR>(fr);                     // the same for every block (MS rows apart)
+    const int fswz = MS == 32 ? swz<CPR>(fr) : swz16(fr);   // the same for every block (MS rows apart)
     const char *const a_read = smem + (g == 0 ? A0_BASE : A1_BASE) + fr * ROWB;
     const char *const b_read = smem + B_BASE + (s * WTN + fr) * ROWB;
 

@@ -237,7 +237,7 @@ template <int NA, int NB, bool FP16, bool OUT_BF16>
 __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) {
     constexpr int BM = 256, BN = 256, KT = 64;         // tile
     constexpr int WTM = 128, WTN = 128, TM = 8, TN = 8;
-    constexpr int ROWB = KT * 2, CPR = ROWB / 16;      // 128-byte LDS rows
+    constexpr int ROWB = KT * 2;                       // 128-byte LDS rows
     constexpr int SLOT = 256 * ROWB;                   // 32 KiB per operand slot
     constexpr int B_BASE = NA * SLOT;
     constexpr int RING_BYTES = (NA + NB) * SLOT;
@@ -266,8 +266,8 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
 
     // Load instruction j of a wave fills slot rows (4 j + wave) * 8 + lane / 8:
     // lane L writes physical chunk L % 8 and fetches logical chunk
-    // (L % 8) ^ swz(row) = (L % 8) ^ (L / 8) ^ (wave % 2), the same for every j.
-    const int chunk = (lane & 7) ^ (lane >> 3) ^ (wave & 1);
+    // (L % 8) ^ swz16(row) = (L % 8) ^ (L / 8), the same for every j.
+    const int chunk = (lane & 7) ^ (lane >> 3);
     const int kel = chunk * 8;
     uint32_t a_off[LPT], b_off[LPT];
 #pragma unroll
@@ -294,7 +294,7 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
     // Fragment reads: lane l reads row l % 16 of each block and chunk
     // 4 step + l / 16 of that row.
     const int fr = lane & 15, fq = lane >> 4;
-    const int fswz = swz<CPR>(fr);                     // the same for every block (16 rows apart)
+    const int fswz = swz16(fr);                        // the same for every block (16 rows apart)
     const int a_read = (wm * WTM + fr) * ROWB;
     const int b_read = (wn * WTN + fr) * ROWB;
 

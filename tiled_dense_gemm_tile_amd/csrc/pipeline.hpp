@@ -104,8 +104,8 @@ __device__ __forceinline__ void epilogue_lds_passes(Stage &&stage, char *smem, i
                 const uint32_t doff = (uint32_t)(row * ldd + gcol) * OS;
                 if constexpr (OUT_BF16) {
                     u32x2 pk;
-                    pk[0] = (uint32_t)f32_to_bf16_rne(o[0]) | ((uint32_t)f32_to_bf16_rne(o[1]) << 16);
-                    pk[1] = (uint32_t)f32_to_bf16_rne(o[2]) | ((uint32_t)f32_to_bf16_rne(o[3]) << 16);
+                    pk[0] = pack_bf16x2(o[0], o[1]);
+                    pk[1] = pack_bf16x2(o[2], o[3]);
                     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, pk), rD, doff, 0, 0);
                 } else {
                     u32x4 pk;

@@ -76,16 +76,35 @@ def test_scale_structure():
     _full_check(x, to_f64(D), True)
 
 
-@pytest.mark.parametrize("cfg", [0, 1, 2, 3])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4])
 def test_every_config(cfg, monkeypatch):
     monkeypatch.setenv("TILEGEMM_MX_CONFIG", str(cfg))
-    for (M, N, K) in [(300, 520, 256), (777, 513, 1024)]:
+    for (M, N, K) in [(300, 520, 256), (777, 513, 1024), (520, 300, 384), (1100, 1030, 2048)]:
         for integer in (True, False):
             x, C = _case(M, N, K, seed=cfg * 13 + M, integer=integer)
             say("mx cfg %d %dx%dx%d integer=%s" % (cfg, M, N, K, integer))
             D = _run(x, C)
             torch.cuda.synchronize()
             _full_check(x, to_f64(D), integer, C)
+
+
+@pytest.mark.parametrize("cfg", [1, 4])
+def test_padded_scale_rows(cfg, monkeypatch):
+    """Scale arrays with leading dimensions past K/32 (multiples of 16 bytes,
+    so the 16-byte scale loads of the ping-pong kernel apply)."""
+    monkeypatch.setenv("TILEGEMM_MX_CONFIG", str(cfg))
+    M, N, K = 300, 290, 1536
+    for integer in (True, False):
+        x, C = _case(M, N, K, seed=31 + cfg, integer=integer)
+        nb = K // 32
+        SFA = torch.full((M, nb + 16), 255, dtype=torch.uint8, device=DEV)   # padding is NaN codes
+        SFB = torch.full((N, nb + 32), 255, dtype=torch.uint8, device=DEV)
+        SFA[:, :nb] = dev8(x["SFA"])
+        SFB[:, :nb] = dev8(x["SFB"])
+        say("mx cfg %d padded scales %dx%dx%d integer=%s" % (cfg, M, N, K, integer))
+        D = tg.gemm_mxfp8(dev8(x["A"]), SFA[:, :nb], dev8(x["B"]), SFB[:, :nb], torch.from_numpy(C).to(DEV))
+        torch.cuda.synchronize()
+        _full_check(x, to_f64(D), integer, C)
 
 
 def test_bf16_output_is_rne_of_fp32():

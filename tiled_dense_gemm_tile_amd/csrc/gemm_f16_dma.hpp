@@ -41,16 +41,6 @@ __device__ __forceinline__ void add_part(Acc &acc, const float *cq, int q) {
     }
 }
 
-// One direct global->LDS load: each lane moves LB bytes from `off` in the
-// resource to LDS at lds + lane * LB.
-template <int LB>
-__device__ __forceinline__ void dma_load(__amdgpu_buffer_rsrc_t r, char *lds, uint32_t off) {
-    if constexpr (LB == 16)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, off, 0, 0, 0);
-    else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 4, off, 0, 0, 0);
-}
-
 template <int BM_, int BN_, int BK_, int WM_, int WN_, int NA_, int NB_>
 struct DmaCfg {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, NA = NA_, NB = NB_;

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include "gemm_mxfp8.hpp"
+#include "gemm_mx_pp.hpp"
 
 namespace tg {
 
@@ -20,9 +21,11 @@ struct MxCfgInfo {
 };
 
 #define TG_MX_INFO(id, bm, bn, wm, wn) {bm, bn, wm, wn},
-constexpr MxCfgInfo kMxCfgs[] = {TG_MX_CONFIGS(TG_MX_INFO)};
+// The last id is the ping-pong kernel (256 x 256, 8 waves, 16x16x128 MFMA).
+constexpr MxCfgInfo kMxCfgs[] = {TG_MX_CONFIGS(TG_MX_INFO){256, 256, 2, 4}};
 #undef TG_MX_INFO
 constexpr int kNumMxCfgs = sizeof(kMxCfgs) / sizeof(kMxCfgs[0]);
+constexpr int kMxPingPong = kNumMxCfgs - 1;
 
 template <bool OUT_BF16>
 hipError_t launch_mx(int cfg, unsigned grid, hipStream_t s, const MxArgs &q, const F16Epi &e);
@@ -34,6 +37,10 @@ namespace tg {
 
 template <>
 hipError_t launch_mx<TG_OUT_BF16>(int cfg, unsigned grid, hipStream_t s, const MxArgs &q, const F16Epi &e) {
+    if (cfg == kMxPingPong) {
+        hipLaunchKernelGGL((gemm_mx_pp_kernel<TG_OUT_BF16>), dim3(grid), dim3(512), 0, s, q, e);
+        return hipGetLastError();
+    }
     switch (cfg) {
 #define TG_MX_CASE(id, bm, bn, wm, wn)                                                                  \
     case id:                                                                                            \

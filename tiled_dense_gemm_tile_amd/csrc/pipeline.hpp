@@ -24,6 +24,16 @@ __device__ __forceinline__ void barrier() {
     asm volatile("" ::: "memory");
 }
 
+// One direct global->LDS load: each lane moves LB bytes from `off` in the
+// resource to LDS at lds + lane * LB.
+template <int LB>
+__device__ __forceinline__ void dma_load(__amdgpu_buffer_rsrc_t r, char *lds, uint32_t off) {
+    if constexpr (LB == 16)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, off, 0, 0, 0);
+    else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 4, off, 0, 0, 0);
+}
+
 // Scheduling masks of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100, kSchedVmemRead = 0x020;
 

@@ -307,16 +307,21 @@ def test_lane4_configs(cfg, pad, monkeypatch):
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 def test_c_streamed_in_k_loop(cfg, out, monkeypatch):
     """K long enough (>= 34 tiles of 64) that C is added during the K loop
-    instead of in the epilogue: ragged M/N, both output types, and C == D."""
+    instead of in the epilogue: ragged M/N, both output types, and C == D.
+    The four-wave kernels also at the stream's threshold: 18 K tiles (C
+    streamed) and 17 (C added in the epilogue)."""
     monkeypatch.setenv("TILEGEMM_F16_CONFIG", str(cfg))
-    M, N, K = 300, 520, 2304
-    for integer in (True, False):
+    M = 300
+    cases = [(520, 2304)]
+    if cfg in (12, 13):   # the stream's threshold; N % 4 != 0 (C added in the epilogue)
+        cases += [(520, 1152), (520, 1088), (518, 2304)]
+    for N, K, integer in [(n, k, i) for (n, k) in cases for i in (True, False)]:
         x, C = _case("bf16", M, N, K, seed=cfg * 7 + (out == "bf16"), integer=integer)
         A, B = dev16(x["A"], "bf16"), dev16(x["B"], "bf16")
         if out == "bf16":
             Cb = torch.from_numpy(C).to(DEV).to(torch.bfloat16)
             Cref = Cb.float().cpu().numpy()
-            say("c-loop cfg %d bf16 out integer=%s" % (cfg, integer))
+            say("c-loop cfg %d N %d K %d bf16 out integer=%s" % (cfg, N, K, integer))
             D16 = run16("bf16", A, B, Cb, out="bf16")
             D32 = run16("bf16", A, B, torch.from_numpy(Cref).to(DEV), out="f32")
             torch.cuda.synchronize()
@@ -324,7 +329,7 @@ def test_c_streamed_in_k_loop(cfg, out, monkeypatch):
             assert np.array_equal(bf16_bits(D16), oracle.rne_bf16_f32(D32.cpu().numpy()))
         else:
             Cd = torch.from_numpy(C).to(DEV)
-            say("c-loop cfg %d f32 out integer=%s" % (cfg, integer))
+            say("c-loop cfg %d N %d K %d f32 out integer=%s" % (cfg, N, K, integer))
             D = run16("bf16", A, B, Cd)
             inplace = Cd.clone()
             run16("bf16", A, B, inplace, D=inplace)

@@ -225,14 +225,17 @@ __global__ void __launch_bounds__(256) gemm_f16_w4_kernel(F16Args p, F16Epi e) {
 // of A(t+NA-1) and B(t+NB-1) go to slots freed at barrier t; A has one
 // tile of time to land, B (with NB = NA + 1) two.
 //
-// With C given and at least 17 K tiles, C is streamed into the accumulators
-// during the first 17 tiles and the epilogue only writes D.  Those tiles are
+// With C given and at least 18 K tiles, C is streamed into the accumulators
+// during the first 18 tiles and the epilogue only writes D.  Those tiles are
 // unrolled so the accumulator blocks they update have fixed register names:
-// tile c + 1 adds C part c -- the four blocks 4c .. 4c+3, loaded during tile
-// c into register set c % 2 -- at a point where no MFMA on those blocks is
-// in flight and many MFMAs separate the add from the block's previous and
-// next update (blocks of rows 0..63 early in the tile, rows 64..127 in its
-// second phase).  C thus arrives over 16 tiles instead of all at the end.
+// C part c -- the four blocks 4c .. 4c+3 -- is loaded at the end of tile c
+// (after the tile's global->LDS loads, into register set c % 3) and added in
+// tile c + 2, at a point where no MFMA on those blocks is in flight and many
+// MFMAs separate the add from the block's previous and next update (blocks
+// of rows 0..63 early in the tile, rows 64..127 in its second phase).  The
+// barrier wait at the end of tile c leaves the part's loads in flight, so
+// they have a whole tile to arrive from memory.  C thus arrives over 16
+// tiles instead of all at the end.
 template <int NA, int NB, bool FP16, bool OUT_BF16>
 __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) {
     constexpr int BM = 256, BN = 256, KT = 64;         // tile
@@ -307,23 +310,24 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
     constexpr int OS = OUT_BF16 ? 2 : 4;
     constexpr int CPARTS = TM * TN / 4;                // 16 parts of 4 blocks
     const int nt = (K + KT - 1) / KT;
-    const bool c_loop = p.C != nullptr && nt >= CPARTS + 1;
+    // (whole 4-column vectors: every C row segment a lane reads is either in
+    // range or past N)
+    const bool c_loop = p.C != nullptr && nt >= CPARTS + 2 && e.vec_c && N % 4 == 0;
     const __amdgpu_buffer_rsrc_t rC =
         make_rsrc(c_loop ? (const char *)p.C + (int64_t)m0 * p.ldc * OS : (const char *)p.D,
                   c_loop ? span_bytes(M - m0, N, p.ldc, OS) : 0u);
-    float cv[2][4][4];                                 // [set][block of the part][row]
-    auto load_c = [&](int part, int u) __attribute__((always_inline)) {               // block u of a part: 4 loads
+    f32x4 cv[3][4];                                    // [set][block of the part]: 4 columns of a row
+    auto load_c = [&](int part, int u) __attribute__((always_inline)) {               // block u of a part: one load
         const int b = 4 * part + u;
-        const int col = n0 + wn * WTN + (b % TN) * 16 + fr;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = wm * WTM + (b / TN) * 16 + 4 * fq + r;   // rows past M lie past the resource
-            const uint32_t off = col < N ? (uint32_t)(row * p.ldc + col) * OS : kOOB;
-            if constexpr (OUT_BF16)
-                cv[part % 2][u][r] =
-                    __builtin_bit_cast(float, (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rC, off, 0, 0) << 16);
-            else
-                cv[part % 2][u][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rC, off, 0, 0));
+        const int row = wm * WTM + (b / TN) * 16 + fr;   // rows past M lie past the resource
+        const int col = n0 + wn * WTN + (b % TN) * 16 + 4 * fq;
+        const uint32_t off = col < N ? (uint32_t)(row * p.ldc + col) * OS : kOOB;
+        if constexpr (OUT_BF16) {
+            const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rC, off, 0, 0));
+            cv[part % 3][u] = f32x4{__builtin_bit_cast(float, v[0] << 16), __builtin_bit_cast(float, v[0] & 0xffff0000u),
+                                   __builtin_bit_cast(float, v[1] << 16), __builtin_bit_cast(float, v[1] & 0xffff0000u)};
+        } else {
+            cv[part % 3][u] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rC, off, 0, 0));
         }
     };
     // Block u of a part += its C.  The empty tied statements pin where the
@@ -337,7 +341,7 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
         asm volatile("" : "+a"(a));
         f32x4 t = a;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) t[r] += cv[part % 2][u][r];
+        for (int r = 0; r < 4; ++r) t[r] += cv[part % 3][u][r];
         asm volatile("" : "+a"(t));
         a = t;
     };
@@ -354,30 +358,29 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
             fb[st][j] = *(const u32x4 *)(smem + B_BASE + (t % NB) * SLOT + b_read + j * 16 * ROWB + coff);
         }
     };
+    // B is the MFMA's first operand and A its second, so block (i, j) holds
+    // the transpose of the D block: lane l has row 16 i + l % 16 of the
+    // quadrant and its four consecutive columns 16 j + 4 (l / 16) .. + 3.
     auto mfma = [&](auto zero, int st, int i, int j) __attribute__((always_inline)) {
         if constexpr (decltype(zero)::value)
-            mfma16_zero_asm<FP16>(acc[i][j], fa[st][i], fb[st][j]);
+            mfma16_zero_asm<FP16>(acc[i][j], fb[st][j], fa[st][i]);
         else
-            mfma16_acc_asm<FP16>(acc[i][j], fa[st][i], fb[st][j]);
+            mfma16_acc_asm<FP16>(acc[i][j], fb[st][j], fa[st][i]);
         __builtin_amdgcn_sched_barrier(0);
     };
     // One tile; FIRST: no previous tile (no deferred MFMAs, accumulators
-    // start from zero).  CP: the C part this tile adds (-1: none, but load
-    // part 0; -2: no C at all); it loads part CP + 1 when that exists.
-    auto tile = [&](auto first, auto cp, int t) __attribute__((always_inline)) {
-        constexpr int CP = decltype(cp)::value;
-        constexpr bool LOAD = CP >= -1 && CP + 1 < CPARTS;
+    // start from zero).  LP: the C part this tile loads (-1: none); AP: the
+    // C part it adds (-1: none).
+    auto tile = [&](auto first, auto lp, auto ap, int t) __attribute__((always_inline)) {
+        constexpr int LP = decltype(lp)::value, AP = decltype(ap)::value;
         // step 1 of tile t-1, blocks i = 4..7, with tile t step 0 reads and A loads
 #pragma unroll
         for (int q = 0; q < 32; ++q) {
             if constexpr (!decltype(first)::value) mfma(std::false_type(), 1, 4 + q / TN, q % TN);
             if (q % 2 == 0) read_frag(t, 0, q / 2);
             if (q % 4 == 1) dma_a(t + NA - 1, q / 4);
-            if constexpr (LOAD) {
-                if (q >= 2 && q < 6) load_c(CP + 1, q - 2);      // ahead of the last A load
-            }
-            if constexpr (CP >= 0 && CP < CPARTS / 2) {
-                if (q >= 16 && q < 20) add_c(CP, q - 16);       // blocks of rows 0..63
+            if constexpr (AP >= 0 && AP < CPARTS / 2) {
+                if (q >= 16 && q < 20) add_c(AP, q - 16);       // blocks of rows 0..63
             }
         }
         // step 0 of tile t, with step 1 reads (first half) and B loads (second half)
@@ -386,23 +389,32 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
             mfma(first, 0, q / TN, q % TN);
             if (q % 2 == 1 && q < 32) read_frag(t, 1, q / 2);
             if (q % 4 == 1 && q >= 32) dma_b(t + NB - 1, (q - 32) / 4);
-            if constexpr (CP >= CPARTS / 2) {
-                if (q >= 16 && q < 20) add_c(CP, q - 16);       // blocks of rows 64..127
+            if constexpr (AP >= CPARTS / 2) {
+                if (q >= 16 && q < 20) add_c(AP, q - 16);       // blocks of rows 64..127
             }
         }
-        // step 1 of tile t, blocks i = 0..3
+        // step 1 of tile t, blocks i = 0..3, with the loads of C part LP
 #pragma unroll
-        for (int q = 0; q < 32; ++q) mfma(std::false_type(), 1, q / TN, q % TN);
-        wait_vmcnt<WAIT_N>();                          // A(t+1), B(t+1) (and C part CP + 1) landed
+        for (int q = 0; q < 32; ++q) {
+            mfma(std::false_type(), 1, q / TN, q % TN);
+            if constexpr (LP >= 0) {
+                if (q % 8 == 1) load_c(LP, q / 8);
+            }
+        }
+        // A(t+1), B(t+1) landed; B(t+NB-1) and this tile's C loads (one per
+        // block of the part) may still run
+        wait_vmcnt<WAIT_N + (LP >= 0 ? 4 : 0)>();
         wait_lgkmcnt0();
         barrier();
     };
-    // tiles 0 .. CPARTS with C parts streamed in, unrolled
-    auto c_tiles = [&](auto self, auto cp) __attribute__((always_inline)) {
-        constexpr int CP = decltype(cp)::value;
-        if constexpr (CP < CPARTS) {
-            tile(std::false_type(), std::integral_constant<int, CP>(), CP + 1);
-            self(self, std::integral_constant<int, CP + 1>());
+    // tiles 1 .. CPARTS + 1 of the C stream, unrolled: tile t loads part t
+    // (while t < CPARTS) and adds part t - 2 (from tile 2 on)
+    auto c_tiles = [&](auto self, auto tc) __attribute__((always_inline)) {
+        constexpr int T = decltype(tc)::value;
+        if constexpr (T <= CPARTS + 1) {
+            tile(std::false_type(), std::integral_constant<int, (T < CPARTS ? T : -1)>(),
+                 std::integral_constant<int, T - 2>(), T);
+            self(self, std::integral_constant<int, T + 1>());
         }
     };
 
@@ -416,15 +428,16 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
             for (int j = 0; j < LPT; ++j) dma_b(b, j);
         wait_vmcnt<(NB - 2) * LPT>();                  // A(0), B(0) landed
         barrier();
+        using none = std::integral_constant<int, -1>;
         int t0 = 1;
         if (c_loop) {
-            tile(std::true_type(), std::integral_constant<int, -1>(), 0);   // loads C part 0
-            c_tiles(c_tiles, std::integral_constant<int, 0>());             // tiles 1 .. CPARTS
-            t0 = CPARTS + 1;
+            tile(std::true_type(), std::integral_constant<int, 0>(), none(), 0);   // loads C part 0
+            c_tiles(c_tiles, std::integral_constant<int, 1>());                    // tiles 1 .. CPARTS + 1
+            t0 = CPARTS + 2;
         } else {
-            tile(std::true_type(), std::integral_constant<int, -2>(), 0);
+            tile(std::true_type(), none(), none(), 0);
         }
-        for (int t = t0; t < nt; ++t) tile(std::false_type(), std::integral_constant<int, -2>(), t);
+        for (int t = t0; t < nt; ++t) tile(std::false_type(), none(), none(), t);
         // the deferred half of the last tile's step 1
 #pragma unroll
         for (int q = 0; q < 32; ++q) mfma(std::false_type(), 1, 4 + q / TN, q % TN);
@@ -439,8 +452,8 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
     wait_vmcnt<0>();
     wait_lgkmcnt0();
     barrier();
-    epilogue_lds16<OUT_BF16, TM, TN, WTM, WTN>(acc, smem, wave, lane, wm, wn, m0, n0, M, N, c_loop ? nullptr : p.C,
-                                               p.ldc, p.D, p.ldd, e);
+    epilogue_lds16t<OUT_BF16, TM, TN, WTM, WTN>(acc, smem, wave, lane, wm, wn, m0, n0, M, N, c_loop ? nullptr : p.C,
+                                                p.ldc, p.D, p.ldd, e);
 }
 
 }  // namespace tg

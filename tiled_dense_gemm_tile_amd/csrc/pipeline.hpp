@@ -179,4 +179,23 @@ __device__ __forceinline__ void epilogue_lds16(const f32x4 (&acc)[TM][TN], char 
     epilogue_lds_passes<OUT_BF16, WTM, WTN, 4>(stage, smem, wave, lane, wm, wn, m0, n0, M, N, C, ldc, D, ldd, e);
 }
 
+// Epilogue for transposed 16x16 MFMA blocks acc[i][j] (lane l, register r
+// holds row l % 16 and column 4 (l / 16) + r of block (i, j)); a pass stages
+// two block rows, one 16-byte LDS write per block.
+template <bool OUT_BF16, int TM, int TN, int WTM, int WTN>
+__device__ __forceinline__ void epilogue_lds16t(const f32x4 (&acc)[TM][TN], char *smem, int wave, int lane, int wm,
+                                                int wn, int m0, int n0, int M, int N, const void *C, int64_t ldc,
+                                                void *D, int64_t ldd, F16Epi e) {
+    static_assert(TM * 16 == WTM && TN * 16 == WTN && TM % 2 == 0, "16x16 blocks");
+    constexpr int EP = WTN + 4;
+    const int fr = lane & 15, fq = lane >> 4;
+    auto stage = [&](int p, float *ep) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) *(f32x4 *)(ep + (16 * h + fr) * EP + j * 16 + 4 * fq) = acc[2 * p + h][j];
+    };
+    epilogue_lds_passes<OUT_BF16, WTM, WTN, 4>(stage, smem, wave, lane, wm, wn, m0, n0, M, N, C, ldc, D, ldd, e);
+}
+
 }  // namespace tg

@@ -307,14 +307,15 @@ def test_lane4_configs(cfg, pad, monkeypatch):
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 def test_c_streamed_in_k_loop(cfg, out, monkeypatch):
     """K long enough (>= 34 tiles of 64) that C is added during the K loop
-    instead of in the epilogue: ragged M/N, both output types, and C == D.
-    The four-wave kernels also at the stream's threshold: 18 K tiles (C
-    streamed) and 17 (C added in the epilogue)."""
+    instead of in the epilogue: ragged M/N, both output types, and C == D."""
     monkeypatch.setenv("TILEGEMM_F16_CONFIG", str(cfg))
     M = 300
     cases = [(520, 2304)]
-    if cfg in (12, 13):   # the stream's threshold; N % 4 != 0 (C added in the epilogue)
-        cases += [(520, 1152), (520, 1088), (518, 2304)]
+    if cfg in (12, 13):
+        # the stream's threshold (20 K tiles with a two-slot B ring, 21 with
+        # three), a ragged K with the stream, and N % 4 != 0 (C added in the
+        # epilogue)
+        cases += [(520, 1344), (520, 1280), (520, 1216), (520, 1300), (518, 2304)]
     for N, K, integer in [(n, k, i) for (n, k) in cases for i in (True, False)]:
         x, C = _case("bf16", M, N, K, seed=cfg * 7 + (out == "bf16"), integer=integer)
         A, B = dev16(x["A"], "bf16"), dev16(x["B"], "bf16")

@@ -279,19 +279,27 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
         a_off[j] = (uint32_t)(row * p.lda * 2) + chunk * 16;
         b_off[j] = (uint32_t)(row * p.ldb * 2) + chunk * 16;
     }
-    auto dma_a = [&](int t, int j) __attribute__((always_inline)) {
+    // Loads of K tile t.  SO: the tile is wholly inside K or wholly past it,
+    // so the K offset is uniform and goes in the scalar offset (bit 31 set
+    // past K: every lane reads zeros) and no vector instruction is spent per
+    // load; otherwise (the tile holding a ragged end of K) each lane adds the
+    // K offset and sets bit 31 itself when its chunk lies past K.
+    auto dma = [&](auto so, __amdgpu_buffer_rsrc_t r, char *d, uint32_t voff, int t) __attribute__((always_inline)) {
         const int k0 = t * KT;
-        const uint32_t oob = (uint32_t)(k0 + kel >= K) << 31;   // offsets stay below 2^31
-        char *d = smem + (t % NA) * SLOT + (j * 4 + wave) * IB;
-        const uint32_t off = (a_off[j] + (uint32_t)k0 * 2) | oob;
-        dma_load<16>(rA, d, off);
+        if constexpr (decltype(so)::value) {
+            const int sk = __builtin_amdgcn_readfirstlane((k0 * 2) | ((int)(k0 >= K) << 31));
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)d, 16, voff, sk, 0, 0);
+        } else {
+            const uint32_t oob = (uint32_t)(k0 + kel >= K) << 31;   // offsets stay below 2^31
+            const uint32_t off = (voff + (uint32_t)k0 * 2) | oob;
+            dma_load<16>(r, d, off);
+        }
     };
-    auto dma_b = [&](int t, int j) __attribute__((always_inline)) {
-        const int k0 = t * KT;
-        const uint32_t oob = (uint32_t)(k0 + kel >= K) << 31;
-        char *d = smem + B_BASE + (t % NB) * SLOT + (j * 4 + wave) * IB;
-        const uint32_t off = (b_off[j] + (uint32_t)k0 * 2) | oob;
-        dma_load<16>(rB, d, off);
+    auto dma_a = [&](auto so, int t, int j) __attribute__((always_inline)) {
+        dma(so, rA, smem + (t % NA) * SLOT + (j * 4 + wave) * IB, a_off[j], t);
+    };
+    auto dma_b = [&](auto so, int t, int j) __attribute__((always_inline)) {
+        dma(so, rB, smem + B_BASE + (t % NB) * SLOT + (j * 4 + wave) * IB, b_off[j], t);
     };
 
     // Fragment reads: lane l reads row l % 16 of each block and chunk
@@ -312,7 +320,8 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
     const int nt = (K + KT - 1) / KT;
     // (whole 4-column vectors: every C row segment a lane reads is either in
     // range or past N)
-    const bool c_loop = p.C != nullptr && nt >= CPARTS + 2 && e.vec_c && N % 4 == 0;
+    // (and the stream's tiles load only whole K tiles: see the loop below)
+    const bool c_loop = p.C != nullptr && nt >= CPARTS + 2 + NB && e.vec_c && N % 4 == 0;
     const __amdgpu_buffer_rsrc_t rC =
         make_rsrc(c_loop ? (const char *)p.C + (int64_t)m0 * p.ldc * OS : (const char *)p.D,
                   c_loop ? span_bytes(M - m0, N, p.ldc, OS) : 0u);
@@ -370,15 +379,15 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
     };
     // One tile; FIRST: no previous tile (no deferred MFMAs, accumulators
     // start from zero).  LP: the C part this tile loads (-1: none); AP: the
-    // C part it adds (-1: none).
-    auto tile = [&](auto first, auto lp, auto ap, int t) __attribute__((always_inline)) {
+    // C part it adds (-1: none); SO: the K tiles it loads are whole.
+    auto tile = [&](auto first, auto lp, auto ap, auto so, int t) __attribute__((always_inline)) {
         constexpr int LP = decltype(lp)::value, AP = decltype(ap)::value;
         // step 1 of tile t-1, blocks i = 4..7, with tile t step 0 reads and A loads
 #pragma unroll
         for (int q = 0; q < 32; ++q) {
             if constexpr (!decltype(first)::value) mfma(std::false_type(), 1, 4 + q / TN, q % TN);
             if (q % 2 == 0) read_frag(t, 0, q / 2);
-            if (q % 4 == 1) dma_a(t + NA - 1, q / 4);
+            if (q % 4 == 1) dma_a(so, t + NA - 1, q / 4);
             if constexpr (AP >= 0 && AP < CPARTS / 2) {
                 if (q >= 16 && q < 20) add_c(AP, q - 16);       // blocks of rows 0..63
             }
@@ -388,7 +397,7 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
         for (int q = 0; q < 64; ++q) {
             mfma(first, 0, q / TN, q % TN);
             if (q % 2 == 1 && q < 32) read_frag(t, 1, q / 2);
-            if (q % 4 == 1 && q >= 32) dma_b(t + NB - 1, (q - 32) / 4);
+            if (q % 4 == 1 && q >= 32) dma_b(so, t + NB - 1, (q - 32) / 4);
             if constexpr (AP >= CPARTS / 2) {
                 if (q >= 16 && q < 20) add_c(AP, q - 16);       // blocks of rows 64..127
             }
@@ -413,7 +422,7 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
         constexpr int T = decltype(tc)::value;
         if constexpr (T <= CPARTS + 1) {
             tile(std::false_type(), std::integral_constant<int, (T < CPARTS ? T : -1)>(),
-                 std::integral_constant<int, T - 2>(), T);
+                 std::integral_constant<int, T - 2>(), std::true_type(), T);
             self(self, std::integral_constant<int, T + 1>());
         }
     };
@@ -421,23 +430,34 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
     if (nt > 0) {
         // A(0); B(0) .. B(NB-2): the loads the first tiles' iterations do not issue
 #pragma unroll
-        for (int j = 0; j < LPT; ++j) dma_a(0, j);
+        for (int j = 0; j < LPT; ++j) dma_a(std::false_type(), 0, j);
 #pragma unroll
         for (int b = 0; b < NB - 1; ++b)
 #pragma unroll
-            for (int j = 0; j < LPT; ++j) dma_b(b, j);
+            for (int j = 0; j < LPT; ++j) dma_b(std::false_type(), b, j);
         wait_vmcnt<(NB - 2) * LPT>();                  // A(0), B(0) landed
         barrier();
         using none = std::integral_constant<int, -1>;
-        int t0 = 1;
-        if (c_loop) {
-            tile(std::true_type(), std::integral_constant<int, 0>(), none(), 0);   // loads C part 0
-            c_tiles(c_tiles, std::integral_constant<int, 1>());                    // tiles 1 .. CPARTS + 1
-            t0 = CPARTS + 2;
+        using yes = std::true_type;
+        using no = std::false_type;
+        // Tile t loads K tiles up to t + NB - 1; only the last K tile can be
+        // ragged, so tiles 0 .. nt - NB - 1 take scalar-offset loads and the
+        // last NB tiles the per-lane form.
+        if (nt > NB) {
+            int t0 = 1;
+            if (c_loop) {
+                tile(yes(), std::integral_constant<int, 0>(), none(), yes(), 0);   // loads C part 0
+                c_tiles(c_tiles, std::integral_constant<int, 1>());               // tiles 1 .. CPARTS + 1
+                t0 = CPARTS + 2;
+            } else {
+                tile(yes(), none(), none(), yes(), 0);
+            }
+            for (int t = t0; t < nt - NB; ++t) tile(no(), none(), none(), yes(), t);
+            for (int t = nt - NB; t < nt; ++t) tile(no(), none(), none(), no(), t);
         } else {
-            tile(std::true_type(), none(), none(), 0);
+            tile(yes(), none(), none(), no(), 0);
+            for (int t = 1; t < nt; ++t) tile(no(), none(), none(), no(), t);
         }
-        for (int t = t0; t < nt; ++t) tile(std::false_type(), none(), none(), t);
         // the deferred half of the last tile's step 1
 #pragma unroll
         for (int q = 0; q < 32; ++q) mfma(std::false_type(), 1, 4 + q / TN, q % TN);

@@ -261,7 +261,7 @@ def test_llm_projection_bf16_out():
 
 # ---- every kernel configuration ------------------------------------------------------------
 
-N_DMA_CFGS = 14
+N_DMA_CFGS = 16
 
 
 @pytest.mark.parametrize("cfg", list(range(N_DMA_CFGS)))
@@ -303,7 +303,7 @@ def test_lane4_configs(cfg, pad, monkeypatch):
             _full_check(in_type, x, to_f64(D), integer, C)
 
 
-@pytest.mark.parametrize("cfg", [1, 3, 6, 8, 9, 10, 11, 12, 13])
+@pytest.mark.parametrize("cfg", [1, 3, 6, 8, 9, 10, 11, 12, 13, 14, 15])
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 def test_c_streamed_in_k_loop(cfg, out, monkeypatch):
     """K long enough (>= 34 tiles of 64) that C is added during the K loop
@@ -311,7 +311,7 @@ def test_c_streamed_in_k_loop(cfg, out, monkeypatch):
     monkeypatch.setenv("TILEGEMM_F16_CONFIG", str(cfg))
     M = 300
     cases = [(520, 2304)]
-    if cfg in (12, 13):
+    if cfg in (12, 13, 14, 15):
         # the stream's threshold (20 K tiles with a two-slot B ring, 21 with
         # three), a ragged K with the stream, and N % 4 != 0 (C added in the
         # epilogue)

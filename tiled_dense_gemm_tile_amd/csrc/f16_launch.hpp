@@ -43,12 +43,18 @@ constexpr F16CfgInfo kF16DmaCfgs[] = {TG_F16_DMA_CONFIGS(TG_F16_INFO){256, 256, 
                                       {256, 256, 32, 2, 2, 5, 5},
                                       {256, 256, 32, 2, 2, 4, 4},
                                       {256, 256, 64, 2, 2, 2, 2},
+                                      {256, 256, 64, 2, 2, 2, 3},
+                                      {256, 256, 64, 2, 2, 2, 2},
                                       {256, 256, 64, 2, 2, 2, 3}};
 #undef TG_F16_INFO
 constexpr int kNumF16DmaCfgs = sizeof(kF16DmaCfgs) / sizeof(kF16DmaCfgs[0]);
-constexpr int kF16PingPong32 = kNumF16DmaCfgs - 6, kF16PingPong16 = kNumF16DmaCfgs - 5;
-constexpr int kF16FourWave5 = kNumF16DmaCfgs - 4, kF16FourWave4 = kNumF16DmaCfgs - 3;
-constexpr int kF16FourWaveT22 = kNumF16DmaCfgs - 2, kF16FourWaveT23 = kNumF16DmaCfgs - 1;
+#define TG_F16_COUNT(...) +1
+constexpr int kF16PingPong32 = 0 TG_F16_DMA_CONFIGS(TG_F16_COUNT), kF16PingPong16 = kF16PingPong32 + 1;
+#undef TG_F16_COUNT
+constexpr int kF16FourWave5 = kF16PingPong32 + 2, kF16FourWave4 = kF16PingPong32 + 3;
+constexpr int kF16FourWaveT22 = kF16PingPong32 + 4, kF16FourWaveT23 = kF16PingPong32 + 5;
+constexpr int kF16FourWaveB22 = kF16PingPong32 + 6, kF16FourWaveB23 = kF16PingPong32 + 7;
+static_assert(kF16FourWaveB23 + 1 == kNumF16DmaCfgs, "configuration table");
 
 // Register-staged fallback (any alignment): 128 x 128 x 64 tiles, 4 waves.
 using StagedCfg = TileCfg<128, 128, 64, 2, 2>;
@@ -85,6 +91,14 @@ hipError_t launch_f16_dma<TG_FP16, TG_OUT_BF16>(int cfg, int lane_bytes, unsigne
             hipLaunchKernelGGL((gemm_f16_w4_kernel<5, TG_FP16, TG_OUT_BF16>), dim3(grid), dim3(256), 0, s, p, e);
         else
             hipLaunchKernelGGL((gemm_f16_w4_kernel<4, TG_FP16, TG_OUT_BF16>), dim3(grid), dim3(256), 0, s, p, e);
+        return hipGetLastError();
+    }
+    if (cfg == kF16FourWaveB22 || cfg == kF16FourWaveB23) {
+        if (lane_bytes != 16) return hipErrorInvalidValue;
+        if (cfg == kF16FourWaveB22)
+            hipLaunchKernelGGL((gemm_f16_w4t_kernel<2, 2, TG_FP16, TG_OUT_BF16, 1>), dim3(grid), dim3(256), 0, s, p, e);
+        else
+            hipLaunchKernelGGL((gemm_f16_w4t_kernel<2, 3, TG_FP16, TG_OUT_BF16, 1>), dim3(grid), dim3(256), 0, s, p, e);
         return hipGetLastError();
     }
     if (cfg == kF16FourWaveT22 || cfg == kF16FourWaveT23) {

@@ -236,7 +236,7 @@ __global__ void __launch_bounds__(256) gemm_f16_w4_kernel(F16Args p, F16Epi e) {
 // barrier wait at the end of tile c leaves the part's loads in flight, so
 // they have a whole tile to arrive from memory.  C thus arrives over 16
 // tiles instead of all at the end.
-template <int NA, int NB, bool FP16, bool OUT_BF16>
+template <int NA, int NB, bool FP16, bool OUT_BF16, int SCHED = 0>
 __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) {
     constexpr int BM = 256, BN = 256, KT = 64;         // tile
     constexpr int WTM = 128, WTN = 128, TM = 8, TN = 8;
@@ -382,6 +382,45 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
     // C part it adds (-1: none); SO: the K tiles it loads are whole.
     auto tile = [&](auto first, auto lp, auto ap, auto so, int t) __attribute__((always_inline)) {
         constexpr int LP = decltype(lp)::value, AP = decltype(ap)::value;
+        if constexpr (SCHED == 1) {
+            // Balanced: the whole step 1 of tile t-1 runs after barrier t
+            // while step 0 of tile t is read (one read per 4 MFMAs), then
+            // step 0 of tile t while step 1 is read (one per 3).  NB = 2: A
+            // and B of tile t+1 load in the first half (one per 4 MFMAs);
+            // NB = 3: A(t+1) in the first half, B(t+2) and C in the second.
+            // Block b gets its C at slot (b + 32) % 64 of the first half,
+            // 32 MFMAs from its updates on either side.
+#pragma unroll
+            for (int q = 0; q < 64; ++q) {
+                if constexpr (!decltype(first)::value) mfma(std::false_type(), 1, q / TN, q % TN);
+                if (q % 4 == 0) read_frag(t, 0, q / 4);
+                if constexpr (NB == 3) {
+                    if (q % 8 == 2) dma_a(so, t + 1, q / 8);
+                } else {
+                    if (q % 8 == 2) dma_a(so, t + 1, q / 8);
+                    if (q % 8 == 6) dma_b(so, t + 1, q / 8);
+                }
+                if constexpr (AP >= 0) {
+                    constexpr int s0 = (4 * AP + 32) % 64;
+                    if (q >= s0 && q < s0 + 4) add_c(AP, q - s0);
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < 64; ++q) {
+                mfma(first, 0, q / TN, q % TN);
+                if (q % 3 == 0 && q / 3 < 16) read_frag(t, 1, q / 3);
+                if constexpr (NB == 3) {
+                    if (q % 8 == 2) dma_b(so, t + 2, q / 8);
+                }
+                if constexpr (LP >= 0) {
+                    if (q % 16 == 6) load_c(LP, q / 16);
+                }
+            }
+            wait_vmcnt<WAIT_N + (LP >= 0 ? 4 : 0)>();
+            wait_lgkmcnt0();
+            barrier();
+            return;
+        }
         // step 1 of tile t-1, blocks i = 4..7, with tile t step 0 reads and A loads
 #pragma unroll
         for (int q = 0; q < 32; ++q) {
@@ -458,9 +497,14 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
             tile(yes(), none(), none(), no(), 0);
             for (int t = 1; t < nt; ++t) tile(no(), none(), none(), no(), t);
         }
-        // the deferred half of the last tile's step 1
+        // the deferred part of the last tile's step 1
+        if constexpr (SCHED == 1) {
 #pragma unroll
-        for (int q = 0; q < 32; ++q) mfma(std::false_type(), 1, 4 + q / TN, q % TN);
+            for (int q = 0; q < 64; ++q) mfma(std::false_type(), 1, q / TN, q % TN);
+        } else {
+#pragma unroll
+            for (int q = 0; q < 32; ++q) mfma(std::false_type(), 1, 4 + q / TN, q % TN);
+        }
         mfma_result_fence<TM, TN>(acc);
     } else {
 #pragma unroll

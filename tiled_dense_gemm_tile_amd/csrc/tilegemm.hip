@@ -104,8 +104,8 @@ int pick_f16_cfg(const Common &a, int lane_bytes) {
     if (forced >= 0 && (lane_bytes == 16 || tg::f16_has_lane4(forced))) return forced;
     if (tiles_of(a, 256, 256) >= 240) {
         if (lane_bytes != 16) return 3;
-        // four-wave kernel, 64-wide K tiles, two slots per operand
-        return tg::kF16FourWaveT22;
+        // four-wave kernel, 64-wide K tiles, two slots per operand, balanced schedule
+        return tg::kF16FourWaveB22;
     }
     if (tiles_of(a, 128, 128) >= 240) return 6;
     return 7;

@@ -116,77 +116,80 @@ __global__ void __launch_bounds__(512) gemm_mx_pp_kernel(MxArgs q, F16Epi e) {
     // Register budget: at two waves per SIMD a wave has 256 VGPRs and the
     // accumulators, fragments and scales of a tile take 227 of them; a spill
     // inside the loop would be fatal (a scratch reload waits on vmcnt, i.e.
-    // on every load in flight).  So per-lane constants are not held across
-    // the loop: they are recomputed from the lane index, which passes
-    // through an empty asm so the compiler cannot hoist them back out.
+    // on every load in flight).  So each per-lane address is held as one base
+    // register: the global loads put the row step and the K offset in the
+    // load's scalar offset, and the LDS reads put block and slot offsets in
+    // the instruction's immediate.
+    const int a_row0 = g == 0 ? 128 : 0;                // group 0 loads half 1, group 1 half 0
+    const uint32_t a_step = (uint32_t)(32 * p.lda), b_step = (uint32_t)(32 * p.ldb);
+    // Operand load instruction j of wave s fills rows (4 j + s) * 8 + lane / 8
+    // of its slot: lane L writes physical chunk L % 8 and fetches logical
+    // chunk (L % 8) ^ (L / 8); instruction j adds 32 j rows.
+    const int lchunk = ((lane & 7) ^ (lane >> 3)) << 4;
+    const uint32_t a_base = (uint32_t)((a_row0 + s * 8 + (lane >> 3)) * p.lda) + lchunk;
+    const uint32_t b_base = (uint32_t)((s * 8 + (lane >> 3)) * p.ldb) + lchunk;
+    // Addresses used once per tile or less are recomputed where used from
+    // the lane index, which passes through an empty asm so the compiler
+    // cannot hoist them out of the loop into registers held across it.
     auto lane_id = [&]() __attribute__((always_inline)) {
         int l = lane;
         asm volatile("" : "+v"(l));
         return l;
     };
-    const int a_row0 = g == 0 ? 128 : 0;                // group 0 loads half 1, group 1 half 0
-    const uint32_t a_step = (uint32_t)(32 * p.lda), b_step = (uint32_t)(32 * p.ldb);
-    // Operand load instruction j of wave s fills rows (4 j + s) * 8 + lane / 8
-    // of its slot: lane L writes physical chunk L % 8 and fetches logical
-    // chunk (L % 8) ^ (L / 8); instruction j adds 32 j rows (a scalar step).
-    auto op_off = [&](int64_t ld, int row0) __attribute__((always_inline)) {
-        const int l = lane_id();
-        return (uint32_t)((row0 + s * 8 + (l >> 3)) * ld) + (((l & 7) ^ (l >> 3)) << 4);
-    };
-    // Scale loads (16-byte lanes): for an A half, lanes 0..31 of wave s bring
-    // rows 32 s .. 32 s + 31 (lanes 32..63 read nothing); for B, lanes 0..63
-    // rows 64 s .. 64 s + 63.  Each wave's instruction fills 1 KiB of the slot.
-    auto sa_off = [&]() __attribute__((always_inline)) {
-        const int l = lane_id();
-        return (uint32_t)((a_row0 + 32 * s + (l & 31)) * q.ldsfa) | (l < 32 ? 0u : kOOB);
-    };
-    auto sb_off = [&]() __attribute__((always_inline)) {
-        const int l = lane_id();
-        return (uint32_t)((64 * s + l) * q.ldsfb);
-    };
+    // K tiles and scale groups past K read from a resource of size zero
+    // (every load returns zeros), so no per-lane offset ever leaves the
+    // resource's own range.
+    const __amdgpu_buffer_rsrc_t rZ = make_rsrc(p.A, 0u);
+    const int nep = nblk / 16;                         // scale groups of 512 K
 
     char *const a_fill = smem + (g == 0 ? A1_BASE : A0_BASE);
     char *const sa_fill = smem + (g == 0 ? SA1_BASE : SA0_BASE);
-    // Out-of-range flags are ORed into the offsets (every real offset is
-    // below 2^31), so no load is predicated by a branch.  The offset base
-    // passes through an empty asm each time so the per-instruction offsets are
-    // recomputed here rather than hoisted out of the loop (a dozen more VGPRs
-    // held across the MFMAs).
     auto fetch_a = [&](int t) {                         // this group's A half of K tile t
-        const uint32_t oob = (uint32_t)(t * BK >= K) << 31;
+        const __amdgpu_buffer_rsrc_t r = t < nk ? rA : rZ;
         char *dst = a_fill + (t & 1) * AH_BYTES + s * IB;
-        const uint32_t ao = op_off(p.lda, a_row0);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const uint32_t off = (ao + j * a_step + (uint32_t)(t * BK)) | oob;
-            dma_load<16>(rA, dst + j * 4 * IB, off);
+            const int so = (int)(j * a_step) + t * BK;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)(dst + j * 4 * IB), 16,
+                                                     a_base, so, 0, 0);
         }
     };
     auto fetch_b = [&](int t) {                         // group 0 only
-        const uint32_t oob = (uint32_t)(t * BK >= K) << 31;
+        const __amdgpu_buffer_rsrc_t r = t < nk ? rB : rZ;
         char *dst = smem + B_BASE + (t & 1) * B_BYTES + s * IB;
-        const uint32_t bo = op_off(p.ldb, 0);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const uint32_t off = (bo + j * b_step + (uint32_t)(t * BK)) | oob;
-            dma_load<16>(rB, dst + j * 4 * IB, off);
+            const int so = (int)(j * b_step) + t * BK;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)(dst + j * 4 * IB), 16,
+                                                     b_base, so, 0, 0);
         }
     };
     // Scales of epoch ep (tiles 4 ep .. 4 ep + 3): group 0 loads B's and A
-    // half 1's, group 1 A half 0's.  Bytes past a row's last block are stale
-    // or zero and only ever scale zero tiles (see the tile mask below).
+    // half 1's, group 1 A half 0's.
+    // Scale loads (16-byte lanes): for an A half, lanes 0..31 of wave s bring
+    // rows 32 s .. 32 s + 31 (lanes 32..63 read nothing); for B, lanes 0..63
+    // rows 64 s .. 64 s + 63.  Each wave's instruction fills 1 KiB of the slot.
     auto fetch_scales = [&](int ep) {
-        const uint32_t eoff = (uint32_t)(ep * 16);
+        const int so = ep * 16;
+        const int l = lane_id();
+        const uint32_t sa_base = (uint32_t)((a_row0 + 32 * s + (l & 31)) * q.ldsfa) | (l < 32 ? 0u : kOOB);
+        const uint32_t sb_base = (uint32_t)((64 * s + l) * q.ldsfb);
         if (g == 0) {
-            const uint32_t off = sb_off() + eoff;
-            dma_load<16>(rSB, smem + SB_BASE + (ep & 1) * SS + s * IB, off);
+            const __amdgpu_buffer_rsrc_t r = ep < nep ? rSB : rZ;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)(smem + SB_BASE + (ep & 1) * SS + s * IB),
+                                                     16, sb_base, so, 0, 0);
         }
-        const uint32_t off = sa_off() + eoff;
-        dma_load<16>(rSA, sa_fill + (ep & 1) * SS + s * IB, off);
+        const __amdgpu_buffer_rsrc_t r = ep < nep ? rSA : rZ;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)(sa_fill + (ep & 1) * SS + s * IB),
+                                                 16, sa_base, so, 0, 0);
     };
 
     // Fragment reads: lane l reads row l % 16 of each block, chunks q and
     // 4 + q (q = l / 16), and the scale byte of (that row, K block q).
+    const int fr = lane & 15, fq = lane >> 4;
+    const int c0 = (fq ^ swz16(fr)) << 4;              // chunk q; chunk 4 + q is c0 ^ 64
+    const int la0 = (g == 0 ? A0_BASE : A1_BASE) + fr * ROWB + c0, la1 = la0 ^ 64;
+    const int lb0 = B_BASE + (s * WTN + fr) * ROWB + c0, lb1 = lb0 ^ 64;
 
     f32x4 acc[TM][TN];
 #pragma unroll
@@ -201,38 +204,37 @@ __global__ void __launch_bounds__(512) gemm_mx_pp_kernel(MxArgs q, F16Epi e) {
     // scale bytes packed four to a register: block i of A is byte i % 4 of
     // sa[i / 4], block j of B byte j of sb (the MFMA's op_sel picks the byte)
     uint32_t sa[TM / 4], sb;
-    // (row0: this lane's row of the block with chunk q applied; chunk 4 + q
-    // is chunk q ^ 4, 64 bytes away in either direction)
-    auto ld32 = [&](const char *row0, const char *row1) {
-        const u32x4 lo = *(const u32x4 *)row0;
-        const u32x4 hi = *(const u32x4 *)row1;
+    auto ld16 = [&](int addr) __attribute__((always_inline)) {
+        return *(const u32x4 *)(smem + addr);
+    };
+    auto ld32 = [&](int a0, int a1) __attribute__((always_inline)) {
+        const u32x4 lo = ld16(a0), hi = ld16(a1);
         return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
     // All fragments and scales of tile t: the scale bytes are read first so
-    // their latency overlaps the fragment reads, and packed last.
+    // their latency overlaps the fragment reads, and packed last.  Every
+    // address is a held base plus a constant (t % 4 is fixed at each call
+    // site) except the scale slot (ep & 1), one addition per tile.
     auto read_frags = [&](int t) {
-        const int l = lane_id();
-        const int fr = l & 15, fq = l >> 4;
-        const int c0 = (fq ^ swz16(fr)) << 4, c1 = c0 ^ 64;
         const int ep = t >> 2, u = t & 3;
-        const char *ssa = smem + (g == 0 ? SA0_BASE : SA1_BASE) + fq + (ep & 1) * SS + u * 4;
-        const char *ssb = smem + SB_BASE + (s * WTN + fr) * 16 + fq + (ep & 1) * SS + u * 4;
+        // scale byte of (row r of the A half, block q of tile u) at
+        // (r / 32) KiB + (r % 32) * 16 + 4 u + q; r = 16 i + fr
+        const int l = lane_id();
+        const int so = (ep & 1) * SS + u * 4 + (l & 15) * 16 + (l >> 4);
+        const int sa_t = (g == 0 ? SA0_BASE : SA1_BASE) + so, sb_t = SB_BASE + s * WTN * 16 + so;
         uint32_t ra[TM], rb[TN];
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            const int r = i * 16 + fr;                 // row of the A half
-            ra[i] = *(const uint8_t *)(ssa + (r >> 5) * IB + (r & 31) * 16);
-        }
+        for (int i = 0; i < TM; ++i)
+            ra[i] = *(const uint8_t *)(smem + sa_t + (i >> 1) * IB + (i & 1) * 256);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) rb[j] = *(const uint8_t *)(ssb + j * 16 * 16);
-        const char *sA = smem + (g == 0 ? A0_BASE : A1_BASE) + fr * ROWB + (t & 1) * AH_BYTES;
-        const char *sB = smem + B_BASE + (s * WTN + fr) * ROWB + (t & 1) * B_BYTES;
+        for (int j = 0; j < TN; ++j) rb[j] = *(const uint8_t *)(smem + sb_t + j * 256);
+        const int oa = (t & 1) * AH_BYTES, ob = (t & 1) * B_BYTES;
         // half of the fragments, then the packing (the raw bytes' registers
         // are freed before the other half is read: fewer VGPRs at the peak)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) fb[j] = ld32(sB + j * 16 * ROWB + c0, sB + j * 16 * ROWB + c1);
+        for (int j = 0; j < TN; ++j) fb[j] = ld32(lb0 + ob + j * 16 * ROWB, lb1 + ob + j * 16 * ROWB);
 #pragma unroll
-        for (int i = 0; i < TM / 2; ++i) fa[i] = ld32(sA + i * 16 * ROWB + c0, sA + i * 16 * ROWB + c1);
+        for (int i = 0; i < TM / 2; ++i) fa[i] = ld32(la0 + oa + i * 16 * ROWB, la1 + oa + i * 16 * ROWB);
         const bool live = t < nk;                      // tiles past K: scale 1.0 (their operands are zero)
 #pragma unroll
         for (int h = 0; h < TM / 4; ++h) {
@@ -242,7 +244,7 @@ __global__ void __launch_bounds__(512) gemm_mx_pp_kernel(MxArgs q, F16Epi e) {
         const uint32_t v = rb[0] | (rb[1] << 8) | (rb[2] << 16) | (rb[3] << 24);
         sb = live ? v : 0x7f7f7f7fu;
 #pragma unroll
-        for (int i = TM / 2; i < TM; ++i) fa[i] = ld32(sA + i * 16 * ROWB + c0, sA + i * 16 * ROWB + c1);
+        for (int i = TM / 2; i < TM; ++i) fa[i] = ld32(la0 + oa + i * 16 * ROWB, la1 + oa + i * 16 * ROWB);
     };
     auto compute = [&]() {
         // (unrolled by hand: the scale-byte selectors must be constants)

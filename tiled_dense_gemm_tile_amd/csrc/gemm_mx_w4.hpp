@@ -1,0 +1,268 @@
+// Block-scaled fp8 D = A.B + C with four waves and
+// v_mfma_scale_f32_16x16x128_f8f6f4, gfx950 (K a multiple of 512).
+//
+// The workgroup computes a 256 x 256 output tile with 4 waves, one per SIMD,
+// each owning a 128 x 128 quadrant as 8 x 8 blocks of 16 x 16 fp32
+// accumulators in AGPRs.  Against the eight-wave ping-pong layout (128 x 64
+// per wave) this reads a third less fragment data from LDS per K tile: per
+// 128-wide K tile a wave reads 32 KiB (A and B rows of its quadrant), the
+// workgroup 128 KiB, next to the 64 KiB the direct global->LDS loads write.
+//
+// Operand placement of the 16x16x128 MFMA (measured with one-hot operands
+// and distinct per-lane scales): lane l supplies row (A) or column (B)
+// l % 16; its bytes 0..15 are K elements [16 q, 16 q + 16) and bytes 16..31
+// are [64 + 16 q, 64 + 16 q + 16) of the 128-wide K tile, q = l / 16; the
+// 32-wide K block b of row r takes its scale from lane 16 b + r.  So lane l
+// reads 16-byte chunks q and 4 + q of its row and the scale byte of (its
+// row, K block q); four blocks' scale bytes share a register, the MFMA's
+// op_sel picks the byte.
+//
+// LDS: A and B rings of two 32 KiB slots (256 rows x 128 bytes, 16-byte
+// chunk c of row r at chunk c ^ (r & 7)), and scales per "epoch" of four K
+// tiles -- 16 bytes per row, the row's 16 blocks of 32 over 512 K -- in two
+// slots per operand (one 16-byte load per row and epoch).
+//
+// Schedule.  Window t is the time between the barriers that open tiles t and
+// t + 1.  In it a wave
+//   - runs the 64 MFMAs of tile t - 1 (row i of blocks: MFMAs 8 i .. 8 i + 7),
+//   - reads tile t's B fragments and scales into the other of two register
+//     buffers, and its A fragments of block row i into the registers of row
+//     i as soon as tile t - 1's row i is done; row 7 alternates between two
+//     registers so its read never waits for the last row,
+//   - issues its quarter of the loads of tile t + 1 (and, in the third window
+//     of an epoch, of the next epoch's scales) into slots freed at barrier t,
+// then waits for its loads and reads and joins barrier t + 1.  K tiles and
+// scale groups past K read from a resource of size zero.
+#pragma once
+
+#include <type_traits>
+
+#include "common.hpp"
+#include "gemm_f16_w4.hpp"
+#include "gemm_mxfp8.hpp"
+#include "pipeline.hpp"
+
+namespace tg {
+
+// f(integral_constant<int, I>) for I = B .. E - 1, each call its own
+// instantiation: the indices are constant expressions however large the body.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F &&f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>());
+        static_for<B + 1, E>(f);
+    }
+}
+
+// One 16x16x128 e4m3 MFMA on an AGPR accumulator block, in place; SA / SB:
+// the byte of each scale register used (encoded in op_sel / op_sel_hi).
+template <int SA, int SB>
+__device__ __forceinline__ void mfma_mx16_acc(f32x4 &acc, const i32x8 &a, const i32x8 &b, uint32_t sa, uint32_t sb) {
+#define TG_STR2(x) #x
+#define TG_STR(x) TG_STR2(x)
+    asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel:[" TG_STR(%c5) "," TG_STR(%c6)
+                 ",0] op_sel_hi:[" TG_STR(%c7) "," TG_STR(%c8) ",0]"
+                 : "+a"(acc)
+                 : "v"(a), "v"(b), "v"(sa), "v"(sb), "n"(SA & 1), "n"(SB & 1), "n"(SA >> 1), "n"(SB >> 1));
+#undef TG_STR
+#undef TG_STR2
+}
+
+template <bool OUT_BF16>
+__global__ void __launch_bounds__(256) gemm_mx_w4_kernel(MxArgs q, F16Epi e) {
+    const F16Args &p = q.g;
+    constexpr int BK = 128, ROWB = 128;                // fp8: one byte per element
+    constexpr int TM = 8, TN = 8, WTM = 128, WTN = 128;
+    constexpr int SLOT = 256 * ROWB;                   // 32 KiB per operand slot
+    constexpr int SS = 256 * 16;                       // one scale slot: 256 rows x 16 bytes
+    constexpr int A_BASE = 0, B_BASE = 2 * SLOT, SA_BASE = 4 * SLOT, SB_BASE = SA_BASE + 2 * SS;
+    constexpr int RING_BYTES = SB_BASE + 2 * SS;
+    constexpr int EPI_BYTES = epilogue_lds_bytes(4, WTN);
+    constexpr int LDS_BYTES = RING_BYTES > EPI_BYTES ? RING_BYTES : EPI_BYTES;
+    constexpr int IB = 1024;                           // one load instruction: 8 rows
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS capacity");
+
+    __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    int tmi, tni;
+    tile_order(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, tmi, tni);
+    const int m0 = tmi * 256, n0 = tni * 256;
+    const int M = p.M, N = p.N, K = p.K;
+    const int nblk = K / 32;
+    const int nk = K / BK, nep = K / 512;
+
+    const __amdgpu_buffer_rsrc_t rA =
+        make_rsrc((const char *)p.A + (int64_t)m0 * p.lda, span_bytes(M - m0, K, p.lda, 1));
+    const __amdgpu_buffer_rsrc_t rB =
+        make_rsrc((const char *)p.B + (int64_t)n0 * p.ldb, span_bytes(N - n0, K, p.ldb, 1));
+    const __amdgpu_buffer_rsrc_t rSA =
+        make_rsrc((const char *)q.SFA + (int64_t)m0 * q.ldsfa, span_bytes(M - m0, nblk, q.ldsfa, 1));
+    const __amdgpu_buffer_rsrc_t rSB =
+        make_rsrc((const char *)q.SFB + (int64_t)n0 * q.ldsfb, span_bytes(N - n0, nblk, q.ldsfb, 1));
+    const __amdgpu_buffer_rsrc_t rZ = make_rsrc(p.A, 0u);
+
+    // Operand loads: instruction j of wave w fills slot rows (4 j + w) * 8 +
+    // lane / 8; lane L writes physical chunk L % 8 and fetches logical chunk
+    // (L % 8) ^ (L / 8).  Row step (32 j rows) and K offset go in the scalar
+    // offset.  Scale loads: lane L of wave w brings row 64 w + L's 16 bytes.
+    const int lchunk = ((lane & 7) ^ (lane >> 3)) << 4;
+    const uint32_t a_base = (uint32_t)((wave * 8 + (lane >> 3)) * p.lda) + lchunk;
+    const uint32_t b_base = (uint32_t)((wave * 8 + (lane >> 3)) * p.ldb) + lchunk;
+    const uint32_t a_step = (uint32_t)(32 * p.lda), b_step = (uint32_t)(32 * p.ldb);
+    auto dma = [&](__amdgpu_buffer_rsrc_t r, int lds, uint32_t voff, int soff) __attribute__((always_inline)) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)(smem + lds), 16, voff,
+                                                 soff, 0, 0);
+    };
+    auto fetch_a = [&](int t, int j) __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t r = t < nk ? rA : rZ;
+        const int so = (int)(j * a_step) + t * BK;
+        dma(r, A_BASE + (t & 1) * SLOT + (j * 4 + wave) * IB, a_base, so);
+    };
+    auto fetch_b = [&](int t, int j) __attribute__((always_inline)) {
+        const __amdgpu_buffer_rsrc_t r = t < nk ? rB : rZ;
+        const int so = (int)(j * b_step) + t * BK;
+        dma(r, B_BASE + (t & 1) * SLOT + (j * 4 + wave) * IB, b_base, so);
+    };
+    // (scale offsets are used once per epoch: recomputed from the lane index,
+    // which passes through an empty asm so they are not held in registers)
+    auto lane_id = [&]() __attribute__((always_inline)) {
+        int l = lane;
+        asm volatile("" : "+v"(l));
+        return l;
+    };
+    auto fetch_scales = [&](int ep) __attribute__((always_inline)) {
+        const int l = lane_id();
+        const int so = ep * 16;
+        const __amdgpu_buffer_rsrc_t ra = ep < nep ? rSA : rZ;
+        const __amdgpu_buffer_rsrc_t rb = ep < nep ? rSB : rZ;
+        dma(ra, SA_BASE + (ep & 1) * SS + wave * IB, (uint32_t)((64 * wave + l) * q.ldsfa), so);
+        dma(rb, SB_BASE + (ep & 1) * SS + wave * IB, (uint32_t)((64 * wave + l) * q.ldsfb), so);
+    };
+
+    // Fragment reads: lane l reads row l % 16 of each block, chunks q and
+    // 4 + q (q = l / 16); rows of a block are 16 apart in the swizzle's
+    // period, so the chunk offsets are the same for every block.
+    const int fr = lane & 15, fq = lane >> 4;
+    const int c0 = (fq ^ swz16(fr)) << 4;              // chunk q; chunk 4 + q is c0 ^ 64
+    const int la0 = A_BASE + (wm * WTM + fr) * ROWB + c0, la1 = la0 ^ 64;
+    const int lb0 = B_BASE + (wn * WTN + fr) * ROWB + c0, lb1 = lb0 ^ 64;
+    auto ld32 = [&](int a0, int a1) __attribute__((always_inline)) {
+        const u32x4 lo = *(const u32x4 *)(smem + a0), hi = *(const u32x4 *)(smem + a1);
+        return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+
+    f32x4 acc[TM][TN];
+    i32x8 fa[TM], fx;                                  // A fragments; fx: row 7 of odd tiles
+    i32x8 fb[2][TN];                                   // B fragments by tile parity
+    uint32_t sa[2][2], sb[2][2];                       // scale bytes by tile parity, 4 blocks each
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    mfma_result_fence<TM, TN>(acc);                    // the zeroing before the first MFMA reads them
+
+    // Reads of tile t, whose position in its epoch U = t % 4 is a
+    // compile-time constant at every call site (the loop advances by whole
+    // epochs), so register buffers are chosen by constant parity.
+    // A fragment of block row I:
+    auto read_a = [&](auto uc, auto ic) __attribute__((always_inline)) {
+        constexpr int P = decltype(uc)::value & 1, I = decltype(ic)::value;
+        constexpr int o = P * SLOT + I * 16 * ROWB;
+        const i32x8 v = ld32(la0 + o, la1 + o);
+        if constexpr (I < TM - 1)
+            fa[I] = v;
+        else if constexpr (P)
+            fx = v;
+        else
+            fa[TM - 1] = v;
+    };
+    auto read_b = [&](auto uc, auto jc) __attribute__((always_inline)) {
+        constexpr int P = decltype(uc)::value & 1, J = decltype(jc)::value;
+        constexpr int o = P * SLOT + J * 16 * ROWB;
+        fb[P][J] = ld32(lb0 + o, lb1 + o);
+    };
+    // Scale bytes: row r of the quadrant, K block q of the tile at r * 16 +
+    // 4 U + q of the epoch's slot; four bytes (blocks 4 h' .. 4 h' + 3) per
+    // register.  H: 0, 1 the A registers, 2, 3 the B ones.
+    auto read_scales = [&](auto uc, auto hc, int t) __attribute__((always_inline)) {
+        constexpr int U = decltype(uc)::value, P = U & 1, H = decltype(hc)::value;
+        const int l = lane_id();
+        const int row = (H < 2 ? wm * WTM : wn * WTN) + (l & 15);
+        const int base = (H < 2 ? SA_BASE : SB_BASE) + row * 16 + (l >> 4) + ((t >> 2) & 1) * SS;
+        uint32_t v = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            v |= (uint32_t)(*(const uint8_t *)(smem + base + U * 4 + (H & 1) * 4 * 256 + u * 256)) << (8 * u);
+        if constexpr (H < 2)
+            sa[P][H] = v;
+        else
+            sb[P][H - 2] = v;
+    };
+    // MFMA Q (row Q / 8, column Q % 8) of a tile of parity P
+    auto mfma = [&](auto pc, auto qc) __attribute__((always_inline)) {
+        constexpr int P = decltype(pc)::value, Q = decltype(qc)::value;
+        constexpr int I = Q / TN, J = Q % TN;
+        if constexpr (I < TM - 1 || !P)
+            mfma_mx16_acc<I % 4, J % 4>(acc[I][J], fa[I], fb[P][J], sa[P][I / 4], sb[P][J / 4]);
+        else
+            mfma_mx16_acc<I % 4, J % 4>(acc[I][J], fx, fb[P][J], sa[P][I / 4], sb[P][J / 4]);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // Window t (U = t % 4): MFMAs of tile t - 1 (unless FIRST), reads of
+    // tile t -- B block j at MFMA 4 j, A row 7 at MFMA 3 and row i - 1
+    // during row i, scales at MFMAs 34 .. 46 -- loads of tile t + 1 at every
+    // third MFMA of the first 48, the next epoch's scales when U == 2.
+    auto window = [&](auto first, auto uc, int t) __attribute__((always_inline)) {
+        constexpr bool F = decltype(first)::value;
+        constexpr int U = decltype(uc)::value;
+        if constexpr (U == 2) fetch_scales((t >> 2) + 1);
+        static_for<0, 64>([&](auto qc) __attribute__((always_inline)) {
+            constexpr int Q = decltype(qc)::value;
+            if constexpr (!F) mfma(std::integral_constant<int, (U + 1) & 1>(), qc);
+            if constexpr (Q % 3 == 1 && Q / 3 < 16) {
+                constexpr int k = Q / 3;
+                if constexpr (k < 8)
+                    fetch_a(t + 1, k);
+                else
+                    fetch_b(t + 1, k - 8);
+            }
+            if constexpr (Q < 32 && Q % 4 == 0) read_b(uc, std::integral_constant<int, Q / 4>());
+            if constexpr (Q == 3) read_a(uc, std::integral_constant<int, TM - 1>());
+            if constexpr (Q >= 8 && Q % 8 == 3) read_a(uc, std::integral_constant<int, Q / 8 - 1>());
+            if constexpr (Q >= 34 && Q <= 46 && Q % 4 == 2) read_scales(uc, std::integral_constant<int, (Q - 34) / 4>(), t);
+        });
+        wait_vmcnt<0>();
+        wait_lgkmcnt0();
+        barrier();
+    };
+
+    if (nk > 0) {
+        // prologue: tile 0 and the first epoch's scales
+#pragma unroll
+        for (int j = 0; j < 8; ++j) fetch_a(0, j);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) fetch_b(0, j);
+        fetch_scales(0);
+        wait_vmcnt<0>();
+        barrier();
+        window(std::true_type(), std::integral_constant<int, 0>(), 0);
+        // windows 1 .. nk (nk a multiple of 4): tiles 0 .. nk - 1 computed
+        for (int t = 1; t <= nk; t += 4) {
+            window(std::false_type(), std::integral_constant<int, 1>(), t);
+            window(std::false_type(), std::integral_constant<int, 2>(), t + 1);
+            window(std::false_type(), std::integral_constant<int, 3>(), t + 2);
+            window(std::false_type(), std::integral_constant<int, 0>(), t + 3);
+        }
+    }
+    mfma_result_fence<TM, TN>(acc);
+    wait_vmcnt<0>();
+    wait_lgkmcnt0();
+    barrier();
+    epilogue_lds16<OUT_BF16, TM, TN, WTM, WTN>(acc, smem, wave, lane, wm, wn, m0, n0, M, N, p.C, p.ldc, p.D, p.ldd, e);
+}
+
+}  // namespace tg

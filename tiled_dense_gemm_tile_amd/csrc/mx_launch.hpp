@@ -6,6 +6,7 @@
 
 #include "gemm_mxfp8.hpp"
 #include "gemm_mx_pp.hpp"
+#include "gemm_mx_w4.hpp"
 
 namespace tg {
 
@@ -21,11 +22,15 @@ struct MxCfgInfo {
 };
 
 #define TG_MX_INFO(id, bm, bn, wm, wn) {bm, bn, wm, wn},
-// The last id is the ping-pong kernel (256 x 256, 8 waves, 16x16x128 MFMA).
-constexpr MxCfgInfo kMxCfgs[] = {TG_MX_CONFIGS(TG_MX_INFO){256, 256, 2, 4}};
+// Then the ping-pong kernel (256 x 256, 8 waves) and the four-wave kernel
+// (256 x 256, 128 x 128 per wave), both 16x16x128 MFMA, K % 512 == 0.
+constexpr MxCfgInfo kMxCfgs[] = {TG_MX_CONFIGS(TG_MX_INFO){256, 256, 2, 4}, {256, 256, 2, 2}};
 #undef TG_MX_INFO
 constexpr int kNumMxCfgs = sizeof(kMxCfgs) / sizeof(kMxCfgs[0]);
-constexpr int kMxPingPong = kNumMxCfgs - 1;
+#define TG_MX_COUNT(...) +1
+constexpr int kMxPingPong = 0 TG_MX_CONFIGS(TG_MX_COUNT), kMxFourWave = kMxPingPong + 1;
+#undef TG_MX_COUNT
+static_assert(kMxFourWave + 1 == kNumMxCfgs, "configuration table");
 
 template <bool OUT_BF16>
 hipError_t launch_mx(int cfg, unsigned grid, hipStream_t s, const MxArgs &q, const F16Epi &e);
@@ -39,6 +44,10 @@ template <>
 hipError_t launch_mx<TG_OUT_BF16>(int cfg, unsigned grid, hipStream_t s, const MxArgs &q, const F16Epi &e) {
     if (cfg == kMxPingPong) {
         hipLaunchKernelGGL((gemm_mx_pp_kernel<TG_OUT_BF16>), dim3(grid), dim3(512), 0, s, q, e);
+        return hipGetLastError();
+    }
+    if (cfg == kMxFourWave) {
+        hipLaunchKernelGGL((gemm_mx_w4_kernel<TG_OUT_BF16>), dim3(grid), dim3(256), 0, s, q, e);
         return hipGetLastError();
     }
     switch (cfg) {

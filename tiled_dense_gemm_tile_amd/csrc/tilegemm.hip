@@ -176,15 +176,16 @@ gemm_status dispatch_mx(const Common &a, const void *SFA, int64_t ldsfa, const v
                       a.ldb % 16 == 0 && (uintptr_t)SFA % 4 == 0 && (uintptr_t)SFB % 4 == 0 && ldsfa % 4 == 0 &&
                       ldsfb % 4 == 0;
     if (!fast && a.K > 0) return GEMM_ERR_UNSUPPORTED;
-    // The ping-pong kernel loads a row's scales 16 bytes (512 K) at a time,
-    // so it needs 16-byte-aligned scale rows and whole groups of 16 blocks.
+    // The four-wave and ping-pong kernels load a row's scales 16 bytes (512
+    // K) at a time, so they need 16-byte-aligned scale rows and whole groups
+    // of 16 blocks.
     const bool scales16 = a.K % 512 == 0 && (uintptr_t)SFA % 16 == 0 && (uintptr_t)SFB % 16 == 0 &&
                           ldsfa % 16 == 0 && ldsfb % 16 == 0;
     int cfg = forced_mx_cfg();
-    if (cfg == tg::kMxPingPong && !scales16) cfg = -1;
+    if ((cfg == tg::kMxPingPong || cfg == tg::kMxFourWave) && !scales16) cfg = -1;
     if (cfg < 0) {
         if (tiles_of(a, 256, 256) >= 240)
-            cfg = scales16 ? tg::kMxPingPong : 1;
+            cfg = scales16 ? tg::kMxFourWave : 1;
         else
             cfg = tiles_of(a, 128, 128) >= 240 ? 2 : 3;
     }

@@ -236,7 +236,7 @@ __global__ void __launch_bounds__(256) gemm_f16_w4_kernel(F16Args p, F16Epi e) {
 // barrier wait at the end of tile c leaves the part's loads in flight, so
 // they have a whole tile to arrive from memory.  C thus arrives over 16
 // tiles instead of all at the end.
-template <int NA, int NB, bool FP16, bool OUT_BF16, int SCHED = 0>
+template <int NA, int NB, bool FP16, bool OUT_BF16, int SCHED = 0, int DAUX = kStoreStream>
 __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) {
     constexpr int BM = 256, BN = 256, KT = 64;         // tile
     constexpr int WTM = 128, WTN = 128, TM = 8, TN = 8;
@@ -516,7 +516,7 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
     wait_vmcnt<0>();
     wait_lgkmcnt0();
     barrier();
-    epilogue_lds16t<OUT_BF16, TM, TN, WTM, WTN>(acc, smem, wave, lane, wm, wn, m0, n0, M, N, c_loop ? nullptr : p.C,
+    epilogue_lds16t<OUT_BF16, TM, TN, WTM, WTN, DAUX>(acc, smem, wave, lane, wm, wn, m0, n0, M, N, c_loop ? nullptr : p.C,
                                                 p.ldc, p.D, p.ldd, e);
 }
 

@@ -68,7 +68,7 @@ __device__ __forceinline__ void mfma_mx16_acc(f32x4 &acc, const i32x8 &a, const 
 #undef TG_STR2
 }
 
-template <bool OUT_BF16>
+template <bool OUT_BF16, int DAUX = kStoreStream>
 __global__ void __launch_bounds__(256) gemm_mx_w4_kernel(MxArgs q, F16Epi e) {
     const F16Args &p = q.g;
     constexpr int BK = 128, ROWB = 128;                // fp8: one byte per element
@@ -262,7 +262,7 @@ __global__ void __launch_bounds__(256) gemm_mx_w4_kernel(MxArgs q, F16Epi e) {
     wait_vmcnt<0>();
     wait_lgkmcnt0();
     barrier();
-    epilogue_lds16<OUT_BF16, TM, TN, WTM, WTN>(acc, smem, wave, lane, wm, wn, m0, n0, M, N, p.C, p.ldc, p.D, p.ldd, e);
+    epilogue_lds16<OUT_BF16, TM, TN, WTM, WTN, DAUX>(acc, smem, wave, lane, wm, wn, m0, n0, M, N, p.C, p.ldc, p.D, p.ldd, e);
 }
 
 }  // namespace tg

@@ -45,6 +45,7 @@ struct F16Epi {
 constexpr int epilogue_lds_bytes(int nwaves, int wtn) { return nwaves * 32 * (wtn + 8) * 4; }
 
 // D = acc + C for one wave's WTM x WTN block of a tile, in WTM / 32 passes
+// (DAUX: cache-policy bits of the D stores)
 // of 32 rows.  stage(pass, ep) writes the accumulators of rows
 // [32 pass, 32 pass + 32) of the wave block into this wave's private LDS
 // area ep (row-major, pitch WTN + PAD floats, PAD chosen by the stager so
@@ -53,7 +54,7 @@ constexpr int epilogue_lds_bytes(int nwaves, int wtn) { return nwaves * 32 * (wt
 // C is read and D written with whole-vector accesses where the row and
 // alignment allow, element-wise at the right edge.
 // The caller guarantees every wave is done with the LDS it reuses.
-template <bool OUT_BF16, int WTM, int WTN, int PAD, class Stage>
+template <bool OUT_BF16, int WTM, int WTN, int PAD, int DAUX = 0, class Stage>
 __device__ __forceinline__ void epilogue_lds_passes(Stage &&stage, char *smem, int wave, int lane, int wm, int wn,
                                                     int m0, int n0, int M, int N, const void *C, int64_t ldc,
                                                     void *D, int64_t ldd, F16Epi e) {
@@ -116,23 +117,23 @@ __device__ __forceinline__ void epilogue_lds_passes(Stage &&stage, char *smem, i
                     u32x2 pk;
                     pk[0] = pack_bf16x2(o[0], o[1]);
                     pk[1] = pack_bf16x2(o[2], o[3]);
-                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, pk), rD, doff, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, pk), rD, doff, 0, DAUX);
                 } else {
                     u32x4 pk;
                     pk[0] = __builtin_bit_cast(uint32_t, o[0]);
                     pk[1] = __builtin_bit_cast(uint32_t, o[1]);
                     pk[2] = __builtin_bit_cast(uint32_t, o[2]);
                     pk[3] = __builtin_bit_cast(uint32_t, o[3]);
-                    __builtin_amdgcn_raw_buffer_store_b128(pk, rD, doff, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b128(pk, rD, doff, 0, DAUX);
                 }
             } else {
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
                     const uint32_t doff = (rin && gcol + u < N) ? (uint32_t)(row * ldd + gcol + u) * OS : kOOB;
                     if constexpr (OUT_BF16)
-                        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(o[u]), rD, doff, 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(o[u]), rD, doff, 0, DAUX);
                     else
-                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o[u]), rD, doff, 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, o[u]), rD, doff, 0, DAUX);
                 }
             }
         }
@@ -161,7 +162,7 @@ __device__ __forceinline__ void epilogue_lds(const f32x16 (&acc)[TM][TN], char *
 
 // Epilogue for 16x16 MFMA accumulators acc[i][j] (lane l, register r holds
 // row 4*(l/16) + r and column l%16 of block (i, j)); a pass stages two block rows.
-template <bool OUT_BF16, int TM, int TN, int WTM, int WTN>
+template <bool OUT_BF16, int TM, int TN, int WTM, int WTN, int DAUX = 0>
 __device__ __forceinline__ void epilogue_lds16(const f32x4 (&acc)[TM][TN], char *smem, int wave, int lane, int wm,
                                                int wn, int m0, int n0, int M, int N, const void *C, int64_t ldc,
                                                void *D, int64_t ldd, F16Epi e) {
@@ -176,13 +177,13 @@ __device__ __forceinline__ void epilogue_lds16(const f32x4 (&acc)[TM][TN], char 
 #pragma unroll
                 for (int r = 0; r < 4; ++r) ep[(16 * h + 4 * fq + r) * EP + j * 16 + fc] = acc[2 * p + h][j][r];
     };
-    epilogue_lds_passes<OUT_BF16, WTM, WTN, 4>(stage, smem, wave, lane, wm, wn, m0, n0, M, N, C, ldc, D, ldd, e);
+    epilogue_lds_passes<OUT_BF16, WTM, WTN, 4, DAUX>(stage, smem, wave, lane, wm, wn, m0, n0, M, N, C, ldc, D, ldd, e);
 }
 
 // Epilogue for transposed 16x16 MFMA blocks acc[i][j] (lane l, register r
 // holds row l % 16 and column 4 (l / 16) + r of block (i, j)); a pass stages
 // two block rows, one 16-byte LDS write per block.
-template <bool OUT_BF16, int TM, int TN, int WTM, int WTN>
+template <bool OUT_BF16, int TM, int TN, int WTM, int WTN, int DAUX = 0>
 __device__ __forceinline__ void epilogue_lds16t(const f32x4 (&acc)[TM][TN], char *smem, int wave, int lane, int wm,
                                                 int wn, int m0, int n0, int M, int N, const void *C, int64_t ldc,
                                                 void *D, int64_t ldd, F16Epi e) {
@@ -195,7 +196,7 @@ __device__ __forceinline__ void epilogue_lds16t(const f32x4 (&acc)[TM][TN], char
 #pragma unroll
             for (int j = 0; j < TN; ++j) *(f32x4 *)(ep + (16 * h + fr) * EP + j * 16 + 4 * fq) = acc[2 * p + h][j];
     };
-    epilogue_lds_passes<OUT_BF16, WTM, WTN, 4>(stage, smem, wave, lane, wm, wn, m0, n0, M, N, C, ldc, D, ldd, e);
+    epilogue_lds_passes<OUT_BF16, WTM, WTN, 4, DAUX>(stage, smem, wave, lane, wm, wn, m0, n0, M, N, C, ldc, D, ldd, e);
 }
 
 }  // namespace tg

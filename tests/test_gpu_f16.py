@@ -337,3 +337,44 @@ def test_c_streamed_in_k_loop(cfg, out, monkeypatch):
             torch.cuda.synchronize()
             _full_check("bf16", x, to_f64(D), integer, C)
             assert torch.equal(D, inplace)
+
+
+# ---- rows only 8-byte aligned: the shifted-row four-wave kernel ---------------------------
+
+N_SHIFTED_CFG = 16
+
+
+@pytest.mark.parametrize("case", [
+    # M, N, K, pad (lda = ldb = K + pad), element offset of A and B, C, output
+    (520, 300, 4100, 0, 0, True, "f32"),     # packed 8-byte rows, ragged last K tile (fix-up)
+    (300, 520, 4100, 0, 4, True, "f32"),     # operands start 8 bytes past a 16-byte boundary
+    (257, 260, 36, 0, 0, True, "f32"),       # one ragged K tile (fix-up in the prologue)
+    (257, 260, 100, 4, 0, False, "f32"),     # two K tiles, padded rows
+    (256, 256, 320, 4, 4, True, "f32"),      # K a multiple of 64, 8-byte rows
+    (300, 520, 2308, 0, 0, True, "f32"),     # C streamed in the K loop
+    (300, 520, 2308, 0, 0, True, "bf16"),
+])
+def test_shifted_rows(case, monkeypatch):
+    monkeypatch.setenv("TILEGEMM_F16_CONFIG", str(N_SHIFTED_CFG))
+    M, N, K, pad, off, with_c, out = case
+    for in_type in ("fp16", "bf16"):
+        for integer in (True, False):
+            x, C = _case(in_type, M, N, K, seed=M + K + pad + off, integer=integer, with_c=with_c)
+            ld = K + pad
+            Ab = np.zeros(off + M * ld, np.uint16); Ab[off:].reshape(M, ld)[:, :K] = x["A"]
+            Bb = np.zeros(off + N * ld, np.uint16); Bb[off:].reshape(N, ld)[:, :K] = x["B"]
+            A = dev16(Ab, in_type)[off:].view(M, ld)[:, :K]
+            B = dev16(Bb, in_type)[off:].view(N, ld)[:, :K]
+            say("shifted rows %dx%dx%d pad %d off %d C %s %s out %s integer=%s" % (M, N, K, pad, off, with_c, in_type, out, integer))
+            if out == "bf16":
+                Cb = torch.from_numpy(C).to(DEV).to(torch.bfloat16) if with_c else None
+                Cref = Cb.float().cpu().numpy() if with_c else None
+                D16 = run16(in_type, A, B, Cb, out="bf16")
+                D32 = run16(in_type, A, B, torch.from_numpy(Cref).to(DEV) if with_c else None, out="f32")
+                torch.cuda.synchronize()
+                _full_check(in_type, x, to_f64(D32), integer, Cref)
+                assert np.array_equal(bf16_bits(D16), oracle.rne_bf16_f32(D32.cpu().numpy()))
+            else:
+                D = run16(in_type, A, B, torch.from_numpy(C).to(DEV) if with_c else None)
+                torch.cuda.synchronize()
+                _full_check(in_type, x, to_f64(D), integer, C if with_c else None)

@@ -45,7 +45,8 @@ constexpr F16CfgInfo kF16DmaCfgs[] = {TG_F16_DMA_CONFIGS(TG_F16_INFO){256, 256, 
                                       {256, 256, 64, 2, 2, 2, 2},
                                       {256, 256, 64, 2, 2, 2, 3},
                                       {256, 256, 64, 2, 2, 2, 2},
-                                      {256, 256, 64, 2, 2, 2, 3}};
+                                      {256, 256, 64, 2, 2, 2, 3},
+                                      {256, 256, 64, 2, 2, 2, 2}};
 #undef TG_F16_INFO
 constexpr int kNumF16DmaCfgs = sizeof(kF16DmaCfgs) / sizeof(kF16DmaCfgs[0]);
 #define TG_F16_COUNT(...) +1
@@ -54,7 +55,11 @@ constexpr int kF16PingPong32 = 0 TG_F16_DMA_CONFIGS(TG_F16_COUNT), kF16PingPong1
 constexpr int kF16FourWave5 = kF16PingPong32 + 2, kF16FourWave4 = kF16PingPong32 + 3;
 constexpr int kF16FourWaveT22 = kF16PingPong32 + 4, kF16FourWaveT23 = kF16PingPong32 + 5;
 constexpr int kF16FourWaveB22 = kF16PingPong32 + 6, kF16FourWaveB23 = kF16PingPong32 + 7;
-static_assert(kF16FourWaveB23 + 1 == kNumF16DmaCfgs, "configuration table");
+// The balanced four-wave kernel for rows that are only 8-byte aligned.
+constexpr int kF16FourWaveS = kF16PingPong32 + 8;
+static_assert(kF16FourWaveS + 1 == kNumF16DmaCfgs, "configuration table");
+// Configurations that take rows only 4- or 8-byte aligned.
+constexpr bool f16_any_rows(int id) { return f16_has_lane4(id) || id == kF16FourWaveS; }
 
 // Register-staged fallback (any alignment): 128 x 128 x 64 tiles, 4 waves.
 using StagedCfg = TileCfg<128, 128, 64, 2, 2>;
@@ -91,6 +96,12 @@ hipError_t launch_f16_dma<TG_FP16, TG_OUT_BF16>(int cfg, int lane_bytes, unsigne
             hipLaunchKernelGGL((gemm_f16_w4_kernel<5, TG_FP16, TG_OUT_BF16>), dim3(grid), dim3(256), 0, s, p, e);
         else
             hipLaunchKernelGGL((gemm_f16_w4_kernel<4, TG_FP16, TG_OUT_BF16>), dim3(grid), dim3(256), 0, s, p, e);
+        return hipGetLastError();
+    }
+    if (cfg == kF16FourWaveS) {
+        // (lane_bytes 16 or 4: rows 16- or 8-byte aligned)
+        hipLaunchKernelGGL((gemm_f16_w4t_kernel<2, 2, TG_FP16, TG_OUT_BF16, 1, kStoreStream, true>), dim3(grid),
+                           dim3(256), 0, s, p, e);
         return hipGetLastError();
     }
     if (cfg == kF16FourWaveB22 || cfg == kF16FourWaveB23) {

@@ -236,20 +236,22 @@ __global__ void __launch_bounds__(256) gemm_f16_w4_kernel(F16Args p, F16Epi e) {
 // barrier wait at the end of tile c leaves the part's loads in flight, so
 // they have a whole tile to arrive from memory.  C thus arrives over 16
 // tiles instead of all at the end.
-template <int NA, int NB, bool FP16, bool OUT_BF16, int SCHED = 0, int DAUX = kStoreStream>
+template <int NA, int NB, bool FP16, bool OUT_BF16, int SCHED = 0, int DAUX = kStoreStream, bool SH = false>
 __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) {
     constexpr int BM = 256, BN = 256, KT = 64;         // tile
     constexpr int WTM = 128, WTN = 128, TM = 8, TN = 8;
-    constexpr int ROWB = KT * 2;                       // 128-byte LDS rows
-    constexpr int SLOT = 256 * ROWB;                   // 32 KiB per operand slot
+    // SH: rows only 8-byte aligned (see the row layout below): 144-byte rows
+    constexpr int ROWB = SH ? KT * 2 + 16 : KT * 2;    // 128-byte LDS rows
+    constexpr int SLOT = 256 * ROWB;                   // 32 KiB per operand slot (36 KiB with SH)
     constexpr int B_BASE = NA * SLOT;
     constexpr int RING_BYTES = (NA + NB) * SLOT;
     constexpr int EPI_BYTES = 4 * 32 * (WTN + 8) * 4;
     constexpr int LDS_BYTES = RING_BYTES > EPI_BYTES ? RING_BYTES : EPI_BYTES;
     constexpr int IB = 1024;                           // one load instruction: 8 rows
-    constexpr int LPT = 8;                             // load instructions per wave per operand per tile
+    constexpr int LPT = SH ? 9 : 8;                    // load instructions per wave per operand per tile
     constexpr int WAIT_N = (NB - NA) * LPT;            // B loads still in flight at a barrier
     static_assert(NA == 2 && (NB == 2 || NB == 3) && LDS_BYTES <= 160 * 1024, "ring");
+    static_assert(!SH || (NB == 2 && SCHED == 1), "shifted rows: balanced schedule, two B slots");
 
     __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
 
@@ -262,52 +264,127 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
     const int m0 = tmi * BM, n0 = tni * BN;
     const int M = p.M, N = p.N, K = p.K;
 
-    const __amdgpu_buffer_rsrc_t rA =
-        make_rsrc((const char *)p.A + (int64_t)m0 * p.lda * 2, span_bytes(M - m0, K, p.lda, 2));
-    const __amdgpu_buffer_rsrc_t rB =
-        make_rsrc((const char *)p.B + (int64_t)n0 * p.ldb * 2, span_bytes(N - n0, K, p.ldb, 2));
+    // Tile bases.  With SH the resources start at the 16-byte boundary at or
+    // below the tile's first element (at most 8 bytes earlier, never across a
+    // page boundary, since the element itself lies 8 bytes into its 16).
+    const char *a_tile = (const char *)p.A + (int64_t)m0 * p.lda * 2;
+    const char *b_tile = (const char *)p.B + (int64_t)n0 * p.ldb * 2;
+    const int a_mis0 = SH ? (int)((uintptr_t)a_tile & 15) : 0;
+    const int b_mis0 = SH ? (int)((uintptr_t)b_tile & 15) : 0;
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(a_tile - a_mis0, span_bytes(M - m0, K, p.lda, 2) + a_mis0);
+    const __amdgpu_buffer_rsrc_t rB = make_rsrc(b_tile - b_mis0, span_bytes(N - n0, K, p.ldb, 2) + b_mis0);
 
-    // Load instruction j of a wave fills slot rows (4 j + wave) * 8 + lane / 8:
-    // lane L writes physical chunk L % 8 and fetches logical chunk
-    // (L % 8) ^ swz16(row) = (L % 8) ^ (L / 8), the same for every j.
+    // 16-byte rows (no SH): load instruction j of a wave fills slot rows
+    // (4 j + wave) * 8 + lane / 8: lane L writes physical chunk L % 8 and
+    // fetches logical chunk (L % 8) ^ swz16(row) = (L % 8) ^ (L / 8), the same
+    // for every j.
+    // 8-byte rows (SH): row r starts s = mis0 + r * ld * 2 bytes after the
+    // resource base, s % 16 = 0 or 8.  Its 64-element K tile is fetched as
+    // the nine aligned 16-byte chunks from s & ~15 on, stored as a 144-byte
+    // LDS row, so the tile's data starts (s % 16) bytes into the row.  Load
+    // instruction j of a wave fills slot chunks (4 j + wave) * 64 + lane (row
+    // chunk / 9, chunk chunk % 9), written linearly.  The 144-byte pitch
+    // spreads the 16 rows of a fragment read over all banks without a swizzle.
     const int chunk = (lane & 7) ^ (lane >> 3);
     const int kel = chunk * 8;
     uint32_t a_off[LPT], b_off[LPT];
+    auto sh_row = [&](int j) __attribute__((always_inline)) { return ((4 * j + wave) * 64 + lane) / 9; };
+    auto sh_chk = [&](int j) __attribute__((always_inline)) { return ((4 * j + wave) * 64 + lane) % 9; };
 #pragma unroll
     for (int j = 0; j < LPT; ++j) {
-        const int row = (4 * j + wave) * 8 + (lane >> 3);
-        a_off[j] = (uint32_t)(row * p.lda * 2) + chunk * 16;
-        b_off[j] = (uint32_t)(row * p.ldb * 2) + chunk * 16;
+        if constexpr (SH) {
+            const int row = sh_row(j), c = sh_chk(j);
+            a_off[j] = ((uint32_t)(a_mis0 + row * p.lda * 2) & ~15u) + c * 16;
+            b_off[j] = ((uint32_t)(b_mis0 + row * p.ldb * 2) & ~15u) + c * 16;
+        } else {
+            const int row = (4 * j + wave) * 8 + (lane >> 3);
+            a_off[j] = (uint32_t)(row * p.lda * 2) + chunk * 16;
+            b_off[j] = (uint32_t)(row * p.ldb * 2) + chunk * 16;
+        }
     }
+    // SH: K element (relative to the tile's K offset) at which chunk c of
+    // row r starts: 8 c - (s % 16) / 2, i.e. -4 for the first chunk of a
+    // shifted row.  A chunk reaching past K is read as zeros (a partly
+    // out-of-range load is never issued); if its first half is valid, the
+    // ragged tile's fix-up writes that half afterwards.
+    auto sh_kel = [&](int mis0, int64_t ld, int j) __attribute__((always_inline)) {
+        const int s_ = mis0 + sh_row(j) * (int)ld * 2;
+        return 8 * sh_chk(j) - ((s_ & 15) >> 1);
+    };
     // Loads of K tile t.  SO: the tile is wholly inside K or wholly past it,
     // so the K offset is uniform and goes in the scalar offset (bit 31 set
     // past K: every lane reads zeros) and no vector instruction is spent per
     // load; otherwise (the tile holding a ragged end of K) each lane adds the
     // K offset and sets bit 31 itself when its chunk lies past K.
-    auto dma = [&](auto so, __amdgpu_buffer_rsrc_t r, char *d, uint32_t voff, int t) __attribute__((always_inline)) {
+    auto dma = [&](auto so, __amdgpu_buffer_rsrc_t r, char *d, uint32_t voff, int t, int kelj) __attribute__((always_inline)) {
         const int k0 = t * KT;
         if constexpr (decltype(so)::value) {
             const int sk = __builtin_amdgcn_readfirstlane((k0 * 2) | ((int)(k0 >= K) << 31));
             __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)d, 16, voff, sk, 0, 0);
         } else {
-            const uint32_t oob = (uint32_t)(k0 + kel >= K) << 31;   // offsets stay below 2^31
+            const uint32_t oob = (uint32_t)(SH ? k0 + kelj + 8 > K : k0 + kelj >= K) << 31;   // offsets stay below 2^31
             const uint32_t off = (voff + (uint32_t)k0 * 2) | oob;
             dma_load<16>(r, d, off);
         }
     };
     auto dma_a = [&](auto so, int t, int j) __attribute__((always_inline)) {
-        dma(so, rA, smem + (t % NA) * SLOT + (j * 4 + wave) * IB, a_off[j], t);
+        const int kelj = SH ? sh_kel(a_mis0, p.lda, j) : kel;
+        dma(so, rA, smem + (t % NA) * SLOT + (j * 4 + wave) * IB, a_off[j], t, kelj);
     };
     auto dma_b = [&](auto so, int t, int j) __attribute__((always_inline)) {
-        dma(so, rB, smem + B_BASE + (t % NB) * SLOT + (j * 4 + wave) * IB, b_off[j], t);
+        const int kelj = SH ? sh_kel(b_mis0, p.ldb, j) : kel;
+        dma(so, rB, smem + B_BASE + (t % NB) * SLOT + (j * 4 + wave) * IB, b_off[j], t, kelj);
+    };
+    // SH, last K tile nt - 1 (after its loads landed, before the barrier
+    // that publishes it): each chunk whose first half is inside K and second
+    // half past it was read as zeros; load its valid 8 bytes with an in-range
+    // 8-byte load and write them into the chunk's first half.  Such chunks
+    // exist whether or not K is a multiple of 64 (the ninth chunk of a row
+    // shifted by 8 bytes ends 4 elements past its tile).
+    auto sh_fixup = [&](int t) __attribute__((always_inline)) {
+        const int k0 = t * KT;
+        u32x2 v[2 * LPT];
+#pragma unroll
+        for (int j = 0; j < 2 * LPT; ++j) {
+            const bool isb = j >= LPT;
+            const int jj = isb ? j - LPT : j;
+            const int kelj = isb ? sh_kel(b_mis0, p.ldb, jj) : sh_kel(a_mis0, p.lda, jj);
+            const bool half = kelj >= 0 && k0 + kelj + 4 <= K && k0 + kelj + 8 > K;
+            const uint32_t off = half ? (isb ? b_off[jj] : a_off[jj]) + (uint32_t)k0 * 2 : kOOB;
+            v[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(isb ? rB : rA, off, 0, 0));
+        }
+        wait_vmcnt<0>();
+#pragma unroll
+        for (int j = 0; j < 2 * LPT; ++j) {
+            const bool isb = j >= LPT;
+            const int jj = isb ? j - LPT : j;
+            const int kelj = isb ? sh_kel(b_mis0, p.ldb, jj) : sh_kel(a_mis0, p.lda, jj);
+            const bool half = kelj >= 0 && k0 + kelj + 4 <= K && k0 + kelj + 8 > K;
+            char *d = smem + (isb ? B_BASE + (t % NB) * SLOT : (t % NA) * SLOT) + (jj * 4 + wave) * IB + lane * 16;
+            if (half) *(u32x2 *)d = v[j];
+        }
+        wait_lgkmcnt0();
     };
 
     // Fragment reads: lane l reads row l % 16 of each block and chunk
-    // 4 step + l / 16 of that row.
+    // 4 step + l / 16 of that row.  With SH the row's data starts (s % 16)
+    // bytes into its LDS row -- the same for all rows of a lane (they are 16
+    // apart) -- and a chunk is read as two 8-byte halves.
     const int fr = lane & 15, fq = lane >> 4;
-    const int fswz = swz16(fr);                        // the same for every block (16 rows apart)
-    const int a_read = (wm * WTM + fr) * ROWB;
-    const int b_read = (wn * WTN + fr) * ROWB;
+    const int fswz = SH ? 0 : swz16(fr);               // the same for every block (16 rows apart)
+    const int a_read = (wm * WTM + fr) * ROWB + (SH ? (a_mis0 + fr * (int)p.lda * 2) & 15 : 0);
+    const int b_read = (wn * WTN + fr) * ROWB + (SH ? (b_mis0 + fr * (int)p.ldb * 2) & 15 : 0);
+    auto ldfrag = [&](int addr) __attribute__((always_inline)) {
+        if constexpr (SH) {
+            // two 8-byte reads, kept apart (volatile): merged into one
+            // 16-byte read at an 8-byte-aligned address they cost far more
+            typedef __attribute__((address_space(3))) volatile const u32x2 lds_u32x2;
+            const u32x2 lo = *(lds_u32x2 *)(smem + addr), hi = *(lds_u32x2 *)(smem + addr + 8);
+            return u32x4{lo[0], lo[1], hi[0], hi[1]};
+        } else {
+            return *(const u32x4 *)(smem + addr);
+        }
+    };
 
     // Accumulators in AGPRs, updated in place by volatile asm MFMAs; a
     // scheduling barrier after each keeps the issue order of the source.
@@ -361,10 +438,10 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
         const int coff = ((4 * st + fq) ^ fswz) << 4;
         if (k == 0 || k >= 9) {
             const int i = k == 0 ? 0 : k - 8;
-            fa[st][i] = *(const u32x4 *)(smem + (t % NA) * SLOT + a_read + i * 16 * ROWB + coff);
+            fa[st][i] = ldfrag((t % NA) * SLOT + a_read + i * 16 * ROWB + coff);
         } else {
             const int j = k - 1;
-            fb[st][j] = *(const u32x4 *)(smem + B_BASE + (t % NB) * SLOT + b_read + j * 16 * ROWB + coff);
+            fb[st][j] = ldfrag(B_BASE + (t % NB) * SLOT + b_read + j * 16 * ROWB + coff);
         }
     };
     // B is the MFMA's first operand and A its second, so block (i, j) holds
@@ -394,7 +471,10 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
             for (int q = 0; q < 64; ++q) {
                 if constexpr (!decltype(first)::value) mfma(std::false_type(), 1, q / TN, q % TN);
                 if (q % 4 == 0) read_frag(t, 0, q / 4);
-                if constexpr (NB == 3) {
+                if constexpr (SH) {
+                    if (q % 7 == 1 && q / 7 < LPT) dma_a(so, t + 1, q / 7);
+                    if (q % 7 == 4 && q / 7 < LPT) dma_b(so, t + 1, q / 7);
+                } else if constexpr (NB == 3) {
                     if (q % 8 == 2) dma_a(so, t + 1, q / 8);
                 } else {
                     if (q % 8 == 2) dma_a(so, t + 1, q / 8);
@@ -418,6 +498,9 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
             }
             wait_vmcnt<WAIT_N + (LP >= 0 ? 4 : 0)>();
             wait_lgkmcnt0();
+            if constexpr (SH && !decltype(so)::value) {
+                if (t + 1 == nt - 1) sh_fixup(t + 1);
+            }
             barrier();
             return;
         }
@@ -475,6 +558,9 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
 #pragma unroll
             for (int j = 0; j < LPT; ++j) dma_b(std::false_type(), b, j);
         wait_vmcnt<(NB - 2) * LPT>();                  // A(0), B(0) landed
+        if constexpr (SH) {
+            if (nt == 1) sh_fixup(0);
+        }
         barrier();
         using none = std::integral_constant<int, -1>;
         using yes = std::true_type;

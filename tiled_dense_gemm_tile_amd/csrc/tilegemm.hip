@@ -98,10 +98,18 @@ int forced_f16_cfg() {
     return (id >= 0 && id < tg::kNumF16DmaCfgs) ? id : -1;
 }
 
-// lane_bytes 4 is only built for the configurations f16_has_lane4 names.
-int pick_f16_cfg(const Common &a, int lane_bytes) {
+// lane_bytes 4 (rows 8- or 4-byte aligned) is only built for the
+// configurations f16_any_rows names.  vec: the widest vector in elements
+// that every row allows (8 or 4 here).
+int pick_f16_cfg(const Common &a, int lane_bytes, int vec) {
     const int forced = forced_f16_cfg();
-    if (forced >= 0 && (lane_bytes == 16 || tg::f16_has_lane4(forced))) return forced;
+    if (forced >= 0 && (lane_bytes == 16 || tg::f16_any_rows(forced))) {
+        if (forced != tg::kF16FourWaveS || vec >= 4) return forced;
+    }
+    // 8-byte rows: the shifted-row four-wave kernel once the 256 x 256 grid
+    // fills most of the chip (a 0.75-wave grid of 256 x 256 tiles still
+    // beats three waves of 128 x 128 tiles)
+    if (vec == 4 && tiles_of(a, 256, 256) >= 160) return tg::kF16FourWaveS;
     if (tiles_of(a, 256, 256) >= 240) {
         if (lane_bytes != 16) return 3;
         // four-wave kernel, 64-wide K tiles, two slots per operand, balanced schedule
@@ -132,7 +140,7 @@ gemm_status dispatch_f16(const Common &a, hipStream_t s) {
     const int lane_bytes = vec == 8 ? 16 : 4;
     int bm = tg::StagedCfg::BM, bn = tg::StagedCfg::BN, cfg = -1;
     if (vec >= 2) {
-        cfg = pick_f16_cfg(a, lane_bytes);
+        cfg = pick_f16_cfg(a, lane_bytes, vec);
         bm = tg::kF16DmaCfgs[cfg].bm;
         bn = tg::kF16DmaCfgs[cfg].bn;
     }

@@ -102,7 +102,7 @@ def main():
              "--warmup", str(args.warmup), "--no-cpu-baseline"]
     short = ["python3", "bench.py", "--workload", args.workload, "--steps", "3", "--warmup", "1",
              "--no-cpu-baseline"]
-    kname = "gemm_mxfp8" if "mxfp8" in args.workload else "gemm_f16"
+    kname = "gemm_mx" if "mxfp8" in args.workload else "gemm_f16"
     src_hash = kernel_source_hash()
 
     if not args.skip_trace:

@@ -187,16 +187,21 @@ __global__ void __launch_bounds__(256) gemm_mx_w4_kernel(MxArgs q, F16Epi e) {
     };
     // Scale bytes: row r of the quadrant, K block q of the tile at r * 16 +
     // 4 U + q of the epoch's slot; four bytes (blocks 4 h' .. 4 h' + 3) per
-    // register.  H: 0, 1 the A registers, 2, 3 the B ones.
+    // register.  H: 0, 1 the A registers, 2, 3 the B ones.  The four lanes of
+    // a row read the same dword (one address: no bank conflict, where four
+    // byte reads of one dword conflicted) and each keeps its byte q.
     auto read_scales = [&](auto uc, auto hc, int t) __attribute__((always_inline)) {
         constexpr int U = decltype(uc)::value, P = U & 1, H = decltype(hc)::value;
         const int l = lane_id();
         const int row = (H < 2 ? wm * WTM : wn * WTN) + (l & 15);
-        const int base = (H < 2 ? SA_BASE : SB_BASE) + row * 16 + (l >> 4) + ((t >> 2) & 1) * SS;
+        const int base = (H < 2 ? SA_BASE : SB_BASE) + row * 16 + ((t >> 2) & 1) * SS;
+        const int sh = (l >> 4) * 8;
         uint32_t v = 0;
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-            v |= (uint32_t)(*(const uint8_t *)(smem + base + U * 4 + (H & 1) * 4 * 256 + u * 256)) << (8 * u);
+        for (int u = 0; u < 4; ++u) {
+            const uint32_t d = *(const uint32_t *)(smem + base + U * 4 + (H & 1) * 4 * 256 + u * 256);
+            v |= ((d >> sh) & 0xffu) << (8 * u);
+        }
         if constexpr (H < 2)
             sa[P][H] = v;
         else

@@ -44,8 +44,8 @@ _SRC = os.path.join(_HERE, "oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
 # element type codes, mirrored from oracle.c
-BF16, FP16, E4M3, F32 = 0, 1, 2, 3
-TYPE_CODES = {"bf16": BF16, "fp16": FP16, "e4m3": E4M3, "f32": F32}
+BF16, FP16, E4M3, F32, E2M1 = 0, 1, 2, 3, 4
+TYPE_CODES = {"bf16": BF16, "fp16": FP16, "e4m3": E4M3, "f32": F32, "e2m1": E2M1}
 
 _lock = threading.Lock()
 _lib = None
@@ -79,6 +79,7 @@ def lib():
                                       i64, vp, dp, dp, ctypes.c_int]
             for name, arg in (("orc_dec_bf16", ctypes.c_uint16), ("orc_dec_fp16", ctypes.c_uint16),
                               ("orc_dec_e4m3", ctypes.c_uint8), ("orc_dec_e8m0", ctypes.c_uint8),
+                              ("orc_dec_e2m1", ctypes.c_uint8),
                               ("orc_dec_f32", ctypes.c_uint32)):
                 f = getattr(L, name)
                 f.restype = ctypes.c_double
@@ -109,8 +110,10 @@ def gemm_ref(in_type: str, A, B, K: int | None = None, C=None, c_type: str = "f3
     """D_ref and S = sum_k |a*b| at the requested elements, in float64.
 
     ``A``: (M, lda) raw element bits (uint16 for bf16/fp16, uint8 for e4m3),
-    row-major; ``B``: (N, ldb) raw bits, row n holds column n of the K x N
-    operand; ``K`` defaults to ``A.shape[1]``.  ``C``: (M, ldc) float32 array
+    row-major; for e2m1 (M, lda / 2) bytes, two elements per byte (element
+    2i in the low nibble of byte i); ``B``: (N, ldb) raw bits, row n holds
+    column n of the K x N operand; ``K`` (elements) defaults to the row
+    length.  ``C``: (M, ldc) float32 array
     (``c_type='f32'``) or uint16 bf16 bits (``c_type='bf16'``), or None.
     ``SFA``/``SFB``: (M, ldsfa) / (N, ldsfb) uint8 e8m0 codes, both or neither.
     ``idx``: flat indices ``m*N + n`` (None: every element, row-major).
@@ -122,6 +125,8 @@ def gemm_ref(in_type: str, A, B, K: int | None = None, C=None, c_type: str = "f3
     B = np.ascontiguousarray(B)
     M, lda = A.shape
     N, ldb = B.shape
+    if in_type == "e2m1":                       # leading dimensions in elements
+        lda, ldb = 2 * lda, 2 * ldb
     if K is None:
         K = lda
     if K > lda or K > ldb:
@@ -172,6 +177,19 @@ def dec_e4m3(bits: int) -> float:
     return lib().orc_dec_e4m3(int(bits))
 
 
+def dec_e2m1(bits: int) -> float:
+    return lib().orc_dec_e2m1(int(bits))
+
+
+def unpack_e2m1(packed) -> np.ndarray:
+    """(R, n) bytes of packed e2m1 -> (R, 2n) codes, element 2i from the low nibble of byte i."""
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = p & 0xF
+    out[..., 1::2] = p >> 4
+    return out
+
+
 def dec_e8m0(bits: int) -> float:
     return lib().orc_dec_e8m0(int(bits))
 
@@ -186,8 +204,8 @@ _TABLES: dict = {}
 def decode_table(in_type: str) -> np.ndarray:
     """Full lookup table code -> float64 built from the C decoders."""
     if in_type not in _TABLES:
-        f = {"bf16": dec_bf16, "fp16": dec_fp16, "e4m3": dec_e4m3, "e8m0": dec_e8m0}[in_type]
-        n = 256 if in_type in ("e4m3", "e8m0") else 65536
+        f = {"bf16": dec_bf16, "fp16": dec_fp16, "e4m3": dec_e4m3, "e8m0": dec_e8m0, "e2m1": dec_e2m1}[in_type]
+        n = {"e4m3": 256, "e8m0": 256, "e2m1": 16}.get(in_type, 65536)
         _TABLES[in_type] = np.array([f(i) for i in range(n)], dtype=np.float64)
     return _TABLES[in_type]
 
@@ -224,6 +242,8 @@ def operands_f64(in_type: str, A, B, K=None, SFA=None, SFB=None):
     """Decoded, scaled operands a(m,k) (M x K) and b(k,n) stored as (N x K), float64."""
     A = np.asarray(A)
     B = np.asarray(B)
+    if in_type == "e2m1":
+        A, B = unpack_e2m1(A), unpack_e2m1(B)
     if K is None:
         K = A.shape[1]
     a = decode(in_type, A[:, :K])

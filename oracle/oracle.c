@@ -15,7 +15,8 @@
  *   D[m,n] = c(m,n) + sum_k a(m,k) * b(k,n)
  *   S[m,n] = sum_k |a(m,k) * b(k,n)|          (feeds the error bound)
  *
- * The scale factors are present only for the block-scaled fp8 form.
+ * The scale factors are present only for the block-scaled forms (fp8
+ * e4m3 and fp4 e2m1 elements).
  *
  * Sources on the pages:
  *  - "Tensor Core 数据布局的演进" (Evolution of Tensor Core data layouts),
@@ -38,6 +39,11 @@
  *  - e4m3: OCP FP8 E4M3 ("fn"), 1-4-3, bias 7, no infinities, only
  *          S.1111.111 is NaN, max 448
  *  - e8m0: 8-bit unsigned biased exponent, value 2^(c-127), 0xFF is NaN
+ *  - e2m1: OCP MX FP4, 1-2-1, bias 1, no infinities or NaN: values 0, 0.5,
+ *          1, 1.5, 2, 3, 4, 6 and their negatives; two per byte, element 2i
+ *          in bits 0-3 and element 2i+1 in bits 4-7 of byte i (the block-
+ *          scaled fp4 reading: the pages print no element format; this is
+ *          the OCP microscaling FP4 type and its packing)
  *
  * Build: gcc -O2 -fopenmp -shared -fPIC (no -ffast-math: the sums must be
  * plain IEEE binary64).
@@ -55,6 +61,7 @@ enum {
     ORC_FP16 = 1,
     ORC_E4M3 = 2,
     ORC_F32 = 3,
+    ORC_E2M1 = 4,
 };
 
 enum {
@@ -108,6 +115,19 @@ double orc_dec_e4m3(uint8_t b)
         v = ldexp((double)f, -6 - 3);            /* f/8 * 2^-6 */
     else
         v = ldexp(1.0 + (double)f / 8.0, e - 7);
+    return s ? -v : v;
+}
+
+double orc_dec_e2m1(uint8_t c)
+{
+    int s = (c >> 3) & 1;
+    int e = (c >> 1) & 0x3;
+    int f = c & 0x1;
+    double v;
+    if (e == 0)
+        v = 0.5 * (double)f;                      /* f/2 * 2^(1-1) */
+    else
+        v = ldexp(1.0 + (double)f / 2.0, e - 1);
     return s ? -v : v;
 }
 
@@ -187,6 +207,10 @@ static double dec_elem(int type, const void *base, int64_t i)
     case ORC_BF16: return orc_dec_bf16(((const uint16_t *)base)[i]);
     case ORC_FP16: return orc_dec_fp16(((const uint16_t *)base)[i]);
     case ORC_E4M3: return orc_dec_e4m3(((const uint8_t *)base)[i]);
+    case ORC_E2M1: {
+        uint8_t byte = ((const uint8_t *)base)[i / 2];
+        return orc_dec_e2m1((uint8_t)((i & 1) ? byte >> 4 : byte & 0xF));
+    }
     case ORC_F32: {
         return orc_dec_f32(((const uint32_t *)base)[i]);
     }
@@ -221,8 +245,10 @@ static void one_element(int in_type, int64_t m, int64_t n, int64_t K,
 /*
  * oracle_gemm -- evaluate D_ref and S at chosen output elements.
  *
- *   in_type : ORC_BF16, ORC_FP16 or ORC_E4M3 (A and B share it)
- *   A       : M x K, row-major, leading dimension lda (elements)
+ *   in_type : ORC_BF16, ORC_FP16, ORC_E4M3 or ORC_E2M1 (A and B share it;
+ *             ORC_E2M1 only in the block-scaled form)
+ *   A       : M x K, row-major, leading dimension lda (elements; for
+ *             ORC_E2M1 even, two elements per byte)
  *   B       : column-major K x N stored as N rows of K, leading dim ldb
  *   SFA/SFB : e8m0 codes, M x ceil(K/32) and N x ceil(K/32), row-major
  *             with leading dims ldsfa/ldsfb; both NULL for the unscaled
@@ -244,7 +270,9 @@ int oracle_gemm(int in_type, int64_t M, int64_t N, int64_t K,
 {
     if (M < 0 || N < 0 || K < 0 || n_out < 0)
         return ORC_ERR_ARG;
-    if (in_type != ORC_BF16 && in_type != ORC_FP16 && in_type != ORC_E4M3)
+    if (in_type != ORC_BF16 && in_type != ORC_FP16 && in_type != ORC_E4M3 && in_type != ORC_E2M1)
+        return ORC_ERR_ARG;
+    if (in_type == ORC_E2M1 && (!SFA || lda % 2 != 0 || ldb % 2 != 0))
         return ORC_ERR_ARG;
     if (C && c_type != ORC_F32 && c_type != ORC_BF16)
         return ORC_ERR_ARG;

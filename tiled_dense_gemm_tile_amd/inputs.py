@@ -15,10 +15,15 @@ Draw recipe (the same for every workload):
   form the e4m3 elements are integers in [-4, 4] and the scale exponents lie
   in {0, 1, 2}, so every partial sum stays an integer below 2^24.
 * e8m0 scales: exponent e uniform in {-4..4}, stored code 127 + e.
+* e2m1 (fp4) elements: codes drawn uniformly from all 16 (each value of
+  {0, 0.5, 1, 1.5, 2, 3, 4, 6} and its negative equally likely), packed two
+  per byte with element 2i in the low nibble of byte i; the integer variant
+  draws the same codes with scale exponents in {1, 2}, so every product is
+  an integer and partial sums stay below 2^24 for K up to 16384.
 
 Each workload keeps its operands as raw element codes (uint16 for bf16/fp16,
-uint8 for e4m3/e8m0) plus float32 C, laid out packed (lda = ldb = K,
-ldc = N).
+uint8 for e4m3/e8m0, packed uint8 pairs for e2m1) plus float32 C, laid out
+packed (lda = ldb = K elements, ldc = N).
 """
 from __future__ import annotations
 
@@ -34,13 +39,13 @@ class Workload:
     M: int
     N: int
     K: int
-    in_type: str            # "bf16" | "fp16" | "e4m3"
+    in_type: str            # "bf16" | "fp16" | "e4m3" | "e2m1"
     out_type: str           # "f32" | "bf16"
     dist_a: tuple
     dist_b: tuple
     dist_c: tuple | None    # None: C absent (C = 0, passed as NULL)
     seed: int
-    scaled: bool = False    # block-scaled e4m3 with e8m0 scales per 32 K
+    scaled: bool = False    # block-scaled e4m3 / e2m1 with e8m0 scales per 32 K
     note: str = ""
 
     @property
@@ -49,6 +54,7 @@ class Workload:
 
 
 U11 = ("uniform", -1.0, 1.0)
+CODES = ("codes",)          # e2m1: every 4-bit code equally likely
 
 WORKLOADS = {
     "square256_bf16": Workload("square256_bf16", 256, 256, 256, "bf16", "f32", U11, U11, U11, 0,
@@ -63,6 +69,8 @@ WORKLOADS = {
                               note="M=16384 N=14336 K=4096 bf16, C=0, bf16 out"),
     "mxfp8_8192": Workload("mxfp8_8192", 8192, 8192, 8192, "e4m3", "f32", U11, U11, None, 4,
                            scaled=True, note="M=N=K=8192 e4m3 + e8m0 per 32 K, C=0, fp32 out"),
+    "mxfp4_8192": Workload("mxfp4_8192", 8192, 8192, 8192, "e2m1", "f32", CODES, CODES, None, 5,
+                           scaled=True, note="M=N=K=8192 e2m1 + e8m0 per 32 K, C=0, fp32 out"),
 }
 
 
@@ -89,6 +97,16 @@ def to_codes(x_f32: np.ndarray, in_type: str) -> np.ndarray:
     raise ValueError(in_type)
 
 
+def pack_e2m1(codes: np.ndarray) -> np.ndarray:
+    """(R, 2n) 4-bit codes -> (R, n) bytes, element 2i in the low nibble."""
+    c = np.asarray(codes, dtype=np.uint8)
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+
+
+def _e2m1(rng, shape):
+    return pack_e2m1(rng.integers(0, 16, size=shape).astype(np.uint8))
+
+
 def generate(w: Workload, integer: bool = False, M=None, N=None, K=None, seed=None):
     """Draw a workload's operands.  Sizes and seed may be overridden (for
     reduced-size parity cases of the same recipe).
@@ -101,7 +119,11 @@ def generate(w: Workload, integer: bool = False, M=None, N=None, K=None, seed=No
     K = w.K if K is None else K
     seed = w.seed if seed is None else seed
     rng = np.random.default_rng(seed)
-    if integer:
+    if w.in_type == "e2m1":
+        A, B, C = _e2m1(rng, (M, K)), _e2m1(rng, (N, K)), None
+        if w.dist_c is not None:
+            C = rng.integers(-4, 5, size=(M, N)).astype(np.float32) if integer else _draw(rng, w.dist_c, (M, N))
+    elif integer:
         A = to_codes(rng.integers(-4, 5, size=(M, K)).astype(np.float32), w.in_type)
         B = to_codes(rng.integers(-4, 5, size=(N, K)).astype(np.float32), w.in_type)
         C = rng.integers(-4, 5, size=(M, N)).astype(np.float32) if w.dist_c is not None else None
@@ -113,8 +135,9 @@ def generate(w: Workload, integer: bool = False, M=None, N=None, K=None, seed=No
     if w.scaled:
         nkb = -(-K // 32)
         if integer:
-            SFA = (127 + rng.integers(0, 3, size=(M, nkb))).astype(np.uint8)
-            SFB = (127 + rng.integers(0, 3, size=(N, nkb))).astype(np.uint8)
+            lo, hi = (1, 3) if w.in_type == "e2m1" else (0, 3)
+            SFA = (127 + rng.integers(lo, hi, size=(M, nkb))).astype(np.uint8)
+            SFB = (127 + rng.integers(lo, hi, size=(N, nkb))).astype(np.uint8)
         else:
             SFA = (127 + rng.integers(-4, 5, size=(M, nkb))).astype(np.uint8)
             SFB = (127 + rng.integers(-4, 5, size=(N, nkb))).astype(np.uint8)
@@ -123,7 +146,11 @@ def generate(w: Workload, integer: bool = False, M=None, N=None, K=None, seed=No
 
 
 def random_codes(rng, in_type, shape, integer=False, dist=U11):
-    """Free-standing operand draw (parity sweeps of odd shapes)."""
+    """Free-standing operand draw (parity sweeps of odd shapes).  For e2m1 the
+    codes are uniform (integer or not: the scales make the values integral)
+    and ``shape[-1]`` is the element count, returned packed two per byte."""
+    if in_type == "e2m1":
+        return _e2m1(rng, shape)
     if integer:
         return to_codes(rng.integers(-4, 5, size=shape).astype(np.float32), in_type)
     return to_codes(_draw(rng, dist, shape), in_type)

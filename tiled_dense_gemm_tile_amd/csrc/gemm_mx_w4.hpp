@@ -185,23 +185,28 @@ __global__ void __launch_bounds__(256) gemm_mx_w4_kernel(MxArgs q, F16Epi e) {
         constexpr int o = P * SLOT + J * 16 * ROWB;
         fb[P][J] = ld32(lb0 + o, lb1 + o);
     };
-    // Scale bytes: row r of the quadrant, K block q of the tile at r * 16 +
-    // 4 U + q of the epoch's slot; four bytes (blocks 4 h' .. 4 h' + 3) per
-    // register.  H: 0, 1 the A registers, 2, 3 the B ones.  The four lanes of
-    // a row read the same dword (one address: no bank conflict, where four
-    // byte reads of one dword conflicted) and each keeps its byte q.
-    auto read_scales = [&](auto uc, auto hc, int t) __attribute__((always_inline)) {
-        constexpr int U = decltype(uc)::value, P = U & 1, H = decltype(hc)::value;
-        const int l = lane_id();
-        const int row = (H < 2 ? wm * WTM : wn * WTN) + (l & 15);
-        const int base = (H < 2 ? SA_BASE : SB_BASE) + row * 16 + ((t >> 2) & 1) * SS;
-        const int sh = (l >> 4) * 8;
-        uint32_t v = 0;
+    // Scale bytes: row r of the quadrant, K block q of tile U at byte
+    // r * 16 + 4 U + q of the epoch's slot; four block rows (16 rows apart)
+    // per register, byte u for block row 4 h' + u; H: 0, 1 the A registers,
+    // 2, 3 the B ones.  A register is built from the four rows' dwords with
+    // two v_perm (each keeps byte q of two dwords; the selectors depend only
+    // on q).  The dword reads (scale_issue) and the assembly (scale_finish)
+    // are 8 MFMAs apart through two stages of raw dwords, so the wave does
+    // not wait for LDS reads still in flight.
+    const uint32_t sel_lo = (uint32_t)fq | ((uint32_t)(fq + 4) << 8) | 0x0c0c0000u;   // 0x0c: a zero byte
+    const uint32_t sel_hi = 0x00000c0cu | ((uint32_t)fq << 16) | ((uint32_t)(fq + 4) << 24);
+    uint32_t sraw[2][4];
+    auto scale_issue = [&](auto uc, auto hc, auto gc, int t) __attribute__((always_inline)) {
+        constexpr int U = decltype(uc)::value, H = decltype(hc)::value, G = decltype(gc)::value;
+        const int row = (H < 2 ? wm * WTM : wn * WTN) + fr;
+        const int base = (H < 2 ? SA_BASE : SB_BASE) + row * 16 + ((t >> 2) & 1) * SS + U * 4 + (H & 1) * 4 * 256;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const uint32_t d = *(const uint32_t *)(smem + base + U * 4 + (H & 1) * 4 * 256 + u * 256);
-            v |= ((d >> sh) & 0xffu) << (8 * u);
-        }
+        for (int u = 0; u < 4; ++u) sraw[G][u] = *(const uint32_t *)(smem + base + u * 256);
+    };
+    auto scale_finish = [&](auto uc, auto hc, auto gc) __attribute__((always_inline)) {
+        constexpr int P = decltype(uc)::value & 1, H = decltype(hc)::value, G = decltype(gc)::value;
+        const uint32_t v = __builtin_amdgcn_perm(sraw[G][1], sraw[G][0], sel_lo) |
+                           __builtin_amdgcn_perm(sraw[G][3], sraw[G][2], sel_hi);
         if constexpr (H < 2)
             sa[P][H] = v;
         else
@@ -219,7 +224,8 @@ __global__ void __launch_bounds__(256) gemm_mx_w4_kernel(MxArgs q, F16Epi e) {
     };
     // Window t (U = t % 4): MFMAs of tile t - 1 (unless FIRST), reads of
     // tile t -- B block j at MFMA 4 j, A row 7 at MFMA 3 and row i - 1
-    // during row i, scales at MFMAs 34 .. 46 -- loads of tile t + 1 at every
+    // during row i, scales read at MFMAs 34 .. 46 and assembled 8 MFMAs
+    // later -- loads of tile t + 1 at every
     // third MFMA of the first 48, the next epoch's scales when U == 2.
     auto window = [&](auto first, auto uc, int t) __attribute__((always_inline)) {
         constexpr bool F = decltype(first)::value;
@@ -238,7 +244,14 @@ __global__ void __launch_bounds__(256) gemm_mx_w4_kernel(MxArgs q, F16Epi e) {
             if constexpr (Q < 32 && Q % 4 == 0) read_b(uc, std::integral_constant<int, Q / 4>());
             if constexpr (Q == 3) read_a(uc, std::integral_constant<int, TM - 1>());
             if constexpr (Q >= 8 && Q % 8 == 3) read_a(uc, std::integral_constant<int, Q / 8 - 1>());
-            if constexpr (Q >= 34 && Q <= 46 && Q % 4 == 2) read_scales(uc, std::integral_constant<int, (Q - 34) / 4>(), t);
+            if constexpr (Q >= 42 && Q <= 54 && Q % 4 == 2) {
+                constexpr int c = (Q - 42) / 4;
+                scale_finish(uc, std::integral_constant<int, c>(), std::integral_constant<int, c % 2>());
+            }
+            if constexpr (Q >= 34 && Q <= 46 && Q % 4 == 2) {
+                constexpr int c = (Q - 34) / 4;
+                scale_issue(uc, std::integral_constant<int, c>(), std::integral_constant<int, c % 2>(), t);
+            }
         });
         wait_vmcnt<0>();
         wait_lgkmcnt0();

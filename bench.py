@@ -23,14 +23,14 @@ if ROOT not in sys.path:
 
 METRIC = "GEMM TFLOP/s and % of MI355X MFMA peak (bf16 4096³; mxfp8 8192³)"
 # MI355X published dense peaks (256 CUs at 2.4 GHz), TFLOP/s
-PEAK_TFLOPS = {"bf16": 2516.6, "fp16": 2516.6, "e4m3": 5033.2}
+PEAK_TFLOPS = {"bf16": 2516.6, "fp16": 2516.6, "e4m3": 5033.2, "e2m1": 10066.3}
 
 
 def algorithmic_bytes(w):
     """Bytes the operation must move at least once: A, B, (C), D, (scales)."""
-    es = 1 if w.in_type == "e4m3" else 2
+    es = {"e4m3": 1.0, "e2m1": 0.5}.get(w.in_type, 2.0)
     os_ = 4 if w.out_type == "f32" else 2
-    b = (w.M * w.K + w.N * w.K) * es + w.M * w.N * os_
+    b = int((w.M * w.K + w.N * w.K) * es) + w.M * w.N * os_
     if w.dist_c is not None:
         b += w.M * w.N * os_
     if w.scaled:
@@ -54,7 +54,7 @@ def measured_traffic(w):
 
 def device_inputs(w, x, torch):
     dev = torch.device("cuda:0")
-    if w.in_type == "e4m3":
+    if w.in_type in ("e4m3", "e2m1"):
         A = torch.from_numpy(x["A"]).to(dev)
         B = torch.from_numpy(x["B"]).to(dev)
         extra = (torch.from_numpy(x["SFA"]).to(dev), torch.from_numpy(x["SFB"]).to(dev))
@@ -74,7 +74,9 @@ def cpu_baseline(w, x, target_rows):
     import oracle
     rows = min(target_rows, w.M)
     idx = np.arange(rows * w.N, dtype=np.int64)
-    oracle.gemm_ref(w.in_type, x["A"][:1], x["B"][:1], C=None, idx=np.zeros(1, np.int64))  # load, warm
+    s1 = (lambda s: s[:1] if s is not None else None)
+    oracle.gemm_ref(w.in_type, x["A"][:1], x["B"][:1], C=None, SFA=s1(x["SFA"]), SFB=s1(x["SFB"]),
+                    idx=np.zeros(1, np.int64))  # load, warm
     t0 = time.perf_counter()
     oracle.gemm_ref(w.in_type, x["A"], x["B"], C=x["C"], SFA=x["SFA"], SFB=x["SFB"], idx=idx)
     dt = time.perf_counter() - t0
@@ -130,7 +132,8 @@ def main():
         step = lambda: tg.gemm_fp16(A, B, C, out_dtype=out_dtype, D=D)
     else:
         SFA, SFB = extra
-        step = lambda: tg.gemm_mxfp8(A, SFA, B, SFB, C, out_dtype=out_dtype, D=D)
+        fn = tg.gemm_mxfp8 if w.in_type == "e4m3" else tg.gemm_mxfp4
+        step = lambda: fn(A, SFA, B, SFB, C, out_dtype=out_dtype, D=D)
 
     # The GPU raises its clocks over the first milliseconds of sustained
     # work; a few warmup launches of a ~0.1 ms kernel end before that, so

@@ -124,6 +124,32 @@ gemm_status gemm_mxfp8(int64_t M, int64_t N, int64_t K,
                        void *D, int64_t ldd,
                        int out_type, hipStream_t stream);
 
+/*
+ * gemm_mxfp4 -- block-scaled fp4: D = A.B + C with
+ *     a(m,k) = e2m1(A, m*lda + k) * 2^(SFA[m*ldsfa + k/32] - 127)
+ *     b(k,n) = e2m1(B, n*ldb + k) * 2^(SFB[n*ldsfb + k/32] - 127)
+ * where e2m1(X, i) is the OCP FP4 E2M1 code in byte i/2 of X, low nibble
+ * for even i, high nibble for odd i (values 0, 0.5, 1, 1.5, 2, 3, 4, 6 and
+ * their negatives; no NaN or infinity).
+ * Source: "Tensor Core 数据布局的演进", section Block-Scaled MMA 的 Scale
+ * Factors (the same per-block scaling as gemm_mxfp8 with 4-bit elements).
+ *   A: M x K elements row-major, lda (elements, even)
+ *   B: N x K elements (column-major K x N), ldb (elements, even)
+ *   SFA, SFB, C, D, out_type: as gemm_mxfp8
+ * Sizes, lda and ldb count ELEMENTS (two per byte).  K must be a multiple
+ * of 32 and lda, ldb even; this version also needs K % 512 == 0, A and B
+ * 16-byte aligned, lda and ldb multiples of 32, SFA and SFB 16-byte aligned
+ * and ldsfa, ldsfb multiples of 16, and returns GEMM_ERR_UNSUPPORTED
+ * otherwise.  Byte limits of the shared convention apply to lda/2, ldb/2.
+ * Scale code 0xFF (NaN) gives NaN in the affected outputs.
+ */
+gemm_status gemm_mxfp4(int64_t M, int64_t N, int64_t K,
+                       const void *A, int64_t lda, const void *SFA, int64_t ldsfa,
+                       const void *B, int64_t ldb, const void *SFB, int64_t ldsfb,
+                       const void *C, int64_t ldc,
+                       void *D, int64_t ldd,
+                       int out_type, hipStream_t stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char *gemm_status_string(int status);
 

@@ -23,8 +23,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["gemm_bf16", "gemm_fp16", "gemm_last_hip_error", "gemm_mxfp8",
-                                    "gemm_status_string"]
+    assert declared_functions() == ["gemm_bf16", "gemm_fp16", "gemm_last_hip_error", "gemm_mxfp4",
+                                    "gemm_mxfp8", "gemm_status_string"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -89,6 +89,39 @@ def test_validation_mxfp8():
     assert call8(SFB=None) == NULL_POINTER
     assert call8(lda=32) == BAD_LD
     assert call8(D=None) == NULL_POINTER
+
+
+def call4(M=64, N=64, K=512, A=P, lda=512, SFA=P + 4096, ldsfa=16, B=P, ldb=512, SFB=P + 8192, ldsfb=16,
+          C=None, ldc=0, D=P + (1 << 24), ldd=64, out=F32):
+    return tg.raw.gemm_mxfp4(M, N, K, A, lda, SFA, ldsfa, B, ldb, SFB, ldsfb, C, ldc, D, ldd, out, None)
+
+
+def test_validation_mxfp4():
+    """Every case is refused before anything is launched (lda, ldb, K in
+    elements, two per byte)."""
+    assert call4(M=-1) == INVALID_SIZE
+    assert call4(K=-2) == INVALID_SIZE
+    assert call4(M=0) == OK
+    assert call4(out=3) == UNSUPPORTED
+    assert call4(lda=510) == BAD_LD
+    assert call4(ldb=2) == BAD_LD
+    assert call4(ldd=32) == BAD_LD
+    assert call4(lda=513) == UNSUPPORTED                   # rows must start on a byte
+    assert call4(ldb=515) == UNSUPPORTED
+    assert call4(K=48, lda=64, ldb=64) == UNSUPPORTED       # K not a multiple of 32
+    assert call4(K=256, lda=256, ldb=256) == UNSUPPORTED    # this version: K % 512 == 0
+    assert call4(ldsfa=15) == BAD_LD
+    assert call4(ldsfb=8) == BAD_LD
+    assert call4(SFA=None) == NULL_POINTER
+    assert call4(SFB=None) == NULL_POINTER
+    assert call4(A=None) == NULL_POINTER
+    assert call4(D=None) == NULL_POINTER
+    assert call4(lda=528) == UNSUPPORTED                    # 264-byte rows: not 16-byte multiples
+    assert call4(A=P + 8) == UNSUPPORTED                    # A not 16-byte aligned
+    assert call4(SFA=P + 4100) == UNSUPPORTED               # scales not 16-byte aligned
+    assert call4(ldsfa=20) == UNSUPPORTED
+    assert call4(lda=16 << 20) == UNSUPPORTED               # 8 MiB rows
+    assert call4(K=1 << 31, lda=1 << 31, ldb=1 << 31) == UNSUPPORTED
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -16,7 +16,7 @@ import ctypes
 import os
 import threading
 
-__all__ = ["gemm_bf16", "gemm_fp16", "gemm_mxfp8", "raw", "GemmError", "LibraryMissing",
+__all__ = ["gemm_bf16", "gemm_fp16", "gemm_mxfp8", "gemm_mxfp4", "raw", "GemmError", "LibraryMissing",
            "library_path", "STATUS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -58,8 +58,10 @@ def _load():
             for name in ("gemm_bf16", "gemm_fp16"):
                 f = getattr(L, name)
                 f.restype, f.argtypes = ci, sig16
-            L.gemm_mxfp8.restype = ci
-            L.gemm_mxfp8.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp, i64, ci, vp]
+            for name in ("gemm_mxfp8", "gemm_mxfp4"):
+                f = getattr(L, name)
+                f.restype = ci
+                f.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp, i64, ci, vp]
             L.gemm_status_string.restype = ctypes.c_char_p
             L.gemm_status_string.argtypes = [ci]
             L.gemm_last_hip_error.restype = ci
@@ -165,5 +167,27 @@ def gemm_mxfp8(A, SFA, B, SFB, C=None, out_dtype=None, D=None):
                             B.data_ptr(), _ld(B, K) if K else 0, SFB.data_ptr(), _ld(SFB, nkb) if K else 0,
                             C.data_ptr() if C is not None else None, _ld(C, N) if C is not None else 0,
                             D.data_ptr(), _ld(D, N), out, stream)
+    _check(st)
+    return D
+
+
+def gemm_mxfp4(A, SFA, B, SFB, C=None, out_dtype=None, D=None):
+    """Block-scaled fp4: A (M, K/2), B (N, K/2) uint8 bytes each holding two
+    e2m1 codes (element 2i in the low nibble of byte i; float4_e2m1fn_x2 is
+    accepted too); SFA (M, K/32), SFB (N, K/32) e8m0 codes.  K is twice the
+    byte width of A."""
+    import torch
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    fp4x2 = getattr(torch, "float4_e2m1fn_x2", torch.uint8)
+    M, N, KB, D, stream, out = _prep(A, B, C, D, out_dtype, (torch.uint8, fp4x2))
+    K = 2 * KB
+    for s, rows in ((SFA, M), (SFB, N)):
+        if s.dtype not in (torch.uint8, torch.float8_e8m0fnu) or not s.is_cuda or s.shape[0] != rows:
+            raise ValueError("scale arrays must be uint8/e8m0 device tensors of shape (rows, K/32)")
+    nkb = K // 32
+    st = _load().gemm_mxfp4(M, N, K, A.data_ptr(), 2 * _ld(A, KB) if K else 0, SFA.data_ptr(),
+                            _ld(SFA, nkb) if K else 0, B.data_ptr(), 2 * _ld(B, KB) if K else 0, SFB.data_ptr(),
+                            _ld(SFB, nkb) if K else 0, C.data_ptr() if C is not None else None,
+                            _ld(C, N) if C is not None else 0, D.data_ptr(), _ld(D, N), out, stream)
     _check(st)
     return D

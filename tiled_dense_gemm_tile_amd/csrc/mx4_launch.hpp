@@ -1,0 +1,27 @@
+// Launcher of the block-scaled fp4 GEMM; one instance translation unit per
+// output type (mx4_<out>.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "gemm_mx4_w4.hpp"
+
+namespace tg {
+
+// 256 x 256 tiles, four waves; q.g.lda / q.g.ldb in bytes.
+template <bool OUT_BF16>
+hipError_t launch_mx4(unsigned grid, hipStream_t s, const MxArgs &q, const F16Epi &e);
+
+}  // namespace tg
+
+#ifdef TG_MX4_INSTANCE
+namespace tg {
+
+template <>
+hipError_t launch_mx4<TG_OUT_BF16>(unsigned grid, hipStream_t s, const MxArgs &q, const F16Epi &e) {
+    hipLaunchKernelGGL((gemm_mx4_w4_kernel<TG_OUT_BF16>), dim3(grid), dim3(256), 0, s, q, e);
+    return hipGetLastError();
+}
+
+}  // namespace tg
+#endif

@@ -47,7 +47,7 @@ def measured_traffic(w):
         return None
     with open(path) as f:
         doc = json.load(f)
-    if doc.get("kernel_sources") != kernel_source_hash():
+    if doc.get("kernel_sources") != kernel_source_hash(w.name):
         return None
     return int(round(doc["traffic_bytes_per_launch"]))
 

@@ -36,13 +36,39 @@ CSRC = os.path.join(ROOT, "tiled_dense_gemm_tile_amd", "csrc")
 COPY_MIB = 256
 
 
-def kernel_source_hash() -> str:
+def instance_file(in_type: str, out_type: str) -> str:
+    """The translation unit holding a workload's kernels."""
+    if in_type in ("bf16", "fp16"):
+        return "f16_%s_%s.hip" % (in_type, out_type)
+    return "%s_%s.hip" % ({"e4m3": "mx", "e2m1": "mx4"}[in_type], out_type)
+
+
+def _include_closure(name, seen):
+    if name in seen:
+        return
+    seen.add(name)
+    with open(os.path.join(CSRC, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line.startswith('#include "'):
+                inc = line.split('"')[1]
+                if os.path.exists(os.path.join(CSRC, inc)):
+                    _include_closure(inc, seen)
+
+
+def kernel_source_hash(workload: str) -> str:
+    """Hash of the sources a workload's kernels are built from: its instance
+    file with everything it includes, and the dispatch code."""
+    from tiled_dense_gemm_tile_amd import inputs
+    w = inputs.WORKLOADS[workload]
+    files = set()
+    _include_closure(instance_file(w.in_type, w.out_type), files)
+    files.add("tilegemm.hip")
     h = hashlib.sha256()
-    for f in sorted(os.listdir(CSRC)):
-        if f.endswith((".hip", ".hpp")):
-            h.update(f.encode())
-            with open(os.path.join(CSRC, f), "rb") as fh:
-                h.update(fh.read())
+    for f in sorted(files):
+        h.update(f.encode())
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
     return h.hexdigest()[:16]
 
 
@@ -102,8 +128,8 @@ def main():
              "--warmup", str(args.warmup), "--no-cpu-baseline"]
     short = ["python3", "bench.py", "--workload", args.workload, "--steps", "3", "--warmup", "1",
              "--no-cpu-baseline"]
-    kname = "gemm_mx" if "mxfp8" in args.workload else "gemm_f16"
-    src_hash = kernel_source_hash()
+    kname = "gemm_mx" if "mxfp" in args.workload else "gemm_f16"
+    src_hash = kernel_source_hash(args.workload)
 
     if not args.skip_trace:
         d = os.path.join(args.out_dir, "trace")
@@ -157,9 +183,11 @@ def main():
         print("wrote", out, "traffic %.1f MB per launch" % (total / 1e6))
 
     if not args.skip_counters:
-        mops = "SQ_INSTS_VALU_MFMA_MOPS_F8" if "mxfp8" in args.workload else "SQ_INSTS_VALU_MFMA_MOPS_BF16"
-        passes = [["GRBM_GUI_ACTIVE", "SQ_BUSY_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", mops, "SQ_WAVE_CYCLES",
-                   "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY"],
+        # (no MOPS counter is used for fp4)
+        mops = {"mxfp8": ["SQ_INSTS_VALU_MFMA_MOPS_F8"], "mxfp4": []}.get(args.workload[:5],
+                                                                         ["SQ_INSTS_VALU_MFMA_MOPS_BF16"])
+        passes = [["GRBM_GUI_ACTIVE", "SQ_BUSY_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES"] + mops +
+                  ["SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY"],
                   ["SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_INSTS_LDS", "SQ_WAIT_INST_LDS",
                    "SQ_LDS_ADDR_CONFLICT", "SQ_LDS_UNALIGNED_STALL"],
                   ["TCC_HIT", "TCC_MISS"]]

@@ -98,6 +98,9 @@ def main():
                          "see the clocks the GPU holds under sustained load (0 disables)")
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="rows of D the CPU baseline evaluates (default: about 1.3e10 multiply-adds)")
+    ap.add_argument("--splits", type=int, default=None,
+                    help="16-bit workloads: run the split-K entry point with this many K ranges (0: the "
+                         "library's choice; the default for workloads with fewer than 128 output tiles)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -126,7 +129,18 @@ def main():
     out_dtype = torch.float32 if w.out_type == "f32" else torch.bfloat16
     D = torch.empty((w.M, w.N), dtype=out_dtype, device="cuda:0")
 
-    if w.in_type == "bf16":
+    splits = args.splits
+    if splits is None and w.in_type in ("bf16", "fp16") and ((w.M + 255) // 256) * ((w.N + 255) // 256) < 128:
+        splits = 0
+    kernels_per_step = 1
+    if w.in_type in ("bf16", "fp16") and splits is not None:
+        # split-K: the workspace is allocated once, outside the timed steps
+        fn = tg.gemm_bf16_splitk if w.in_type == "bf16" else tg.gemm_fp16_splitk
+        nbytes = tg.splitk_workspace_bytes(w.M, w.N, w.K, splits)
+        ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda:0") if nbytes else None
+        kernels_per_step = 2 if nbytes else 1
+        step = lambda: fn(A, B, C, out_dtype=out_dtype, D=D, splits=splits, workspace=ws)
+    elif w.in_type == "bf16":
         step = lambda: tg.gemm_bf16(A, B, C, out_dtype=out_dtype, D=D)
     elif w.in_type == "fp16":
         step = lambda: tg.gemm_fp16(A, B, C, out_dtype=out_dtype, D=D)
@@ -156,7 +170,8 @@ def main():
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kernel_ms = ev0.elapsed_time(ev1) / args.steps     # one kernel launch per step
+    # one GEMM launch per step (split-K: the GEMM and the reduction of its partials)
+    kernel_ms = ev0.elapsed_time(ev1) / args.steps
     ms_per_step = wall * 1e3 / args.steps
 
     tflops = w.flops / (kernel_ms * 1e-3) / 1e12
@@ -176,10 +191,11 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "in": w.in_type, "out": w.out_type,
                    "C": "fp32 U[-1,1]" if w.dist_c else "none", "layout": "A row-major, B column-major (N x K)",
-                   "seed": w.seed, "note": w.note},
+                   "seed": w.seed, "note": w.note,
+                   "splits": None if splits is None else (splits or "auto")},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(tflops / peak, 4), "traffic": measured_traffic(w),
-                     "kernel_ms": round(kernel_ms, 5),
+                     "kernel_ms": round(kernel_ms, 5), "kernels_per_step": kernels_per_step,
                      "algorithmic_bytes": algorithmic_bytes(w)},
     }
     if not args.no_cpu_baseline:

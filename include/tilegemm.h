@@ -64,7 +64,8 @@ typedef enum {
     GEMM_ERR_BAD_LD = 3,         /* a leading dimension is too small */
     GEMM_ERR_MISALIGNED = 4,     /* a pointer is not aligned to its element size */
     GEMM_ERR_UNSUPPORTED = 5,    /* valid but outside this library's limits */
-    GEMM_ERR_HIP = 6             /* the HIP runtime reported an error */
+    GEMM_ERR_HIP = 6,            /* the HIP runtime reported an error */
+    GEMM_ERR_WORKSPACE = 7       /* a required workspace is NULL or smaller than needed */
 } gemm_status;
 
 typedef enum {
@@ -149,6 +150,53 @@ gemm_status gemm_mxfp4(int64_t M, int64_t N, int64_t K,
                        const void *C, int64_t ldc,
                        void *D, int64_t ldd,
                        int out_type, hipStream_t stream);
+
+/*
+ * gemm_bf16_splitk, gemm_fp16_splitk -- as gemm_bf16 / gemm_fp16, with K cut
+ * into `splits` ranges computed by separate workgroups (more workgroups for
+ * grids too small to fill the GPU: few output tiles, long K).  Each range's
+ * fp32 partial product goes to the caller's workspace; a second kernel on
+ * the same stream sums the partials in range order, adds C and writes D, so
+ * the result is the same on every call.  Source: "（二）CUTLASS —— 掌握
+ * Tensor Memory Accelerator（TMA）", section TMA Store Reduce (several CTAs
+ * accumulating tiles into one global tile); here the accumulation is a
+ * separate pass over fp32 partials rather than a reducing store.
+ *   splits: 0 = the library's choice (split only grids of fewer than 128
+ *     tiles of 256 x 256, up to 256 workgroups, at least 4096 K per range),
+ *     1 = no split, up to 64; fewer are used when K has fewer 64-wide tiles,
+ *     and none when rows are not 8-byte aligned.  Else GEMM_ERR_UNSUPPORTED.
+ *   workspace: device memory, 256-byte aligned (else GEMM_ERR_MISALIGNED), of
+ *     at least gemm_splitk_workspace_bytes(M, N, K, splits) bytes (else
+ *     GEMM_ERR_WORKSPACE); untouched when no split is used (then it may be
+ *     NULL).  Owned by the caller; its contents need no initialisation and
+ *     are garbage afterwards.  Calls sharing a workspace must be ordered
+ *     (e.g. on one stream); a workspace overlapping A, B, C or D is
+ *     undefined behaviour.
+ * Everything else (layouts, validation, out_type, C == D) is as gemm_bf16.
+ */
+gemm_status gemm_bf16_splitk(int64_t M, int64_t N, int64_t K,
+                             const void *A, int64_t lda,
+                             const void *B, int64_t ldb,
+                             const void *C, int64_t ldc,
+                             void *D, int64_t ldd,
+                             int out_type, int splits,
+                             void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+gemm_status gemm_fp16_splitk(int64_t M, int64_t N, int64_t K,
+                             const void *A, int64_t lda,
+                             const void *B, int64_t ldb,
+                             const void *C, int64_t ldc,
+                             void *D, int64_t ldd,
+                             int out_type, int splits,
+                             void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Workspace bytes gemm_bf16_splitk / gemm_fp16_splitk need for these sizes
+ * and `splits` (0 = the library's choice): splits_used * M * (N rounded up
+ * to a multiple of 4) * 4; 0 when no split would be used or the arguments
+ * are invalid.
+ */
+size_t gemm_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K, int splits);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char *gemm_status_string(int status);

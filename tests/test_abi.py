@@ -11,7 +11,7 @@ import tiled_dense_gemm_tile_amd as tg
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "tilegemm.h")
 
-OK, INVALID_SIZE, NULL_POINTER, BAD_LD, MISALIGNED, UNSUPPORTED = 0, 1, 2, 3, 4, 5
+OK, INVALID_SIZE, NULL_POINTER, BAD_LD, MISALIGNED, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3, 4, 5, 7
 F32, BF16 = 0, 1
 P = 0x10000000  # a fake, aligned device address: never dereferenced by these calls
 
@@ -23,8 +23,9 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["gemm_bf16", "gemm_fp16", "gemm_last_hip_error", "gemm_mxfp4",
-                                    "gemm_mxfp8", "gemm_status_string"]
+    assert declared_functions() == ["gemm_bf16", "gemm_bf16_splitk", "gemm_fp16", "gemm_fp16_splitk",
+                                    "gemm_last_hip_error", "gemm_mxfp4", "gemm_mxfp8", "gemm_splitk_workspace_bytes",
+                                    "gemm_status_string"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -38,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for s in range(7):
+    for s in range(8):
         assert tg.raw.status_string(s).startswith(tg.STATUS[s])
     assert "unknown" in tg.raw.status_string(99)
     assert tg.raw.gemm_last_hip_error() == 0
@@ -122,6 +123,47 @@ def test_validation_mxfp4():
     assert call4(ldsfa=20) == UNSUPPORTED
     assert call4(lda=16 << 20) == UNSUPPORTED               # 8 MiB rows
     assert call4(K=1 << 31, lda=1 << 31, ldb=1 << 31) == UNSUPPORTED
+
+
+def splitk_bytes(M, N, K, splits):
+    return tg.raw.gemm_splitk_workspace_bytes(M, N, K, splits)
+
+
+def test_splitk_workspace_bytes():
+    # splits_used * M * round_up(N, 4) * 4
+    assert splitk_bytes(256, 256, 4096, 4) == 4 * 256 * 256 * 4
+    assert splitk_bytes(300, 201, 5000, 3) == 3 * 300 * 204 * 4
+    assert splitk_bytes(64, 64, 8192, 1) == 0                 # no split
+    assert splitk_bytes(64, 64, 64, 4) == 0                   # one K tile: nothing to split
+    assert splitk_bytes(64, 64, 192, 8) == 3 * 64 * 64 * 4    # at most one split per 64-wide K tile
+    assert splitk_bytes(64, 64, 640, 4) == 4 * 64 * 64 * 4    # 10 K tiles: ranges of 3, 3, 3, 1
+    assert splitk_bytes(64, 64, 576, 4) == 3 * 64 * 64 * 4    # 9 K tiles: ranges of 3 -> 3 splits
+    assert splitk_bytes(1024, 1024, 65536, 0) == 16 * 1024 * 1024 * 4   # 16 tiles, 1024 K tiles: 16 splits
+    assert splitk_bytes(4096, 4096, 4096, 0) == 0             # 256 tiles: the library does not split
+    assert splitk_bytes(512, 512, 8192, 0) == 2 * 512 * 512 * 4   # 4 tiles, 128 K tiles: 2 splits of 4096
+    assert splitk_bytes(64, 64, 4096, 65) == 0 and splitk_bytes(-1, 64, 4096, 2) == 0
+
+
+def call16s(fn="gemm_bf16_splitk", M=256, N=256, K=4096, A=P, lda=4096, B=P, ldb=4096, C=None, ldc=0,
+            D=P + (1 << 24), ldd=256, out=F32, splits=4, ws=P + (1 << 26), wsb=None):
+    if wsb is None:
+        wsb = splitk_bytes(M, N, K, splits)
+    return getattr(tg.raw, fn)(M, N, K, A, lda, B, ldb, C, ldc, D, ldd, out, splits, ws, wsb, None)
+
+
+@pytest.mark.parametrize("fn", ["gemm_bf16_splitk", "gemm_fp16_splitk"])
+def test_validation_splitk(fn):
+    """Every case is refused before anything is launched."""
+    assert call16s(fn, M=-1) == INVALID_SIZE
+    assert call16s(fn, M=0) == OK
+    assert call16s(fn, lda=100) == BAD_LD
+    assert call16s(fn, D=None) == NULL_POINTER
+    assert call16s(fn, out=9) == UNSUPPORTED
+    assert call16s(fn, splits=-1) == UNSUPPORTED
+    assert call16s(fn, splits=65) == UNSUPPORTED
+    assert call16s(fn, ws=None) == WORKSPACE
+    assert call16s(fn, wsb=4 * 256 * 256 * 4 - 1) == WORKSPACE
+    assert call16s(fn, ws=P + (1 << 26) + 128) == MISALIGNED
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

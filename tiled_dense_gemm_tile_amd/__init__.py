@@ -16,14 +16,15 @@ import ctypes
 import os
 import threading
 
-__all__ = ["gemm_bf16", "gemm_fp16", "gemm_mxfp8", "gemm_mxfp4", "raw", "GemmError", "LibraryMissing",
+__all__ = ["gemm_bf16", "gemm_fp16", "gemm_bf16_splitk", "gemm_fp16_splitk", "splitk_workspace_bytes",
+           "gemm_mxfp8", "gemm_mxfp4", "raw", "GemmError", "LibraryMissing",
            "library_path", "STATUS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libtilegemm.so")
 
 STATUS = {0: "GEMM_OK", 1: "GEMM_ERR_INVALID_SIZE", 2: "GEMM_ERR_NULL_POINTER", 3: "GEMM_ERR_BAD_LD",
-          4: "GEMM_ERR_MISALIGNED", 5: "GEMM_ERR_UNSUPPORTED", 6: "GEMM_ERR_HIP"}
+          4: "GEMM_ERR_MISALIGNED", 5: "GEMM_ERR_UNSUPPORTED", 6: "GEMM_ERR_HIP", 7: "GEMM_ERR_WORKSPACE"}
 OUT_F32, OUT_BF16 = 0, 1
 
 
@@ -58,6 +59,12 @@ def _load():
             for name in ("gemm_bf16", "gemm_fp16"):
                 f = getattr(L, name)
                 f.restype, f.argtypes = ci, sig16
+            sz = ctypes.c_size_t
+            for name in ("gemm_bf16_splitk", "gemm_fp16_splitk"):
+                f = getattr(L, name)
+                f.restype, f.argtypes = ci, sig16[:-1] + [ci, vp, sz, vp]
+            L.gemm_splitk_workspace_bytes.restype = sz
+            L.gemm_splitk_workspace_bytes.argtypes = [i64, i64, i64, ci]
             for name in ("gemm_mxfp8", "gemm_mxfp4"):
                 f = getattr(L, name)
                 f.restype = ci
@@ -151,6 +158,43 @@ def gemm_fp16(A, B, C=None, out_dtype=None, D=None):
     """As :func:`gemm_bf16` with float16 A and B."""
     import torch
     return _call16("gemm_fp16", A, B, C, torch.float32 if out_dtype is None else out_dtype, D, torch.float16)
+
+
+def splitk_workspace_bytes(M: int, N: int, K: int, splits: int = 0) -> int:
+    """Workspace bytes the split-K calls need (0: no split would be used)."""
+    return int(_load().gemm_splitk_workspace_bytes(M, N, K, splits))
+
+
+def _call16_split(name, A, B, C, out_dtype, D, dtype, splits, workspace):
+    import torch
+    M, N, K, D, stream, out = _prep(A, B, C, D, out_dtype, (dtype,))
+    need = splitk_workspace_bytes(M, N, K, splits) if M and N and K else 0
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=A.device)
+    wp = workspace.data_ptr() if workspace is not None else None
+    wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = getattr(_load(), name)(M, N, K, A.data_ptr(), _ld(A, K) if K else 0, B.data_ptr(), _ld(B, K) if K else 0,
+                                C.data_ptr() if C is not None else None, _ld(C, N) if C is not None else 0,
+                                D.data_ptr(), _ld(D, N), out, splits, wp, wb, stream)
+    _check(st)
+    return D
+
+
+def gemm_bf16_splitk(A, B, C=None, out_dtype=None, D=None, splits=0, workspace=None):
+    """:func:`gemm_bf16` with K split over ``splits`` ranges (0: the library's
+    choice).  ``workspace``: a device tensor of at least
+    :func:`splitk_workspace_bytes` bytes, 256-byte aligned; allocated per
+    call when not given."""
+    import torch
+    return _call16_split("gemm_bf16_splitk", A, B, C, torch.float32 if out_dtype is None else out_dtype, D,
+                         torch.bfloat16, splits, workspace)
+
+
+def gemm_fp16_splitk(A, B, C=None, out_dtype=None, D=None, splits=0, workspace=None):
+    """As :func:`gemm_bf16_splitk` with float16 A and B."""
+    import torch
+    return _call16_split("gemm_fp16_splitk", A, B, C, torch.float32 if out_dtype is None else out_dtype, D,
+                         torch.float16, splits, workspace)
 
 
 def gemm_mxfp8(A, SFA, B, SFB, C=None, out_dtype=None, D=None):

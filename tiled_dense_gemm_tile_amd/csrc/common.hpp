@@ -98,4 +98,24 @@ __device__ __forceinline__ void tile_order(int wg, int nwg, int tiles_m, int til
     tn = in_group / gm;
 }
 
+// Split-K work item of workgroup wg out of nwg = tiles * splits: the same
+// XCD renumbering as tile_order, then split = id / tiles and the tile from
+// id % tiles in groups of `group_m` tile-rows, so the workgroups running
+// together on an XCD share the K range of their A and B panels.
+__device__ __forceinline__ void tile_order_split(int wg, int nwg, int tiles_m, int tiles_n, int group_m, int &tm,
+                                                 int &tn, int &split) {
+    const int q = nwg >> 3, r = nwg & 7, x = wg & 7;
+    const int lid = x * q + (x < r ? x : r) + (wg >> 3);
+    const int tiles = tiles_m * tiles_n;
+    split = lid / tiles;
+    const int in_split = lid - split * tiles;
+    const int group_size = group_m * tiles_n;
+    const int group = in_split / group_size;
+    const int first_m = group * group_m;
+    const int gm = (tiles_m - first_m) < group_m ? (tiles_m - first_m) : group_m;
+    const int in_group = in_split - group * group_size;
+    tm = first_m + in_group % gm;
+    tn = in_group / gm;
+}
+
 }  // namespace tg

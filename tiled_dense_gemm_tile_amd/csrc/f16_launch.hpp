@@ -69,6 +69,12 @@ template <bool FP16, bool OUT_BF16>
 hipError_t launch_f16_dma(int cfg, int lane_bytes, unsigned grid, hipStream_t s, const F16Args &p,
                           const F16Epi &e);
 
+// Split-K partial products (fp32 partial tiles into p.ws; instantiated in
+// the fp32-output translation units): the four-wave kernel, 16-byte rows
+// (sh false) or 8-byte rows (sh true).
+template <bool FP16, bool OUT_BF16>
+hipError_t launch_f16_split(bool sh, unsigned grid, hipStream_t s, const F16Args &p, const F16Epi &e);
+
 template <bool FP16, bool OUT_BF16>
 hipError_t launch_f16_staged(int vec, unsigned grid, hipStream_t s, const F16Args &p);
 
@@ -142,6 +148,23 @@ hipError_t launch_f16_dma<TG_FP16, TG_OUT_BF16>(int cfg, int lane_bytes, unsigne
         return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+template <>
+hipError_t launch_f16_split<TG_FP16, TG_OUT_BF16>(bool sh, unsigned grid, hipStream_t s, const F16Args &p,
+                                                   const F16Epi &e) {
+#if TG_OUT_BF16
+    (void)sh, (void)grid, (void)s, (void)p, (void)e;
+    return hipErrorInvalidValue;
+#else
+    if (sh)
+        hipLaunchKernelGGL((gemm_f16_w4t_kernel<2, 2, TG_FP16, false, 1, kStoreStream, true, true>), dim3(grid),
+                           dim3(256), 0, s, p, e);
+    else
+        hipLaunchKernelGGL((gemm_f16_w4t_kernel<2, 2, TG_FP16, false, 1, kStoreStream, false, true>), dim3(grid),
+                           dim3(256), 0, s, p, e);
+    return hipGetLastError();
+#endif
 }
 
 template <>

@@ -27,6 +27,12 @@ struct F16Args {
     int64_t lda, ldb, ldc, ldd;
     int M, N, K;
     int tiles_m, tiles_n, group_m;
+    // split-K (kernels instantiated with SPLIT only): K is cut into ranges
+    // of `kt_split` K tiles; split s writes its fp32 partial tile to the
+    // M x ldw matrix at ws + s * M * ldw (C and D are left to the reduction)
+    int kt_split = 0;
+    float *ws = nullptr;
+    int64_t ldw = 0;
 };
 
 template <int BM_, int BN_, int BK_, int WM_, int WN_>

@@ -236,7 +236,15 @@ __global__ void __launch_bounds__(256) gemm_f16_w4_kernel(F16Args p, F16Epi e) {
 // barrier wait at the end of tile c leaves the part's loads in flight, so
 // they have a whole tile to arrive from memory.  C thus arrives over 16
 // tiles instead of all at the end.
-template <int NA, int NB, bool FP16, bool OUT_BF16, int SCHED = 0, int DAUX = kStoreStream, bool SH = false>
+//
+// SPLIT (split-K): workgroup (split s, tile) multiplies K tiles
+// [s * kt_split, (s + 1) * kt_split) of its output tile -- the A and B tile
+// bases move by the range's first K element and the K loop runs over the
+// range as if it were the whole K -- and writes the fp32 partial tile to
+// workspace slice s through the same epilogue, with no C; the reduction
+// kernel adds the slices and C.
+template <int NA, int NB, bool FP16, bool OUT_BF16, int SCHED = 0, int DAUX = kStoreStream, bool SH = false,
+          bool SPLIT = false>
 __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) {
     constexpr int BM = 256, BN = 256, KT = 64;         // tile
     constexpr int WTM = 128, WTN = 128, TM = 8, TN = 8;
@@ -252,6 +260,7 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
     constexpr int WAIT_N = (NB - NA) * LPT;            // B loads still in flight at a barrier
     static_assert(NA == 2 && (NB == 2 || NB == 3) && LDS_BYTES <= 160 * 1024, "ring");
     static_assert(!SH || (NB == 2 && SCHED == 1), "shifted rows: balanced schedule, two B slots");
+    static_assert(!SPLIT || !OUT_BF16, "split-K partial tiles are fp32");
 
     __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
 
@@ -259,16 +268,23 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
-    int tmi, tni;
-    tile_order(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, tmi, tni);
+    int tmi, tni, split = 0;
+    if constexpr (SPLIT)
+        tile_order_split(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, tmi, tni, split);
+    else
+        tile_order(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, tmi, tni);
     const int m0 = tmi * BM, n0 = tni * BN;
-    const int M = p.M, N = p.N, K = p.K;
+    const int k_lo = SPLIT ? split * p.kt_split * KT : 0;          // first K element of this range
+    const int M = p.M, N = p.N;
+    const int K = SPLIT ? (p.K - k_lo < p.kt_split * KT ? p.K - k_lo : p.kt_split * KT) : p.K;
 
     // Tile bases.  With SH the resources start at the 16-byte boundary at or
     // below the tile's first element (at most 8 bytes earlier, never across a
     // page boundary, since the element itself lies 8 bytes into its 16).
-    const char *a_tile = (const char *)p.A + (int64_t)m0 * p.lda * 2;
-    const char *b_tile = (const char *)p.B + (int64_t)n0 * p.ldb * 2;
+    // (SPLIT: k_lo is a multiple of 64 elements, 128 bytes: the alignment of
+    // the rows within 16 bytes does not change)
+    const char *a_tile = (const char *)p.A + (int64_t)m0 * p.lda * 2 + (int64_t)k_lo * 2;
+    const char *b_tile = (const char *)p.B + (int64_t)n0 * p.ldb * 2 + (int64_t)k_lo * 2;
     const int a_mis0 = SH ? (int)((uintptr_t)a_tile & 15) : 0;
     const int b_mis0 = SH ? (int)((uintptr_t)b_tile & 15) : 0;
     const __amdgpu_buffer_rsrc_t rA = make_rsrc(a_tile - a_mis0, span_bytes(M - m0, K, p.lda, 2) + a_mis0);
@@ -398,7 +414,7 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
     // (whole 4-column vectors: every C row segment a lane reads is either in
     // range or past N)
     // (and the stream's tiles load only whole K tiles: see the loop below)
-    const bool c_loop = p.C != nullptr && nt >= CPARTS + 2 + NB && e.vec_c && N % 4 == 0;
+    const bool c_loop = !SPLIT && p.C != nullptr && nt >= CPARTS + 2 + NB && e.vec_c && N % 4 == 0;
     const __amdgpu_buffer_rsrc_t rC =
         make_rsrc(c_loop ? (const char *)p.C + (int64_t)m0 * p.ldc * OS : (const char *)p.D,
                   c_loop ? span_bytes(M - m0, N, p.ldc, OS) : 0u);
@@ -602,8 +618,15 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
     wait_vmcnt<0>();
     wait_lgkmcnt0();
     barrier();
-    epilogue_lds16t<OUT_BF16, TM, TN, WTM, WTN, DAUX>(acc, smem, wave, lane, wm, wn, m0, n0, M, N, c_loop ? nullptr : p.C,
-                                                p.ldc, p.D, p.ldd, e);
+    if constexpr (SPLIT) {
+        // partial tiles stay cacheable: the reduction reads them right after
+        float *part = p.ws + (int64_t)split * M * p.ldw;
+        epilogue_lds16t<false, TM, TN, WTM, WTN, 0>(acc, smem, wave, lane, wm, wn, m0, n0, M, N, nullptr, 0, part,
+                                                    p.ldw, e);
+    } else {
+        epilogue_lds16t<OUT_BF16, TM, TN, WTM, WTN, DAUX>(acc, smem, wave, lane, wm, wn, m0, n0, M, N,
+                                                          c_loop ? nullptr : p.C, p.ldc, p.D, p.ldd, e);
+    }
 }
 
 }  // namespace tg

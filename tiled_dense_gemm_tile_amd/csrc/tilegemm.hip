@@ -11,6 +11,7 @@
 #include "f16_launch.hpp"
 #include "mx4_launch.hpp"
 #include "mx_launch.hpp"
+#include "splitk.hpp"
 
 namespace {
 
@@ -169,6 +170,99 @@ gemm_status run_f16(bool fp16, const Common &a, hipStream_t s) {
     return a.out_type == GEMM_OUT_BF16 ? dispatch_f16<false, true>(a, s) : dispatch_f16<false, false>(a, s);
 }
 
+// ---- split-K (16-bit inputs) ------------------------------------------------
+
+constexpr int kMaxSplits = 64;
+
+// Split count actually used for a requested one: at most one split per K tile
+// of 64, and every split non-empty (ranges of ceil(kt / s) K tiles).
+int effective_splits(int64_t K, int splits) {
+    const int64_t kt = (K + 63) / 64;
+    if (kt <= 1 || splits <= 1) return 1;
+    const int64_t s = splits > kt ? kt : splits;
+    const int64_t kps = (kt + s - 1) / s;
+    return (int)((kt + kps - 1) / kps);
+}
+
+// The library's choice: split only grids of fewer than 128 tiles of 256 x 256,
+// up to one wave of 256 workgroups, keeping at least 64 K tiles (4096 K) per
+// split so that writing and re-reading a split's fp32 partial tile stays small
+// next to its multiply work.
+int auto_splits(int64_t M, int64_t N, int64_t K) {
+    const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+    if (tiles <= 0 || tiles >= 128) return 1;
+    int64_t s = 256 / tiles;
+    const int64_t by_k = ((K + 63) / 64) / 64;
+    if (by_k < s) s = by_k;
+    if (s > kMaxSplits) s = kMaxSplits;
+    return s < 2 ? 1 : (int)s;
+}
+
+int64_t splitk_ldw(int64_t N) { return (N + 3) / 4 * 4; }
+
+size_t splitk_bytes(int64_t M, int64_t N, int splits) {
+    return splits <= 1 ? 0 : (size_t)splits * (size_t)M * (size_t)splitk_ldw(N) * 4;
+}
+
+gemm_status run_f16_splitk(bool fp16, const Common &a, int splits, void *ws, size_t ws_bytes, hipStream_t s) {
+    bool none = false;
+    gemm_status st = validate(a, &none);
+    if (st != GEMM_OK || none) return st;
+    if (splits < 0 || splits > kMaxSplits) return GEMM_ERR_UNSUPPORTED;
+    const int S = effective_splits(a.K, splits == 0 ? auto_splits(a.M, a.N, a.K) : splits);
+    const int vec = pick_vec(a);
+    // rows only 4- or 2-byte aligned have no four-wave kernel: unsplit
+    if (S == 1 || vec < 4) return run_f16(fp16, a, s);
+    if (!ws || ws_bytes < splitk_bytes(a.M, a.N, S)) return GEMM_ERR_WORKSPACE;
+    if ((uintptr_t)ws % 256 != 0) return GEMM_ERR_MISALIGNED;
+    const int64_t ldw = splitk_ldw(a.N);
+    if (ldw * 4 >= kMaxLdBytes) return GEMM_ERR_UNSUPPORTED;
+    const int64_t kt = (a.K + 63) / 64;
+    tg::F16Args p;
+    p.A = a.A;
+    p.B = a.B;
+    p.C = nullptr;
+    p.D = nullptr;
+    p.lda = a.lda;
+    p.ldb = a.ldb;
+    p.ldc = 0;
+    p.ldd = 0;
+    p.M = (int)a.M;
+    p.N = (int)a.N;
+    p.K = (int)a.K;
+    p.group_m = 4;
+    p.tiles_m = (int)((a.M + 255) / 256);
+    p.tiles_n = (int)((a.N + 255) / 256);
+    p.kt_split = (int)((kt + S - 1) / S);
+    p.ws = (float *)ws;
+    p.ldw = ldw;
+    const int64_t grid = (int64_t)p.tiles_m * p.tiles_n * S;
+    if (grid >= kMaxDim) return GEMM_ERR_UNSUPPORTED;
+    tg::F16Epi e;
+    e.vec_c = false;
+    e.vec_d = true;                                    // 256-byte aligned base, ldw % 4 == 0
+    const bool sh = vec == 4;                          // 8-byte rows: the shifted-row variant
+    hipError_t err = fp16 ? tg::launch_f16_split<true, false>(sh, (unsigned)grid, s, p, e)
+                          : tg::launch_f16_split<false, false>(sh, (unsigned)grid, s, p, e);
+    if (err != hipSuccess) return launched(err);
+    const bool bf16 = a.out_type == GEMM_OUT_BF16;
+    const uintptr_t vb = bf16 ? 8 : 16;
+    tg::SplitReduceArgs r;
+    r.ws = (const float *)ws;
+    r.ldw = ldw;
+    r.slice = a.M * ldw;
+    r.splits = S;
+    r.C = a.C;
+    r.ldc = a.ldc;
+    r.D = a.D;
+    r.ldd = a.ldd;
+    r.M = (int)a.M;
+    r.N = (int)a.N;
+    r.vec_c = a.C && ((uintptr_t)a.C % vb) == 0 && a.ldc % 4 == 0;
+    r.vec_d = ((uintptr_t)a.D % vb) == 0 && a.ldd % 4 == 0;
+    return launched(tg::launch_splitk_reduce(bf16, s, r));
+}
+
 // ---- block-scaled fp8 ------------------------------------------------------
 
 int forced_mx_cfg() {
@@ -290,6 +384,25 @@ gemm_status gemm_fp16(int64_t M, int64_t N, int64_t K, const void *A, int64_t ld
     return run_f16(true, a, stream);
 }
 
+size_t gemm_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K, int splits) {
+    if (M <= 0 || N <= 0 || K <= 0 || splits < 0 || splits > kMaxSplits) return 0;
+    return splitk_bytes(M, N, effective_splits(K, splits == 0 ? auto_splits(M, N, K) : splits));
+}
+
+gemm_status gemm_bf16_splitk(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B, int64_t ldb,
+                             const void *C, int64_t ldc, void *D, int64_t ldd, int out_type, int splits,
+                             void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    Common a{M, N, K, A, lda, B, ldb, C, ldc, D, ldd, out_type, 2};
+    return run_f16_splitk(false, a, splits, workspace, workspace_bytes, stream);
+}
+
+gemm_status gemm_fp16_splitk(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B, int64_t ldb,
+                             const void *C, int64_t ldc, void *D, int64_t ldd, int out_type, int splits,
+                             void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    Common a{M, N, K, A, lda, B, ldb, C, ldc, D, ldd, out_type, 2};
+    return run_f16_splitk(true, a, splits, workspace, workspace_bytes, stream);
+}
+
 gemm_status gemm_mxfp8(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *SFA, int64_t ldsfa,
                        const void *B, int64_t ldb, const void *SFB, int64_t ldsfb, const void *C, int64_t ldc,
                        void *D, int64_t ldd, int out_type, hipStream_t stream) {
@@ -337,6 +450,7 @@ const char *gemm_status_string(int s) {
     case GEMM_ERR_MISALIGNED: return "GEMM_ERR_MISALIGNED: a pointer is not aligned to its element size";
     case GEMM_ERR_UNSUPPORTED: return "GEMM_ERR_UNSUPPORTED: outside the library's limits";
     case GEMM_ERR_HIP: return "GEMM_ERR_HIP: the HIP runtime reported an error";
+    case GEMM_ERR_WORKSPACE: return "GEMM_ERR_WORKSPACE: the workspace is missing or too small";
     default: return "unknown gemm_status";
     }
 }

@@ -161,15 +161,17 @@ def main():
         step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
+    # an event before every step and after the last, all on the launch stream
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     t0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
+    evs[0].record(stream)
+    for i in range(args.steps):
         step()
-    ev1.record(stream)
+        evs[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    ev0, ev1 = evs[0], evs[-1]
+    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
     # one GEMM launch per step (split-K: the GEMM and the reduction of its partials)
     kernel_ms = ev0.elapsed_time(ev1) / args.steps
     ms_per_step = wall * 1e3 / args.steps
@@ -195,7 +197,8 @@ def main():
                    "splits": None if splits is None else (splits or "auto")},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(tflops / peak, 4), "traffic": measured_traffic(w),
-                     "kernel_ms": round(kernel_ms, 5), "kernels_per_step": kernels_per_step,
+                     "kernel_ms": round(kernel_ms, 5), "kernel_ms_median": round(per_step[len(per_step) // 2], 5),
+                     "kernel_ms_min": round(per_step[0], 5), "kernels_per_step": kernels_per_step,
                      "algorithmic_bytes": algorithmic_bytes(w)},
     }
     if not args.no_cpu_baseline:

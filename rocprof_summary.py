@@ -64,6 +64,8 @@ def kernel_source_hash(workload: str) -> str:
     files = set()
     _include_closure(instance_file(w.in_type, w.out_type), files)
     files.add("tilegemm.hip")
+    if w.in_type in ("bf16", "fp16"):
+        _include_closure("splitk.hip", files)          # the split-K reduction
     h = hashlib.sha256()
     for f in sorted(files):
         h.update(f.encode())
@@ -91,7 +93,8 @@ def csv_rows(d, pattern):
 
 
 def counter_per_dispatch(d, name_filter):
-    """{dispatch_id: {counter: value}} summed over instances, for kernels whose name matches."""
+    """{dispatch_id: {counter: value}} summed over instances, for kernels whose name matches,
+    with the dispatch's duration in ns under "duration_ns"."""
     out = {}
     for r in csv_rows(d, "*counter_collection.csv"):
         if name_filter not in r["Kernel_Name"]:
@@ -99,6 +102,8 @@ def counter_per_dispatch(d, name_filter):
         did = int(r["Dispatch_Id"])
         e = out.setdefault(did, {"kernel": r["Kernel_Name"]})
         e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        if r.get("Start_Timestamp") and r.get("End_Timestamp"):
+            e["duration_ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
     return out
 
 
@@ -209,6 +214,11 @@ def main():
                 # busy cycles are summed over the 1024 SIMDs, GUI-active cycles over the 8 XCDs
                 lines.append("  MFMA busy fraction = (busy / 1024) / (gui_active / 8) = %.3f"
                              % ((per[did]["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024) / (per[did]["GRBM_GUI_ACTIVE"] / 8)))
+                if per[did].get("duration_ns"):
+                    ghz = per[did]["GRBM_GUI_ACTIVE"] / 8 / per[did]["duration_ns"]
+                    lines.append("  shader clock over this dispatch = (gui_active / 8) / duration = %.3f GHz "
+                                 "(%.1f us); the dense peak at this clock is %.1f %% of the 2.4 GHz figure"
+                                 % (ghz, per[did]["duration_ns"] / 1e3, 100 * ghz / 2.4))
             lines.append("")
         out = os.path.join(args.dest, "%s_%s_counters.txt" % (kname, args.workload))
         with open(out, "w") as f:

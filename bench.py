@@ -101,6 +101,10 @@ def main():
     ap.add_argument("--splits", type=int, default=None,
                     help="16-bit workloads: run the split-K entry point with this many K ranges (0: the "
                          "library's choice; the default for workloads with fewer than 128 output tiles)")
+    ap.add_argument("--a-order", choices=("k", "mn"), default="k",
+                    help="16-bit workloads: store A K-contiguous (M x K) or MN-contiguous (K x M), same values")
+    ap.add_argument("--b-order", choices=("k", "mn"), default="k",
+                    help="16-bit workloads: store B K-contiguous (N x K) or MN-contiguous (K x N), same values")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -126,6 +130,12 @@ def main():
     w = inputs.WORKLOADS[args.workload]
     x = inputs.generate(w)
     A, B, C, extra = device_inputs(w, x, torch)
+    if w.in_type in ("bf16", "fp16"):
+        # MN-contiguous storage: the transposed copy, viewed back as (rows, K)
+        if args.a_order == "mn":
+            A = A.t().contiguous().t()
+        if args.b_order == "mn":
+            B = B.t().contiguous().t()
     out_dtype = torch.float32 if w.out_type == "f32" else torch.bfloat16
     D = torch.empty((w.M, w.N), dtype=out_dtype, device="cuda:0")
 
@@ -194,7 +204,9 @@ def main():
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "in": w.in_type, "out": w.out_type,
                    "C": "fp32 U[-1,1]" if w.dist_c else "none", "layout": "A row-major, B column-major (N x K)",
                    "seed": w.seed, "note": w.note,
-                   "splits": None if splits is None else (splits or "auto")},
+                   "splits": None if splits is None else (splits or "auto"),
+                   "storage": {"A": "K x M" if args.a_order == "mn" else "M x K",
+                               "B": "K x N" if args.b_order == "mn" else "N x K"}},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(tflops / peak, 4), "traffic": measured_traffic(w),
                      "kernel_ms": round(kernel_ms, 5), "kernel_ms_median": round(per_step[len(per_step) // 2], 5),

@@ -73,6 +73,11 @@ typedef enum {
     GEMM_OUT_BF16 = 1            /* D (and C) are bf16; fp32 sums rounded to nearest even */
 } gemm_out_type;
 
+typedef enum {
+    GEMM_K_CONTIGUOUS = 0,       /* A: a(m,k) = A[m*lda + k]   B: b(k,n) = B[n*ldb + k] */
+    GEMM_MN_CONTIGUOUS = 1       /* A: a(m,k) = A[k*lda + m]   B: b(k,n) = B[k*ldb + n] */
+} gemm_operand_order;
+
 /*
  * gemm_bf16 -- D = A.B + C with bf16 A and B, fp32 accumulation.
  * Source: "Tensor Core 数据布局的演进", section 一个具体的 fragment 映射
@@ -99,6 +104,38 @@ gemm_status gemm_fp16(int64_t M, int64_t N, int64_t K,
                       const void *C, int64_t ldc,
                       void *D, int64_t ldd,
                       int out_type, hipStream_t stream);
+
+/*
+ * gemm_bf16_ex, gemm_fp16_ex -- as gemm_bf16 / gemm_fp16 with each operand's
+ * storage order chosen (a_order, b_order: gemm_operand_order):
+ *   A K-contiguous: M x K row-major, lda >= K (as gemm_bf16)
+ *   A MN-contiguous: K x M row-major (M x K column-major), lda >= M
+ *   B K-contiguous: stored N x K (K x N column-major), ldb >= K (as gemm_bf16)
+ *   B MN-contiguous: K x N row-major, ldb >= N
+ * Source: "Tensor Core 数据布局的演进", section ldmatrix：从 shared memory
+ * 构造 fragment (the .trans form loads each 8x8 block column-major) and the
+ * matrix descriptor's major modes (K-major or MN-major operand tiles); here
+ * an MN-contiguous tile is read into K-ordered MFMA fragments with gfx950's
+ * LDS transpose read.
+ * Both K-contiguous: exactly gemm_bf16 / gemm_fp16.  Otherwise this version
+ * needs A and B 16-byte aligned, lda and ldb multiples of 8 and, for a
+ * K-contiguous operand, K % 8 == 0 (GEMM_ERR_UNSUPPORTED otherwise); an
+ * order other than the two values is GEMM_ERR_UNSUPPORTED.  Everything
+ * else as gemm_bf16 (the byte limit applies to lda*2 and ldb*2).
+ */
+gemm_status gemm_bf16_ex(int64_t M, int64_t N, int64_t K,
+                         const void *A, int64_t lda, int a_order,
+                         const void *B, int64_t ldb, int b_order,
+                         const void *C, int64_t ldc,
+                         void *D, int64_t ldd,
+                         int out_type, hipStream_t stream);
+
+gemm_status gemm_fp16_ex(int64_t M, int64_t N, int64_t K,
+                         const void *A, int64_t lda, int a_order,
+                         const void *B, int64_t ldb, int b_order,
+                         const void *C, int64_t ldc,
+                         void *D, int64_t ldd,
+                         int out_type, hipStream_t stream);
 
 /*
  * gemm_mxfp8 -- block-scaled fp8: D = A.B + C with

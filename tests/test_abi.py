@@ -23,9 +23,9 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["gemm_bf16", "gemm_bf16_splitk", "gemm_fp16", "gemm_fp16_splitk",
-                                    "gemm_last_hip_error", "gemm_mxfp4", "gemm_mxfp8", "gemm_splitk_workspace_bytes",
-                                    "gemm_status_string"]
+    assert declared_functions() == ["gemm_bf16", "gemm_bf16_ex", "gemm_bf16_splitk", "gemm_fp16", "gemm_fp16_ex",
+                                    "gemm_fp16_splitk", "gemm_last_hip_error", "gemm_mxfp4", "gemm_mxfp8",
+                                    "gemm_splitk_workspace_bytes", "gemm_status_string"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -164,6 +164,30 @@ def test_validation_splitk(fn):
     assert call16s(fn, ws=None) == WORKSPACE
     assert call16s(fn, wsb=4 * 256 * 256 * 4 - 1) == WORKSPACE
     assert call16s(fn, ws=P + (1 << 26) + 128) == MISALIGNED
+
+
+def callx(fn="gemm_bf16_ex", M=256, N=256, K=512, A=P, lda=256, ao=1, B=P, ldb=512, bo=0, C=None, ldc=0,
+          D=P + (1 << 24), ldd=256, out=F32):
+    return getattr(tg.raw, fn)(M, N, K, A, lda, ao, B, ldb, bo, C, ldc, D, ldd, out, None)
+
+
+@pytest.mark.parametrize("fn", ["gemm_bf16_ex", "gemm_fp16_ex"])
+def test_validation_orders(fn):
+    """MN-contiguous operands: leading dimension against M (N); every case is
+    refused before anything is launched."""
+    assert callx(fn, M=-1) == INVALID_SIZE
+    assert callx(fn, M=0) == OK
+    assert callx(fn, ao=2) == UNSUPPORTED
+    assert callx(fn, bo=-1) == UNSUPPORTED
+    assert callx(fn, lda=255) == BAD_LD                        # A stored K x M: lda >= M
+    assert callx(fn, ao=0, lda=511, bo=1, ldb=256) == BAD_LD   # A K-contiguous: lda >= K
+    assert callx(fn, bo=1, ldb=255) == BAD_LD                  # B stored K x N: ldb >= N
+    assert callx(fn, lda=260) == UNSUPPORTED                   # rows not 16-byte multiples
+    assert callx(fn, K=500, ldb=504) == UNSUPPORTED            # K-contiguous B with K % 8 != 0
+    assert callx(fn, A=P + 8) == UNSUPPORTED                   # A not 16-byte aligned
+    assert callx(fn, A=P + 1) == MISALIGNED
+    assert callx(fn, D=None) == NULL_POINTER
+    assert callx(fn, lda=8 << 20) == UNSUPPORTED               # 16 MiB rows
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

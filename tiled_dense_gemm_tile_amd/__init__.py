@@ -6,9 +6,12 @@ kernels.  PyTorch supplies device memory and the stream.  When the library is
 not built the calls raise :class:`LibraryMissing`; there is no fallback.
 
 Tensor conventions (same as the C ABI):
-  A: (M, K) row-major;  B: (N, K), i.e. the K x N operand stored column by
-  column;  C, D: (M, N) row-major.  The last stride of every tensor must be 1;
-  the first stride is passed as the leading dimension.
+  A: (M, K);  B: (N, K), i.e. the K x N operand indexed [n, k];  C, D: (M, N)
+  row-major.  C and D need a last stride of 1 (the first stride is the
+  leading dimension).  For the 16-bit calls A and B may each be K-contiguous
+  (last stride 1) or MN-contiguous (first stride 1, e.g. ``X.t()`` of a
+  contiguous K x M or K x N tensor); the binding passes the storage order to
+  ``gemm_bf16_ex`` / ``gemm_fp16_ex`` when one is MN-contiguous.
 """
 from __future__ import annotations
 
@@ -59,6 +62,9 @@ def _load():
             for name in ("gemm_bf16", "gemm_fp16"):
                 f = getattr(L, name)
                 f.restype, f.argtypes = ci, sig16
+            for name in ("gemm_bf16_ex", "gemm_fp16_ex"):
+                f = getattr(L, name)
+                f.restype, f.argtypes = ci, [i64, i64, i64, vp, i64, ci, vp, i64, ci, vp, i64, vp, i64, ci, vp]
             sz = ctypes.c_size_t
             for name in ("gemm_bf16_splitk", "gemm_fp16_splitk"):
                 f = getattr(L, name)
@@ -132,14 +138,32 @@ def _prep(A, B, C, D, out_dtype, in_dtypes):
     return M, N, K, D, stream, out
 
 
+K_CONTIGUOUS, MN_CONTIGUOUS = 0, 1
+
+
+def _order(t):
+    """(storage order, leading dimension) of a 2-D operand viewed (rows, K)."""
+    rows, cols = t.shape
+    if cols <= 1 or t.stride(1) == 1:
+        return K_CONTIGUOUS, _ld(t, cols)
+    if rows <= 1 or t.stride(0) == 1:
+        return MN_CONTIGUOUS, max(t.stride(1), rows)
+    raise ValueError("each operand needs a unit stride along K or along M/N")
+
+
 def _call16(name, A, B, C, out_dtype, D, dtype):
     M, N, K, D, stream, out = _prep(A, B, C, D, out_dtype, (dtype,))
-    lda = _ld(A, K) if K else 0
-    ldb = _ld(B, K) if K else 0
-    fn = getattr(_load(), name)
-    st = fn(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb,
-            C.data_ptr() if C is not None else None, _ld(C, N) if C is not None else 0,
-            D.data_ptr(), _ld(D, N), out, stream)
+    (ao, lda), (bo, ldb) = _order(A), _order(B)
+    if not K:
+        ao, lda, bo, ldb = K_CONTIGUOUS, 0, K_CONTIGUOUS, 0
+    cptr, ldc = (C.data_ptr(), _ld(C, N)) if C is not None else (None, 0)
+    L = _load()
+    if ao == K_CONTIGUOUS and bo == K_CONTIGUOUS:
+        st = getattr(L, name)(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, cptr, ldc, D.data_ptr(), _ld(D, N),
+                              out, stream)
+    else:
+        st = getattr(L, name + "_ex")(M, N, K, A.data_ptr(), lda, ao, B.data_ptr(), ldb, bo, cptr, ldc,
+                                      D.data_ptr(), _ld(D, N), out, stream)
     _check(st)
     return D
 

@@ -69,6 +69,11 @@ template <bool FP16, bool OUT_BF16>
 hipError_t launch_f16_dma(int cfg, int lane_bytes, unsigned grid, hipStream_t s, const F16Args &p,
                           const F16Epi &e);
 
+// Operands stored MN-contiguous (at: A as K x M, bt: B as K x N; at least
+// one set): the four-wave kernel, 16-byte rows, 256 x 256 tiles.
+template <bool FP16, bool OUT_BF16>
+hipError_t launch_f16_mn(bool at, bool bt, unsigned grid, hipStream_t s, const F16Args &p, const F16Epi &e);
+
 // Split-K partial products (fp32 partial tiles into p.ws; instantiated in
 // the fp32-output translation units): the four-wave kernel, 16-byte rows
 // (sh false) or 8-byte rows (sh true).
@@ -147,6 +152,23 @@ hipError_t launch_f16_dma<TG_FP16, TG_OUT_BF16>(int cfg, int lane_bytes, unsigne
     default:
         return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+
+template <>
+hipError_t launch_f16_mn<TG_FP16, TG_OUT_BF16>(bool at, bool bt, unsigned grid, hipStream_t s, const F16Args &p,
+                                               const F16Epi &e) {
+    if (at && bt)
+        hipLaunchKernelGGL((gemm_f16_w4t_kernel<2, 2, TG_FP16, TG_OUT_BF16, 1, kStoreStream, false, false, true, true>),
+                           dim3(grid), dim3(256), 0, s, p, e);
+    else if (at)
+        hipLaunchKernelGGL((gemm_f16_w4t_kernel<2, 2, TG_FP16, TG_OUT_BF16, 1, kStoreStream, false, false, true, false>),
+                           dim3(grid), dim3(256), 0, s, p, e);
+    else if (bt)
+        hipLaunchKernelGGL((gemm_f16_w4t_kernel<2, 2, TG_FP16, TG_OUT_BF16, 1, kStoreStream, false, false, false, true>),
+                           dim3(grid), dim3(256), 0, s, p, e);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

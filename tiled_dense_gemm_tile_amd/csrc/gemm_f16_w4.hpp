@@ -243,8 +243,40 @@ __global__ void __launch_bounds__(256) gemm_f16_w4_kernel(F16Args p, F16Epi e) {
 // range as if it were the whole K -- and writes the fp32 partial tile to
 // workspace slice s through the same epilogue, with no C; the reduction
 // kernel adds the slices and C.
+//
+// AT / BT: A (B) is stored MN-contiguous -- a(m,k) = A[k*lda + m] (b(k,n) =
+// B[k*ldb + n]), i.e. K rows of M (N) elements -- instead of K-contiguous.
+// Such an operand's K tile is loaded as it lies, 64 LDS rows of the tile's
+// 256 M (N) elements (512 bytes), and its MFMA fragments (eight K-consecutive
+// values of one column per lane) are read with ds_read_b64_tr_b16: within a
+// 16-lane group, output lane i receives element i % 4 of the 8-byte reads of
+// lanes 4 r + i / 4, r = 0..3 (probed on gfx950), so lanes reading four
+// K-consecutive rows x 16 columns hand each lane one column's four K values;
+// two such reads make a fragment.  The 32-byte chunk c of LDS row r sits at
+// chunk c ^ (r & 3) ^ 4 * ((r >> 3) & 1): the four rows of one read and the
+// two 16-lane groups read together fall on distinct banks.  The tile's K
+// offset moves the base of a per-tile buffer resource whose extent ends at
+// row K, so rows past K read as zeros; columns past M (N) feed only outputs
+// that are never stored.
+// With the balanced schedule, the step-0 fragments of tile t are read in the
+// first half of window t and used by its second half.  Reads issued as asm
+// (the transpose reads) are not tracked by the compiler, so before block row
+// i of the second half the kernel waits explicitly until at most
+// tr_row_wait(i) LDS operations remain: those issued after the reads row i
+// needs -- A rows i + 1 .. 7 of the first half, and the step-1 reads the
+// second half has issued before its MFMA 8 i (one per three MFMAs) -- where
+// a transposed operand's read counts two operations (CA, CB).  A count above
+// the field's 15 only makes the wait stricter.
+template <int CA, int CB>
+constexpr int tr_row_wait(int i) {
+    int n = (7 - i) * CA;
+    const int issued = (8 * i + 2) / 3;
+    for (int m = 0; m < issued && m < 16; ++m) n += (m >= 1 && m <= 8) ? CB : CA;
+    return n > 15 ? 15 : n;
+}
+
 template <int NA, int NB, bool FP16, bool OUT_BF16, int SCHED = 0, int DAUX = kStoreStream, bool SH = false,
-          bool SPLIT = false>
+          bool SPLIT = false, bool AT = false, bool BT = false>
 __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) {
     constexpr int BM = 256, BN = 256, KT = 64;         // tile
     constexpr int WTM = 128, WTN = 128, TM = 8, TN = 8;
@@ -261,6 +293,7 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
     static_assert(NA == 2 && (NB == 2 || NB == 3) && LDS_BYTES <= 160 * 1024, "ring");
     static_assert(!SH || (NB == 2 && SCHED == 1), "shifted rows: balanced schedule, two B slots");
     static_assert(!SPLIT || !OUT_BF16, "split-K partial tiles are fp32");
+    static_assert(!(AT || BT) || (!SH && !SPLIT && SCHED == 1 && NB == 2), "MN-contiguous operands: 16-byte rows");
 
     __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
 
@@ -306,6 +339,15 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
     uint32_t a_off[LPT], b_off[LPT];
     auto sh_row = [&](int j) __attribute__((always_inline)) { return ((4 * j + wave) * 64 + lane) / 9; };
     auto sh_chk = [&](int j) __attribute__((always_inline)) { return ((4 * j + wave) * 64 + lane) % 9; };
+    // MN-contiguous operand: load instruction j of a wave fills LDS rows
+    // 2 (4 j + wave) + lane / 32 of the tile (1 KiB: two 512-byte rows);
+    // lane L writes 16 bytes at physical chunk (L % 32) / 2, half L % 2, and
+    // fetches the columns of the logical chunk that lands there.
+    auto mn_off = [&](int64_t ld, int j) __attribute__((always_inline)) {
+        const int row = 2 * (4 * j + wave) + (lane >> 5);
+        const int lchk = ((lane & 31) >> 1) ^ (row & 3) ^ (((row >> 3) & 1) << 2);
+        return (uint32_t)((row * ld + lchk * 16 + (lane & 1) * 8) * 2);
+    };
 #pragma unroll
     for (int j = 0; j < LPT; ++j) {
         if constexpr (SH) {
@@ -314,8 +356,8 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
             b_off[j] = ((uint32_t)(b_mis0 + row * p.ldb * 2) & ~15u) + c * 16;
         } else {
             const int row = (4 * j + wave) * 8 + (lane >> 3);
-            a_off[j] = (uint32_t)(row * p.lda * 2) + chunk * 16;
-            b_off[j] = (uint32_t)(row * p.ldb * 2) + chunk * 16;
+            a_off[j] = AT ? mn_off(p.lda, j) : (uint32_t)(row * p.lda * 2) + chunk * 16;
+            b_off[j] = BT ? mn_off(p.ldb, j) : (uint32_t)(row * p.ldb * 2) + chunk * 16;
         }
     }
     // SH: K element (relative to the tile's K offset) at which chunk c of
@@ -343,13 +385,37 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
             dma_load<16>(r, d, off);
         }
     };
+    // MN-contiguous operand, K tile t: a resource based at row 64 t, column
+    // e0 of the K x (M or N) storage, ending with the 16-byte block that
+    // holds the last row's last element.  (The range check is per dword: an
+    // odd M or N would otherwise lose the last element of row K - 1 with the
+    // dword it shares.  The base is 16-byte aligned -- aligned operand, ld
+    // a multiple of 8, e0 a multiple of 256 -- so the block lies in the same
+    // page as that element.)
+    auto dma_mn = [&](const void *base, int64_t ld, int e0, int ext, char *d, uint32_t voff, int t)
+        __attribute__((always_inline)) {
+        const int k0 = t * KT;
+        const uint32_t span = (span_bytes(K - k0, ext - e0, ld, 2) + 15u) & ~15u;
+        const __amdgpu_buffer_rsrc_t r = make_rsrc((const char *)base + ((int64_t)k0 * ld + e0) * 2, span);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)d, 16, voff, 0, 0, 0);
+    };
     auto dma_a = [&](auto so, int t, int j) __attribute__((always_inline)) {
-        const int kelj = SH ? sh_kel(a_mis0, p.lda, j) : kel;
-        dma(so, rA, smem + (t % NA) * SLOT + (j * 4 + wave) * IB, a_off[j], t, kelj);
+        char *d = smem + (t % NA) * SLOT + (j * 4 + wave) * IB;
+        if constexpr (AT) {
+            dma_mn(p.A, p.lda, m0, M, d, a_off[j], t);
+        } else {
+            const int kelj = SH ? sh_kel(a_mis0, p.lda, j) : kel;
+            dma(so, rA, d, a_off[j], t, kelj);
+        }
     };
     auto dma_b = [&](auto so, int t, int j) __attribute__((always_inline)) {
-        const int kelj = SH ? sh_kel(b_mis0, p.ldb, j) : kel;
-        dma(so, rB, smem + B_BASE + (t % NB) * SLOT + (j * 4 + wave) * IB, b_off[j], t, kelj);
+        char *d = smem + B_BASE + (t % NB) * SLOT + (j * 4 + wave) * IB;
+        if constexpr (BT) {
+            dma_mn(p.B, p.ldb, n0, N, d, b_off[j], t);
+        } else {
+            const int kelj = SH ? sh_kel(b_mis0, p.ldb, j) : kel;
+            dma(so, rB, d, b_off[j], t, kelj);
+        }
     };
     // SH, last K tile nt - 1 (after its loads landed, before the barrier
     // that publishes it): each chunk whose first half is inside K and second
@@ -400,6 +466,37 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
         } else {
             return *(const u32x4 *)(smem + addr);
         }
+    };
+
+    // MN-contiguous operand: lane (group q, i = lane % 16) reads, for block b
+    // (columns 16 b .. 16 b + 15 of the wave's 128), rows 32 st + 8 q + 4 h +
+    // i / 4 (h = 0, 1: K 8 q .. 8 q + 3 and 8 q + 4 .. 8 q + 7 of step st) at
+    // columns 4 (i % 4) .. + 3.  The chunk's swizzle depends only on i / 4
+    // and q % 2, so per block one lane-dependent base holds the XOR and the
+    // slot, step and half go in the read's immediate offset.
+    auto mn_base = [&](int wb, int b) __attribute__((always_inline)) {
+        const int g = (fr >> 2) ^ ((fq & 1) << 2);
+        return (8 * fq + (fr >> 2)) * 512 + (wb * 8 + (b ^ g)) * 32 + (fr & 3) * 8;
+    };
+    int a_mn[AT ? TM : 1], b_mn[BT ? TN : 1];
+#pragma unroll
+    for (int b = 0; b < (AT ? TM : 1); ++b) a_mn[b] = AT ? mn_base(wm, b) : 0;
+#pragma unroll
+    for (int b = 0; b < (BT ? TN : 1); ++b) b_mn[b] = BT ? B_BASE + mn_base(wn, b) : 0;
+    // The transpose reads are asm: through the compiler builtin every read
+    // waited for all direct-to-LDS loads in flight (the compiler cannot tell
+    // it from a write into the slots being loaded), which serialised the
+    // loads of tile t + 1 with the reads of tile t.  Uncounted, they make the
+    // compiler's own lgkmcnt waits only stricter; their own results are
+    // waited for explicitly (tr_row_wait, and lgkmcnt(0) at each window's
+    // end).
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char *)smem;
+    auto ldfrag_tr = [&](int addr) __attribute__((always_inline)) {
+        u32x2 lo, hi;
+        const uint32_t a = lds0 + (uint32_t)addr;
+        asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(lo) : "v"(a));
+        asm volatile("ds_read_b64_tr_b16 %0, %1 offset:2048" : "=v"(hi) : "v"(a));
+        return u32x4{lo[0], lo[1], hi[0], hi[1]};
     };
 
     // Accumulators in AGPRs, updated in place by volatile asm MFMAs; a
@@ -454,10 +551,16 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
         const int coff = ((4 * st + fq) ^ fswz) << 4;
         if (k == 0 || k >= 9) {
             const int i = k == 0 ? 0 : k - 8;
-            fa[st][i] = ldfrag((t % NA) * SLOT + a_read + i * 16 * ROWB + coff);
+            if constexpr (AT)
+                fa[st][i] = ldfrag_tr(a_mn[i] + (t % NA) * SLOT + st * 32 * 512);
+            else
+                fa[st][i] = ldfrag((t % NA) * SLOT + a_read + i * 16 * ROWB + coff);
         } else {
             const int j = k - 1;
-            fb[st][j] = ldfrag(B_BASE + (t % NB) * SLOT + b_read + j * 16 * ROWB + coff);
+            if constexpr (BT)
+                fb[st][j] = ldfrag_tr(b_mn[j] + (t % NB) * SLOT + st * 32 * 512);
+            else
+                fb[st][j] = ldfrag(B_BASE + (t % NB) * SLOT + b_read + j * 16 * ROWB + coff);
         }
     };
     // B is the MFMA's first operand and A its second, so block (i, j) holds
@@ -503,6 +606,18 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
             }
 #pragma unroll
             for (int q = 0; q < 64; ++q) {
+                if constexpr (AT || BT) {
+                    constexpr int CA = AT ? 2 : 1, CB = BT ? 2 : 1;
+                    if (q % TN == 0) {
+                        switch (q / TN) {
+#define TG_TR_WAIT(i) \
+    case i: __builtin_amdgcn_s_waitcnt(0xC07F | (tr_row_wait<CA, CB>(i) << 8)); break;
+                            TG_TR_WAIT(0) TG_TR_WAIT(1) TG_TR_WAIT(2) TG_TR_WAIT(3)
+                            TG_TR_WAIT(4) TG_TR_WAIT(5) TG_TR_WAIT(6) TG_TR_WAIT(7)
+#undef TG_TR_WAIT
+                        }
+                    }
+                }
                 mfma(first, 0, q / TN, q % TN);
                 if (q % 3 == 0 && q / 3 < 16) read_frag(t, 1, q / 3);
                 if constexpr (NB == 3) {

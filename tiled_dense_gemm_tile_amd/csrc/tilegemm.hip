@@ -170,6 +170,60 @@ gemm_status run_f16(bool fp16, const Common &a, hipStream_t s) {
     return a.out_type == GEMM_OUT_BF16 ? dispatch_f16<false, true>(a, s) : dispatch_f16<false, false>(a, s);
 }
 
+// ---- operand storage orders (16-bit inputs) ---------------------------------
+
+gemm_status run_f16_ex(bool fp16, const Common &a, int a_order, int b_order, hipStream_t s) {
+    if ((a_order != GEMM_K_CONTIGUOUS && a_order != GEMM_MN_CONTIGUOUS) ||
+        (b_order != GEMM_K_CONTIGUOUS && b_order != GEMM_MN_CONTIGUOUS))
+        return GEMM_ERR_UNSUPPORTED;
+    if (a_order == GEMM_K_CONTIGUOUS && b_order == GEMM_K_CONTIGUOUS) return run_f16(fp16, a, s);
+    const bool at = a_order == GEMM_MN_CONTIGUOUS, bt = b_order == GEMM_MN_CONTIGUOUS;
+    if (a.M < 0 || a.N < 0 || a.K < 0) return GEMM_ERR_INVALID_SIZE;
+    // an MN-contiguous operand's leading dimension spans its M (N) elements
+    if (a.M > 0 && a.N > 0 && ((at && a.lda < a.M) || (bt && a.ldb < a.N))) return GEMM_ERR_BAD_LD;
+    Common v = a;
+    if (at) v.lda = a.K;                               // checked above
+    if (bt) v.ldb = a.K;
+    bool none = false;
+    gemm_status st = validate(v, &none);
+    if (st != GEMM_OK || none) return st;
+    if ((at && a.lda * 2 >= kMaxLdBytes) || (bt && a.ldb * 2 >= kMaxLdBytes)) return GEMM_ERR_UNSUPPORTED;
+    // this kernel: 16-byte rows for both operands
+    const bool rows16 = (uintptr_t)a.A % 16 == 0 && (uintptr_t)a.B % 16 == 0 && a.lda % 8 == 0 && a.ldb % 8 == 0 &&
+                        ((at && bt) || a.K % 8 == 0);
+    if (!rows16 && a.K > 0) return GEMM_ERR_UNSUPPORTED;
+    tg::F16Args p;
+    p.A = a.A ? a.A : a.D;                             // K == 0 reads no operand
+    p.B = a.B ? a.B : a.D;
+    p.C = a.C;
+    p.D = a.D;
+    p.lda = a.lda;
+    p.ldb = a.ldb;
+    p.ldc = a.ldc;
+    p.ldd = a.ldd;
+    p.M = (int)a.M;
+    p.N = (int)a.N;
+    p.K = (int)a.K;
+    p.group_m = 4;
+    p.tiles_m = (int)((a.M + 255) / 256);
+    p.tiles_n = (int)((a.N + 255) / 256);
+    const int64_t tiles = (int64_t)p.tiles_m * p.tiles_n;
+    if (tiles >= kMaxDim) return GEMM_ERR_UNSUPPORTED;
+    const bool bf16 = a.out_type == GEMM_OUT_BF16;
+    const uintptr_t vb = (uintptr_t)(bf16 ? 2 : 4) * 4;
+    tg::F16Epi e;
+    e.vec_d = ((uintptr_t)a.D % vb) == 0 && a.ldd % 4 == 0;
+    e.vec_c = a.C && ((uintptr_t)a.C % vb) == 0 && a.ldc % 4 == 0;
+    hipError_t err;
+    if (fp16)
+        err = bf16 ? tg::launch_f16_mn<true, true>(at, bt, (unsigned)tiles, s, p, e)
+                   : tg::launch_f16_mn<true, false>(at, bt, (unsigned)tiles, s, p, e);
+    else
+        err = bf16 ? tg::launch_f16_mn<false, true>(at, bt, (unsigned)tiles, s, p, e)
+                   : tg::launch_f16_mn<false, false>(at, bt, (unsigned)tiles, s, p, e);
+    return launched(err);
+}
+
 // ---- split-K (16-bit inputs) ------------------------------------------------
 
 constexpr int kMaxSplits = 64;
@@ -382,6 +436,20 @@ gemm_status gemm_fp16(int64_t M, int64_t N, int64_t K, const void *A, int64_t ld
                       const void *C, int64_t ldc, void *D, int64_t ldd, int out_type, hipStream_t stream) {
     Common a{M, N, K, A, lda, B, ldb, C, ldc, D, ldd, out_type, 2};
     return run_f16(true, a, stream);
+}
+
+gemm_status gemm_bf16_ex(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int a_order, const void *B,
+                         int64_t ldb, int b_order, const void *C, int64_t ldc, void *D, int64_t ldd, int out_type,
+                         hipStream_t stream) {
+    Common a{M, N, K, A, lda, B, ldb, C, ldc, D, ldd, out_type, 2};
+    return run_f16_ex(false, a, a_order, b_order, stream);
+}
+
+gemm_status gemm_fp16_ex(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int a_order, const void *B,
+                         int64_t ldb, int b_order, const void *C, int64_t ldc, void *D, int64_t ldd, int out_type,
+                         hipStream_t stream) {
+    Common a{M, N, K, A, lda, B, ldb, C, ldc, D, ldd, out_type, 2};
+    return run_f16_ex(true, a, a_order, b_order, stream);
 }
 
 size_t gemm_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K, int splits) {

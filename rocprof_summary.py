@@ -52,18 +52,21 @@ def _include_closure(name, seen):
             line = line.strip()
             if line.startswith('#include "'):
                 inc = line.split('"')[1]
-                if os.path.exists(os.path.join(CSRC, inc)):
+                # (the public header holds declarations only: not hashed)
+                if not inc.startswith("..") and os.path.exists(os.path.join(CSRC, inc)):
                     _include_closure(inc, seen)
 
 
 def kernel_source_hash(workload: str) -> str:
     """Hash of the sources a workload's kernels are built from: its instance
-    file with everything it includes, and the dispatch code."""
+    file and its family's entry-point file (validation and dispatch) with
+    everything they include."""
     from tiled_dense_gemm_tile_amd import inputs
     w = inputs.WORKLOADS[workload]
     files = set()
     _include_closure(instance_file(w.in_type, w.out_type), files)
-    files.add("tilegemm.hip")
+    api = {"e4m3": "mx_api.hip", "e2m1": "mx4_api.hip"}.get(w.in_type, "tilegemm.hip")
+    _include_closure(api, files)
     if w.in_type in ("bf16", "fp16"):
         _include_closure("splitk.hip", files)          # the split-K reduction
     h = hashlib.sha256()

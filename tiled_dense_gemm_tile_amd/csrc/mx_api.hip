@@ -1,0 +1,92 @@
+// C ABI of the tiled GEMM library, block-scaled fp8 inputs: argument
+// validation, kernel selection and launch on the caller's stream.  The
+// declarations and their contract are in include/tilegemm.h.
+#include <stdlib.h>
+
+#include "api.hpp"
+#include "mx_launch.hpp"
+
+using namespace tg_api;
+
+namespace {
+
+int forced_mx_cfg() {
+    const char *e = getenv("TILEGEMM_MX_CONFIG");
+    if (!e || !*e) return -1;
+    const int id = atoi(e);
+    return (id >= 0 && id < tg::kNumMxCfgs) ? id : -1;
+}
+
+gemm_status dispatch_mx(const Common &a, const void *SFA, int64_t ldsfa, const void *SFB, int64_t ldsfb,
+                        hipStream_t s) {
+    // The kernel streams 16-byte A/B chunks and 4-byte scale words per K tile of 128.
+    const bool fast = a.K % 128 == 0 && (uintptr_t)a.A % 16 == 0 && (uintptr_t)a.B % 16 == 0 && a.lda % 16 == 0 &&
+                      a.ldb % 16 == 0 && (uintptr_t)SFA % 4 == 0 && (uintptr_t)SFB % 4 == 0 && ldsfa % 4 == 0 &&
+                      ldsfb % 4 == 0;
+    if (!fast && a.K > 0) return GEMM_ERR_UNSUPPORTED;
+    // The four-wave and ping-pong kernels load a row's scales 16 bytes (512
+    // K) at a time, so they need 16-byte-aligned scale rows and whole groups
+    // of 16 blocks.
+    const bool scales16 = a.K % 512 == 0 && (uintptr_t)SFA % 16 == 0 && (uintptr_t)SFB % 16 == 0 &&
+                          ldsfa % 16 == 0 && ldsfb % 16 == 0;
+    int cfg = forced_mx_cfg();
+    if ((cfg == tg::kMxPingPong || cfg == tg::kMxFourWave) && !scales16) cfg = -1;
+    if (cfg < 0) {
+        if (tiles_of(a, 256, 256) >= 240)
+            cfg = scales16 ? tg::kMxFourWave : 1;
+        else
+            cfg = tiles_of(a, 128, 128) >= 240 ? 2 : 3;
+    }
+    tg::MxArgs q;
+    q.g.A = a.A;
+    q.g.B = a.B;
+    q.g.C = a.C;
+    q.g.D = a.D;
+    q.g.lda = a.lda;
+    q.g.ldb = a.ldb;
+    q.g.ldc = a.ldc;
+    q.g.ldd = a.ldd;
+    q.g.M = (int)a.M;
+    q.g.N = (int)a.N;
+    q.g.K = (int)a.K;
+    q.g.group_m = 4;
+    q.g.tiles_m = (int)((a.M + tg::kMxCfgs[cfg].bm - 1) / tg::kMxCfgs[cfg].bm);
+    q.g.tiles_n = (int)((a.N + tg::kMxCfgs[cfg].bn - 1) / tg::kMxCfgs[cfg].bn);
+    // K == 0 reads no scales: any valid address stands in for NULL ones
+    q.SFA = SFA ? SFA : a.D;
+    q.SFB = SFB ? SFB : a.D;
+    q.ldsfa = ldsfa;
+    q.ldsfb = ldsfb;
+    const int64_t tiles = (int64_t)q.g.tiles_m * q.g.tiles_n;
+    if (tiles >= kMaxDim) return GEMM_ERR_UNSUPPORTED;
+    const bool bf16 = a.out_type == GEMM_OUT_BF16;
+    const int os = bf16 ? 2 : 4;
+    const uintptr_t vb = (uintptr_t)os * 4;
+    tg::F16Epi e;
+    e.vec_d = ((uintptr_t)a.D % vb) == 0 && a.ldd % 4 == 0;
+    e.vec_c = a.C && ((uintptr_t)a.C % vb) == 0 && a.ldc % 4 == 0;
+    return launched(bf16 ? tg::launch_mx<true>(cfg, (unsigned)tiles, s, q, e)
+                         : tg::launch_mx<false>(cfg, (unsigned)tiles, s, q, e));
+}
+
+}  // namespace
+
+extern "C" {
+
+gemm_status gemm_mxfp8(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *SFA, int64_t ldsfa,
+                       const void *B, int64_t ldb, const void *SFB, int64_t ldsfb, const void *C, int64_t ldc,
+                       void *D, int64_t ldd, int out_type, hipStream_t stream) {
+    Common a{M, N, K, A, lda, B, ldb, C, ldc, D, ldd, out_type, 1};
+    bool none = false;
+    gemm_status st = validate(a, &none);
+    if (st != GEMM_OK || none) return st;
+    if (K > 0) {
+        if (ldsfa < K / 32 || ldsfb < K / 32) return GEMM_ERR_BAD_LD;
+        if (!SFA || !SFB) return GEMM_ERR_NULL_POINTER;
+    }
+    if (K % 32 != 0) return GEMM_ERR_UNSUPPORTED;
+    if (ldsfa >= kMaxLdBytes || ldsfb >= kMaxLdBytes) return GEMM_ERR_UNSUPPORTED;
+    return dispatch_mx(a, SFA, ldsfa, SFB, ldsfb, stream);
+}
+
+}  // extern "C"

@@ -1,82 +1,15 @@
-// C ABI of the tiled GEMM library: argument validation, kernel selection
-// and launch on the caller's stream.  The declarations and their contract
-// are in include/tilegemm.h.
-#include "../../include/tilegemm.h"
-
-#include <hip/hip_runtime.h>
-#include <stdint.h>
-
+// C ABI of the tiled GEMM library, 16-bit inputs: argument validation,
+// kernel selection and launch on the caller's stream, plus the status
+// helpers.  The declarations and their contract are in include/tilegemm.h.
 #include <stdlib.h>
 
+#include "api.hpp"
 #include "f16_launch.hpp"
-#include "mx4_launch.hpp"
-#include "mx_launch.hpp"
 #include "splitk.hpp"
 
+using namespace tg_api;
+
 namespace {
-
-thread_local int g_last_hip_error = 0;
-
-constexpr int64_t kMaxDim = (int64_t)1 << 31;
-// Each tile's rows are addressed with 32-bit offsets from a per-tile base:
-// 256 rows of the widest leading dimension must stay below 2^31 bytes.
-constexpr int64_t kMaxLdBytes = ((int64_t)1 << 31) / 256;
-
-struct Common {
-    int64_t M, N, K;
-    const void *A;
-    int64_t lda;
-    const void *B;
-    int64_t ldb;
-    const void *C;
-    int64_t ldc;
-    void *D;
-    int64_t ldd;
-    int out_type;
-    int in_size;   // bytes per A/B element
-};
-
-bool misaligned(const void *p, int size) { return p && (((uintptr_t)p) % (uintptr_t)size) != 0; }
-
-// Validation shared by every entry point; returns GEMM_OK when a launch may
-// proceed (and sets *nothing_to_do when M or N is zero).
-gemm_status validate(const Common &a, bool *nothing_to_do) {
-    *nothing_to_do = false;
-    if (a.M < 0 || a.N < 0 || a.K < 0) return GEMM_ERR_INVALID_SIZE;
-    if (a.M >= kMaxDim || a.N >= kMaxDim || a.K >= kMaxDim) return GEMM_ERR_UNSUPPORTED;
-    if (a.out_type != GEMM_OUT_F32 && a.out_type != GEMM_OUT_BF16) return GEMM_ERR_UNSUPPORTED;
-    if (a.M == 0 || a.N == 0) {
-        *nothing_to_do = true;
-        return GEMM_OK;
-    }
-    if (a.lda < a.K || a.ldb < a.K || a.ldd < a.N || (a.C && a.ldc < a.N)) return GEMM_ERR_BAD_LD;
-    if (!a.D) return GEMM_ERR_NULL_POINTER;
-    if (a.K > 0 && (!a.A || !a.B)) return GEMM_ERR_NULL_POINTER;
-    const int os = a.out_type == GEMM_OUT_BF16 ? 2 : 4;
-    if (misaligned(a.A, a.in_size) || misaligned(a.B, a.in_size) || misaligned(a.C, os) ||
-        misaligned(a.D, os))
-        return GEMM_ERR_MISALIGNED;
-    if (a.lda * a.in_size >= kMaxLdBytes || a.ldb * a.in_size >= kMaxLdBytes ||
-        a.ldd * os >= kMaxLdBytes || (a.C && a.ldc * os >= kMaxLdBytes))
-        return GEMM_ERR_UNSUPPORTED;
-    if (a.C && a.C != a.D) {
-        const uintptr_t c0 = (uintptr_t)a.C, c1 = c0 + (uintptr_t)(((a.M - 1) * a.ldc + a.N) * os);
-        const uintptr_t d0 = (uintptr_t)a.D, d1 = d0 + (uintptr_t)(((a.M - 1) * a.ldd + a.N) * os);
-        if (c0 < d1 && d0 < c1) return GEMM_ERR_UNSUPPORTED;
-    }
-    if (a.C && a.C == a.D && a.ldc != a.ldd) return GEMM_ERR_UNSUPPORTED;
-    return GEMM_OK;
-}
-
-gemm_status launched(hipError_t e) {
-    if (e != hipSuccess) {
-        g_last_hip_error = (int)e;
-        return GEMM_ERR_HIP;
-    }
-    return GEMM_OK;
-}
-
-// ---- 16-bit inputs ------------------------------------------------------
 
 // Widest vector (in elements) that every row start and K boundary allows.
 int pick_vec(const Common &a) {
@@ -88,8 +21,6 @@ int pick_vec(const Common &a) {
     }
     return 1;
 }
-
-int64_t tiles_of(const Common &a, int bm, int bn) { return ((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn); }
 
 // Tuning override: TILEGEMM_F16_CONFIG=<id> forces one direct-to-LDS
 // configuration (read at every call; ignored when out of range).
@@ -317,111 +248,6 @@ gemm_status run_f16_splitk(bool fp16, const Common &a, int splits, void *ws, siz
     return launched(tg::launch_splitk_reduce(bf16, s, r));
 }
 
-// ---- block-scaled fp8 ------------------------------------------------------
-
-int forced_mx_cfg() {
-    const char *e = getenv("TILEGEMM_MX_CONFIG");
-    if (!e || !*e) return -1;
-    const int id = atoi(e);
-    return (id >= 0 && id < tg::kNumMxCfgs) ? id : -1;
-}
-
-gemm_status dispatch_mx(const Common &a, const void *SFA, int64_t ldsfa, const void *SFB, int64_t ldsfb,
-                        hipStream_t s) {
-    // The kernel streams 16-byte A/B chunks and 4-byte scale words per K tile of 128.
-    const bool fast = a.K % 128 == 0 && (uintptr_t)a.A % 16 == 0 && (uintptr_t)a.B % 16 == 0 && a.lda % 16 == 0 &&
-                      a.ldb % 16 == 0 && (uintptr_t)SFA % 4 == 0 && (uintptr_t)SFB % 4 == 0 && ldsfa % 4 == 0 &&
-                      ldsfb % 4 == 0;
-    if (!fast && a.K > 0) return GEMM_ERR_UNSUPPORTED;
-    // The four-wave and ping-pong kernels load a row's scales 16 bytes (512
-    // K) at a time, so they need 16-byte-aligned scale rows and whole groups
-    // of 16 blocks.
-    const bool scales16 = a.K % 512 == 0 && (uintptr_t)SFA % 16 == 0 && (uintptr_t)SFB % 16 == 0 &&
-                          ldsfa % 16 == 0 && ldsfb % 16 == 0;
-    int cfg = forced_mx_cfg();
-    if ((cfg == tg::kMxPingPong || cfg == tg::kMxFourWave) && !scales16) cfg = -1;
-    if (cfg < 0) {
-        if (tiles_of(a, 256, 256) >= 240)
-            cfg = scales16 ? tg::kMxFourWave : 1;
-        else
-            cfg = tiles_of(a, 128, 128) >= 240 ? 2 : 3;
-    }
-    tg::MxArgs q;
-    q.g.A = a.A;
-    q.g.B = a.B;
-    q.g.C = a.C;
-    q.g.D = a.D;
-    q.g.lda = a.lda;
-    q.g.ldb = a.ldb;
-    q.g.ldc = a.ldc;
-    q.g.ldd = a.ldd;
-    q.g.M = (int)a.M;
-    q.g.N = (int)a.N;
-    q.g.K = (int)a.K;
-    q.g.group_m = 4;
-    q.g.tiles_m = (int)((a.M + tg::kMxCfgs[cfg].bm - 1) / tg::kMxCfgs[cfg].bm);
-    q.g.tiles_n = (int)((a.N + tg::kMxCfgs[cfg].bn - 1) / tg::kMxCfgs[cfg].bn);
-    // K == 0 reads no scales: any valid address stands in for NULL ones
-    q.SFA = SFA ? SFA : a.D;
-    q.SFB = SFB ? SFB : a.D;
-    q.ldsfa = ldsfa;
-    q.ldsfb = ldsfb;
-    const int64_t tiles = (int64_t)q.g.tiles_m * q.g.tiles_n;
-    if (tiles >= kMaxDim) return GEMM_ERR_UNSUPPORTED;
-    const bool bf16 = a.out_type == GEMM_OUT_BF16;
-    const int os = bf16 ? 2 : 4;
-    const uintptr_t vb = (uintptr_t)os * 4;
-    tg::F16Epi e;
-    e.vec_d = ((uintptr_t)a.D % vb) == 0 && a.ldd % 4 == 0;
-    e.vec_c = a.C && ((uintptr_t)a.C % vb) == 0 && a.ldc % 4 == 0;
-    return launched(bf16 ? tg::launch_mx<true>(cfg, (unsigned)tiles, s, q, e)
-                         : tg::launch_mx<false>(cfg, (unsigned)tiles, s, q, e));
-}
-
-// ---- block-scaled fp4 ------------------------------------------------------
-
-// a.lda and a.ldb are in elements (even); the kernel takes them in bytes.
-gemm_status dispatch_mx4(const Common &a, const void *SFA, int64_t ldsfa, const void *SFB, int64_t ldsfb,
-                         hipStream_t s) {
-    // 16-byte A/B chunks (32 elements), 16-byte scale words (512 K) per row
-    const bool fast = a.K % 512 == 0 && (uintptr_t)a.A % 16 == 0 && (uintptr_t)a.B % 16 == 0 && a.lda % 32 == 0 &&
-                      a.ldb % 32 == 0 && (uintptr_t)SFA % 16 == 0 && (uintptr_t)SFB % 16 == 0 &&
-                      ldsfa % 16 == 0 && ldsfb % 16 == 0;
-    if (!fast && a.K > 0) return GEMM_ERR_UNSUPPORTED;
-    tg::MxArgs q;
-    q.g.A = a.A;
-    q.g.B = a.B;
-    q.g.C = a.C;
-    q.g.D = a.D;
-    q.g.lda = a.lda / 2;
-    q.g.ldb = a.ldb / 2;
-    q.g.ldc = a.ldc;
-    q.g.ldd = a.ldd;
-    q.g.M = (int)a.M;
-    q.g.N = (int)a.N;
-    q.g.K = (int)a.K;
-    q.g.group_m = 4;
-    q.g.tiles_m = (int)((a.M + 255) / 256);
-    q.g.tiles_n = (int)((a.N + 255) / 256);
-    // K == 0 reads no operand or scale: any valid address stands in for NULL ones
-    if (!q.g.A) q.g.A = a.D;
-    if (!q.g.B) q.g.B = a.D;
-    q.SFA = SFA ? SFA : a.D;
-    q.SFB = SFB ? SFB : a.D;
-    q.ldsfa = ldsfa;
-    q.ldsfb = ldsfb;
-    const int64_t tiles = (int64_t)q.g.tiles_m * q.g.tiles_n;
-    if (tiles >= kMaxDim) return GEMM_ERR_UNSUPPORTED;
-    const bool bf16 = a.out_type == GEMM_OUT_BF16;
-    const int os = bf16 ? 2 : 4;
-    const uintptr_t vb = (uintptr_t)os * 4;
-    tg::F16Epi e;
-    e.vec_d = ((uintptr_t)a.D % vb) == 0 && a.ldd % 4 == 0;
-    e.vec_c = a.C && ((uintptr_t)a.C % vb) == 0 && a.ldc % 4 == 0;
-    return launched(bf16 ? tg::launch_mx4<true>((unsigned)tiles, s, q, e)
-                         : tg::launch_mx4<false>((unsigned)tiles, s, q, e));
-}
-
 }  // namespace
 
 extern "C" {
@@ -469,44 +295,6 @@ gemm_status gemm_fp16_splitk(int64_t M, int64_t N, int64_t K, const void *A, int
                              void *workspace, size_t workspace_bytes, hipStream_t stream) {
     Common a{M, N, K, A, lda, B, ldb, C, ldc, D, ldd, out_type, 2};
     return run_f16_splitk(true, a, splits, workspace, workspace_bytes, stream);
-}
-
-gemm_status gemm_mxfp8(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *SFA, int64_t ldsfa,
-                       const void *B, int64_t ldb, const void *SFB, int64_t ldsfb, const void *C, int64_t ldc,
-                       void *D, int64_t ldd, int out_type, hipStream_t stream) {
-    Common a{M, N, K, A, lda, B, ldb, C, ldc, D, ldd, out_type, 1};
-    bool none = false;
-    gemm_status st = validate(a, &none);
-    if (st != GEMM_OK || none) return st;
-    if (K > 0) {
-        if (ldsfa < K / 32 || ldsfb < K / 32) return GEMM_ERR_BAD_LD;
-        if (!SFA || !SFB) return GEMM_ERR_NULL_POINTER;
-    }
-    if (K % 32 != 0) return GEMM_ERR_UNSUPPORTED;
-    if (ldsfa >= kMaxLdBytes || ldsfb >= kMaxLdBytes) return GEMM_ERR_UNSUPPORTED;
-    return dispatch_mx(a, SFA, ldsfa, SFB, ldsfb, stream);
-}
-
-gemm_status gemm_mxfp4(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *SFA, int64_t ldsfa,
-                       const void *B, int64_t ldb, const void *SFB, int64_t ldsfb, const void *C, int64_t ldc,
-                       void *D, int64_t ldd, int out_type, hipStream_t stream) {
-    Common a{M, N, K, A, lda, B, ldb, C, ldc, D, ldd, out_type, 1};
-    bool none = false;
-    // A and B extents validated in bytes (half the element counts; for even
-    // K, lda / 2 < K / 2 exactly when lda < K, and odd K is unsupported)
-    Common bytes = a;
-    bytes.K = K / 2;
-    bytes.lda = lda / 2;
-    bytes.ldb = ldb / 2;
-    gemm_status st = validate(bytes, &none);
-    if (st != GEMM_OK || none) return st;
-    if (K >= kMaxDim || K % 32 != 0 || lda % 2 != 0 || ldb % 2 != 0) return GEMM_ERR_UNSUPPORTED;
-    if (K > 0) {
-        if (ldsfa < K / 32 || ldsfb < K / 32) return GEMM_ERR_BAD_LD;
-        if (!SFA || !SFB) return GEMM_ERR_NULL_POINTER;
-    }
-    if (ldsfa >= kMaxLdBytes || ldsfb >= kMaxLdBytes) return GEMM_ERR_UNSUPPORTED;
-    return dispatch_mx4(a, SFA, ldsfa, SFB, ldsfb, stream);
 }
 
 const char *gemm_status_string(int s) {

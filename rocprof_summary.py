@@ -128,6 +128,9 @@ def main():
     ap.add_argument("--skip-traffic", action="store_true")
     ap.add_argument("--skip-counters", action="store_true")
     ap.add_argument("--dest", default=PROFILES, help="directory the summaries are written to")
+    ap.add_argument("--reparse", action="store_true",
+                    help="counters: rewrite the summary from the csv files already under --out-dir "
+                         "(no GPU run)")
     args = ap.parse_args()
     os.makedirs(args.out_dir, exist_ok=True)
     os.makedirs(args.dest, exist_ok=True)
@@ -201,7 +204,8 @@ def main():
                   ["TCC_HIT", "TCC_MISS"]]
         lines = ["# rocprofv3 counters: %s" % args.workload, "kernel sources: %s" % src_hash, ""]
         for i, pc in enumerate(passes):
-            d = pmc(pc, short, args.out_dir, "pmc_pass%d" % i)
+            d = os.path.join(args.out_dir, "pmc_pass%d" % i) if args.reparse else pmc(pc, short, args.out_dir,
+                                                                                     "pmc_pass%d" % i)
             per = counter_per_dispatch(d, kname)
             did = sorted(per)[-1]
             lines.append("command: rocprofv3 --pmc %s -- %s" % (" ".join(pc), " ".join(short)))
@@ -218,10 +222,12 @@ def main():
                 lines.append("  MFMA busy fraction = (busy / 1024) / (gui_active / 8) = %.3f"
                              % ((per[did]["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024) / (per[did]["GRBM_GUI_ACTIVE"] / 8)))
                 if per[did].get("duration_ns"):
+                    # (the counters' window can extend past the dispatch's
+                    # timestamps, so this overestimates the clock)
                     ghz = per[did]["GRBM_GUI_ACTIVE"] / 8 / per[did]["duration_ns"]
-                    lines.append("  shader clock over this dispatch = (gui_active / 8) / duration = %.3f GHz "
-                                 "(%.1f us); the dense peak at this clock is %.1f %% of the 2.4 GHz figure"
-                                 % (ghz, per[did]["duration_ns"] / 1e3, 100 * ghz / 2.4))
+                    lines.append("  clock bound = (gui_active / 8) / dispatch duration = %.3f GHz (%.1f us; an "
+                                 "upper bound: gui_active may count past the dispatch's timestamps)"
+                                 % (ghz, per[did]["duration_ns"] / 1e3))
             lines.append("")
         out = os.path.join(args.dest, "%s_%s_counters.txt" % (kname, args.workload))
         with open(out, "w") as f:

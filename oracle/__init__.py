@@ -44,8 +44,9 @@ _SRC = os.path.join(_HERE, "oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
 # element type codes, mirrored from oracle.c
-BF16, FP16, E4M3, F32, E2M1 = 0, 1, 2, 3, 4
-TYPE_CODES = {"bf16": BF16, "fp16": FP16, "e4m3": E4M3, "f32": F32, "e2m1": E2M1}
+BF16, FP16, E4M3, F32, E2M1, E2M3, E3M2 = 0, 1, 2, 3, 4, 5, 6
+TYPE_CODES = {"bf16": BF16, "fp16": FP16, "e4m3": E4M3, "f32": F32, "e2m1": E2M1, "e2m3": E2M3, "e3m2": E3M2}
+FP6 = ("e2m3", "e3m2")
 
 _lock = threading.Lock()
 _lib = None
@@ -80,6 +81,8 @@ def lib():
             for name, arg in (("orc_dec_bf16", ctypes.c_uint16), ("orc_dec_fp16", ctypes.c_uint16),
                               ("orc_dec_e4m3", ctypes.c_uint8), ("orc_dec_e8m0", ctypes.c_uint8),
                               ("orc_dec_e2m1", ctypes.c_uint8),
+                              ("orc_dec_e2m3", ctypes.c_uint8),
+                              ("orc_dec_e3m2", ctypes.c_uint8),
                               ("orc_dec_f32", ctypes.c_uint32)):
                 f = getattr(L, name)
                 f.restype = ctypes.c_double
@@ -127,6 +130,10 @@ def gemm_ref(in_type: str, A, B, K: int | None = None, C=None, c_type: str = "f3
     N, ldb = B.shape
     if in_type == "e2m1":                       # leading dimensions in elements
         lda, ldb = 2 * lda, 2 * ldb
+    elif in_type in FP6:
+        if lda % 3 or ldb % 3:
+            raise ValueError("fp6 rows are whole groups of three bytes")
+        lda, ldb = lda // 3 * 4, ldb // 3 * 4
     if K is None:
         K = lda
     if K > lda or K > ldb:
@@ -181,6 +188,26 @@ def dec_e2m1(bits: int) -> float:
     return lib().orc_dec_e2m1(int(bits))
 
 
+def dec_e2m3(bits: int) -> float:
+    return lib().orc_dec_e2m3(int(bits))
+
+
+def dec_e3m2(bits: int) -> float:
+    return lib().orc_dec_e3m2(int(bits))
+
+
+def unpack_fp6(packed) -> np.ndarray:
+    """(R, 3n) bytes of packed fp6 -> (R, 4n) six-bit codes, element k at
+    bits 6k .. 6k+5 of the row read as a little-endian bit string."""
+    p = np.asarray(packed, dtype=np.uint8)
+    g = p.reshape(p.shape[:-1] + (-1, 3)).astype(np.uint32)
+    w = g[..., 0] | (g[..., 1] << 8) | (g[..., 2] << 16)      # 24 bits: four elements
+    out = np.empty(p.shape[:-1] + (g.shape[-2], 4), dtype=np.uint8)
+    for j in range(4):
+        out[..., j] = (w >> (6 * j)) & 0x3F
+    return out.reshape(p.shape[:-1] + (-1,))
+
+
 def unpack_e2m1(packed) -> np.ndarray:
     """(R, n) bytes of packed e2m1 -> (R, 2n) codes, element 2i from the low nibble of byte i."""
     p = np.asarray(packed, dtype=np.uint8)
@@ -204,8 +231,9 @@ _TABLES: dict = {}
 def decode_table(in_type: str) -> np.ndarray:
     """Full lookup table code -> float64 built from the C decoders."""
     if in_type not in _TABLES:
-        f = {"bf16": dec_bf16, "fp16": dec_fp16, "e4m3": dec_e4m3, "e8m0": dec_e8m0, "e2m1": dec_e2m1}[in_type]
-        n = {"e4m3": 256, "e8m0": 256, "e2m1": 16}.get(in_type, 65536)
+        f = {"bf16": dec_bf16, "fp16": dec_fp16, "e4m3": dec_e4m3, "e8m0": dec_e8m0, "e2m1": dec_e2m1,
+             "e2m3": dec_e2m3, "e3m2": dec_e3m2}[in_type]
+        n = {"e4m3": 256, "e8m0": 256, "e2m1": 16, "e2m3": 64, "e3m2": 64}.get(in_type, 65536)
         _TABLES[in_type] = np.array([f(i) for i in range(n)], dtype=np.float64)
     return _TABLES[in_type]
 
@@ -244,6 +272,8 @@ def operands_f64(in_type: str, A, B, K=None, SFA=None, SFB=None):
     B = np.asarray(B)
     if in_type == "e2m1":
         A, B = unpack_e2m1(A), unpack_e2m1(B)
+    elif in_type in FP6:
+        A, B = unpack_fp6(A), unpack_fp6(B)
     if K is None:
         K = A.shape[1]
     a = decode(in_type, A[:, :K])

@@ -44,6 +44,13 @@
  *          in bits 0-3 and element 2i+1 in bits 4-7 of byte i (the block-
  *          scaled fp4 reading: the pages print no element format; this is
  *          the OCP microscaling FP4 type and its packing)
+ *  - e2m3: OCP MX FP6 E2M3, 1-2-3, bias 1, no infinities or NaN: max 7.5,
+ *          subnormals f/8; e3m2: OCP MX FP6 E3M2, 1-3-2, bias 3, no
+ *          infinities or NaN: max 28, subnormals f/16.  Packed six bits per
+ *          element: element k of a row occupies bits 6k .. 6k+5 of the row
+ *          read as a little-endian bit string (byte j holds bits 8j..8j+7),
+ *          four elements per three bytes (the block-scaled fp6 reading, as
+ *          for fp4)
  *
  * Build: gcc -O2 -fopenmp -shared -fPIC (no -ffast-math: the sums must be
  * plain IEEE binary64).
@@ -62,6 +69,8 @@ enum {
     ORC_E4M3 = 2,
     ORC_F32 = 3,
     ORC_E2M1 = 4,
+    ORC_E2M3 = 5,
+    ORC_E3M2 = 6,
 };
 
 enum {
@@ -129,6 +138,44 @@ double orc_dec_e2m1(uint8_t c)
     else
         v = ldexp(1.0 + (double)f / 2.0, e - 1);
     return s ? -v : v;
+}
+
+double orc_dec_e2m3(uint8_t c)
+{
+    int s = (c >> 5) & 1;
+    int e = (c >> 3) & 0x3;
+    int f = c & 0x7;
+    double v;
+    if (e == 0)
+        v = (double)f / 8.0;                      /* f/8 * 2^(1-1) */
+    else
+        v = ldexp(1.0 + (double)f / 8.0, e - 1);
+    return s ? -v : v;
+}
+
+double orc_dec_e3m2(uint8_t c)
+{
+    int s = (c >> 5) & 1;
+    int e = (c >> 2) & 0x7;
+    int f = c & 0x3;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f / 4.0, 1 - 3);        /* f/4 * 2^(1-3) */
+    else
+        v = ldexp(1.0 + (double)f / 4.0, e - 3);
+    return s ? -v : v;
+}
+
+/* Six-bit code k of a packed row: bits 6k .. 6k+5, little-endian. */
+static uint8_t fp6_code(const uint8_t *base, int64_t k)
+{
+    const int64_t bit = 6 * k;
+    const int64_t byte = bit >> 3;
+    const int sh = (int)(bit & 7);
+    unsigned v = base[byte];
+    if (sh > 2)                                   /* the field reaches into the next byte */
+        v |= (unsigned)base[byte + 1] << 8;
+    return (uint8_t)((v >> sh) & 0x3F);
 }
 
 double orc_dec_e8m0(uint8_t c)
@@ -211,6 +258,8 @@ static double dec_elem(int type, const void *base, int64_t i)
         uint8_t byte = ((const uint8_t *)base)[i / 2];
         return orc_dec_e2m1((uint8_t)((i & 1) ? byte >> 4 : byte & 0xF));
     }
+    case ORC_E2M3: return orc_dec_e2m3(fp6_code((const uint8_t *)base, i));
+    case ORC_E3M2: return orc_dec_e3m2(fp6_code((const uint8_t *)base, i));
     case ORC_F32: {
         return orc_dec_f32(((const uint32_t *)base)[i]);
     }
@@ -245,10 +294,12 @@ static void one_element(int in_type, int64_t m, int64_t n, int64_t K,
 /*
  * oracle_gemm -- evaluate D_ref and S at chosen output elements.
  *
- *   in_type : ORC_BF16, ORC_FP16, ORC_E4M3 or ORC_E2M1 (A and B share it;
- *             ORC_E2M1 only in the block-scaled form)
+ *   in_type : ORC_BF16, ORC_FP16, ORC_E4M3, ORC_E2M1, ORC_E2M3 or ORC_E3M2
+ *             (A and B share it; the fp4 and fp6 types only in the
+ *             block-scaled form)
  *   A       : M x K, row-major, leading dimension lda (elements; for
- *             ORC_E2M1 even, two elements per byte)
+ *             ORC_E2M1 even, two elements per byte; for the fp6 types a
+ *             multiple of 4, four elements per three bytes)
  *   B       : column-major K x N stored as N rows of K, leading dim ldb
  *   SFA/SFB : e8m0 codes, M x ceil(K/32) and N x ceil(K/32), row-major
  *             with leading dims ldsfa/ldsfb; both NULL for the unscaled
@@ -270,9 +321,12 @@ int oracle_gemm(int in_type, int64_t M, int64_t N, int64_t K,
 {
     if (M < 0 || N < 0 || K < 0 || n_out < 0)
         return ORC_ERR_ARG;
-    if (in_type != ORC_BF16 && in_type != ORC_FP16 && in_type != ORC_E4M3 && in_type != ORC_E2M1)
+    if (in_type != ORC_BF16 && in_type != ORC_FP16 && in_type != ORC_E4M3 && in_type != ORC_E2M1 &&
+        in_type != ORC_E2M3 && in_type != ORC_E3M2)
         return ORC_ERR_ARG;
     if (in_type == ORC_E2M1 && (!SFA || lda % 2 != 0 || ldb % 2 != 0))
+        return ORC_ERR_ARG;
+    if ((in_type == ORC_E2M3 || in_type == ORC_E3M2) && (!SFA || lda % 4 != 0 || ldb % 4 != 0))
         return ORC_ERR_ARG;
     if (C && c_type != ORC_F32 && c_type != ORC_BF16)
         return ORC_ERR_ARG;

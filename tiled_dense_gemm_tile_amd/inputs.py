@@ -20,6 +20,12 @@ Draw recipe (the same for every workload):
   per byte with element 2i in the low nibble of byte i; the integer variant
   draws the same codes with scale exponents in {1, 2}, so every product is
   an integer and partial sums stay below 2^24 for K up to 16384.
+* e2m3 / e3m2 (fp6) elements: codes drawn uniformly from all 64, packed six
+  bits each (element k at bits 6k .. 6k+5 of the row as a little-endian bit
+  string, four per three bytes); the integer variant draws codes of
+  magnitude at most 1 with scale exponent 3 (e2m3) or 4 (e3m2), so every
+  product is an integer of magnitude at most 64 (256) and partial sums stay
+  below 2^24 for K up to 65536.
 
 Each workload keeps its operands as raw element codes (uint16 for bf16/fp16,
 uint8 for e4m3/e8m0, packed uint8 pairs for e2m1) plus float32 C, laid out
@@ -71,6 +77,8 @@ WORKLOADS = {
                             note="M=N=1024 K=65536 bf16, C=0, fp32 out (16 output tiles: split-K)"),
     "mxfp8_8192": Workload("mxfp8_8192", 8192, 8192, 8192, "e4m3", "f32", U11, U11, None, 4,
                            scaled=True, note="M=N=K=8192 e4m3 + e8m0 per 32 K, C=0, fp32 out"),
+    "mxfp6_8192": Workload("mxfp6_8192", 8192, 8192, 8192, "e2m3", "f32", CODES, CODES, None, 7,
+                           scaled=True, note="M=N=K=8192 fp6 e2m3 + e8m0 per 32 K, C=0, fp32 out"),
     "mxfp4_8192": Workload("mxfp4_8192", 8192, 8192, 8192, "e2m1", "f32", CODES, CODES, None, 5,
                            scaled=True, note="M=N=K=8192 e2m1 + e8m0 per 32 K, C=0, fp32 out"),
 }
@@ -109,6 +117,34 @@ def _e2m1(rng, shape):
     return pack_e2m1(rng.integers(0, 16, size=shape).astype(np.uint8))
 
 
+FP6 = ("e2m3", "e3m2")
+# codes of magnitude <= 1 (sign bit 0x20 free): e2m3 0..8 (0 .. 1 in steps of
+# 1/8), e3m2 0..12 (0 .. 1: subnormals 1/16 .. 3/16, then 0.25 .. 1)
+_FP6_UNIT = {"e2m3": 9, "e3m2": 13}
+_FP6_INT_SCALE = {"e2m3": 3, "e3m2": 4}
+
+
+def pack_fp6(codes: np.ndarray) -> np.ndarray:
+    """(R, 4n) six-bit codes -> (R, 3n) bytes, element k at bits 6k .. 6k+5
+    of the row read as a little-endian bit string."""
+    c = np.asarray(codes, dtype=np.uint32)
+    g = c.reshape(c.shape[:-1] + (-1, 4))
+    w = g[..., 0] | (g[..., 1] << 6) | (g[..., 2] << 12) | (g[..., 3] << 18)
+    out = np.empty(c.shape[:-1] + (g.shape[-2], 3), dtype=np.uint8)
+    for j in range(3):
+        out[..., j] = (w >> (8 * j)) & 0xFF
+    return out.reshape(c.shape[:-1] + (-1,))
+
+
+def _fp6(rng, in_type, shape, integer=False):
+    if integer:
+        mag = rng.integers(0, _FP6_UNIT[in_type], size=shape)
+        codes = mag | (rng.integers(0, 2, size=shape) << 5)
+    else:
+        codes = rng.integers(0, 64, size=shape)
+    return pack_fp6(codes.astype(np.uint8))
+
+
 def generate(w: Workload, integer: bool = False, M=None, N=None, K=None, seed=None):
     """Draw a workload's operands.  Sizes and seed may be overridden (for
     reduced-size parity cases of the same recipe).
@@ -121,7 +157,11 @@ def generate(w: Workload, integer: bool = False, M=None, N=None, K=None, seed=No
     K = w.K if K is None else K
     seed = w.seed if seed is None else seed
     rng = np.random.default_rng(seed)
-    if w.in_type == "e2m1":
+    if w.in_type in FP6:
+        A, B, C = _fp6(rng, w.in_type, (M, K), integer), _fp6(rng, w.in_type, (N, K), integer), None
+        if w.dist_c is not None:
+            C = rng.integers(-4, 5, size=(M, N)).astype(np.float32) if integer else _draw(rng, w.dist_c, (M, N))
+    elif w.in_type == "e2m1":
         A, B, C = _e2m1(rng, (M, K)), _e2m1(rng, (N, K)), None
         if w.dist_c is not None:
             C = rng.integers(-4, 5, size=(M, N)).astype(np.float32) if integer else _draw(rng, w.dist_c, (M, N))
@@ -136,7 +176,11 @@ def generate(w: Workload, integer: bool = False, M=None, N=None, K=None, seed=No
     SFA = SFB = None
     if w.scaled:
         nkb = -(-K // 32)
-        if integer:
+        if integer and w.in_type in FP6:
+            lo, hi = _FP6_INT_SCALE[w.in_type], _FP6_INT_SCALE[w.in_type] + 1
+            SFA = (127 + rng.integers(lo, hi, size=(M, nkb))).astype(np.uint8)
+            SFB = (127 + rng.integers(lo, hi, size=(N, nkb))).astype(np.uint8)
+        elif integer:
             lo, hi = (1, 3) if w.in_type == "e2m1" else (0, 3)
             SFA = (127 + rng.integers(lo, hi, size=(M, nkb))).astype(np.uint8)
             SFB = (127 + rng.integers(lo, hi, size=(N, nkb))).astype(np.uint8)
@@ -150,12 +194,21 @@ def generate(w: Workload, integer: bool = False, M=None, N=None, K=None, seed=No
 def random_codes(rng, in_type, shape, integer=False, dist=U11):
     """Free-standing operand draw (parity sweeps of odd shapes).  For e2m1 the
     codes are uniform (integer or not: the scales make the values integral)
-    and ``shape[-1]`` is the element count, returned packed two per byte."""
+    and ``shape[-1]`` is the element count, returned packed two per byte;
+    for the fp6 types likewise, packed four per three bytes (integer: the
+    codes of magnitude at most 1, for use with ``fp6_integer_scale``)."""
     if in_type == "e2m1":
         return _e2m1(rng, shape)
+    if in_type in FP6:
+        return _fp6(rng, in_type, shape, integer)
     if integer:
         return to_codes(rng.integers(-4, 5, size=shape).astype(np.float32), in_type)
     return to_codes(_draw(rng, dist, shape), in_type)
+
+
+def fp6_integer_scale(in_type: str) -> int:
+    """The e8m0 exponent that makes the integer variant's fp6 values integers."""
+    return _FP6_INT_SCALE[in_type]
 
 
 def sample_indices(M: int, N: int, seed: int, count: int = 4096):

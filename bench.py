@@ -23,12 +23,15 @@ if ROOT not in sys.path:
 
 METRIC = "GEMM TFLOP/s and % of MI355X MFMA peak (bf16 4096³; mxfp8 8192³)"
 # MI355X published dense peaks (256 CUs at 2.4 GHz), TFLOP/s
-PEAK_TFLOPS = {"bf16": 2516.6, "fp16": 2516.6, "e4m3": 5033.2, "e2m1": 10066.3}
+PEAK_TFLOPS = {"bf16": 2516.6, "fp16": 2516.6, "e4m3": 5033.2, "e2m3": 10066.3, "e3m2": 10066.3,
+               "e2m1": 10066.3}
+# bytes per element of A and B
+ELEMENT_BYTES = {"e4m3": 1.0, "e2m3": 0.75, "e3m2": 0.75, "e2m1": 0.5}
 
 
 def algorithmic_bytes(w):
     """Bytes the operation must move at least once: A, B, (C), D, (scales)."""
-    es = {"e4m3": 1.0, "e2m1": 0.5}.get(w.in_type, 2.0)
+    es = ELEMENT_BYTES.get(w.in_type, 2.0)
     os_ = 4 if w.out_type == "f32" else 2
     b = int((w.M * w.K + w.N * w.K) * es) + w.M * w.N * os_
     if w.dist_c is not None:
@@ -54,7 +57,7 @@ def measured_traffic(w):
 
 def device_inputs(w, x, torch):
     dev = torch.device("cuda:0")
-    if w.in_type in ("e4m3", "e2m1"):
+    if w.in_type in ELEMENT_BYTES:
         A = torch.from_numpy(x["A"]).to(dev)
         B = torch.from_numpy(x["B"]).to(dev)
         extra = (torch.from_numpy(x["SFA"]).to(dev), torch.from_numpy(x["SFB"]).to(dev))
@@ -156,8 +159,11 @@ def main():
         step = lambda: tg.gemm_fp16(A, B, C, out_dtype=out_dtype, D=D)
     else:
         SFA, SFB = extra
-        fn = tg.gemm_mxfp8 if w.in_type == "e4m3" else tg.gemm_mxfp4
-        step = lambda: fn(A, SFA, B, SFB, C, out_dtype=out_dtype, D=D)
+        if w.in_type in ("e2m3", "e3m2"):
+            step = lambda: tg.gemm_mxfp6(A, SFA, B, SFB, C, out_dtype=out_dtype, D=D, fmt=w.in_type)
+        else:
+            fn = tg.gemm_mxfp8 if w.in_type == "e4m3" else tg.gemm_mxfp4
+            step = lambda: fn(A, SFA, B, SFB, C, out_dtype=out_dtype, D=D)
 
     # The GPU raises its clocks over the first milliseconds of sustained
     # work; a few warmup launches of a ~0.1 ms kernel end before that, so

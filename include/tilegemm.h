@@ -78,6 +78,11 @@ typedef enum {
     GEMM_MN_CONTIGUOUS = 1       /* A: a(m,k) = A[k*lda + m]   B: b(k,n) = B[k*ldb + n] */
 } gemm_operand_order;
 
+typedef enum {
+    GEMM_FP6_E2M3 = 0,           /* OCP FP6 E2M3: 1 sign, 2 exponent (bias 1), 3 mantissa bits; max 7.5 */
+    GEMM_FP6_E3M2 = 1            /* OCP FP6 E3M2: 1 sign, 3 exponent (bias 3), 2 mantissa bits; max 28 */
+} gemm_fp6_format;
+
 /*
  * gemm_bf16 -- D = A.B + C with bf16 A and B, fp32 accumulation.
  * Source: "Tensor Core 数据布局的演进", section 一个具体的 fragment 映射
@@ -187,6 +192,35 @@ gemm_status gemm_mxfp4(int64_t M, int64_t N, int64_t K,
                        const void *C, int64_t ldc,
                        void *D, int64_t ldd,
                        int out_type, hipStream_t stream);
+
+/*
+ * gemm_mxfp6 -- block-scaled fp6: D = A.B + C with
+ *     a(m,k) = fp6(A, m*lda + k) * 2^(SFA[m*ldsfa + k/32] - 127)
+ *     b(k,n) = fp6(B, n*ldb + k) * 2^(SFB[n*ldsfb + k/32] - 127)
+ * where fp6(X, i) is the six-bit code at bits 6i .. 6i+5 of X read as a
+ * little-endian bit string (four elements in three bytes, the first in the
+ * low six bits of the first byte), in the format given by `format`
+ * (GEMM_FP6_E2M3 or GEMM_FP6_E3M2, else GEMM_ERR_UNSUPPORTED; no NaN or
+ * infinity in either).  Source: "Tensor Core 数据布局的演进", section
+ * Block-Scaled MMA 的 Scale Factors (the same per-block scaling as
+ * gemm_mxfp8 with 6-bit elements).
+ *   A: M x K elements row-major, lda (elements, a multiple of 4)
+ *   B: N x K elements (column-major K x N), ldb (elements, a multiple of 4)
+ *   SFA, SFB, C, D, out_type: as gemm_mxfp8
+ * Sizes, lda and ldb count ELEMENTS (three bytes per four).  K must be a
+ * multiple of 32 and lda, ldb multiples of 4; this version also needs
+ * K % 512 == 0, A and B 16-byte aligned, lda and ldb multiples of 64 (rows of
+ * a multiple of 48 bytes), SFA and SFB 16-byte aligned and ldsfa, ldsfb
+ * multiples of 16, and returns GEMM_ERR_UNSUPPORTED otherwise.  Byte limits
+ * of the shared convention apply to 3*lda/4 and 3*ldb/4.  Scale code 0xFF
+ * (NaN) gives NaN in the affected outputs.
+ */
+gemm_status gemm_mxfp6(int64_t M, int64_t N, int64_t K,
+                       const void *A, int64_t lda, const void *SFA, int64_t ldsfa,
+                       const void *B, int64_t ldb, const void *SFB, int64_t ldsfb,
+                       const void *C, int64_t ldc,
+                       void *D, int64_t ldd,
+                       int format, int out_type, hipStream_t stream);
 
 /*
  * gemm_bf16_splitk, gemm_fp16_splitk -- as gemm_bf16 / gemm_fp16, with K cut

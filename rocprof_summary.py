@@ -40,7 +40,7 @@ def instance_file(in_type: str, out_type: str) -> str:
     """The translation unit holding a workload's kernels."""
     if in_type in ("bf16", "fp16"):
         return "f16_%s_%s.hip" % (in_type, out_type)
-    return "%s_%s.hip" % ({"e4m3": "mx", "e2m1": "mx4"}[in_type], out_type)
+    return "%s_%s.hip" % ({"e4m3": "mx", "e2m3": "mx6", "e3m2": "mx6", "e2m1": "mx4"}[in_type], out_type)
 
 
 def _include_closure(name, seen):
@@ -65,7 +65,8 @@ def kernel_source_hash(workload: str) -> str:
     w = inputs.WORKLOADS[workload]
     files = set()
     _include_closure(instance_file(w.in_type, w.out_type), files)
-    api = {"e4m3": "mx_api.hip", "e2m1": "mx4_api.hip"}.get(w.in_type, "tilegemm.hip")
+    api = {"e4m3": "mx_api.hip", "e2m3": "mx6_api.hip", "e3m2": "mx6_api.hip",
+           "e2m1": "mx4_api.hip"}.get(w.in_type, "tilegemm.hip")
     _include_closure(api, files)
     if w.in_type in ("bf16", "fp16"):
         _include_closure("splitk.hip", files)          # the split-K reduction
@@ -194,8 +195,8 @@ def main():
         print("wrote", out, "traffic %.1f MB per launch" % (total / 1e6))
 
     if not args.skip_counters:
-        # (no MOPS counter is used for fp4)
-        mops = {"mxfp8": ["SQ_INSTS_VALU_MFMA_MOPS_F8"], "mxfp4": []}.get(args.workload[:5],
+        # (no MOPS counter is used for fp4 and fp6)
+        mops = {"mxfp8": ["SQ_INSTS_VALU_MFMA_MOPS_F8"], "mxfp4": [], "mxfp6": []}.get(args.workload[:5],
                                                                          ["SQ_INSTS_VALU_MFMA_MOPS_BF16"])
         passes = [["GRBM_GUI_ACTIVE", "SQ_BUSY_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES"] + mops +
                   ["SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY"],

@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["gemm_bf16", "gemm_bf16_ex", "gemm_bf16_splitk", "gemm_fp16", "gemm_fp16_ex",
-                                    "gemm_fp16_splitk", "gemm_last_hip_error", "gemm_mxfp4", "gemm_mxfp8",
+                                    "gemm_fp16_splitk", "gemm_last_hip_error", "gemm_mxfp4", "gemm_mxfp6", "gemm_mxfp8",
                                     "gemm_splitk_workspace_bytes", "gemm_status_string"]
 
 
@@ -123,6 +123,41 @@ def test_validation_mxfp4():
     assert call4(ldsfa=20) == UNSUPPORTED
     assert call4(lda=16 << 20) == UNSUPPORTED               # 8 MiB rows
     assert call4(K=1 << 31, lda=1 << 31, ldb=1 << 31) == UNSUPPORTED
+
+
+def call6(M=64, N=64, K=512, A=P, lda=512, SFA=P + 4096, ldsfa=16, B=P, ldb=512, SFB=P + 8192, ldsfb=16,
+          C=None, ldc=0, D=P + (1 << 24), ldd=64, fmt=0, out=F32):
+    return tg.raw.gemm_mxfp6(M, N, K, A, lda, SFA, ldsfa, B, ldb, SFB, ldsfb, C, ldc, D, ldd, fmt, out, None)
+
+
+def test_validation_mxfp6():
+    """Every case is refused before anything is launched (lda, ldb, K in
+    elements, four per three bytes)."""
+    assert call6(M=-1) == INVALID_SIZE
+    assert call6(K=-4) == INVALID_SIZE
+    assert call6(M=0) == OK
+    assert call6(out=3) == UNSUPPORTED
+    assert call6(fmt=2) == UNSUPPORTED
+    assert call6(fmt=-1) == UNSUPPORTED
+    assert call6(lda=508) == BAD_LD
+    assert call6(ldb=4) == BAD_LD
+    assert call6(ldd=32) == BAD_LD
+    assert call6(lda=514) == UNSUPPORTED                   # rows must start on a byte
+    assert call6(ldb=513) == UNSUPPORTED
+    assert call6(K=48, lda=64, ldb=64) == UNSUPPORTED       # K not a multiple of 32
+    assert call6(K=256, lda=256, ldb=256) == UNSUPPORTED    # this version: K % 512 == 0
+    assert call6(ldsfa=15) == BAD_LD
+    assert call6(ldsfb=8) == BAD_LD
+    assert call6(SFA=None) == NULL_POINTER
+    assert call6(SFB=None) == NULL_POINTER
+    assert call6(A=None) == NULL_POINTER
+    assert call6(D=None) == NULL_POINTER
+    assert call6(lda=544) == UNSUPPORTED                    # 408-byte rows: not 16-byte multiples
+    assert call6(A=P + 8) == UNSUPPORTED                    # A not 16-byte aligned
+    assert call6(SFA=P + 4100) == UNSUPPORTED               # scales not 16-byte aligned
+    assert call6(ldsfa=20) == UNSUPPORTED
+    assert call6(lda=16 << 20) == UNSUPPORTED               # 12 MiB rows
+    assert call6(K=1 << 31, lda=1 << 31, ldb=1 << 31) == UNSUPPORTED
 
 
 def splitk_bytes(M, N, K, splits):

@@ -20,7 +20,7 @@ import os
 import threading
 
 __all__ = ["gemm_bf16", "gemm_fp16", "gemm_bf16_splitk", "gemm_fp16_splitk", "splitk_workspace_bytes",
-           "gemm_mxfp8", "gemm_mxfp4", "raw", "GemmError", "LibraryMissing",
+           "gemm_mxfp8", "gemm_mxfp4", "gemm_mxfp6", "raw", "GemmError", "LibraryMissing",
            "library_path", "STATUS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -75,6 +75,8 @@ def _load():
                 f = getattr(L, name)
                 f.restype = ci
                 f.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp, i64, ci, vp]
+            L.gemm_mxfp6.restype = ci
+            L.gemm_mxfp6.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp, i64, ci, ci, vp]
             L.gemm_status_string.restype = ctypes.c_char_p
             L.gemm_status_string.argtypes = [ci]
             L.gemm_last_hip_error.restype = ci
@@ -257,5 +259,39 @@ def gemm_mxfp4(A, SFA, B, SFB, C=None, out_dtype=None, D=None):
                             _ld(SFA, nkb) if K else 0, B.data_ptr(), 2 * _ld(B, KB) if K else 0, SFB.data_ptr(),
                             _ld(SFB, nkb) if K else 0, C.data_ptr() if C is not None else None,
                             _ld(C, N) if C is not None else 0, D.data_ptr(), _ld(D, N), out, stream)
+    _check(st)
+    return D
+
+
+FP6_FORMATS = {"e2m3": 0, "e3m2": 1}
+
+
+def gemm_mxfp6(A, SFA, B, SFB, C=None, out_dtype=None, D=None, fmt="e2m3"):
+    """Block-scaled fp6: A (M, 3K/4), B (N, 3K/4) uint8 bytes holding six-bit
+    codes (element k at bits 6k .. 6k+5 of a row read as a little-endian bit
+    string) in format ``fmt`` ("e2m3" or "e3m2"); SFA (M, K/32), SFB (N, K/32)
+    e8m0 codes.  K is four thirds of the byte width of A."""
+    import torch
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    if fmt not in FP6_FORMATS:
+        raise ValueError("fmt must be 'e2m3' or 'e3m2'")
+    M, N, KB, D, stream, out = _prep(A, B, C, D, out_dtype, (torch.uint8,))
+    if KB % 3:
+        raise ValueError("the byte width of A and B must be a multiple of 3 (four elements per three bytes)")
+    K = KB // 3 * 4
+    for s, rows in ((SFA, M), (SFB, N)):
+        if s.dtype not in (torch.uint8, torch.float8_e8m0fnu) or not s.is_cuda or s.shape[0] != rows:
+            raise ValueError("scale arrays must be uint8/e8m0 device tensors of shape (rows, K/32)")
+    lds = []
+    for X in (A, B):
+        ldb_ = _ld(X, KB) if K else 0
+        if ldb_ % 3:
+            raise ValueError("row strides of A and B must be multiples of 3 bytes")
+        lds.append(ldb_ // 3 * 4)
+    nkb = K // 32
+    st = _load().gemm_mxfp6(M, N, K, A.data_ptr(), lds[0], SFA.data_ptr(), _ld(SFA, nkb) if K else 0,
+                            B.data_ptr(), lds[1], SFB.data_ptr(), _ld(SFB, nkb) if K else 0,
+                            C.data_ptr() if C is not None else None, _ld(C, N) if C is not None else 0,
+                            D.data_ptr(), _ld(D, N), FP6_FORMATS[fmt], out, stream)
     _check(st)
     return D

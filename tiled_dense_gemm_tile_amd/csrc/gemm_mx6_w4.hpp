@@ -1,0 +1,287 @@
+// Block-scaled fp6 D = A.B + C with four waves and
+// v_mfma_scale_f32_16x16x128_f8f6f4 on e2m3 (FMT 2) or e3m2 (FMT 3)
+// operands, gfx950 (K a multiple of 512):
+//     a(m,k) = fp6(A, m, k) * 2^(SFA[m][k/32] - 127)
+//     b(k,n) = fp6(B, n, k) * 2^(SFB[n][k/32] - 127)
+// A and B hold six bits per element: element k of a row at bits 6k .. 6k+5
+// of the row read as a little-endian bit string (four per three bytes).
+//
+// Same frame as the four-wave fp8 kernel: a 256 x 256 output tile, one wave
+// per SIMD owning a 128 x 128 quadrant as 8 x 8 blocks of 16 x 16 fp32
+// accumulators in AGPRs, 128-wide K tiles filled by direct global->LDS
+// loads, scales in epochs of four K tiles.  The operand rings have three
+// slots (the 24 KiB slots of fp6 leave room for a third, 160 KiB in all):
+// the loads of tile t + 2 are issued in window t and only waited for at
+// the end of window t + 1, so each load has two windows of MFMAs (2048
+// cycles) to arrive instead of one.
+//
+// Operand placement (measured: B all ones, one bit of A at a time): lane l
+// supplies row (A) or column (B) l % 16 and, as six registers, the 32
+// elements of K block q = l / 16 packed exactly as in memory (element i at
+// bits 6i .. 6i+5 of the 192 bits) -- 24 consecutive bytes of the row; the
+// block's scale comes from the same lane, op_sel picking the byte.
+//
+// LDS: a K tile's row is 96 bytes, six 16-byte chunks, rows one after the
+// other (the direct loads fill 64 consecutive chunk positions per
+// instruction, so a wave's lanes fetch whole rows).  In rows 8 .. 15 of
+// every 16 the chunks of each pair (0, 1), (2, 3), (4, 5) trade places:
+// rows 96 bytes apart start 6 chunk columns apart, which repeats every 8
+// rows, and the swap moves rows 8 .. 15 onto the other parity, so the 16
+// rows of a fragment read (8 bytes per lane, one K block) sit in 16
+// different 16-byte bank columns.
+#pragma once
+
+#include <type_traits>
+
+#include "common.hpp"
+#include "gemm_mx_w4.hpp"
+#include "pipeline.hpp"
+
+namespace tg {
+
+typedef uint32_t u32x6 __attribute__((ext_vector_type(6)));
+
+// One 16x16x128 fp6 MFMA on an AGPR accumulator block, in place; SA / SB:
+// the byte of each scale register used; FMT: 2 e2m3, 3 e3m2.
+template <int SA, int SB, int FMT>
+__device__ __forceinline__ void mfma_mx6_acc(f32x4 &acc, const u32x6 &a, const u32x6 &b, uint32_t sa, uint32_t sb) {
+#define TG_STR2(x) #x
+#define TG_STR(x) TG_STR2(x)
+    if constexpr (FMT == 2)
+        asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel:[" TG_STR(%c5) "," TG_STR(%c6)
+                     ",0] op_sel_hi:[" TG_STR(%c7) "," TG_STR(%c8) ",0] cbsz:2 blgp:2"
+                     : "+a"(acc)
+                     : "v"(a), "v"(b), "v"(sa), "v"(sb), "n"(SA & 1), "n"(SB & 1), "n"(SA >> 1), "n"(SB >> 1));
+    else
+        asm volatile("v_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel:[" TG_STR(%c5) "," TG_STR(%c6)
+                     ",0] op_sel_hi:[" TG_STR(%c7) "," TG_STR(%c8) ",0] cbsz:3 blgp:3"
+                     : "+a"(acc)
+                     : "v"(a), "v"(b), "v"(sa), "v"(sb), "n"(SA & 1), "n"(SB & 1), "n"(SA >> 1), "n"(SB >> 1));
+#undef TG_STR
+#undef TG_STR2
+}
+
+// q.g.lda and q.g.ldb are in BYTES here (three quarters of the leading
+// dimension in elements); q.g.K is in elements.
+template <bool OUT_BF16, int FMT, int DAUX = kStoreStream>
+__global__ void __launch_bounds__(256) gemm_mx6_w4_kernel(MxArgs q, F16Epi e) {
+    static_assert(FMT == 2 || FMT == 3, "fp6 formats");
+    const F16Args &p = q.g;
+    constexpr int ROWB = 96;                           // bytes per K tile (128 elements) and LDS row
+    constexpr int TM = 8, TN = 8, WTM = 128, WTN = 128;
+    constexpr int SLOT = 256 * ROWB;                   // 24 KiB per operand slot
+    constexpr int SS = 256 * 16;                       // one scale slot: 256 rows x 16 bytes
+    constexpr int NS = 3;                              // slots per operand ring
+    constexpr int A_BASE = 0, B_BASE = NS * SLOT, SA_BASE = 2 * NS * SLOT, SB_BASE = SA_BASE + 2 * SS;
+    constexpr int RING_BYTES = SB_BASE + 2 * SS;
+    constexpr int EPI_BYTES = epilogue_lds_bytes(4, WTN);
+    constexpr int LDS_BYTES = RING_BYTES > EPI_BYTES ? RING_BYTES : EPI_BYTES;
+    constexpr int IB = 1024;                           // one load instruction: 64 chunks
+    constexpr int LPW = 6;                             // load instructions per wave and operand per tile
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS capacity");
+    static_assert(4 * LPW * 64 == 256 * (ROWB / 16), "a tile's chunks are split evenly over the waves");
+
+    __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    int tmi, tni;
+    tile_order(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, tmi, tni);
+    const int m0 = tmi * 256, n0 = tni * 256;
+    const int M = p.M, N = p.N, K = p.K;
+    const int kb = K / 4 * 3, nblk = K / 32;
+    const int nk = K / 128, nep = K / 512;
+
+    const __amdgpu_buffer_rsrc_t rA =
+        make_rsrc((const char *)p.A + (int64_t)m0 * p.lda, span_bytes(M - m0, kb, p.lda, 1));
+    const __amdgpu_buffer_rsrc_t rB =
+        make_rsrc((const char *)p.B + (int64_t)n0 * p.ldb, span_bytes(N - n0, kb, p.ldb, 1));
+    const __amdgpu_buffer_rsrc_t rSA =
+        make_rsrc((const char *)q.SFA + (int64_t)m0 * q.ldsfa, span_bytes(M - m0, nblk, q.ldsfa, 1));
+    const __amdgpu_buffer_rsrc_t rSB =
+        make_rsrc((const char *)q.SFB + (int64_t)n0 * q.ldsfb, span_bytes(N - n0, nblk, q.ldsfb, 1));
+    const __amdgpu_buffer_rsrc_t rZ = make_rsrc(p.A, 0u);
+
+    // Operand loads: chunk position c = (4 j + wave) * 64 + lane of a slot
+    // is row c / 6, logical chunk (c % 6) ^ (row bit 3); the K offset goes
+    // in the scalar offset.  Scale loads: lane L of wave w brings row
+    // 64 w + L's 16 bytes.
+    uint32_t a_off[LPW], b_off[LPW];
+#pragma unroll
+    for (int j = 0; j < LPW; ++j) {
+        const int c = (4 * j + wave) * 64 + lane;
+        const int row = c / 6, chunk = (c % 6) ^ ((row >> 3) & 1);
+        a_off[j] = (uint32_t)(row * p.lda) + chunk * 16;
+        b_off[j] = (uint32_t)(row * p.ldb) + chunk * 16;
+    }
+    auto dma = [&](__amdgpu_buffer_rsrc_t r, int lds, uint32_t voff, int soff) __attribute__((always_inline)) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)(smem + lds), 16, voff,
+                                                 soff, 0, 0);
+    };
+    // load k (0 .. 11) of tile t into ring slot `slot`: A instruction k, or
+    // B instruction k - 6
+    auto fetch = [&](int t, int k, int slot) __attribute__((always_inline)) {
+        const bool isa = k < LPW;
+        const int j = isa ? k : k - LPW;
+        const __amdgpu_buffer_rsrc_t r = t < nk ? (isa ? rA : rB) : rZ;
+        const uint32_t voff = isa ? a_off[j] : b_off[j];
+        const int lds = (isa ? A_BASE : B_BASE) + slot * SLOT + (j * 4 + wave) * IB;
+        dma(r, lds, voff, t * ROWB);
+    };
+    auto lane_id = [&]() __attribute__((always_inline)) {
+        int l = lane;
+        asm volatile("" : "+v"(l));
+        return l;
+    };
+    auto fetch_scales = [&](int ep) __attribute__((always_inline)) {
+        const int l = lane_id();
+        const int so = ep * 16;
+        const __amdgpu_buffer_rsrc_t ra = ep < nep ? rSA : rZ;
+        const __amdgpu_buffer_rsrc_t rb = ep < nep ? rSB : rZ;
+        dma(ra, SA_BASE + (ep & 1) * SS + wave * IB, (uint32_t)((64 * wave + l) * q.ldsfa), so);
+        dma(rb, SB_BASE + (ep & 1) * SS + wave * IB, (uint32_t)((64 * wave + l) * q.ldsfb), so);
+    };
+
+    // Fragment reads: lane l reads bytes 24 q .. 24 q + 23 (q = l / 16) of
+    // row l % 16 of each block as 8-byte units 3 q + s, s = 0, 1, 2: unit u
+    // is half u % 2 of logical chunk u / 2.
+    const int fr = lane & 15, fq = lane >> 4;
+    auto unit = [&](int u) { return fr * ROWB + (((u >> 1) ^ (fr >> 3)) << 4) + (u & 1) * 8; };
+    const int la0 = A_BASE + wm * WTM * ROWB + unit(3 * fq), la1 = A_BASE + wm * WTM * ROWB + unit(3 * fq + 1),
+              la2 = A_BASE + wm * WTM * ROWB + unit(3 * fq + 2);
+    const int lb0 = B_BASE + wn * WTN * ROWB + unit(3 * fq), lb1 = B_BASE + wn * WTN * ROWB + unit(3 * fq + 1),
+              lb2 = B_BASE + wn * WTN * ROWB + unit(3 * fq + 2);
+    constexpr int GB = 16 * ROWB;                      // bytes of a block's 16 rows
+    auto ld24 = [&](int a0, int a1, int a2) __attribute__((always_inline)) {
+        const u32x2 x = *(const u32x2 *)(smem + a0), y = *(const u32x2 *)(smem + a1),
+                    z = *(const u32x2 *)(smem + a2);
+        return u32x6{x[0], x[1], y[0], y[1], z[0], z[1]};
+    };
+
+    f32x4 acc[TM][TN];
+    u32x6 fa[TM], fx;                                  // A fragments; fx: row 7 of odd tiles
+    u32x6 fb[2][TN];                                   // B fragments by tile parity
+    uint32_t sa[2][2], sb[2][2];                       // scale registers by tile parity
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    mfma_result_fence<TM, TN>(acc);                    // the zeroing before the first MFMA reads them
+
+    // Reads of tile t from ring slot rs; its place in its epoch U = t % 4 is
+    // a compile-time constant at every call site (the loop advances by whole
+    // epochs), so register buffers are chosen by constant parity.
+    auto read_a = [&](auto uc, auto ic, int rs) __attribute__((always_inline)) {
+        constexpr int P = decltype(uc)::value & 1, I = decltype(ic)::value;
+        const int o = rs * SLOT + I * GB;
+        const u32x6 v = ld24(la0 + o, la1 + o, la2 + o);
+        if constexpr (I < TM - 1 || !P)
+            fa[I] = v;
+        else
+            fx = v;
+    };
+    auto read_b = [&](auto uc, auto jc, int rs) __attribute__((always_inline)) {
+        constexpr int P = decltype(uc)::value & 1, J = decltype(jc)::value;
+        const int o = rs * SLOT + J * GB;
+        fb[P][J] = ld24(lb0 + o, lb1 + o, lb2 + o);
+    };
+    // Scale registers: as in the fp8 kernel (byte u of register h' = block
+    // row 4 h' + u, K block q of tile U at byte 4 U + q of the row's 16),
+    // assembled with two v_perm 8 MFMAs after their dword reads.
+    const uint32_t sel_lo = (uint32_t)fq | ((uint32_t)(fq + 4) << 8) | 0x0c0c0000u;   // 0x0c: a zero byte
+    const uint32_t sel_hi = 0x00000c0cu | ((uint32_t)fq << 16) | ((uint32_t)(fq + 4) << 24);
+    uint32_t sraw[2][4];
+    auto scale_issue = [&](auto uc, auto hc, auto gc, int t) __attribute__((always_inline)) {
+        constexpr int U = decltype(uc)::value, H = decltype(hc)::value, G = decltype(gc)::value;
+        const int row = (H < 2 ? wm * WTM : wn * WTN) + fr;
+        const int base = (H < 2 ? SA_BASE : SB_BASE) + row * 16 + ((t >> 2) & 1) * SS + U * 4 + (H & 1) * 4 * 256;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) sraw[G][u] = *(const uint32_t *)(smem + base + u * 256);
+    };
+    auto scale_finish = [&](auto uc, auto hc, auto gc) __attribute__((always_inline)) {
+        constexpr int P = decltype(uc)::value & 1, H = decltype(hc)::value, G = decltype(gc)::value;
+        const uint32_t v = __builtin_amdgcn_perm(sraw[G][1], sraw[G][0], sel_lo) |
+                           __builtin_amdgcn_perm(sraw[G][3], sraw[G][2], sel_hi);
+        if constexpr (H < 2)
+            sa[P][H] = v;
+        else
+            sb[P][H - 2] = v;
+    };
+    // MFMA Q (row Q / 8, column Q % 8) of a tile of parity P
+    auto mfma = [&](auto pc, auto qc) __attribute__((always_inline)) {
+        constexpr int P = decltype(pc)::value, Q = decltype(qc)::value;
+        constexpr int I = Q / TN, J = Q % TN;
+        if constexpr (I < TM - 1 || !P)
+            mfma_mx6_acc<I % 4, J % 4, FMT>(acc[I][J], fa[I], fb[P][J], sa[P][I / 4], sb[P][J / 4]);
+        else
+            mfma_mx6_acc<I % 4, J % 4, FMT>(acc[I][J], fx, fb[P][J], sa[P][I / 4], sb[P][J / 4]);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // Window t (U = t % 4, tile t in slot rs): MFMAs of tile t - 1 (unless
+    // FIRST), reads of tile t -- B block j at MFMA 4 j, A row 7 at MFMA 3 and
+    // row i - 1 during row i, scales read at MFMAs 34 .. 46 and assembled 8
+    // MFMAs later -- loads of tile t + 2 during the first 12 MFMAs into the
+    // slot tile t - 1 held (its fragments were read in window t - 1), the
+    // next epoch's scales when U == 2; then a wait for the loads of tile
+    // t + 1 (everything but the 12 just issued).
+    auto window = [&](auto first, auto uc, int t, int rs) __attribute__((always_inline)) {
+        constexpr bool F = decltype(first)::value;
+        constexpr int U = decltype(uc)::value;
+        const int ws = rs == 0 ? NS - 1 : rs - 1;      // (rs + 2) % 3
+        if constexpr (U == 2) fetch_scales((t >> 2) + 1);
+        static_for<0, 64>([&](auto qc) __attribute__((always_inline)) {
+            constexpr int Q = decltype(qc)::value;
+            if constexpr (!F) mfma(std::integral_constant<int, (U + 1) & 1>(), qc);
+            if constexpr (Q < 2 * LPW) fetch(t + 2, Q, ws);
+            if constexpr (Q < 32 && Q % 4 == 0) read_b(uc, std::integral_constant<int, Q / 4>(), rs);
+            if constexpr (Q == 3) read_a(uc, std::integral_constant<int, TM - 1>(), rs);
+            if constexpr (Q >= 8 && Q % 8 == 3) read_a(uc, std::integral_constant<int, Q / 8 - 1>(), rs);
+            if constexpr (Q >= 42 && Q <= 54 && Q % 4 == 2) {
+                constexpr int c = (Q - 42) / 4;
+                scale_finish(uc, std::integral_constant<int, c>(), std::integral_constant<int, c % 2>());
+            }
+            if constexpr (Q >= 34 && Q <= 46 && Q % 4 == 2) {
+                constexpr int c = (Q - 34) / 4;
+                scale_issue(uc, std::integral_constant<int, c>(), std::integral_constant<int, c % 2>(), t);
+            }
+        });
+        wait_vmcnt<2 * LPW>();
+        wait_lgkmcnt0();
+        barrier();
+    };
+
+    if (nk > 0) {
+        // prologue: tile 0 (slot 0), the first epoch's scales, tile 1 (slot
+        // 1); wait for all but tile 1's loads
+#pragma unroll
+        for (int k = 0; k < 2 * LPW; ++k) fetch(0, k, 0);
+        fetch_scales(0);
+#pragma unroll
+        for (int k = 0; k < 2 * LPW; ++k) fetch(1, k, 1);
+        wait_vmcnt<2 * LPW>();
+        barrier();
+        window(std::true_type(), std::integral_constant<int, 0>(), 0, 0);
+        // windows 1 .. nk (nk a multiple of 4): tiles 0 .. nk - 1 computed
+        int rs = 1;
+        auto next = [](int r) { return r == NS - 1 ? 0 : r + 1; };
+        for (int t = 1; t <= nk; t += 4) {
+            window(std::false_type(), std::integral_constant<int, 1>(), t, rs);
+            rs = next(rs);
+            window(std::false_type(), std::integral_constant<int, 2>(), t + 1, rs);
+            rs = next(rs);
+            window(std::false_type(), std::integral_constant<int, 3>(), t + 2, rs);
+            rs = next(rs);
+            window(std::false_type(), std::integral_constant<int, 0>(), t + 3, rs);
+            rs = next(rs);
+        }
+    }
+    mfma_result_fence<TM, TN>(acc);
+    wait_vmcnt<0>();
+    wait_lgkmcnt0();
+    barrier();
+    epilogue_lds16<OUT_BF16, TM, TN, WTM, WTN, DAUX>(acc, smem, wave, lane, wm, wn, m0, n0, M, N, p.C, p.ldc, p.D, p.ldd, e);
+}
+
+}  // namespace tg

@@ -1,0 +1,31 @@
+// Launcher of the block-scaled fp6 GEMM; one instance translation unit per
+// output type (mx6_<out>.hip), each holding both fp6 formats.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "gemm_mx6_w4.hpp"
+
+namespace tg {
+
+// 256 x 256 tiles, four waves; q.g.lda / q.g.ldb in bytes; e3m2 selects
+// the E3M2 format (else E2M3).
+template <bool OUT_BF16>
+hipError_t launch_mx6(bool e3m2, unsigned grid, hipStream_t s, const MxArgs &q, const F16Epi &e);
+
+}  // namespace tg
+
+#ifdef TG_MX6_INSTANCE
+namespace tg {
+
+template <>
+hipError_t launch_mx6<TG_OUT_BF16>(bool e3m2, unsigned grid, hipStream_t s, const MxArgs &q, const F16Epi &e) {
+    if (e3m2)
+        hipLaunchKernelGGL((gemm_mx6_w4_kernel<TG_OUT_BF16, 3>), dim3(grid), dim3(256), 0, s, q, e);
+    else
+        hipLaunchKernelGGL((gemm_mx6_w4_kernel<TG_OUT_BF16, 2>), dim3(grid), dim3(256), 0, s, q, e);
+    return hipGetLastError();
+}
+
+}  // namespace tg
+#endif

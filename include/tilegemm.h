@@ -262,10 +262,51 @@ gemm_status gemm_fp16_splitk(int64_t M, int64_t N, int64_t K,
                              void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
- * Workspace bytes gemm_bf16_splitk / gemm_fp16_splitk need for these sizes
- * and `splits` (0 = the library's choice): splits_used * M * (N rounded up
- * to a multiple of 4) * 4; 0 when no split would be used or the arguments
- * are invalid.
+ * gemm_mxfp8_splitk, gemm_mxfp4_splitk, gemm_mxfp6_splitk -- as gemm_mxfp8 /
+ * gemm_mxfp4 / gemm_mxfp6, with K cut into `splits` ranges of whole groups
+ * of 512 K (16 scale blocks) computed by separate workgroups, each range's
+ * fp32 partial product going to the caller's workspace, and a second kernel
+ * on the same stream summing the partials in range order, adding C and
+ * writing D (the same result on every call).  Source: as gemm_bf16_splitk.
+ *   splits: as gemm_bf16_splitk, with at most one split per 512 K; calls
+ *     outside the library's fast path for the type (see gemm_mxfp8 /
+ *     gemm_mxfp4 / gemm_mxfp6: K % 512 == 0, 16-byte rows and scale rows)
+ *     run unsplit, or are refused exactly as the unsplit call would be.
+ *   workspace: as gemm_bf16_splitk; gemm_splitk_workspace_bytes(M, N, K,
+ *     splits) bytes always suffice.
+ * Everything else (layouts, scales, validation, out_type, C == D) is as the
+ * unsplit call.
+ */
+gemm_status gemm_mxfp8_splitk(int64_t M, int64_t N, int64_t K,
+                              const void *A, int64_t lda, const void *SFA, int64_t ldsfa,
+                              const void *B, int64_t ldb, const void *SFB, int64_t ldsfb,
+                              const void *C, int64_t ldc,
+                              void *D, int64_t ldd,
+                              int out_type, int splits,
+                              void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+gemm_status gemm_mxfp4_splitk(int64_t M, int64_t N, int64_t K,
+                              const void *A, int64_t lda, const void *SFA, int64_t ldsfa,
+                              const void *B, int64_t ldb, const void *SFB, int64_t ldsfb,
+                              const void *C, int64_t ldc,
+                              void *D, int64_t ldd,
+                              int out_type, int splits,
+                              void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+gemm_status gemm_mxfp6_splitk(int64_t M, int64_t N, int64_t K,
+                              const void *A, int64_t lda, const void *SFA, int64_t ldsfa,
+                              const void *B, int64_t ldb, const void *SFB, int64_t ldsfb,
+                              const void *C, int64_t ldc,
+                              void *D, int64_t ldd,
+                              int format, int out_type, int splits,
+                              void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Workspace bytes the split-K calls need for these sizes and `splits` (0 =
+ * the library's choice): splits_used * M * (N rounded up to a multiple of 4)
+ * * 4, with splits_used counted for 64-wide K tiles (the block-scaled calls,
+ * cut at multiples of 512 K, never use more); 0 when no split would be used
+ * or the arguments are invalid.
  */
 size_t gemm_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K, int splits);
 

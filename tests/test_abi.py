@@ -24,7 +24,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["gemm_bf16", "gemm_bf16_ex", "gemm_bf16_splitk", "gemm_fp16", "gemm_fp16_ex",
-                                    "gemm_fp16_splitk", "gemm_last_hip_error", "gemm_mxfp4", "gemm_mxfp6", "gemm_mxfp8",
+                                    "gemm_fp16_splitk", "gemm_last_hip_error", "gemm_mxfp4", "gemm_mxfp4_splitk", "gemm_mxfp6",
+                                    "gemm_mxfp6_splitk", "gemm_mxfp8", "gemm_mxfp8_splitk",
                                     "gemm_splitk_workspace_bytes", "gemm_status_string"]
 
 
@@ -199,6 +200,37 @@ def test_validation_splitk(fn):
     assert call16s(fn, ws=None) == WORKSPACE
     assert call16s(fn, wsb=4 * 256 * 256 * 4 - 1) == WORKSPACE
     assert call16s(fn, ws=P + (1 << 26) + 128) == MISALIGNED
+
+
+def callms(fn, M=256, N=256, K=4096, A=P, lda=4096, SFA=P + 4096, ldsfa=128, B=P, ldb=4096, SFB=P + 8192,
+           ldsfb=128, C=None, ldc=0, D=P + (1 << 24), ldd=256, out=F32, splits=4, ws=P + (1 << 26), wsb=None,
+           fmt=0):
+    if wsb is None:
+        wsb = splitk_bytes(M, N, K, splits)
+    args = [M, N, K, A, lda, SFA, ldsfa, B, ldb, SFB, ldsfb, C, ldc, D, ldd]
+    if fn == "gemm_mxfp6_splitk":
+        args.append(fmt)
+    return getattr(tg.raw, fn)(*args, out, splits, ws, wsb, None)
+
+
+@pytest.mark.parametrize("fn", ["gemm_mxfp8_splitk", "gemm_mxfp4_splitk", "gemm_mxfp6_splitk"])
+def test_validation_mx_splitk(fn):
+    """Every case is refused before anything is launched (the arguments are a
+    valid fast-path call apart from the one changed)."""
+    assert callms(fn, M=-1) == INVALID_SIZE
+    assert callms(fn, M=0) == OK
+    assert callms(fn, lda=100) == BAD_LD
+    assert callms(fn, ldsfa=100) == BAD_LD
+    assert callms(fn, SFB=None) == NULL_POINTER
+    assert callms(fn, D=None) == NULL_POINTER
+    assert callms(fn, out=9) == UNSUPPORTED
+    assert callms(fn, splits=-1) == UNSUPPORTED
+    assert callms(fn, splits=65) == UNSUPPORTED
+    assert callms(fn, ws=None) == WORKSPACE
+    assert callms(fn, wsb=4 * 256 * 256 * 4 - 1) == WORKSPACE
+    assert callms(fn, ws=P + (1 << 26) + 128) == MISALIGNED
+    if fn == "gemm_mxfp6_splitk":
+        assert callms(fn, fmt=2) == UNSUPPORTED
 
 
 def callx(fn="gemm_bf16_ex", M=256, N=256, K=512, A=P, lda=256, ao=1, B=P, ldb=512, bo=0, C=None, ldc=0,

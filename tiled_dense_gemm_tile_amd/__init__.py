@@ -20,7 +20,7 @@ import os
 import threading
 
 __all__ = ["gemm_bf16", "gemm_fp16", "gemm_bf16_splitk", "gemm_fp16_splitk", "splitk_workspace_bytes",
-           "gemm_mxfp8", "gemm_mxfp4", "gemm_mxfp6", "raw", "GemmError", "LibraryMissing",
+           "gemm_mxfp8", "gemm_mxfp4", "gemm_mxfp6", "gemm_mxfp8_splitk", "gemm_mxfp4_splitk", "gemm_mxfp6_splitk", "raw", "GemmError", "LibraryMissing",
            "library_path", "STATUS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -77,6 +77,12 @@ def _load():
                 f.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp, i64, ci, vp]
             L.gemm_mxfp6.restype = ci
             L.gemm_mxfp6.argtypes = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp, i64, ci, ci, vp]
+            smx = [i64, i64, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp, i64, vp, i64]
+            for name in ("gemm_mxfp8_splitk", "gemm_mxfp4_splitk"):
+                f = getattr(L, name)
+                f.restype, f.argtypes = ci, smx + [ci, ci, vp, sz, vp]
+            L.gemm_mxfp6_splitk.restype = ci
+            L.gemm_mxfp6_splitk.argtypes = smx + [ci, ci, ci, vp, sz, vp]
             L.gemm_status_string.restype = ctypes.c_char_p
             L.gemm_status_string.argtypes = [ci]
             L.gemm_last_hip_error.restype = ci
@@ -223,21 +229,70 @@ def gemm_fp16_splitk(A, B, C=None, out_dtype=None, D=None, splits=0, workspace=N
                          torch.float16, splits, workspace)
 
 
-def gemm_mxfp8(A, SFA, B, SFB, C=None, out_dtype=None, D=None):
-    """Block-scaled fp8: A (M, K), B (N, K) e4m3 (float8_e4m3fn or uint8 codes);
-    SFA (M, K/32), SFB (N, K/32) e8m0 codes (uint8 or float8_e8m0fnu)."""
+def _scales(SFA, SFB, M, N):
     import torch
-    out_dtype = torch.float32 if out_dtype is None else out_dtype
-    M, N, K, D, stream, out = _prep(A, B, C, D, out_dtype, (torch.float8_e4m3fn, torch.uint8))
     for s, rows in ((SFA, M), (SFB, N)):
         if s.dtype not in (torch.uint8, torch.float8_e8m0fnu) or not s.is_cuda or s.shape[0] != rows:
             raise ValueError("scale arrays must be uint8/e8m0 device tensors of shape (rows, K/32)")
+
+
+def _split_tail(M, N, K, A, splits, workspace):
+    """(splits, workspace pointer, workspace bytes, kept tensor) of a split-K call."""
+    import torch
+    need = splitk_workspace_bytes(M, N, K, splits) if M and N and K else 0
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=A.device)
+    wp = workspace.data_ptr() if workspace is not None else None
+    wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    return [splits, wp, wb], workspace
+
+
+def _mx8(name, A, SFA, B, SFB, C, out_dtype, D, split):
+    import torch
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    M, N, K, D, stream, out = _prep(A, B, C, D, out_dtype, (torch.float8_e4m3fn, torch.uint8))
+    _scales(SFA, SFB, M, N)
     nkb = K // 32
-    st = _load().gemm_mxfp8(M, N, K, A.data_ptr(), _ld(A, K) if K else 0, SFA.data_ptr(), _ld(SFA, nkb) if K else 0,
-                            B.data_ptr(), _ld(B, K) if K else 0, SFB.data_ptr(), _ld(SFB, nkb) if K else 0,
-                            C.data_ptr() if C is not None else None, _ld(C, N) if C is not None else 0,
-                            D.data_ptr(), _ld(D, N), out, stream)
-    _check(st)
+    args = [M, N, K, A.data_ptr(), _ld(A, K) if K else 0, SFA.data_ptr(), _ld(SFA, nkb) if K else 0,
+            B.data_ptr(), _ld(B, K) if K else 0, SFB.data_ptr(), _ld(SFB, nkb) if K else 0,
+            C.data_ptr() if C is not None else None, _ld(C, N) if C is not None else 0, D.data_ptr(), _ld(D, N), out]
+    keep = None
+    if split is not None:
+        tail, keep = _split_tail(M, N, K, A, *split)
+        args += tail
+    _check(getattr(_load(), name)(*args, stream))
+    return D
+
+
+def gemm_mxfp8(A, SFA, B, SFB, C=None, out_dtype=None, D=None):
+    """Block-scaled fp8: A (M, K), B (N, K) e4m3 (float8_e4m3fn or uint8 codes);
+    SFA (M, K/32), SFB (N, K/32) e8m0 codes (uint8 or float8_e8m0fnu)."""
+    return _mx8("gemm_mxfp8", A, SFA, B, SFB, C, out_dtype, D, None)
+
+
+def gemm_mxfp8_splitk(A, SFA, B, SFB, C=None, out_dtype=None, D=None, splits=0, workspace=None):
+    """:func:`gemm_mxfp8` with K split over ``splits`` ranges of whole 512-K
+    groups (0: the library's choice); ``workspace`` as
+    :func:`gemm_bf16_splitk`."""
+    return _mx8("gemm_mxfp8_splitk", A, SFA, B, SFB, C, out_dtype, D, (splits, workspace))
+
+
+def _mx4(name, A, SFA, B, SFB, C, out_dtype, D, split):
+    import torch
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    fp4x2 = getattr(torch, "float4_e2m1fn_x2", torch.uint8)
+    M, N, KB, D, stream, out = _prep(A, B, C, D, out_dtype, (torch.uint8, fp4x2))
+    K = 2 * KB
+    _scales(SFA, SFB, M, N)
+    nkb = K // 32
+    args = [M, N, K, A.data_ptr(), 2 * _ld(A, KB) if K else 0, SFA.data_ptr(), _ld(SFA, nkb) if K else 0,
+            B.data_ptr(), 2 * _ld(B, KB) if K else 0, SFB.data_ptr(), _ld(SFB, nkb) if K else 0,
+            C.data_ptr() if C is not None else None, _ld(C, N) if C is not None else 0, D.data_ptr(), _ld(D, N), out]
+    keep = None
+    if split is not None:
+        tail, keep = _split_tail(M, N, K, A, *split)
+        args += tail
+    _check(getattr(_load(), name)(*args, stream))
     return D
 
 
@@ -246,31 +301,20 @@ def gemm_mxfp4(A, SFA, B, SFB, C=None, out_dtype=None, D=None):
     e2m1 codes (element 2i in the low nibble of byte i; float4_e2m1fn_x2 is
     accepted too); SFA (M, K/32), SFB (N, K/32) e8m0 codes.  K is twice the
     byte width of A."""
-    import torch
-    out_dtype = torch.float32 if out_dtype is None else out_dtype
-    fp4x2 = getattr(torch, "float4_e2m1fn_x2", torch.uint8)
-    M, N, KB, D, stream, out = _prep(A, B, C, D, out_dtype, (torch.uint8, fp4x2))
-    K = 2 * KB
-    for s, rows in ((SFA, M), (SFB, N)):
-        if s.dtype not in (torch.uint8, torch.float8_e8m0fnu) or not s.is_cuda or s.shape[0] != rows:
-            raise ValueError("scale arrays must be uint8/e8m0 device tensors of shape (rows, K/32)")
-    nkb = K // 32
-    st = _load().gemm_mxfp4(M, N, K, A.data_ptr(), 2 * _ld(A, KB) if K else 0, SFA.data_ptr(),
-                            _ld(SFA, nkb) if K else 0, B.data_ptr(), 2 * _ld(B, KB) if K else 0, SFB.data_ptr(),
-                            _ld(SFB, nkb) if K else 0, C.data_ptr() if C is not None else None,
-                            _ld(C, N) if C is not None else 0, D.data_ptr(), _ld(D, N), out, stream)
-    _check(st)
-    return D
+    return _mx4("gemm_mxfp4", A, SFA, B, SFB, C, out_dtype, D, None)
+
+
+def gemm_mxfp4_splitk(A, SFA, B, SFB, C=None, out_dtype=None, D=None, splits=0, workspace=None):
+    """:func:`gemm_mxfp4` with K split over ``splits`` ranges of whole 512-K
+    groups (0: the library's choice); ``workspace`` as
+    :func:`gemm_bf16_splitk`."""
+    return _mx4("gemm_mxfp4_splitk", A, SFA, B, SFB, C, out_dtype, D, (splits, workspace))
 
 
 FP6_FORMATS = {"e2m3": 0, "e3m2": 1}
 
 
-def gemm_mxfp6(A, SFA, B, SFB, C=None, out_dtype=None, D=None, fmt="e2m3"):
-    """Block-scaled fp6: A (M, 3K/4), B (N, 3K/4) uint8 bytes holding six-bit
-    codes (element k at bits 6k .. 6k+5 of a row read as a little-endian bit
-    string) in format ``fmt`` ("e2m3" or "e3m2"); SFA (M, K/32), SFB (N, K/32)
-    e8m0 codes.  K is four thirds of the byte width of A."""
+def _mx6(name, A, SFA, B, SFB, C, out_dtype, D, fmt, split):
     import torch
     out_dtype = torch.float32 if out_dtype is None else out_dtype
     if fmt not in FP6_FORMATS:
@@ -279,9 +323,7 @@ def gemm_mxfp6(A, SFA, B, SFB, C=None, out_dtype=None, D=None, fmt="e2m3"):
     if KB % 3:
         raise ValueError("the byte width of A and B must be a multiple of 3 (four elements per three bytes)")
     K = KB // 3 * 4
-    for s, rows in ((SFA, M), (SFB, N)):
-        if s.dtype not in (torch.uint8, torch.float8_e8m0fnu) or not s.is_cuda or s.shape[0] != rows:
-            raise ValueError("scale arrays must be uint8/e8m0 device tensors of shape (rows, K/32)")
+    _scales(SFA, SFB, M, N)
     lds = []
     for X in (A, B):
         ldb_ = _ld(X, KB) if K else 0
@@ -289,9 +331,28 @@ def gemm_mxfp6(A, SFA, B, SFB, C=None, out_dtype=None, D=None, fmt="e2m3"):
             raise ValueError("row strides of A and B must be multiples of 3 bytes")
         lds.append(ldb_ // 3 * 4)
     nkb = K // 32
-    st = _load().gemm_mxfp6(M, N, K, A.data_ptr(), lds[0], SFA.data_ptr(), _ld(SFA, nkb) if K else 0,
-                            B.data_ptr(), lds[1], SFB.data_ptr(), _ld(SFB, nkb) if K else 0,
-                            C.data_ptr() if C is not None else None, _ld(C, N) if C is not None else 0,
-                            D.data_ptr(), _ld(D, N), FP6_FORMATS[fmt], out, stream)
-    _check(st)
+    args = [M, N, K, A.data_ptr(), lds[0], SFA.data_ptr(), _ld(SFA, nkb) if K else 0,
+            B.data_ptr(), lds[1], SFB.data_ptr(), _ld(SFB, nkb) if K else 0,
+            C.data_ptr() if C is not None else None, _ld(C, N) if C is not None else 0,
+            D.data_ptr(), _ld(D, N), FP6_FORMATS[fmt], out]
+    keep = None
+    if split is not None:
+        tail, keep = _split_tail(M, N, K, A, *split)
+        args += tail
+    _check(getattr(_load(), name)(*args, stream))
     return D
+
+
+def gemm_mxfp6(A, SFA, B, SFB, C=None, out_dtype=None, D=None, fmt="e2m3"):
+    """Block-scaled fp6: A (M, 3K/4), B (N, 3K/4) uint8 bytes holding six-bit
+    codes (element k at bits 6k .. 6k+5 of a row read as a little-endian bit
+    string) in format ``fmt`` ("e2m3" or "e3m2"); SFA (M, K/32), SFB (N, K/32)
+    e8m0 codes.  K is four thirds of the byte width of A."""
+    return _mx6("gemm_mxfp6", A, SFA, B, SFB, C, out_dtype, D, fmt, None)
+
+
+def gemm_mxfp6_splitk(A, SFA, B, SFB, C=None, out_dtype=None, D=None, fmt="e2m3", splits=0, workspace=None):
+    """:func:`gemm_mxfp6` with K split over ``splits`` ranges of whole 512-K
+    groups (0: the library's choice); ``workspace`` as
+    :func:`gemm_bf16_splitk`."""
+    return _mx6("gemm_mxfp6_splitk", A, SFA, B, SFB, C, out_dtype, D, fmt, (splits, workspace))

@@ -8,6 +8,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "splitk.hpp"
+
 namespace tg_api {
 
 // hipError_t of the calling thread's last failed launch (gemm_last_hip_error)
@@ -75,5 +77,73 @@ inline gemm_status launched(hipError_t e) {
 }
 
 inline int64_t tiles_of(const Common &a, int bm, int bn) { return ((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn); }
+
+// ---- split-K (every input family) ------------------------------------------
+
+constexpr int kMaxSplits = 64;
+
+// Split count actually used for a requested one when K is cut at multiples
+// of `unit` elements (the kernel's K tile or scale epoch): at most one split
+// per unit, every split non-empty (ranges of ceil(units / s) units).
+inline int effective_splits(int64_t K, int splits, int64_t unit = 64) {
+    const int64_t kt = (K + unit - 1) / unit;
+    if (kt <= 1 || splits <= 1) return 1;
+    const int64_t s = splits > kt ? kt : splits;
+    const int64_t kps = (kt + s - 1) / s;
+    return (int)((kt + kps - 1) / kps);
+}
+
+// The library's choice: split only grids of fewer than 128 tiles of 256 x 256,
+// up to one wave of 256 workgroups, keeping at least 4096 K per split so that
+// writing and re-reading a split's fp32 partial tile stays small next to its
+// multiply work.
+inline int auto_splits(int64_t M, int64_t N, int64_t K) {
+    const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+    if (tiles <= 0 || tiles >= 128) return 1;
+    int64_t s = 256 / tiles;
+    const int64_t by_k = ((K + 63) / 64) / 64;
+    if (by_k < s) s = by_k;
+    if (s > kMaxSplits) s = kMaxSplits;
+    return s < 2 ? 1 : (int)s;
+}
+
+inline int64_t splitk_ldw(int64_t N) { return (N + 3) / 4 * 4; }
+
+// Workspace bytes for S splits: S fp32 partial matrices of M x splitk_ldw(N).
+// A coarser unit never yields more splits than 64-element K tiles for the
+// same request (ceil(8E / ceil(8E / s)) >= ceil(E / ceil(E / s))), so the
+// 64-tile count bounds every family's need.
+inline size_t splitk_bytes(int64_t M, int64_t N, int splits) {
+    return splits <= 1 ? 0 : (size_t)splits * (size_t)M * (size_t)splitk_ldw(N) * 4;
+}
+
+inline gemm_status check_workspace(const Common &a, int S, const void *ws, size_t ws_bytes) {
+    if (!ws || ws_bytes < splitk_bytes(a.M, a.N, S)) return GEMM_ERR_WORKSPACE;
+    if ((uintptr_t)ws % 256 != 0) return GEMM_ERR_MISALIGNED;
+    if (splitk_ldw(a.N) * 4 >= kMaxLdBytes) return GEMM_ERR_UNSUPPORTED;
+    return GEMM_OK;
+}
+
+// Second pass of a split call, on the same stream: D = the S partial slices
+// summed in order, plus C, rounded to the output type.
+inline gemm_status reduce_splits(const Common &a, const void *ws, int S, hipStream_t s) {
+    const bool bf16 = a.out_type == GEMM_OUT_BF16;
+    const uintptr_t vb = bf16 ? 8 : 16;
+    const int64_t ldw = splitk_ldw(a.N);
+    tg::SplitReduceArgs r;
+    r.ws = (const float *)ws;
+    r.ldw = ldw;
+    r.slice = a.M * ldw;
+    r.splits = S;
+    r.C = a.C;
+    r.ldc = a.ldc;
+    r.D = a.D;
+    r.ldd = a.ldd;
+    r.M = (int)a.M;
+    r.N = (int)a.N;
+    r.vec_c = a.C && ((uintptr_t)a.C % vb) == 0 && a.ldc % 4 == 0;
+    r.vec_d = ((uintptr_t)a.D % vb) == 0 && a.ldd % 4 == 0;
+    return launched(tg::launch_splitk_reduce(bf16, s, r));
+}
 
 }  // namespace tg_api

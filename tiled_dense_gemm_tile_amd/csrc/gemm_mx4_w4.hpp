@@ -57,7 +57,7 @@ __device__ __forceinline__ void mfma_mx4_acc(f32x4 &acc, const u32x4 &a, const u
 
 // q.g.lda and q.g.ldb are in BYTES here (half the leading dimension in
 // elements); q.g.K is in elements.
-template <bool OUT_BF16, int DAUX = kStoreStream>
+template <bool OUT_BF16, int DAUX = kStoreStream, bool SPLIT = false>
 __global__ void __launch_bounds__(256) gemm_mx4_w4_kernel(MxArgs q, F16Epi e) {
     const F16Args &p = q.g;
     constexpr int ROWB = 128, BKB = 128;               // bytes per LDS row = bytes per K tile (256 elements)
@@ -77,21 +77,20 @@ __global__ void __launch_bounds__(256) gemm_mx4_w4_kernel(MxArgs q, F16Epi e) {
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
-    int tmi, tni;
-    tile_order(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, tmi, tni);
-    const int m0 = tmi * 256, n0 = tni * 256;
-    const int M = p.M, N = p.N, K = p.K;
+    int m0, n0, split, k_lo, K;
+    mx_work_item<SPLIT>(p, m0, n0, split, k_lo, K);
+    const int M = p.M, N = p.N;
     const int kb = K / 2, nblk = K / 32;
     const int nk = K / 256, nep = K / 512;
 
     const __amdgpu_buffer_rsrc_t rA =
-        make_rsrc((const char *)p.A + (int64_t)m0 * p.lda, span_bytes(M - m0, kb, p.lda, 1));
+        make_rsrc((const char *)p.A + (int64_t)m0 * p.lda + k_lo / 2, span_bytes(M - m0, kb, p.lda, 1));
     const __amdgpu_buffer_rsrc_t rB =
-        make_rsrc((const char *)p.B + (int64_t)n0 * p.ldb, span_bytes(N - n0, kb, p.ldb, 1));
+        make_rsrc((const char *)p.B + (int64_t)n0 * p.ldb + k_lo / 2, span_bytes(N - n0, kb, p.ldb, 1));
     const __amdgpu_buffer_rsrc_t rSA =
-        make_rsrc((const char *)q.SFA + (int64_t)m0 * q.ldsfa, span_bytes(M - m0, nblk, q.ldsfa, 1));
+        make_rsrc((const char *)q.SFA + (int64_t)m0 * q.ldsfa + k_lo / 32, span_bytes(M - m0, nblk, q.ldsfa, 1));
     const __amdgpu_buffer_rsrc_t rSB =
-        make_rsrc((const char *)q.SFB + (int64_t)n0 * q.ldsfb, span_bytes(N - n0, nblk, q.ldsfb, 1));
+        make_rsrc((const char *)q.SFB + (int64_t)n0 * q.ldsfb + k_lo / 32, span_bytes(N - n0, nblk, q.ldsfb, 1));
     const __amdgpu_buffer_rsrc_t rZ = make_rsrc(p.A, 0u);
 
     // Operand loads: instruction j of wave w fills slot rows (4 j + w) * 8 +
@@ -266,7 +265,7 @@ __global__ void __launch_bounds__(256) gemm_mx4_w4_kernel(MxArgs q, F16Epi e) {
     wait_vmcnt<0>();
     wait_lgkmcnt0();
     barrier();
-    epilogue_lds16<OUT_BF16, TM, TN, WTM, WTN, DAUX>(acc, smem, wave, lane, wm, wn, m0, n0, M, N, p.C, p.ldc, p.D, p.ldd, e);
+    mx_epilogue<OUT_BF16, DAUX, SPLIT>(acc, smem, wave, lane, wm, wn, m0, n0, p, split, e);
 }
 
 }  // namespace tg

@@ -54,6 +54,42 @@ __device__ __forceinline__ void static_for(F &&f) {
     }
 }
 
+// Work item of a four-wave block-scaled workgroup: its 256 x 256 output
+// tile and, with SPLIT (split-K), its K range [k_lo, k_lo + K) -- split s of
+// ranges of p.kt_split scale epochs (512 K each), the last one shorter.
+template <bool SPLIT>
+__device__ __forceinline__ void mx_work_item(const F16Args &p, int &m0, int &n0, int &split, int &k_lo, int &K) {
+    int tmi, tni;
+    split = 0;
+    if constexpr (SPLIT)
+        tile_order_split(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, tmi, tni, split);
+    else
+        tile_order(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, tmi, tni);
+    m0 = tmi * 256;
+    n0 = tni * 256;
+    k_lo = SPLIT ? split * p.kt_split * 512 : 0;
+    K = SPLIT ? (p.K - k_lo < p.kt_split * 512 ? p.K - k_lo : p.kt_split * 512) : p.K;
+}
+
+// Epilogue of the four-wave block-scaled kernels: D = acc + C, or with SPLIT
+// the fp32 partial tile of split `split` into the workspace (no C: the
+// reduction adds the slices and C; partial tiles stay cacheable, the
+// reduction reads them right after).
+template <bool OUT_BF16, int DAUX, bool SPLIT, int TM, int TN>
+__device__ __forceinline__ void mx_epilogue(const f32x4 (&acc)[TM][TN], char *smem, int wave, int lane, int wm,
+                                            int wn, int m0, int n0, const F16Args &p, int split, const F16Epi &e) {
+    constexpr int WTM = TM * 16, WTN = TN * 16;        // the wave's quadrant
+    if constexpr (SPLIT) {
+        static_assert(!OUT_BF16, "split-K partial tiles are fp32");
+        float *part = p.ws + (int64_t)split * p.M * p.ldw;
+        epilogue_lds16<false, TM, TN, WTM, WTN, 0>(acc, smem, wave, lane, wm, wn, m0, n0, p.M, p.N, nullptr, 0, part,
+                                                   p.ldw, e);
+    } else {
+        epilogue_lds16<OUT_BF16, TM, TN, WTM, WTN, DAUX>(acc, smem, wave, lane, wm, wn, m0, n0, p.M, p.N, p.C, p.ldc,
+                                                         p.D, p.ldd, e);
+    }
+}
+
 // One 16x16x128 e4m3 MFMA on an AGPR accumulator block, in place; SA / SB:
 // the byte of each scale register used (encoded in op_sel / op_sel_hi).
 template <int SA, int SB>
@@ -68,7 +104,7 @@ __device__ __forceinline__ void mfma_mx16_acc(f32x4 &acc, const i32x8 &a, const 
 #undef TG_STR2
 }
 
-template <bool OUT_BF16, int DAUX = kStoreStream>
+template <bool OUT_BF16, int DAUX = kStoreStream, bool SPLIT = false>
 __global__ void __launch_bounds__(256) gemm_mx_w4_kernel(MxArgs q, F16Epi e) {
     const F16Args &p = q.g;
     constexpr int BK = 128, ROWB = 128;                // fp8: one byte per element
@@ -88,21 +124,20 @@ __global__ void __launch_bounds__(256) gemm_mx_w4_kernel(MxArgs q, F16Epi e) {
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
-    int tmi, tni;
-    tile_order(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, tmi, tni);
-    const int m0 = tmi * 256, n0 = tni * 256;
-    const int M = p.M, N = p.N, K = p.K;
+    int m0, n0, split, k_lo, K;
+    mx_work_item<SPLIT>(p, m0, n0, split, k_lo, K);
+    const int M = p.M, N = p.N;
     const int nblk = K / 32;
     const int nk = K / BK, nep = K / 512;
 
     const __amdgpu_buffer_rsrc_t rA =
-        make_rsrc((const char *)p.A + (int64_t)m0 * p.lda, span_bytes(M - m0, K, p.lda, 1));
+        make_rsrc((const char *)p.A + (int64_t)m0 * p.lda + k_lo, span_bytes(M - m0, K, p.lda, 1));
     const __amdgpu_buffer_rsrc_t rB =
-        make_rsrc((const char *)p.B + (int64_t)n0 * p.ldb, span_bytes(N - n0, K, p.ldb, 1));
+        make_rsrc((const char *)p.B + (int64_t)n0 * p.ldb + k_lo, span_bytes(N - n0, K, p.ldb, 1));
     const __amdgpu_buffer_rsrc_t rSA =
-        make_rsrc((const char *)q.SFA + (int64_t)m0 * q.ldsfa, span_bytes(M - m0, nblk, q.ldsfa, 1));
+        make_rsrc((const char *)q.SFA + (int64_t)m0 * q.ldsfa + k_lo / 32, span_bytes(M - m0, nblk, q.ldsfa, 1));
     const __amdgpu_buffer_rsrc_t rSB =
-        make_rsrc((const char *)q.SFB + (int64_t)n0 * q.ldsfb, span_bytes(N - n0, nblk, q.ldsfb, 1));
+        make_rsrc((const char *)q.SFB + (int64_t)n0 * q.ldsfb + k_lo / 32, span_bytes(N - n0, nblk, q.ldsfb, 1));
     const __amdgpu_buffer_rsrc_t rZ = make_rsrc(p.A, 0u);
 
     // Operand loads: instruction j of wave w fills slot rows (4 j + w) * 8 +
@@ -280,7 +315,7 @@ __global__ void __launch_bounds__(256) gemm_mx_w4_kernel(MxArgs q, F16Epi e) {
     wait_vmcnt<0>();
     wait_lgkmcnt0();
     barrier();
-    epilogue_lds16<OUT_BF16, TM, TN, WTM, WTN, DAUX>(acc, smem, wave, lane, wm, wn, m0, n0, M, N, p.C, p.ldc, p.D, p.ldd, e);
+    mx_epilogue<OUT_BF16, DAUX, SPLIT>(acc, smem, wave, lane, wm, wn, m0, n0, p, split, e);
 }
 
 }  // namespace tg

@@ -12,6 +12,10 @@ namespace tg {
 template <bool OUT_BF16>
 hipError_t launch_mx4(unsigned grid, hipStream_t s, const MxArgs &q, const F16Epi &e);
 
+// Split-K partial tiles (fp32, into q.g.ws); defined in the fp32-output
+// translation unit.
+hipError_t launch_mx4_split(unsigned grid, hipStream_t s, const MxArgs &q, const F16Epi &e);
+
 }  // namespace tg
 
 #ifdef TG_MX4_INSTANCE
@@ -22,6 +26,13 @@ hipError_t launch_mx4<TG_OUT_BF16>(unsigned grid, hipStream_t s, const MxArgs &q
     hipLaunchKernelGGL((gemm_mx4_w4_kernel<TG_OUT_BF16>), dim3(grid), dim3(256), 0, s, q, e);
     return hipGetLastError();
 }
+
+#if !TG_OUT_BF16
+hipError_t launch_mx4_split(unsigned grid, hipStream_t s, const MxArgs &q, const F16Epi &e) {
+    hipLaunchKernelGGL((gemm_mx4_w4_kernel<false, kStoreStream, true>), dim3(grid), dim3(256), 0, s, q, e);
+    return hipGetLastError();
+}
+#endif
 
 }  // namespace tg
 #endif

@@ -10,16 +10,17 @@ using namespace tg_api;
 
 namespace {
 
-// a.lda and a.ldb are in elements (multiples of 4); the kernel takes them in
-// bytes (three quarters of that).
-gemm_status dispatch_mx6(const Common &a, bool e3m2, const void *SFA, int64_t ldsfa, const void *SFB, int64_t ldsfb,
-                         hipStream_t s) {
-    // 16-byte A/B rows (lda multiple of 64 elements), 16-byte scale words
-    // (512 K) per row
-    const bool fast = a.K % 512 == 0 && (uintptr_t)a.A % 16 == 0 && (uintptr_t)a.B % 16 == 0 && a.lda % 64 == 0 &&
-                      a.ldb % 64 == 0 && (uintptr_t)SFA % 16 == 0 && (uintptr_t)SFB % 16 == 0 &&
-                      ldsfa % 16 == 0 && ldsfb % 16 == 0;
-    if (!fast && a.K > 0) return GEMM_ERR_UNSUPPORTED;
+// 16-byte A/B rows (lda multiple of 64 elements), 16-byte scale words (512
+// K) per row
+bool fast_mx6(const Common &a, const void *SFA, int64_t ldsfa, const void *SFB, int64_t ldsfb) {
+    return a.K % 512 == 0 && (uintptr_t)a.A % 16 == 0 && (uintptr_t)a.B % 16 == 0 && a.lda % 64 == 0 &&
+           a.ldb % 64 == 0 && (uintptr_t)SFA % 16 == 0 && (uintptr_t)SFB % 16 == 0 && ldsfa % 16 == 0 &&
+           ldsfb % 16 == 0;
+}
+
+// Kernel arguments; a.lda and a.ldb are in elements (multiples of 4), the
+// kernel takes them in bytes (three quarters of that).
+tg::MxArgs mx6_args(const Common &a, const void *SFA, int64_t ldsfa, const void *SFB, int64_t ldsfb) {
     tg::MxArgs q;
     q.g.A = a.A;
     q.g.B = a.B;
@@ -42,6 +43,13 @@ gemm_status dispatch_mx6(const Common &a, bool e3m2, const void *SFA, int64_t ld
     q.SFB = SFB ? SFB : a.D;
     q.ldsfa = ldsfa;
     q.ldsfb = ldsfb;
+    return q;
+}
+
+gemm_status dispatch_mx6(const Common &a, bool e3m2, const void *SFA, int64_t ldsfa, const void *SFB, int64_t ldsfb,
+                         hipStream_t s) {
+    if (!fast_mx6(a, SFA, ldsfa, SFB, ldsfb) && a.K > 0) return GEMM_ERR_UNSUPPORTED;
+    const tg::MxArgs q = mx6_args(a, SFA, ldsfa, SFB, ldsfb);
     const int64_t tiles = (int64_t)q.g.tiles_m * q.g.tiles_n;
     if (tiles >= kMaxDim) return GEMM_ERR_UNSUPPORTED;
     const bool bf16 = a.out_type == GEMM_OUT_BF16;
@@ -54,6 +62,61 @@ gemm_status dispatch_mx6(const Common &a, bool e3m2, const void *SFA, int64_t ld
                          : tg::launch_mx6<false>(e3m2, (unsigned)tiles, s, q, e));
 }
 
+// Checks of a gemm_mxfp6 call beyond the shared ones (A and B extents in
+// bytes: three quarters of the element counts; for K and lda multiples of 4,
+// lda < K exactly when the byte counts compare so, and other K or lda are
+// unsupported).
+gemm_status validate_mx6(const Common &a, int format, const void *SFA, int64_t ldsfa, const void *SFB,
+                         int64_t ldsfb, bool *none) {
+    *none = false;
+    if (format != GEMM_FP6_E2M3 && format != GEMM_FP6_E3M2) return GEMM_ERR_UNSUPPORTED;
+    Common bytes = a;
+    bytes.K = a.K / 4 * 3;
+    bytes.lda = a.lda / 4 * 3;
+    bytes.ldb = a.ldb / 4 * 3;
+    gemm_status st = validate(bytes, none);
+    if (st != GEMM_OK || *none) return st;
+    if (a.K >= kMaxDim || a.K % 32 != 0 || a.lda % 4 != 0 || a.ldb % 4 != 0) return GEMM_ERR_UNSUPPORTED;
+    if (a.K > 0) {
+        if (ldsfa < a.K / 32 || ldsfb < a.K / 32) return GEMM_ERR_BAD_LD;
+        if (!SFA || !SFB) return GEMM_ERR_NULL_POINTER;
+    }
+    if (ldsfa >= kMaxLdBytes || ldsfb >= kMaxLdBytes) return GEMM_ERR_UNSUPPORTED;
+    return GEMM_OK;
+}
+
+// Split-K: the kernel per (K range of whole scale epochs, tile), then the
+// reduction.
+gemm_status run_mx6_splitk(const Common &a, int format, const void *SFA, int64_t ldsfa, const void *SFB,
+                           int64_t ldsfb, int splits, void *ws, size_t ws_bytes, hipStream_t s) {
+    bool none = false;
+    gemm_status st = validate_mx6(a, format, SFA, ldsfa, SFB, ldsfb, &none);
+    if (st != GEMM_OK || none) return st;
+    if (splits < 0 || splits > kMaxSplits) return GEMM_ERR_UNSUPPORTED;
+    const bool e3m2 = format == GEMM_FP6_E3M2;
+    const int S = effective_splits(a.K, splits == 0 ? auto_splits(a.M, a.N, a.K) : splits, 512);
+    if (S == 1 || !fast_mx6(a, SFA, ldsfa, SFB, ldsfb)) return dispatch_mx6(a, e3m2, SFA, ldsfa, SFB, ldsfb, s);
+    st = check_workspace(a, S, ws, ws_bytes);
+    if (st != GEMM_OK) return st;
+    tg::MxArgs q = mx6_args(a, SFA, ldsfa, SFB, ldsfb);
+    q.g.C = nullptr;
+    q.g.D = nullptr;
+    q.g.ldc = 0;
+    q.g.ldd = 0;
+    const int64_t epochs = a.K / 512;
+    q.g.kt_split = (int)((epochs + S - 1) / S);
+    q.g.ws = (float *)ws;
+    q.g.ldw = splitk_ldw(a.N);
+    const int64_t grid = (int64_t)q.g.tiles_m * q.g.tiles_n * S;
+    if (grid >= kMaxDim) return GEMM_ERR_UNSUPPORTED;
+    tg::F16Epi e;
+    e.vec_c = false;
+    e.vec_d = true;                                    // 256-byte aligned base, ldw % 4 == 0
+    hipError_t err = tg::launch_mx6_split(e3m2, (unsigned)grid, s, q, e);
+    if (err != hipSuccess) return launched(err);
+    return reduce_splits(a, ws, S, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -62,24 +125,18 @@ gemm_status gemm_mxfp6(int64_t M, int64_t N, int64_t K, const void *A, int64_t l
                        const void *B, int64_t ldb, const void *SFB, int64_t ldsfb, const void *C, int64_t ldc,
                        void *D, int64_t ldd, int format, int out_type, hipStream_t stream) {
     Common a{M, N, K, A, lda, B, ldb, C, ldc, D, ldd, out_type, 1};
-    if (format != GEMM_FP6_E2M3 && format != GEMM_FP6_E3M2) return GEMM_ERR_UNSUPPORTED;
     bool none = false;
-    // A and B extents validated in bytes (three quarters of the element
-    // counts; for K and lda multiples of 4, lda < K exactly when the byte
-    // counts compare so, and other K or lda are unsupported)
-    Common bytes = a;
-    bytes.K = K / 4 * 3;
-    bytes.lda = lda / 4 * 3;
-    bytes.ldb = ldb / 4 * 3;
-    gemm_status st = validate(bytes, &none);
+    gemm_status st = validate_mx6(a, format, SFA, ldsfa, SFB, ldsfb, &none);
     if (st != GEMM_OK || none) return st;
-    if (K >= kMaxDim || K % 32 != 0 || lda % 4 != 0 || ldb % 4 != 0) return GEMM_ERR_UNSUPPORTED;
-    if (K > 0) {
-        if (ldsfa < K / 32 || ldsfb < K / 32) return GEMM_ERR_BAD_LD;
-        if (!SFA || !SFB) return GEMM_ERR_NULL_POINTER;
-    }
-    if (ldsfa >= kMaxLdBytes || ldsfb >= kMaxLdBytes) return GEMM_ERR_UNSUPPORTED;
     return dispatch_mx6(a, format == GEMM_FP6_E3M2, SFA, ldsfa, SFB, ldsfb, stream);
+}
+
+gemm_status gemm_mxfp6_splitk(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *SFA,
+                              int64_t ldsfa, const void *B, int64_t ldb, const void *SFB, int64_t ldsfb,
+                              const void *C, int64_t ldc, void *D, int64_t ldd, int format, int out_type,
+                              int splits, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    Common a{M, N, K, A, lda, B, ldb, C, ldc, D, ldd, out_type, 1};
+    return run_mx6_splitk(a, format, SFA, ldsfa, SFB, ldsfb, splits, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -13,6 +13,10 @@ namespace tg {
 template <bool OUT_BF16>
 hipError_t launch_mx6(bool e3m2, unsigned grid, hipStream_t s, const MxArgs &q, const F16Epi &e);
 
+// Split-K partial tiles (fp32, into q.g.ws); defined in the fp32-output
+// translation unit.
+hipError_t launch_mx6_split(bool e3m2, unsigned grid, hipStream_t s, const MxArgs &q, const F16Epi &e);
+
 }  // namespace tg
 
 #ifdef TG_MX6_INSTANCE
@@ -26,6 +30,16 @@ hipError_t launch_mx6<TG_OUT_BF16>(bool e3m2, unsigned grid, hipStream_t s, cons
         hipLaunchKernelGGL((gemm_mx6_w4_kernel<TG_OUT_BF16, 2>), dim3(grid), dim3(256), 0, s, q, e);
     return hipGetLastError();
 }
+
+#if !TG_OUT_BF16
+hipError_t launch_mx6_split(bool e3m2, unsigned grid, hipStream_t s, const MxArgs &q, const F16Epi &e) {
+    if (e3m2)
+        hipLaunchKernelGGL((gemm_mx6_w4_kernel<false, 3, kStoreStream, true>), dim3(grid), dim3(256), 0, s, q, e);
+    else
+        hipLaunchKernelGGL((gemm_mx6_w4_kernel<false, 2, kStoreStream, true>), dim3(grid), dim3(256), 0, s, q, e);
+    return hipGetLastError();
+}
+#endif
 
 }  // namespace tg
 #endif

@@ -69,6 +69,68 @@ gemm_status dispatch_mx(const Common &a, const void *SFA, int64_t ldsfa, const v
                          : tg::launch_mx<false>(cfg, (unsigned)tiles, s, q, e));
 }
 
+// Checks of a gemm_mxfp8 call beyond the shared ones.
+gemm_status validate_mx8(const Common &a, const void *SFA, int64_t ldsfa, const void *SFB, int64_t ldsfb,
+                         bool *none) {
+    gemm_status st = validate(a, none);
+    if (st != GEMM_OK || *none) return st;
+    if (a.K > 0) {
+        if (ldsfa < a.K / 32 || ldsfb < a.K / 32) return GEMM_ERR_BAD_LD;
+        if (!SFA || !SFB) return GEMM_ERR_NULL_POINTER;
+    }
+    if (a.K % 32 != 0) return GEMM_ERR_UNSUPPORTED;
+    if (ldsfa >= kMaxLdBytes || ldsfb >= kMaxLdBytes) return GEMM_ERR_UNSUPPORTED;
+    return GEMM_OK;
+}
+
+// Split-K: the four-wave kernel per (K range of whole scale epochs, tile),
+// then the reduction.  Calls the four-wave kernel cannot take run unsplit.
+gemm_status run_mx8_splitk(const Common &a, const void *SFA, int64_t ldsfa, const void *SFB, int64_t ldsfb,
+                           int splits, void *ws, size_t ws_bytes, hipStream_t s) {
+    bool none = false;
+    gemm_status st = validate_mx8(a, SFA, ldsfa, SFB, ldsfb, &none);
+    if (st != GEMM_OK || none) return st;
+    if (splits < 0 || splits > kMaxSplits) return GEMM_ERR_UNSUPPORTED;
+    const int S = effective_splits(a.K, splits == 0 ? auto_splits(a.M, a.N, a.K) : splits, 512);
+    const bool four_wave = a.K % 512 == 0 && (uintptr_t)a.A % 16 == 0 && (uintptr_t)a.B % 16 == 0 &&
+                           a.lda % 16 == 0 && a.ldb % 16 == 0 && (uintptr_t)SFA % 16 == 0 &&
+                           (uintptr_t)SFB % 16 == 0 && ldsfa % 16 == 0 && ldsfb % 16 == 0;
+    if (S == 1 || !four_wave) return dispatch_mx(a, SFA, ldsfa, SFB, ldsfb, s);
+    st = check_workspace(a, S, ws, ws_bytes);
+    if (st != GEMM_OK) return st;
+    tg::MxArgs q;
+    q.g.A = a.A;
+    q.g.B = a.B;
+    q.g.C = nullptr;
+    q.g.D = nullptr;
+    q.g.lda = a.lda;
+    q.g.ldb = a.ldb;
+    q.g.ldc = 0;
+    q.g.ldd = 0;
+    q.g.M = (int)a.M;
+    q.g.N = (int)a.N;
+    q.g.K = (int)a.K;
+    q.g.group_m = 4;
+    q.g.tiles_m = (int)((a.M + 255) / 256);
+    q.g.tiles_n = (int)((a.N + 255) / 256);
+    const int64_t epochs = a.K / 512;
+    q.g.kt_split = (int)((epochs + S - 1) / S);
+    q.g.ws = (float *)ws;
+    q.g.ldw = splitk_ldw(a.N);
+    q.SFA = SFA;
+    q.SFB = SFB;
+    q.ldsfa = ldsfa;
+    q.ldsfb = ldsfb;
+    const int64_t grid = (int64_t)q.g.tiles_m * q.g.tiles_n * S;
+    if (grid >= kMaxDim) return GEMM_ERR_UNSUPPORTED;
+    tg::F16Epi e;
+    e.vec_c = false;
+    e.vec_d = true;                                    // 256-byte aligned base, ldw % 4 == 0
+    hipError_t err = tg::launch_mx_split((unsigned)grid, s, q, e);
+    if (err != hipSuccess) return launched(err);
+    return reduce_splits(a, ws, S, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -78,15 +140,17 @@ gemm_status gemm_mxfp8(int64_t M, int64_t N, int64_t K, const void *A, int64_t l
                        void *D, int64_t ldd, int out_type, hipStream_t stream) {
     Common a{M, N, K, A, lda, B, ldb, C, ldc, D, ldd, out_type, 1};
     bool none = false;
-    gemm_status st = validate(a, &none);
+    gemm_status st = validate_mx8(a, SFA, ldsfa, SFB, ldsfb, &none);
     if (st != GEMM_OK || none) return st;
-    if (K > 0) {
-        if (ldsfa < K / 32 || ldsfb < K / 32) return GEMM_ERR_BAD_LD;
-        if (!SFA || !SFB) return GEMM_ERR_NULL_POINTER;
-    }
-    if (K % 32 != 0) return GEMM_ERR_UNSUPPORTED;
-    if (ldsfa >= kMaxLdBytes || ldsfb >= kMaxLdBytes) return GEMM_ERR_UNSUPPORTED;
     return dispatch_mx(a, SFA, ldsfa, SFB, ldsfb, stream);
+}
+
+gemm_status gemm_mxfp8_splitk(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *SFA,
+                              int64_t ldsfa, const void *B, int64_t ldb, const void *SFB, int64_t ldsfb,
+                              const void *C, int64_t ldc, void *D, int64_t ldd, int out_type, int splits,
+                              void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    Common a{M, N, K, A, lda, B, ldb, C, ldc, D, ldd, out_type, 1};
+    return run_mx8_splitk(a, SFA, ldsfa, SFB, ldsfb, splits, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -35,6 +35,10 @@ static_assert(kMxFourWave + 1 == kNumMxCfgs, "configuration table");
 template <bool OUT_BF16>
 hipError_t launch_mx(int cfg, unsigned grid, hipStream_t s, const MxArgs &q, const F16Epi &e);
 
+// Split-K partial tiles (fp32, into q.g.ws): the four-wave kernel with SPLIT;
+// defined in the fp32-output translation unit.
+hipError_t launch_mx_split(unsigned grid, hipStream_t s, const MxArgs &q, const F16Epi &e);
+
 }  // namespace tg
 
 #ifdef TG_MX_INSTANCE
@@ -63,6 +67,13 @@ hipError_t launch_mx<TG_OUT_BF16>(int cfg, unsigned grid, hipStream_t s, const M
     }
     return hipGetLastError();
 }
+
+#if !TG_OUT_BF16
+hipError_t launch_mx_split(unsigned grid, hipStream_t s, const MxArgs &q, const F16Epi &e) {
+    hipLaunchKernelGGL((gemm_mx_w4_kernel<false, kStoreStream, true>), dim3(grid), dim3(256), 0, s, q, e);
+    return hipGetLastError();
+}
+#endif
 
 }  // namespace tg
 #endif

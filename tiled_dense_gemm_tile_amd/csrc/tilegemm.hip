@@ -5,7 +5,6 @@
 
 #include "api.hpp"
 #include "f16_launch.hpp"
-#include "splitk.hpp"
 
 using namespace tg_api;
 
@@ -157,38 +156,6 @@ gemm_status run_f16_ex(bool fp16, const Common &a, int a_order, int b_order, hip
 
 // ---- split-K (16-bit inputs) ------------------------------------------------
 
-constexpr int kMaxSplits = 64;
-
-// Split count actually used for a requested one: at most one split per K tile
-// of 64, and every split non-empty (ranges of ceil(kt / s) K tiles).
-int effective_splits(int64_t K, int splits) {
-    const int64_t kt = (K + 63) / 64;
-    if (kt <= 1 || splits <= 1) return 1;
-    const int64_t s = splits > kt ? kt : splits;
-    const int64_t kps = (kt + s - 1) / s;
-    return (int)((kt + kps - 1) / kps);
-}
-
-// The library's choice: split only grids of fewer than 128 tiles of 256 x 256,
-// up to one wave of 256 workgroups, keeping at least 64 K tiles (4096 K) per
-// split so that writing and re-reading a split's fp32 partial tile stays small
-// next to its multiply work.
-int auto_splits(int64_t M, int64_t N, int64_t K) {
-    const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
-    if (tiles <= 0 || tiles >= 128) return 1;
-    int64_t s = 256 / tiles;
-    const int64_t by_k = ((K + 63) / 64) / 64;
-    if (by_k < s) s = by_k;
-    if (s > kMaxSplits) s = kMaxSplits;
-    return s < 2 ? 1 : (int)s;
-}
-
-int64_t splitk_ldw(int64_t N) { return (N + 3) / 4 * 4; }
-
-size_t splitk_bytes(int64_t M, int64_t N, int splits) {
-    return splits <= 1 ? 0 : (size_t)splits * (size_t)M * (size_t)splitk_ldw(N) * 4;
-}
-
 gemm_status run_f16_splitk(bool fp16, const Common &a, int splits, void *ws, size_t ws_bytes, hipStream_t s) {
     bool none = false;
     gemm_status st = validate(a, &none);
@@ -198,10 +165,9 @@ gemm_status run_f16_splitk(bool fp16, const Common &a, int splits, void *ws, siz
     const int vec = pick_vec(a);
     // rows only 4- or 2-byte aligned have no four-wave kernel: unsplit
     if (S == 1 || vec < 4) return run_f16(fp16, a, s);
-    if (!ws || ws_bytes < splitk_bytes(a.M, a.N, S)) return GEMM_ERR_WORKSPACE;
-    if ((uintptr_t)ws % 256 != 0) return GEMM_ERR_MISALIGNED;
+    st = check_workspace(a, S, ws, ws_bytes);
+    if (st != GEMM_OK) return st;
     const int64_t ldw = splitk_ldw(a.N);
-    if (ldw * 4 >= kMaxLdBytes) return GEMM_ERR_UNSUPPORTED;
     const int64_t kt = (a.K + 63) / 64;
     tg::F16Args p;
     p.A = a.A;
@@ -230,22 +196,7 @@ gemm_status run_f16_splitk(bool fp16, const Common &a, int splits, void *ws, siz
     hipError_t err = fp16 ? tg::launch_f16_split<true, false>(sh, (unsigned)grid, s, p, e)
                           : tg::launch_f16_split<false, false>(sh, (unsigned)grid, s, p, e);
     if (err != hipSuccess) return launched(err);
-    const bool bf16 = a.out_type == GEMM_OUT_BF16;
-    const uintptr_t vb = bf16 ? 8 : 16;
-    tg::SplitReduceArgs r;
-    r.ws = (const float *)ws;
-    r.ldw = ldw;
-    r.slice = a.M * ldw;
-    r.splits = S;
-    r.C = a.C;
-    r.ldc = a.ldc;
-    r.D = a.D;
-    r.ldd = a.ldd;
-    r.M = (int)a.M;
-    r.N = (int)a.N;
-    r.vec_c = a.C && ((uintptr_t)a.C % vb) == 0 && a.ldc % 4 == 0;
-    r.vec_d = ((uintptr_t)a.D % vb) == 0 && a.ldd % 4 == 0;
-    return launched(tg::launch_splitk_reduce(bf16, s, r));
+    return reduce_splits(a, ws, S, s);
 }
 
 }  // namespace

@@ -102,8 +102,8 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=0,
                     help="rows of D the CPU baseline evaluates (default: about 1.3e10 multiply-adds)")
     ap.add_argument("--splits", type=int, default=None,
-                    help="16-bit workloads: run the split-K entry point with this many K ranges (0: the "
-                         "library's choice; the default for workloads with fewer than 128 output tiles)")
+                    help="run the split-K entry point with this many K ranges (0: the library's choice; the "
+                         "default for workloads with fewer than 128 output tiles)")
     ap.add_argument("--a-order", choices=("k", "mn"), default="k",
                     help="16-bit workloads: store A K-contiguous (M x K) or MN-contiguous (K x M), same values")
     ap.add_argument("--b-order", choices=("k", "mn"), default="k",
@@ -143,7 +143,7 @@ def main():
     D = torch.empty((w.M, w.N), dtype=out_dtype, device="cuda:0")
 
     splits = args.splits
-    if splits is None and w.in_type in ("bf16", "fp16") and ((w.M + 255) // 256) * ((w.N + 255) // 256) < 128:
+    if splits is None and ((w.M + 255) // 256) * ((w.N + 255) // 256) < 128:
         splits = 0
     kernels_per_step = 1
     if w.in_type in ("bf16", "fp16") and splits is not None:
@@ -159,11 +159,17 @@ def main():
         step = lambda: tg.gemm_fp16(A, B, C, out_dtype=out_dtype, D=D)
     else:
         SFA, SFB = extra
-        if w.in_type in ("e2m3", "e3m2"):
-            step = lambda: tg.gemm_mxfp6(A, SFA, B, SFB, C, out_dtype=out_dtype, D=D, fmt=w.in_type)
+        kw = {} if w.in_type not in ("e2m3", "e3m2") else {"fmt": w.in_type}
+        if splits is not None:
+            # split-K: the workspace is allocated once, outside the timed steps
+            nbytes = tg.splitk_workspace_bytes(w.M, w.N, w.K, splits)
+            ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda:0") if nbytes else None
+            kernels_per_step = 2 if nbytes else 1
+            fn = {"e4m3": tg.gemm_mxfp8_splitk, "e2m1": tg.gemm_mxfp4_splitk}.get(w.in_type, tg.gemm_mxfp6_splitk)
+            kw.update(splits=splits, workspace=ws)
         else:
-            fn = tg.gemm_mxfp8 if w.in_type == "e4m3" else tg.gemm_mxfp4
-            step = lambda: fn(A, SFA, B, SFB, C, out_dtype=out_dtype, D=D)
+            fn = {"e4m3": tg.gemm_mxfp8, "e2m1": tg.gemm_mxfp4}.get(w.in_type, tg.gemm_mxfp6)
+        step = lambda: fn(A, SFA, B, SFB, C, out_dtype=out_dtype, D=D, **kw)
 
     # The GPU raises its clocks over the first milliseconds of sustained
     # work; a few warmup launches of a ~0.1 ms kernel end before that, so

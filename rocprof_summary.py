@@ -68,8 +68,7 @@ def kernel_source_hash(workload: str) -> str:
     api = {"e4m3": "mx_api.hip", "e2m3": "mx6_api.hip", "e3m2": "mx6_api.hip",
            "e2m1": "mx4_api.hip"}.get(w.in_type, "tilegemm.hip")
     _include_closure(api, files)
-    if w.in_type in ("bf16", "fp16"):
-        _include_closure("splitk.hip", files)          # the split-K reduction
+    _include_closure("splitk.hip", files)              # the split-K reduction
     h = hashlib.sha256()
     for f in sorted(files):
         h.update(f.encode())

@@ -184,3 +184,34 @@ def test_outside_the_fast_path():
         with pytest.raises(tg.GemmError) as ei:
             _run(t, xt, splits=2)
         assert ei.value.status == 5
+
+
+def _big(integer):
+    w = inputs.WORKLOADS["largek_mxfp8"]
+    x = inputs.generate(w, integer=integer)
+    say("mx splitk %s integer=%s splits=auto" % (w.name, integer))
+    D = _run("e4m3", x)
+    torch.cuda.synchronize()
+    Dg = D.cpu().numpy()
+    rand, forced = inputs.sample_indices(w.M, w.N, w.seed)
+    a, b = oracle.operands_f64("e4m3", x["A"], x["B"], SFA=x["SFA"], SFB=x["SFB"])
+    for name, idx in (("random", rand), ("forced", forced)):
+        Dr, S = oracle.gemm_ref("e4m3", x["A"], x["B"], SFA=x["SFA"], SFB=x["SFB"], idx=idx)
+        got = Dg.ravel()[idx].astype(np.float64)
+        if integer:
+            assert np.array_equal(got, Dr), name
+        else:
+            rep = check.report(got, Dr, S)
+            say("  %s: %s" % (name, rep))
+            assert rep["fail"] == 0, (name, rep)
+    ok, ratio = check.freivalds_blocks(Dg, a, b, None, block=64, integer=integer)
+    say("  freivalds ok=%s worst %.3g" % (ok, ratio))
+    assert ok
+
+
+def test_largek_mxfp8():
+    _big(False)
+
+
+def test_largek_mxfp8_integer():
+    _big(True)

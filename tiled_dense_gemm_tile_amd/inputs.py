@@ -77,6 +77,8 @@ WORKLOADS = {
                             note="M=N=1024 K=65536 bf16, C=0, fp32 out (16 output tiles: split-K)"),
     "mxfp8_8192": Workload("mxfp8_8192", 8192, 8192, 8192, "e4m3", "f32", U11, U11, None, 4,
                            scaled=True, note="M=N=K=8192 e4m3 + e8m0 per 32 K, C=0, fp32 out"),
+    "largek_mxfp8": Workload("largek_mxfp8", 1024, 1024, 65536, "e4m3", "f32", U11, U11, None, 8, scaled=True,
+                             note="M=N=1024 K=65536 e4m3 + e8m0 per 32 K, C=0, fp32 out (16 output tiles: split-K)"),
     "mxfp6_8192": Workload("mxfp6_8192", 8192, 8192, 8192, "e2m3", "f32", CODES, CODES, None, 7,
                            scaled=True, note="M=N=K=8192 fp6 e2m3 + e8m0 per 32 K, C=0, fp32 out"),
     "mxfp4_8192": Workload("mxfp4_8192", 8192, 8192, 8192, "e2m1", "f32", CODES, CODES, None, 5,

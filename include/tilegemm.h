@@ -154,11 +154,12 @@ gemm_status gemm_fp16_ex(int64_t M, int64_t N, int64_t K,
  *   B: e4m3 bytes, N x K (column-major K x N)     SFB: e8m0 bytes, N x K/32, ldsfb
  *   C, D, out_type: as gemm_bf16
  * ldsfa, ldsfb >= K/32 (else GEMM_ERR_BAD_LD); SFA and SFB non-NULL when
- * M*N*K > 0 (else GEMM_ERR_NULL_POINTER).  K must be a multiple of 32; this
- * version also needs K % 128 == 0, A, B and lda, ldb 16-byte aligned and
- * SFA, SFB and ldsfa, ldsfb 4-byte aligned, and returns
- * GEMM_ERR_UNSUPPORTED otherwise.  Scale code 0xFF (NaN) and e4m3 NaN
- * inputs give NaN in the affected outputs.
+ * M*N*K > 0 (else GEMM_ERR_NULL_POINTER).  K must be a multiple of 32 (else
+ * GEMM_ERR_UNSUPPORTED); rows and scale rows may start at any byte.  The
+ * tiled kernels take K % 128 == 0 with A, B and lda, ldb 16-byte aligned and
+ * SFA, SFB and ldsfa, ldsfb 4-byte aligned (fastest with K % 512 == 0 and
+ * 16-byte scale rows); other calls run a slower general kernel.  Scale code
+ * 0xFF (NaN) and e4m3 NaN inputs give NaN in the affected outputs.
  */
 gemm_status gemm_mxfp8(int64_t M, int64_t N, int64_t K,
                        const void *A, int64_t lda, const void *SFA, int64_t ldsfa,
@@ -180,10 +181,11 @@ gemm_status gemm_mxfp8(int64_t M, int64_t N, int64_t K,
  *   B: N x K elements (column-major K x N), ldb (elements, even)
  *   SFA, SFB, C, D, out_type: as gemm_mxfp8
  * Sizes, lda and ldb count ELEMENTS (two per byte).  K must be a multiple
- * of 32 and lda, ldb even; this version also needs K % 512 == 0, A and B
+ * of 32 and lda, ldb even (else GEMM_ERR_UNSUPPORTED); rows and scale rows
+ * may start at any byte.  The tiled kernel takes K % 512 == 0, A and B
  * 16-byte aligned, lda and ldb multiples of 32, SFA and SFB 16-byte aligned
- * and ldsfa, ldsfb multiples of 16, and returns GEMM_ERR_UNSUPPORTED
- * otherwise.  Byte limits of the shared convention apply to lda/2, ldb/2.
+ * and ldsfa, ldsfb multiples of 16; other calls run a slower general
+ * kernel.  Byte limits of the shared convention apply to lda/2, ldb/2.
  * Scale code 0xFF (NaN) gives NaN in the affected outputs.
  */
 gemm_status gemm_mxfp4(int64_t M, int64_t N, int64_t K,
@@ -208,11 +210,12 @@ gemm_status gemm_mxfp4(int64_t M, int64_t N, int64_t K,
  *   B: N x K elements (column-major K x N), ldb (elements, a multiple of 4)
  *   SFA, SFB, C, D, out_type: as gemm_mxfp8
  * Sizes, lda and ldb count ELEMENTS (three bytes per four).  K must be a
- * multiple of 32 and lda, ldb multiples of 4; this version also needs
+ * multiple of 32 and lda, ldb multiples of 4 (else GEMM_ERR_UNSUPPORTED);
+ * rows and scale rows may start at any byte.  The tiled kernel takes
  * K % 512 == 0, A and B 16-byte aligned, lda and ldb multiples of 64 (rows of
  * a multiple of 48 bytes), SFA and SFB 16-byte aligned and ldsfa, ldsfb
- * multiples of 16, and returns GEMM_ERR_UNSUPPORTED otherwise.  Byte limits
- * of the shared convention apply to 3*lda/4 and 3*ldb/4.  Scale code 0xFF
+ * multiples of 16; other calls run a slower general kernel.  Byte limits of
+ * the shared convention apply to 3*lda/4 and 3*ldb/4.  Scale code 0xFF
  * (NaN) gives NaN in the affected outputs.
  */
 gemm_status gemm_mxfp6(int64_t M, int64_t N, int64_t K,
@@ -269,9 +272,8 @@ gemm_status gemm_fp16_splitk(int64_t M, int64_t N, int64_t K,
  * on the same stream summing the partials in range order, adding C and
  * writing D (the same result on every call).  Source: as gemm_bf16_splitk.
  *   splits: as gemm_bf16_splitk, with at most one split per 512 K; calls
- *     outside the library's fast path for the type (see gemm_mxfp8 /
- *     gemm_mxfp4 / gemm_mxfp6: K % 512 == 0, 16-byte rows and scale rows)
- *     run unsplit, or are refused exactly as the unsplit call would be.
+ *     the tiled kernels do not take (see gemm_mxfp8 / gemm_mxfp4 /
+ *     gemm_mxfp6: K % 512 == 0, 16-byte rows and scale rows) run unsplit.
  *   workspace: as gemm_bf16_splitk; gemm_splitk_workspace_bytes(M, N, K,
  *     splits) bytes always suffice.
  * Everything else (layouts, scales, validation, out_type, C == D) is as the

@@ -1,0 +1,178 @@
+// Block-scaled GEMM for every call the tiled kernels do not take: any K that
+// is a multiple of 32, rows and scale rows at any byte alignment, all four
+// element formats (e4m3, e2m3, e3m2, e2m1), gfx950.
+//
+// A workgroup of four waves computes a 64 x 64 output tile, each wave a 32 x
+// 32 quadrant as 2 x 2 blocks of v_mfma_scale_f32_16x16x128_f8f6f4.  There is
+// no LDS: every lane loads its own operand bytes and scale bytes from memory
+// with range-checked buffer loads, one 128-wide K step at a time, and feeds
+// them straight to the MFMA.  Operand placement (measured): lane l supplies
+// row (A) or column (B) l % 16; for fp8 its bytes 0..15 are K elements
+// 16 q .. 16 q + 15 and bytes 16..31 elements 64 + 16 q .. of the step, for
+// fp6 and fp4 its registers hold the 32 elements of K block q of the step
+// (q = l / 16), packed as in memory; the scale of block q comes from lane
+// 16 q + l % 16.  K is a multiple of 32, so a lane's bytes always lie in
+// whole 32-element blocks: a block at or past K is loaded from an offset
+// beyond the resource (zeros, scale code 0), and contributes nothing.  Rows
+// past M or N read zeros from the per-tile resources and are not stored.
+// Output: lane l of block (i, j) holds rows 4 (l / 16) .. + 3, column l % 16.
+#pragma once
+
+#include "common.hpp"
+#include "gemm_mxfp8.hpp"
+
+namespace tg {
+
+// FMT: 0 e4m3, 2 e2m3, 3 e3m2, 4 e2m1 (the MFMA's cbsz / blgp codes).
+template <int FMT>
+struct MxAnyFmt {
+    static constexpr int kRegs = FMT == 0 ? 8 : FMT == 4 ? 4 : 6;   // operand registers per lane
+};
+
+// One scaled MFMA with scale byte 0 of each scale register; VGPR
+// accumulator.  The s_nop keeps VALU writes of the operands (the unaligned
+// path assembles them from bytes) out of the MFMA's read window: the
+// compiler inserts no wait states around inline asm.
+template <int FMT>
+__device__ __forceinline__ void mx_any_mfma(f32x4 &acc, const uint32_t (&a)[MxAnyFmt<FMT>::kRegs],
+                                            const uint32_t (&b)[MxAnyFmt<FMT>::kRegs], uint32_t sa, uint32_t sb) {
+    if constexpr (FMT == 0) {
+        const i32x8 va = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)a[4], (int)a[5], (int)a[6], (int)a[7]};
+        const i32x8 vb = {(int)b[0], (int)b[1], (int)b[2], (int)b[3], (int)b[4], (int)b[5], (int)b[6], (int)b[7]};
+        asm volatile("s_nop 4\n\tv_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0]"
+                     : "+v"(acc) : "v"(va), "v"(vb), "v"(sa), "v"(sb));
+    } else if constexpr (FMT == 4) {
+        const u32x4 va = {a[0], a[1], a[2], a[3]}, vb = {b[0], b[1], b[2], b[3]};
+        asm volatile("s_nop 4\n\tv_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0] cbsz:4 blgp:4"
+                     : "+v"(acc) : "v"(va), "v"(vb), "v"(sa), "v"(sb));
+    } else {
+        typedef uint32_t v6 __attribute__((ext_vector_type(6)));
+        const v6 va = {a[0], a[1], a[2], a[3], a[4], a[5]}, vb = {b[0], b[1], b[2], b[3], b[4], b[5]};
+        if constexpr (FMT == 2)
+            asm volatile("s_nop 4\n\tv_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0] cbsz:2 blgp:2"
+                         : "+v"(acc) : "v"(va), "v"(vb), "v"(sa), "v"(sb));
+        else
+            asm volatile("s_nop 4\n\tv_mfma_scale_f32_16x16x128_f8f6f4 %0, %1, %2, %0, %3, %4 op_sel_hi:[0,0,0] cbsz:3 blgp:3"
+                         : "+v"(acc) : "v"(va), "v"(vb), "v"(sa), "v"(sb));
+    }
+}
+
+// N consecutive dwords at byte offset `off` of resource r: dword loads when
+// ALIGNED (the offset is a multiple of 4), else each dword from four byte
+// loads.  off == kOOB reads zeros.
+template <int N, bool ALIGNED>
+__device__ __forceinline__ void mx_any_load(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t *dst) {
+#pragma unroll
+    for (int d = 0; d < N; ++d) {
+        const uint32_t o = off == kOOB ? kOOB : off + 4 * d;
+        if constexpr (ALIGNED) {
+            dst[d] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, o, 0, 0);
+        } else {
+            uint32_t v = 0;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const uint32_t ob = o == kOOB ? kOOB : o + b;
+                v |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, ob, 0, 0) << (8 * b);
+            }
+            dst[d] = v;
+        }
+    }
+}
+
+// q.g.lda / q.g.ldb in BYTES; q.g.K in elements (a multiple of 32).
+template <int FMT, bool OUT_BF16, bool ALIGNED>
+__global__ void __launch_bounds__(256) gemm_mx_any_kernel(MxArgs q) {
+    constexpr int R = MxAnyFmt<FMT>::kRegs;
+    const F16Args &p = q.g;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int tm = blockIdx.x % p.tiles_m, tn = blockIdx.x / p.tiles_m;
+    const int m0 = tm * 64, n0 = tn * 64;
+    const int M = p.M, N = p.N, K = p.K;
+    const int nblk = K / 32;
+    // bytes of a row's K elements
+    const int64_t kbytes = FMT == 0 ? K : FMT == 4 ? K / 2 : K / 4 * 3;
+    const __amdgpu_buffer_rsrc_t rA =
+        make_rsrc((const char *)p.A + (int64_t)m0 * p.lda, span_bytes(M - m0, (int)kbytes, p.lda, 1));
+    const __amdgpu_buffer_rsrc_t rB =
+        make_rsrc((const char *)p.B + (int64_t)n0 * p.ldb, span_bytes(N - n0, (int)kbytes, p.ldb, 1));
+    const __amdgpu_buffer_rsrc_t rSA =
+        make_rsrc((const char *)q.SFA + (int64_t)m0 * q.ldsfa, span_bytes(M - m0, nblk, q.ldsfa, 1));
+    const __amdgpu_buffer_rsrc_t rSB =
+        make_rsrc((const char *)q.SFB + (int64_t)n0 * q.ldsfb, span_bytes(N - n0, nblk, q.ldsfb, 1));
+
+    const int fr = lane & 15, fq = lane >> 4;
+    f32x4 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    for (int k0 = 0; k0 < K; k0 += 128) {
+        const int blk = k0 / 32 + fq;                  // the K block whose scale this lane supplies
+        uint32_t fa[2][R], fb[2][R], sa[2], sb[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int ra = 32 * wm + 16 * h + fr, rb = 32 * wn + 16 * h + fr;   // rows within the tile
+            if constexpr (FMT == 0) {
+                // elements k0 + 16 q .. + 15 (block k0/32 + q/2) and k0 + 64 + 16 q .. (block k0/32 + 2 + q/2)
+                const int e0 = k0 + 16 * fq, e1 = k0 + 64 + 16 * fq;
+                const uint32_t oa0 = e0 < K ? (uint32_t)(ra * p.lda + e0) : kOOB;
+                const uint32_t oa1 = e1 < K ? (uint32_t)(ra * p.lda + e1) : kOOB;
+                const uint32_t ob0 = e0 < K ? (uint32_t)(rb * p.ldb + e0) : kOOB;
+                const uint32_t ob1 = e1 < K ? (uint32_t)(rb * p.ldb + e1) : kOOB;
+                mx_any_load<4, ALIGNED>(rA, oa0, fa[h]);
+                mx_any_load<4, ALIGNED>(rA, oa1, fa[h] + 4);
+                mx_any_load<4, ALIGNED>(rB, ob0, fb[h]);
+                mx_any_load<4, ALIGNED>(rB, ob1, fb[h] + 4);
+            } else {
+                // block blk: 16 bytes (fp4) or 24 bytes (fp6)
+                const int bb = FMT == 4 ? 16 : 24;
+                const uint32_t oa = blk < nblk ? (uint32_t)(ra * p.lda + blk * bb) : kOOB;
+                const uint32_t ob = blk < nblk ? (uint32_t)(rb * p.ldb + blk * bb) : kOOB;
+                mx_any_load<R, ALIGNED>(rA, oa, fa[h]);
+                mx_any_load<R, ALIGNED>(rB, ob, fb[h]);
+            }
+            const uint32_t osa = blk < nblk ? (uint32_t)(ra * q.ldsfa + blk) : kOOB;
+            const uint32_t osb = blk < nblk ? (uint32_t)(rb * q.ldsfb + blk) : kOOB;
+            sa[h] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rSA, osa, 0, 0);
+            sb[h] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rSB, osb, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) mx_any_mfma<FMT>(acc[i][j], fa[i], fb[j], sa[i], sb[j]);
+    }
+    // the MFMA results before any other instruction reads them
+    asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 3"
+                 : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[1][0]), "+v"(acc[1][1]));
+
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int n = n0 + 32 * wn + 16 * j + fr;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int m = m0 + 32 * wm + 16 * i + 4 * fq + r;
+                if (m >= M || n >= N) continue;
+                float v = acc[i][j][r];
+                if constexpr (OUT_BF16) {
+                    if (p.C) {
+                        const uint32_t c = ((const uint16_t *)p.C)[(int64_t)m * p.ldc + n];
+                        v += __builtin_bit_cast(float, c << 16);
+                    }
+                    ((uint16_t *)p.D)[(int64_t)m * p.ldd + n] = f32_to_bf16_rne(v);
+                } else {
+                    if (p.C) v += ((const float *)p.C)[(int64_t)m * p.ldc + n];
+                    ((float *)p.D)[(int64_t)m * p.ldd + n] = v;
+                }
+            }
+        }
+}
+
+// Launch over ceil(M / 64) x ceil(N / 64) workgroups of 256 threads; fmt as
+// FMT above, aligned: every operand row starts at a multiple of 4 bytes.
+hipError_t launch_mx_any(int fmt, bool out_bf16, bool aligned, unsigned grid, hipStream_t s, const MxArgs &q);
+
+}  // namespace tg

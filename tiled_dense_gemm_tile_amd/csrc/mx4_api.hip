@@ -5,6 +5,7 @@
 
 #include "api.hpp"
 #include "mx4_launch.hpp"
+#include "mx_any_api.hpp"
 
 using namespace tg_api;
 
@@ -47,7 +48,9 @@ tg::MxArgs mx4_args(const Common &a, const void *SFA, int64_t ldsfa, const void 
 
 gemm_status dispatch_mx4(const Common &a, const void *SFA, int64_t ldsfa, const void *SFB, int64_t ldsfb,
                          hipStream_t s) {
-    if (!fast_mx4(a, SFA, ldsfa, SFB, ldsfb) && a.K > 0) return GEMM_ERR_UNSUPPORTED;
+    // other K % 32 and alignments: the general kernel
+    if (!fast_mx4(a, SFA, ldsfa, SFB, ldsfb) && a.K > 0)
+        return run_mx_any(a, 4, a.lda / 2, a.ldb / 2, SFA, ldsfa, SFB, ldsfb, s);
     const tg::MxArgs q = mx4_args(a, SFA, ldsfa, SFB, ldsfb);
     const int64_t tiles = (int64_t)q.g.tiles_m * q.g.tiles_n;
     if (tiles >= kMaxDim) return GEMM_ERR_UNSUPPORTED;

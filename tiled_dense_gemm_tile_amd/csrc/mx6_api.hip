@@ -5,6 +5,7 @@
 
 #include "api.hpp"
 #include "mx6_launch.hpp"
+#include "mx_any_api.hpp"
 
 using namespace tg_api;
 
@@ -48,7 +49,9 @@ tg::MxArgs mx6_args(const Common &a, const void *SFA, int64_t ldsfa, const void 
 
 gemm_status dispatch_mx6(const Common &a, bool e3m2, const void *SFA, int64_t ldsfa, const void *SFB, int64_t ldsfb,
                          hipStream_t s) {
-    if (!fast_mx6(a, SFA, ldsfa, SFB, ldsfb) && a.K > 0) return GEMM_ERR_UNSUPPORTED;
+    // other K % 32 and alignments: the general kernel
+    if (!fast_mx6(a, SFA, ldsfa, SFB, ldsfb) && a.K > 0)
+        return run_mx_any(a, e3m2 ? 3 : 2, a.lda / 4 * 3, a.ldb / 4 * 3, SFA, ldsfa, SFB, ldsfb, s);
     const tg::MxArgs q = mx6_args(a, SFA, ldsfa, SFB, ldsfb);
     const int64_t tiles = (int64_t)q.g.tiles_m * q.g.tiles_n;
     if (tiles >= kMaxDim) return GEMM_ERR_UNSUPPORTED;

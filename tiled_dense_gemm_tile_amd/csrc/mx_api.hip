@@ -4,6 +4,7 @@
 #include <stdlib.h>
 
 #include "api.hpp"
+#include "mx_any_api.hpp"
 #include "mx_launch.hpp"
 
 using namespace tg_api;
@@ -23,7 +24,8 @@ gemm_status dispatch_mx(const Common &a, const void *SFA, int64_t ldsfa, const v
     const bool fast = a.K % 128 == 0 && (uintptr_t)a.A % 16 == 0 && (uintptr_t)a.B % 16 == 0 && a.lda % 16 == 0 &&
                       a.ldb % 16 == 0 && (uintptr_t)SFA % 4 == 0 && (uintptr_t)SFB % 4 == 0 && ldsfa % 4 == 0 &&
                       ldsfb % 4 == 0;
-    if (!fast && a.K > 0) return GEMM_ERR_UNSUPPORTED;
+    // other K % 32 and alignments: the general kernel
+    if (!fast && a.K > 0) return run_mx_any(a, 0, a.lda, a.ldb, SFA, ldsfa, SFB, ldsfb, s);
     // The four-wave and ping-pong kernels load a row's scales 16 bytes (512
     // K) at a time, so they need 16-byte-aligned scale rows and whole groups
     // of 16 blocks.

@@ -265,6 +265,48 @@ gemm_status gemm_fp16_splitk(int64_t M, int64_t N, int64_t K,
                              void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * gemm_mxfp8_ex, gemm_mxfp4_ex, gemm_mxfp6_ex -- as gemm_mxfp8 / gemm_mxfp4 /
+ * gemm_mxfp6 with each operand's storage order chosen (a_order, b_order:
+ * gemm_operand_order):
+ *   A K-contiguous: M x K row-major, lda >= K (as the plain call)
+ *   A MN-contiguous: K x M row-major, element (m, k) at element k*lda + m,
+ *     lda >= M
+ *   B K-contiguous: N x K (as the plain call)
+ *   B MN-contiguous: K x N row-major, element (k, n) at element k*ldb + n,
+ *     ldb >= N
+ * Elements are packed along the contiguous dimension as in the plain calls
+ * (fp4 two per byte, fp6 four per three bytes; lda, ldb even for fp4 and
+ * multiples of 4 for fp6), and the scales keep their layout (SFA M x K/32,
+ * SFB N x K/32: one per row or column and 32-element K block).  Source:
+ * "Tensor Core 数据布局的演进", the descriptors' K-major and MN-major modes
+ * and the transposing fragment load.  Both K-contiguous: exactly the plain
+ * call.  Otherwise the call runs the general kernel, each lane gathering its
+ * K-ordered elements from the MN-contiguous storage (correct for every
+ * shape; far slower than the tiled kernels).  An order other than the two
+ * values is GEMM_ERR_UNSUPPORTED; everything else as the plain call.
+ */
+gemm_status gemm_mxfp8_ex(int64_t M, int64_t N, int64_t K,
+                          const void *A, int64_t lda, int a_order, const void *SFA, int64_t ldsfa,
+                          const void *B, int64_t ldb, int b_order, const void *SFB, int64_t ldsfb,
+                          const void *C, int64_t ldc,
+                          void *D, int64_t ldd,
+                          int out_type, hipStream_t stream);
+
+gemm_status gemm_mxfp4_ex(int64_t M, int64_t N, int64_t K,
+                          const void *A, int64_t lda, int a_order, const void *SFA, int64_t ldsfa,
+                          const void *B, int64_t ldb, int b_order, const void *SFB, int64_t ldsfb,
+                          const void *C, int64_t ldc,
+                          void *D, int64_t ldd,
+                          int out_type, hipStream_t stream);
+
+gemm_status gemm_mxfp6_ex(int64_t M, int64_t N, int64_t K,
+                          const void *A, int64_t lda, int a_order, const void *SFA, int64_t ldsfa,
+                          const void *B, int64_t ldb, int b_order, const void *SFB, int64_t ldsfb,
+                          const void *C, int64_t ldc,
+                          void *D, int64_t ldd,
+                          int format, int out_type, hipStream_t stream);
+
+/*
  * gemm_mxfp8_splitk, gemm_mxfp4_splitk, gemm_mxfp6_splitk -- as gemm_mxfp8 /
  * gemm_mxfp4 / gemm_mxfp6, with K cut into `splits` ranges of whole groups
  * of 512 K (16 scale blocks) computed by separate workgroups, each range's

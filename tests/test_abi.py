@@ -24,8 +24,9 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["gemm_bf16", "gemm_bf16_ex", "gemm_bf16_splitk", "gemm_fp16", "gemm_fp16_ex",
-                                    "gemm_fp16_splitk", "gemm_last_hip_error", "gemm_mxfp4", "gemm_mxfp4_splitk", "gemm_mxfp6",
-                                    "gemm_mxfp6_splitk", "gemm_mxfp8", "gemm_mxfp8_splitk",
+                                    "gemm_fp16_splitk", "gemm_last_hip_error", "gemm_mxfp4", "gemm_mxfp4_ex", "gemm_mxfp4_splitk",
+                                    "gemm_mxfp6", "gemm_mxfp6_ex", "gemm_mxfp6_splitk", "gemm_mxfp8",
+                                    "gemm_mxfp8_ex", "gemm_mxfp8_splitk",
                                     "gemm_splitk_workspace_bytes", "gemm_status_string"]
 
 
@@ -221,6 +222,34 @@ def test_validation_mx_splitk(fn):
     assert callms(fn, ws=P + (1 << 26) + 128) == MISALIGNED
     if fn == "gemm_mxfp6_splitk":
         assert callms(fn, fmt=2) == UNSUPPORTED
+
+
+def callmx(fn, M=256, N=192, K=512, A=P, lda=256, ao=1, SFA=P + 4096, ldsfa=16, B=P, ldb=512, bo=0,
+           SFB=P + 8192, ldsfb=16, C=None, ldc=0, D=P + (1 << 24), ldd=192, out=F32, fmt=0):
+    args = [M, N, K, A, lda, ao, SFA, ldsfa, B, ldb, bo, SFB, ldsfb, C, ldc, D, ldd]
+    if fn == "gemm_mxfp6_ex":
+        args.append(fmt)
+    return getattr(tg.raw, fn)(*args, out, None)
+
+
+@pytest.mark.parametrize("fn", ["gemm_mxfp8_ex", "gemm_mxfp4_ex", "gemm_mxfp6_ex"])
+def test_validation_mx_orders(fn):
+    """MN-contiguous block-scaled operands: leading dimension against M (N);
+    every case is refused before anything is launched."""
+    assert callmx(fn, M=-1) == INVALID_SIZE
+    assert callmx(fn, M=0) == OK
+    assert callmx(fn, ao=2) == UNSUPPORTED
+    assert callmx(fn, bo=-1) == UNSUPPORTED
+    assert callmx(fn, lda=252) == BAD_LD                  # A stored K x M: lda >= M
+    assert callmx(fn, ao=0, bo=1, lda=512, ldb=188) == BAD_LD
+    assert callmx(fn, ldb=508) == BAD_LD                  # B K-contiguous: ldb >= K
+    assert callmx(fn, SFA=None) == NULL_POINTER
+    assert callmx(fn, ldsfa=15) == BAD_LD
+    assert callmx(fn, K=48) == UNSUPPORTED                # K % 32
+    if fn != "gemm_mxfp8_ex":
+        assert callmx(fn, lda=257 if fn == "gemm_mxfp4_ex" else 258) == UNSUPPORTED   # whole-byte rows
+    if fn == "gemm_mxfp6_ex":
+        assert callmx(fn, fmt=7) == UNSUPPORTED
 
 
 def callx(fn="gemm_bf16_ex", M=256, N=256, K=512, A=P, lda=256, ao=1, B=P, ldb=512, bo=0, C=None, ldc=0,

@@ -83,6 +83,12 @@ def _load():
                 f.restype, f.argtypes = ci, smx + [ci, ci, vp, sz, vp]
             L.gemm_mxfp6_splitk.restype = ci
             L.gemm_mxfp6_splitk.argtypes = smx + [ci, ci, ci, vp, sz, vp]
+            sex = [i64, i64, i64, vp, i64, ci, vp, i64, vp, i64, ci, vp, i64, vp, i64, vp, i64]
+            for name in ("gemm_mxfp8_ex", "gemm_mxfp4_ex"):
+                f = getattr(L, name)
+                f.restype, f.argtypes = ci, sex + [ci, vp]
+            L.gemm_mxfp6_ex.restype = ci
+            L.gemm_mxfp6_ex.argtypes = sex + [ci, ci, vp]
             L.gemm_status_string.restype = ctypes.c_char_p
             L.gemm_status_string.argtypes = [ci]
             L.gemm_last_hip_error.restype = ci
@@ -247,6 +253,61 @@ def _split_tail(M, N, K, A, splits, workspace):
     return [splits, wp, wb], workspace
 
 
+# elements per byte of the block-scaled formats, as (numerator, denominator)
+_EPB = {"e4m3": (1, 1), "e2m1": (2, 1), "e2m3": (4, 3), "e3m2": (4, 3)}
+_ORDERS = {"k": K_CONTIGUOUS, "mn": MN_CONTIGUOUS}
+
+
+def _mx_operand(t, X, order):
+    """(rows, K, leading dimension in elements) of a block-scaled operand
+    given as its byte storage: (rows, K bytes) K-contiguous or (K, rows
+    bytes) MN-contiguous."""
+    num, den = _EPB[t]
+    r, c = X.shape
+    if c > 1 and X.stride(1) != 1:
+        raise ValueError("the byte storage needs a unit last stride")
+    sb = X.stride(0) if r > 1 else c
+    if (c * num) % den or (sb * num) % den:
+        raise ValueError("rows must hold whole groups of elements (fp6: multiples of 3 bytes)")
+    elems, ld = c * num // den, sb * num // den
+    return (r, elems, ld) if order == "k" else (elems, r, ld)
+
+
+def _mx_ex(t, A, SFA, B, SFB, C, out_dtype, D, a_order, b_order, fmt=None):
+    """A block-scaled call with explicit storage orders (the *_ex entry points)."""
+    import torch
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    if a_order not in _ORDERS or b_order not in _ORDERS:
+        raise ValueError("orders are 'k' or 'mn'")
+    ok = (torch.uint8, torch.float8_e4m3fn) if t == "e4m3" else (torch.uint8,)
+    if A.dtype not in ok or B.dtype not in ok or not (A.is_cuda and B.is_cuda):
+        raise TypeError("A and B must be device byte tensors")
+    M, K, lda = _mx_operand(t, A, a_order)
+    N, KB, ldb = _mx_operand(t, B, b_order)
+    if K != KB:
+        raise ValueError("A and B disagree on K")
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out_dtype must be float32 or bfloat16")
+    if D is None:
+        D = torch.empty((M, N), dtype=out_dtype, device=A.device)
+    if D.dtype != out_dtype or tuple(D.shape) != (M, N):
+        raise ValueError("D must be (M, N) of out_dtype")
+    if C is not None and (C.dtype != out_dtype or tuple(C.shape) != (M, N)):
+        raise ValueError("C must be (M, N) of out_dtype")
+    _scales(SFA, SFB, M, N)
+    nkb = K // 32
+    stream = torch.cuda.current_stream(A.device).cuda_stream
+    out = OUT_BF16 if out_dtype == torch.bfloat16 else OUT_F32
+    args = [M, N, K, A.data_ptr(), lda if K else 0, _ORDERS[a_order], SFA.data_ptr(), _ld(SFA, nkb) if K else 0,
+            B.data_ptr(), ldb if K else 0, _ORDERS[b_order], SFB.data_ptr(), _ld(SFB, nkb) if K else 0,
+            C.data_ptr() if C is not None else None, _ld(C, N) if C is not None else 0, D.data_ptr(), _ld(D, N)]
+    name = {"e4m3": "gemm_mxfp8_ex", "e2m1": "gemm_mxfp4_ex"}.get(t, "gemm_mxfp6_ex")
+    if fmt is not None:
+        args.append(FP6_FORMATS[fmt])
+    _check(getattr(_load(), name)(*args, out, stream))
+    return D
+
+
 def _mx8(name, A, SFA, B, SFB, C, out_dtype, D, split):
     import torch
     out_dtype = torch.float32 if out_dtype is None else out_dtype
@@ -264,9 +325,13 @@ def _mx8(name, A, SFA, B, SFB, C, out_dtype, D, split):
     return D
 
 
-def gemm_mxfp8(A, SFA, B, SFB, C=None, out_dtype=None, D=None):
+def gemm_mxfp8(A, SFA, B, SFB, C=None, out_dtype=None, D=None, a_order="k", b_order="k"):
     """Block-scaled fp8: A (M, K), B (N, K) e4m3 (float8_e4m3fn or uint8 codes);
-    SFA (M, K/32), SFB (N, K/32) e8m0 codes (uint8 or float8_e8m0fnu)."""
+    SFA (M, K/32), SFB (N, K/32) e8m0 codes (uint8 or float8_e8m0fnu).
+    ``a_order="mn"``: A given as its K x M storage (element (m, k) at [k, m]);
+    ``b_order="mn"``: B as K x N (gemm_mxfp8_ex)."""
+    if a_order != "k" or b_order != "k":
+        return _mx_ex("e4m3", A, SFA, B, SFB, C, out_dtype, D, a_order, b_order)
     return _mx8("gemm_mxfp8", A, SFA, B, SFB, C, out_dtype, D, None)
 
 
@@ -296,11 +361,14 @@ def _mx4(name, A, SFA, B, SFB, C, out_dtype, D, split):
     return D
 
 
-def gemm_mxfp4(A, SFA, B, SFB, C=None, out_dtype=None, D=None):
+def gemm_mxfp4(A, SFA, B, SFB, C=None, out_dtype=None, D=None, a_order="k", b_order="k"):
     """Block-scaled fp4: A (M, K/2), B (N, K/2) uint8 bytes each holding two
     e2m1 codes (element 2i in the low nibble of byte i; float4_e2m1fn_x2 is
     accepted too); SFA (M, K/32), SFB (N, K/32) e8m0 codes.  K is twice the
-    byte width of A."""
+    byte width of A.  ``a_order="mn"``: A given as its K x M storage, (K,
+    M/2) bytes packed along M; ``b_order="mn"`` likewise (gemm_mxfp4_ex)."""
+    if a_order != "k" or b_order != "k":
+        return _mx_ex("e2m1", A, SFA, B, SFB, C, out_dtype, D, a_order, b_order)
     return _mx4("gemm_mxfp4", A, SFA, B, SFB, C, out_dtype, D, None)
 
 
@@ -343,11 +411,17 @@ def _mx6(name, A, SFA, B, SFB, C, out_dtype, D, fmt, split):
     return D
 
 
-def gemm_mxfp6(A, SFA, B, SFB, C=None, out_dtype=None, D=None, fmt="e2m3"):
+def gemm_mxfp6(A, SFA, B, SFB, C=None, out_dtype=None, D=None, fmt="e2m3", a_order="k", b_order="k"):
     """Block-scaled fp6: A (M, 3K/4), B (N, 3K/4) uint8 bytes holding six-bit
     codes (element k at bits 6k .. 6k+5 of a row read as a little-endian bit
     string) in format ``fmt`` ("e2m3" or "e3m2"); SFA (M, K/32), SFB (N, K/32)
-    e8m0 codes.  K is four thirds of the byte width of A."""
+    e8m0 codes.  K is four thirds of the byte width of A.  ``a_order="mn"``:
+    A given as its K x M storage, (K, 3M/4) bytes packed along M;
+    ``b_order="mn"`` likewise (gemm_mxfp6_ex)."""
+    if a_order != "k" or b_order != "k":
+        if fmt not in FP6_FORMATS:
+            raise ValueError("fmt must be 'e2m3' or 'e3m2'")
+        return _mx_ex(fmt, A, SFA, B, SFB, C, out_dtype, D, a_order, b_order, fmt)
     return _mx6("gemm_mxfp6", A, SFA, B, SFB, C, out_dtype, D, fmt, None)
 
 

@@ -39,8 +39,10 @@ struct Common {
 inline bool misaligned(const void *p, int size) { return p && (((uintptr_t)p) % (uintptr_t)size) != 0; }
 
 // Validation shared by every entry point; returns GEMM_OK when a launch may
-// proceed (and sets *nothing_to_do when M or N is zero).
-inline gemm_status validate(const Common &a, bool *nothing_to_do) {
+// proceed (and sets *nothing_to_do when M or N is zero).  lda_min / ldb_min:
+// the shortest leading dimension of each operand (negative: K, for
+// K-contiguous storage).
+inline gemm_status validate(const Common &a, bool *nothing_to_do, int64_t lda_min = -1, int64_t ldb_min = -1) {
     *nothing_to_do = false;
     if (a.M < 0 || a.N < 0 || a.K < 0) return GEMM_ERR_INVALID_SIZE;
     if (a.M >= kMaxDim || a.N >= kMaxDim || a.K >= kMaxDim) return GEMM_ERR_UNSUPPORTED;
@@ -49,7 +51,9 @@ inline gemm_status validate(const Common &a, bool *nothing_to_do) {
         *nothing_to_do = true;
         return GEMM_OK;
     }
-    if (a.lda < a.K || a.ldb < a.K || a.ldd < a.N || (a.C && a.ldc < a.N)) return GEMM_ERR_BAD_LD;
+    if (a.lda < (lda_min < 0 ? a.K : lda_min) || a.ldb < (ldb_min < 0 ? a.K : ldb_min) || a.ldd < a.N ||
+        (a.C && a.ldc < a.N))
+        return GEMM_ERR_BAD_LD;
     if (!a.D) return GEMM_ERR_NULL_POINTER;
     if (a.K > 0 && (!a.A || !a.B)) return GEMM_ERR_NULL_POINTER;
     const int os = a.out_type == GEMM_OUT_BF16 ? 2 : 4;

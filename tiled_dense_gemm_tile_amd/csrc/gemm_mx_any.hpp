@@ -16,6 +16,13 @@
 // beyond the resource (zeros, scale code 0), and contributes nothing.  Rows
 // past M or N read zeros from the per-tile resources and are not stored.
 // Output: lane l of block (i, j) holds rows 4 (l / 16) .. + 3, column l % 16.
+//
+// AMN / BMN: A (B) is stored MN-contiguous -- K rows of lda (ldb) elements,
+// element (m, k) at element k * lda + m, packed along M as along K in the
+// K-contiguous form.  Each lane then gathers its 32 elements one by one
+// (byte loads at the element's bit offset from a resource over the K
+// step's rows) and packs them into its operand registers; elements past K
+// or past M (N) are zero.
 #pragma once
 
 #include "common.hpp"
@@ -79,8 +86,42 @@ __device__ __forceinline__ void mx_any_load(__amdgpu_buffer_rsrc_t r, uint32_t o
     }
 }
 
+// Bits per element of format FMT.
+template <int FMT>
+constexpr int mx_any_bits() { return FMT == 0 ? 8 : FMT == 4 ? 4 : 6; }
+
+// The 32 elements of an MN-contiguous operand that lane (row `row` of the
+// operand, quarter fq) supplies for the K step at k0 (see the placement
+// above), gathered from storage X (K rows of ld_b bytes) into dst.
+// `rows`: the operand's M (N).
+template <int FMT>
+__device__ __forceinline__ void mx_any_gather(const char *X, int64_t ld_b, int rows, int K, int row, int k0, int fq,
+                                              uint32_t (&dst)[MxAnyFmt<FMT>::kRegs]) {
+    constexpr int BITS = mx_any_bits<FMT>(), R = MxAnyFmt<FMT>::kRegs;
+    const int nk = K - k0 < 128 ? K - k0 : 128;         // rows of this K step
+    const int64_t row_bytes = ((int64_t)rows * BITS + 7) / 8;
+    const __amdgpu_buffer_rsrc_t r =
+        make_rsrc(X + (int64_t)k0 * ld_b, (uint32_t)((int64_t)(nk - 1) * ld_b + row_bytes));
+    const uint32_t bit = (uint32_t)row * BITS;           // the element's bit offset within its storage row
+#pragma unroll
+    for (int d = 0; d < R; ++d) dst[d] = 0;
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+        const int dk = FMT == 0 ? (e < 16 ? 16 * fq + e : 64 + 16 * fq + e - 16) : 32 * fq + e;
+        const bool ok = k0 + dk < K && row < rows;
+        const uint32_t off = ok ? (uint32_t)(dk * ld_b) + (bit >> 3) : kOOB;
+        uint32_t v = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
+        if constexpr (BITS == 6)
+            v |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, ok ? off + 1 : kOOB, 0, 0) << 8;
+        const uint32_t code = (v >> (bit & 7)) & ((1u << BITS) - 1);
+        const int pos = e * BITS, w = pos / 32, sh = pos % 32;   // constants once unrolled
+        dst[w] |= code << sh;
+        if (sh + BITS > 32) dst[w + 1] |= code >> (32 - sh);
+    }
+}
+
 // q.g.lda / q.g.ldb in BYTES; q.g.K in elements (a multiple of 32).
-template <int FMT, bool OUT_BF16, bool ALIGNED>
+template <int FMT, bool OUT_BF16, bool ALIGNED, bool AMN = false, bool BMN = false>
 __global__ void __launch_bounds__(256) gemm_mx_any_kernel(MxArgs q) {
     constexpr int R = MxAnyFmt<FMT>::kRegs;
     const F16Args &p = q.g;
@@ -114,6 +155,12 @@ __global__ void __launch_bounds__(256) gemm_mx_any_kernel(MxArgs q) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int ra = 32 * wm + 16 * h + fr, rb = 32 * wn + 16 * h + fr;   // rows within the tile
+            if constexpr (AMN || BMN) {
+                if constexpr (AMN)
+                    mx_any_gather<FMT>((const char *)p.A, p.lda, M, K, m0 + ra, k0, fq, fa[h]);
+                if constexpr (BMN)
+                    mx_any_gather<FMT>((const char *)p.B, p.ldb, N, K, n0 + rb, k0, fq, fb[h]);
+            }
             if constexpr (FMT == 0) {
                 // elements k0 + 16 q .. + 15 (block k0/32 + q/2) and k0 + 64 + 16 q .. (block k0/32 + 2 + q/2)
                 const int e0 = k0 + 16 * fq, e1 = k0 + 64 + 16 * fq;
@@ -121,17 +168,21 @@ __global__ void __launch_bounds__(256) gemm_mx_any_kernel(MxArgs q) {
                 const uint32_t oa1 = e1 < K ? (uint32_t)(ra * p.lda + e1) : kOOB;
                 const uint32_t ob0 = e0 < K ? (uint32_t)(rb * p.ldb + e0) : kOOB;
                 const uint32_t ob1 = e1 < K ? (uint32_t)(rb * p.ldb + e1) : kOOB;
-                mx_any_load<4, ALIGNED>(rA, oa0, fa[h]);
-                mx_any_load<4, ALIGNED>(rA, oa1, fa[h] + 4);
-                mx_any_load<4, ALIGNED>(rB, ob0, fb[h]);
-                mx_any_load<4, ALIGNED>(rB, ob1, fb[h] + 4);
+                if constexpr (!AMN) {
+                    mx_any_load<4, ALIGNED>(rA, oa0, fa[h]);
+                    mx_any_load<4, ALIGNED>(rA, oa1, fa[h] + 4);
+                }
+                if constexpr (!BMN) {
+                    mx_any_load<4, ALIGNED>(rB, ob0, fb[h]);
+                    mx_any_load<4, ALIGNED>(rB, ob1, fb[h] + 4);
+                }
             } else {
                 // block blk: 16 bytes (fp4) or 24 bytes (fp6)
                 const int bb = FMT == 4 ? 16 : 24;
                 const uint32_t oa = blk < nblk ? (uint32_t)(ra * p.lda + blk * bb) : kOOB;
                 const uint32_t ob = blk < nblk ? (uint32_t)(rb * p.ldb + blk * bb) : kOOB;
-                mx_any_load<R, ALIGNED>(rA, oa, fa[h]);
-                mx_any_load<R, ALIGNED>(rB, ob, fb[h]);
+                if constexpr (!AMN) mx_any_load<R, ALIGNED>(rA, oa, fa[h]);
+                if constexpr (!BMN) mx_any_load<R, ALIGNED>(rB, ob, fb[h]);
             }
             const uint32_t osa = blk < nblk ? (uint32_t)(ra * q.ldsfa + blk) : kOOB;
             const uint32_t osb = blk < nblk ? (uint32_t)(rb * q.ldsfb + blk) : kOOB;
@@ -173,6 +224,8 @@ __global__ void __launch_bounds__(256) gemm_mx_any_kernel(MxArgs q) {
 
 // Launch over ceil(M / 64) x ceil(N / 64) workgroups of 256 threads; fmt as
 // FMT above, aligned: every operand row starts at a multiple of 4 bytes.
-hipError_t launch_mx_any(int fmt, bool out_bf16, bool aligned, unsigned grid, hipStream_t s, const MxArgs &q);
+// amn / bmn: A / B stored MN-contiguous (then `aligned` is ignored).
+hipError_t launch_mx_any(int fmt, bool out_bf16, bool aligned, bool amn, bool bmn, unsigned grid, hipStream_t s,
+                         const MxArgs &q);
 
 }  // namespace tg

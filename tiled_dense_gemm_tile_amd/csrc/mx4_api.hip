@@ -67,13 +67,15 @@ gemm_status dispatch_mx4(const Common &a, const void *SFA, int64_t ldsfa, const 
 // Checks of a gemm_mxfp4 call beyond the shared ones (A and B extents in
 // bytes: half the element counts; for even K, lda / 2 < K / 2 exactly when
 // lda < K, and odd K is unsupported).
+// amn / bmn: A / B stored MN-contiguous (leading dimension at least M / N).
 gemm_status validate_mx4(const Common &a, const void *SFA, int64_t ldsfa, const void *SFB, int64_t ldsfb,
-                         bool *none) {
+                         bool *none, bool amn = false, bool bmn = false) {
     Common bytes = a;
     bytes.K = a.K / 2;
     bytes.lda = a.lda / 2;
     bytes.ldb = a.ldb / 2;
-    gemm_status st = validate(bytes, none);
+    // (for even lda: lda / 2 >= ceil(M / 2) exactly when lda >= M)
+    gemm_status st = validate(bytes, none, amn ? (a.M + 1) / 2 : -1, bmn ? (a.N + 1) / 2 : -1);
     if (st != GEMM_OK || *none) return st;
     if (a.K >= kMaxDim || a.K % 32 != 0 || a.lda % 2 != 0 || a.ldb % 2 != 0) return GEMM_ERR_UNSUPPORTED;
     if (a.K > 0) {
@@ -127,6 +129,24 @@ gemm_status gemm_mxfp4(int64_t M, int64_t N, int64_t K, const void *A, int64_t l
     gemm_status st = validate_mx4(a, SFA, ldsfa, SFB, ldsfb, &none);
     if (st != GEMM_OK || none) return st;
     return dispatch_mx4(a, SFA, ldsfa, SFB, ldsfb, stream);
+}
+
+gemm_status gemm_mxfp4_ex(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int a_order,
+                          const void *SFA, int64_t ldsfa, const void *B, int64_t ldb, int b_order, const void *SFB,
+                          int64_t ldsfb, const void *C, int64_t ldc, void *D, int64_t ldd, int out_type,
+                          hipStream_t stream) {
+    if ((a_order != GEMM_K_CONTIGUOUS && a_order != GEMM_MN_CONTIGUOUS) ||
+        (b_order != GEMM_K_CONTIGUOUS && b_order != GEMM_MN_CONTIGUOUS))
+        return GEMM_ERR_UNSUPPORTED;
+    const bool amn = a_order == GEMM_MN_CONTIGUOUS, bmn = b_order == GEMM_MN_CONTIGUOUS;
+    if (!amn && !bmn)
+        return gemm_mxfp4(M, N, K, A, lda, SFA, ldsfa, B, ldb, SFB, ldsfb, C, ldc, D, ldd, out_type, stream);
+    Common a{M, N, K, A, lda, B, ldb, C, ldc, D, ldd, out_type, 1};
+    bool none = false;
+    gemm_status st = validate_mx4(a, SFA, ldsfa, SFB, ldsfb, &none, amn, bmn);
+    if (st != GEMM_OK || none) return st;
+    if (K == 0) return dispatch_mx4(a, SFA, ldsfa, SFB, ldsfb, stream);
+    return run_mx_any(a, 4, lda / 2, ldb / 2, SFA, ldsfa, SFB, ldsfb, stream, amn, bmn);
 }
 
 gemm_status gemm_mxfp4_splitk(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *SFA,

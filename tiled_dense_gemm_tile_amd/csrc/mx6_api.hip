@@ -69,15 +69,17 @@ gemm_status dispatch_mx6(const Common &a, bool e3m2, const void *SFA, int64_t ld
 // bytes: three quarters of the element counts; for K and lda multiples of 4,
 // lda < K exactly when the byte counts compare so, and other K or lda are
 // unsupported).
+// amn / bmn: A / B stored MN-contiguous (leading dimension at least M / N).
 gemm_status validate_mx6(const Common &a, int format, const void *SFA, int64_t ldsfa, const void *SFB,
-                         int64_t ldsfb, bool *none) {
+                         int64_t ldsfb, bool *none, bool amn = false, bool bmn = false) {
     *none = false;
     if (format != GEMM_FP6_E2M3 && format != GEMM_FP6_E3M2) return GEMM_ERR_UNSUPPORTED;
     Common bytes = a;
     bytes.K = a.K / 4 * 3;
     bytes.lda = a.lda / 4 * 3;
     bytes.ldb = a.ldb / 4 * 3;
-    gemm_status st = validate(bytes, none);
+    // (for lda a multiple of 4: lda * 3 / 4 >= ceil(M / 4) * 3 exactly when lda >= M)
+    gemm_status st = validate(bytes, none, amn ? (a.M + 3) / 4 * 3 : -1, bmn ? (a.N + 3) / 4 * 3 : -1);
     if (st != GEMM_OK || *none) return st;
     if (a.K >= kMaxDim || a.K % 32 != 0 || a.lda % 4 != 0 || a.ldb % 4 != 0) return GEMM_ERR_UNSUPPORTED;
     if (a.K > 0) {
@@ -132,6 +134,26 @@ gemm_status gemm_mxfp6(int64_t M, int64_t N, int64_t K, const void *A, int64_t l
     gemm_status st = validate_mx6(a, format, SFA, ldsfa, SFB, ldsfb, &none);
     if (st != GEMM_OK || none) return st;
     return dispatch_mx6(a, format == GEMM_FP6_E3M2, SFA, ldsfa, SFB, ldsfb, stream);
+}
+
+gemm_status gemm_mxfp6_ex(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int a_order,
+                          const void *SFA, int64_t ldsfa, const void *B, int64_t ldb, int b_order, const void *SFB,
+                          int64_t ldsfb, const void *C, int64_t ldc, void *D, int64_t ldd, int format,
+                          int out_type, hipStream_t stream) {
+    if ((a_order != GEMM_K_CONTIGUOUS && a_order != GEMM_MN_CONTIGUOUS) ||
+        (b_order != GEMM_K_CONTIGUOUS && b_order != GEMM_MN_CONTIGUOUS))
+        return GEMM_ERR_UNSUPPORTED;
+    const bool amn = a_order == GEMM_MN_CONTIGUOUS, bmn = b_order == GEMM_MN_CONTIGUOUS;
+    if (!amn && !bmn)
+        return gemm_mxfp6(M, N, K, A, lda, SFA, ldsfa, B, ldb, SFB, ldsfb, C, ldc, D, ldd, format, out_type,
+                          stream);
+    Common a{M, N, K, A, lda, B, ldb, C, ldc, D, ldd, out_type, 1};
+    bool none = false;
+    gemm_status st = validate_mx6(a, format, SFA, ldsfa, SFB, ldsfb, &none, amn, bmn);
+    if (st != GEMM_OK || none) return st;
+    const bool e3m2 = format == GEMM_FP6_E3M2;
+    if (K == 0) return dispatch_mx6(a, e3m2, SFA, ldsfa, SFB, ldsfb, stream);
+    return run_mx_any(a, e3m2 ? 3 : 2, lda / 4 * 3, ldb / 4 * 3, SFA, ldsfa, SFB, ldsfb, stream, amn, bmn);
 }
 
 gemm_status gemm_mxfp6_splitk(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *SFA,

@@ -8,9 +8,11 @@
 namespace tg_api {
 
 // fmt: 0 e4m3, 2 e2m3, 3 e3m2, 4 e2m1; lda_b / ldb_b: leading dimensions in
-// bytes.  The call has been validated (K % 32 == 0, whole-byte rows).
+// bytes; amn / bmn: A / B stored MN-contiguous.  The call has been validated
+// (K % 32 == 0, whole-byte rows).
 inline gemm_status run_mx_any(const Common &a, int fmt, int64_t lda_b, int64_t ldb_b, const void *SFA,
-                              int64_t ldsfa, const void *SFB, int64_t ldsfb, hipStream_t s) {
+                              int64_t ldsfa, const void *SFB, int64_t ldsfb, hipStream_t s, bool amn = false,
+                              bool bmn = false) {
     tg::MxArgs q;
     q.g.A = a.A ? a.A : a.D;                            // K == 0 reads nothing
     q.g.B = a.B ? a.B : a.D;
@@ -33,7 +35,7 @@ inline gemm_status run_mx_any(const Common &a, int fmt, int64_t lda_b, int64_t l
     const int64_t grid = (int64_t)q.g.tiles_m * q.g.tiles_n;
     if (grid >= kMaxDim) return GEMM_ERR_UNSUPPORTED;
     const bool aligned = (uintptr_t)q.g.A % 4 == 0 && (uintptr_t)q.g.B % 4 == 0 && lda_b % 4 == 0 && ldb_b % 4 == 0;
-    return launched(tg::launch_mx_any(fmt, a.out_type == GEMM_OUT_BF16, aligned, (unsigned)grid, s, q));
+    return launched(tg::launch_mx_any(fmt, a.out_type == GEMM_OUT_BF16, aligned, amn, bmn, (unsigned)grid, s, q));
 }
 
 }  // namespace tg_api

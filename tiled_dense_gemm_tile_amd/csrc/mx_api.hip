@@ -72,9 +72,10 @@ gemm_status dispatch_mx(const Common &a, const void *SFA, int64_t ldsfa, const v
 }
 
 // Checks of a gemm_mxfp8 call beyond the shared ones.
+// lda_min / ldb_min: as validate (MN-contiguous operands: M, N).
 gemm_status validate_mx8(const Common &a, const void *SFA, int64_t ldsfa, const void *SFB, int64_t ldsfb,
-                         bool *none) {
-    gemm_status st = validate(a, none);
+                         bool *none, int64_t lda_min = -1, int64_t ldb_min = -1) {
+    gemm_status st = validate(a, none, lda_min, ldb_min);
     if (st != GEMM_OK || *none) return st;
     if (a.K > 0) {
         if (ldsfa < a.K / 32 || ldsfb < a.K / 32) return GEMM_ERR_BAD_LD;
@@ -145,6 +146,24 @@ gemm_status gemm_mxfp8(int64_t M, int64_t N, int64_t K, const void *A, int64_t l
     gemm_status st = validate_mx8(a, SFA, ldsfa, SFB, ldsfb, &none);
     if (st != GEMM_OK || none) return st;
     return dispatch_mx(a, SFA, ldsfa, SFB, ldsfb, stream);
+}
+
+gemm_status gemm_mxfp8_ex(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int a_order,
+                          const void *SFA, int64_t ldsfa, const void *B, int64_t ldb, int b_order, const void *SFB,
+                          int64_t ldsfb, const void *C, int64_t ldc, void *D, int64_t ldd, int out_type,
+                          hipStream_t stream) {
+    if ((a_order != GEMM_K_CONTIGUOUS && a_order != GEMM_MN_CONTIGUOUS) ||
+        (b_order != GEMM_K_CONTIGUOUS && b_order != GEMM_MN_CONTIGUOUS))
+        return GEMM_ERR_UNSUPPORTED;
+    const bool amn = a_order == GEMM_MN_CONTIGUOUS, bmn = b_order == GEMM_MN_CONTIGUOUS;
+    if (!amn && !bmn)
+        return gemm_mxfp8(M, N, K, A, lda, SFA, ldsfa, B, ldb, SFB, ldsfb, C, ldc, D, ldd, out_type, stream);
+    Common a{M, N, K, A, lda, B, ldb, C, ldc, D, ldd, out_type, 1};
+    bool none = false;
+    gemm_status st = validate_mx8(a, SFA, ldsfa, SFB, ldsfb, &none, amn ? M : -1, bmn ? N : -1);
+    if (st != GEMM_OK || none) return st;
+    if (K == 0) return dispatch_mx(a, SFA, ldsfa, SFB, ldsfb, stream);
+    return run_mx_any(a, 0, lda, ldb, SFA, ldsfa, SFB, ldsfb, stream, amn, bmn);
 }
 
 gemm_status gemm_mxfp8_splitk(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *SFA,

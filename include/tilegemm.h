@@ -212,7 +212,7 @@ gemm_status gemm_mxfp4(int64_t M, int64_t N, int64_t K,
  * Sizes, lda and ldb count ELEMENTS (three bytes per four).  K must be a
  * multiple of 32 and lda, ldb multiples of 4 (else GEMM_ERR_UNSUPPORTED);
  * rows and scale rows may start at any byte.  The tiled kernel takes
- * K % 512 == 0, A and B 16-byte aligned, lda and ldb multiples of 64 (rows of
+ * K % 128 == 0, A and B 16-byte aligned, lda and ldb multiples of 64 (rows of
  * a multiple of 48 bytes), SFA and SFB 16-byte aligned and ldsfa, ldsfb
  * multiples of 16; other calls run a slower general kernel.  Byte limits of
  * the shared convention apply to 3*lda/4 and 3*ldb/4.  Scale code 0xFF

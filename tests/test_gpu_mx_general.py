@@ -140,3 +140,46 @@ def test_same_as_tiled_kernel_on_integers():
         g = _run(t, x, C, soffset=1, spad=1)
         f = _run(t, x, C)
         assert torch.equal(g, f), t
+
+
+# K off the 512 step with operand rows 16-byte multiples and scale rows
+# padded to 16 bytes with NaN codes (0xFF) past each row's last block, which
+# no kernel may apply: fp6 with K % 128 == 0 and fp8 with K % 128 == 0 run
+# tiled kernels (fp6 the four-wave one, clearing the last scale group's
+# bytes past K), the other K the general kernel
+TAIL_K = {"e4m3": [32, 160, 640, 1056, 4128], "e2m1": [32, 96, 544, 1056, 4128],
+          "e2m3": [128, 640, 1152], "e3m2": [128, 640, 1152]}
+
+
+@pytest.mark.parametrize("t", TYPES)
+def test_k_tails_with_padded_scales(t):
+    for K in TAIL_K[t]:
+        for M, N in ((300, 264), (64, 64)):
+            for integer in (True, False):
+                x, C = _case(t, M, N, K, seed=K + M + len(t), integer=integer)
+                spad = (-(K // 32)) % 16
+                say("mx tiled tail %s %dx%dx%d integer=%s" % (t, M, N, K, integer))
+                D = _run(t, x, C, spad=spad)
+                _check(t, x, to_f64(D), integer, C)
+
+
+@pytest.mark.parametrize("t", ["e4m3", "e2m1", "e2m3"])
+def test_k_tail_split(t):
+    """Split-K with K off the 512 step: fp6 splits on the four-wave kernel
+    (the last range holds the partial scale group), fp8 and fp4 run unsplit."""
+    M, N, K = 256, 192, 4224
+    x, C = _case(t, M, N, K, seed=3, integer=True)
+    spad = (-(K // 32)) % 16
+    A, _a = _dev(x["A"], 0, 0)
+    B, _b = _dev(x["B"], 0, 0)
+    SFA, _sa = _dev(x["SFA"], spad, 0)
+    SFB, _sb = _dev(x["SFB"], spad, 0)
+    Cd = torch.from_numpy(C).to(DEV)
+    if t == "e4m3":
+        D = tg.gemm_mxfp8_splitk(A, SFA, B, SFB, Cd, splits=5)
+    elif t == "e2m1":
+        D = tg.gemm_mxfp4_splitk(A, SFA, B, SFB, Cd, splits=5)
+    else:
+        D = tg.gemm_mxfp6_splitk(A, SFA, B, SFB, Cd, splits=5, fmt=t)
+    torch.cuda.synchronize()
+    _check(t, x, to_f64(D), True, C)

@@ -90,17 +90,19 @@ __global__ void __launch_bounds__(256) gemm_mx6_w4_kernel(MxArgs q, F16Epi e) {
     int m0, n0, split, k_lo, K;
     mx_work_item<SPLIT>(p, m0, n0, split, k_lo, K);
     const int M = p.M, N = p.N;
-    const int kb = K / 4 * 3, nblk = K / 32;
-    const int nk = K / 128, nep = K / 512;
+    // K % 128 == 0: whole K tiles; the loop runs whole groups of four, reading
+    // zeros past nk
+    const int kb = K / 4 * 3, nblk = K / 32, rem = nblk % 16;
+    const int nk = K / 128, nep = (K + 511) / 512;
 
     const __amdgpu_buffer_rsrc_t rA =
         make_rsrc((const char *)p.A + (int64_t)m0 * p.lda + k_lo / 4 * 3, span_bytes(M - m0, kb, p.lda, 1));
     const __amdgpu_buffer_rsrc_t rB =
         make_rsrc((const char *)p.B + (int64_t)n0 * p.ldb + k_lo / 4 * 3, span_bytes(N - n0, kb, p.ldb, 1));
     const __amdgpu_buffer_rsrc_t rSA =
-        make_rsrc((const char *)q.SFA + (int64_t)m0 * q.ldsfa + k_lo / 32, span_bytes(M - m0, nblk, q.ldsfa, 1));
+        make_rsrc((const char *)q.SFA + (int64_t)m0 * q.ldsfa + k_lo / 32, scale_span(M - m0, nblk, q.ldsfa));
     const __amdgpu_buffer_rsrc_t rSB =
-        make_rsrc((const char *)q.SFB + (int64_t)n0 * q.ldsfb + k_lo / 32, span_bytes(N - n0, nblk, q.ldsfb, 1));
+        make_rsrc((const char *)q.SFB + (int64_t)n0 * q.ldsfb + k_lo / 32, scale_span(N - n0, nblk, q.ldsfb));
     const __amdgpu_buffer_rsrc_t rZ = make_rsrc(p.A, 0u);
 
     // Operand loads: chunk position c = (4 j + wave) * 64 + lane of a slot
@@ -248,6 +250,11 @@ __global__ void __launch_bounds__(256) gemm_mx6_w4_kernel(MxArgs q, F16Epi e) {
         });
         wait_vmcnt<2 * LPW>();
         wait_lgkmcnt0();
+        if constexpr (U == 2) {
+            if (rem != 0 && (t >> 2) + 1 == nep - 1)
+                mx_scale_tail_fixup(smem, SA_BASE + ((nep - 1) & 1) * SS + wave * IB,
+                                    SB_BASE + ((nep - 1) & 1) * SS + wave * IB, lane_id(), rem);
+        }
         barrier();
     };
 
@@ -260,9 +267,11 @@ __global__ void __launch_bounds__(256) gemm_mx6_w4_kernel(MxArgs q, F16Epi e) {
 #pragma unroll
         for (int k = 0; k < 2 * LPW; ++k) fetch(1, k, 1);
         wait_vmcnt<2 * LPW>();
+        if (rem != 0 && nep == 1) mx_scale_tail_fixup(smem, SA_BASE + wave * IB, SB_BASE + wave * IB, lane_id(), rem);
         barrier();
         window(std::true_type(), std::integral_constant<int, 0>(), 0, 0);
-        // windows 1 .. nk (nk a multiple of 4): tiles 0 .. nk - 1 computed
+        // windows 1 .. (nk rounded up to a multiple of 4): tiles 0 .. nk - 1
+        // computed, then zero tiles
         int rs = 1;
         auto next = [](int r) { return r == NS - 1 ? 0 : r + 1; };
         for (int t = 1; t <= nk; t += 4) {

@@ -54,6 +54,34 @@ __device__ __forceinline__ void static_for(F &&f) {
     }
 }
 
+// Extent of a tile's scale resource: through the 16-byte word (a scale
+// load's unit) holding the last row's last block.  Range checks are per
+// dword and a dword partly past the end reads as zero, so an extent ending
+// inside the word would lose the last row's final scales when a row's
+// block count is not a multiple of 16.  The tile base is 16-byte aligned,
+// so the word never reaches past the 16-byte block -- and the page --
+// holding that block.
+__device__ __forceinline__ uint32_t scale_span(int rows_left, int nblk, int64_t ld) {
+    return (span_bytes(rows_left, nblk, ld, 1) + 15u) & ~15u;
+}
+
+// K tails (K not a multiple of 512): the last scale group's 16-byte word per
+// row holds bytes past the row's last block (padding, or a later row's
+// scales) which must not be applied: the data of those blocks is zero, but
+// a NaN scale code times zero is NaN.  Lane l of wave w holds row 64 w + l's
+// word of each operand (where the scale loads put it); its bytes rem .. 15
+// (rem: valid blocks, 1 .. 15) are cleared.  Called after the group's loads
+// have landed, before the barrier that publishes them; byte stores, so that
+// it needs no registers beyond an address where the fragments are live.
+__device__ __forceinline__ void mx_scale_tail_fixup(char *smem, int sa_off, int sb_off, int lane, int rem) {
+    char *wa = smem + sa_off + lane * 16, *wb = smem + sb_off + lane * 16;
+    for (int b = rem; b < 16; ++b) {
+        wa[b] = 0;
+        wb[b] = 0;
+    }
+    wait_lgkmcnt0();
+}
+
 // Work item of a four-wave block-scaled workgroup: its 256 x 256 output
 // tile and, with SPLIT (split-K), its K range [k_lo, k_lo + K) -- split s of
 // ranges of p.kt_split scale epochs (512 K each), the last one shorter.

@@ -12,9 +12,9 @@ using namespace tg_api;
 namespace {
 
 // 16-byte A/B rows (lda multiple of 64 elements), 16-byte scale words (512
-// K) per row
+// K) per row, whole 128-wide K tiles (scale bytes past K cleared)
 bool fast_mx6(const Common &a, const void *SFA, int64_t ldsfa, const void *SFB, int64_t ldsfb) {
-    return a.K % 512 == 0 && (uintptr_t)a.A % 16 == 0 && (uintptr_t)a.B % 16 == 0 && a.lda % 64 == 0 &&
+    return a.K % 128 == 0 && (uintptr_t)a.A % 16 == 0 && (uintptr_t)a.B % 16 == 0 && a.lda % 64 == 0 &&
            a.ldb % 64 == 0 && (uintptr_t)SFA % 16 == 0 && (uintptr_t)SFB % 16 == 0 && ldsfa % 16 == 0 &&
            ldsfb % 16 == 0;
 }
@@ -108,7 +108,7 @@ gemm_status run_mx6_splitk(const Common &a, int format, const void *SFA, int64_t
     q.g.D = nullptr;
     q.g.ldc = 0;
     q.g.ldd = 0;
-    const int64_t epochs = a.K / 512;
+    const int64_t epochs = (a.K + 511) / 512;           // the last may be partial
     q.g.kt_split = (int)((epochs + S - 1) / S);
     q.g.ws = (float *)ws;
     q.g.ldw = splitk_ldw(a.N);

@@ -64,15 +64,32 @@ __device__ __forceinline__ void mx_any_mfma(f32x4 &acc, const uint32_t (&a)[MxAn
     }
 }
 
-// N consecutive dwords at byte offset `off` of resource r: dword loads when
-// ALIGNED (the offset is a multiple of 4), else each dword from four byte
-// loads.  off == kOOB reads zeros.
-template <int N, bool ALIGNED>
+// N consecutive dwords at byte offset `off` of resource r, with loads of
+// VEC bytes (16, 8 or 4: the offset is a multiple of VEC; 1: each dword
+// from four byte loads).  off == kOOB reads zeros.
+template <int N, int VEC>
 __device__ __forceinline__ void mx_any_load(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t *dst) {
+    if constexpr (VEC == 16 && N % 4 == 0) {
+#pragma unroll
+        for (int d = 0; d < N; d += 4) {
+            const u32x4 v = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off == kOOB ? kOOB : off + 4 * d, 0, 0));
+            dst[d] = v[0], dst[d + 1] = v[1], dst[d + 2] = v[2], dst[d + 3] = v[3];
+        }
+        return;
+    } else if constexpr (VEC >= 8 && N % 2 == 0) {
+#pragma unroll
+        for (int d = 0; d < N; d += 2) {
+            const u32x2 v = __builtin_bit_cast(
+                u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off == kOOB ? kOOB : off + 4 * d, 0, 0));
+            dst[d] = v[0], dst[d + 1] = v[1];
+        }
+        return;
+    }
 #pragma unroll
     for (int d = 0; d < N; ++d) {
         const uint32_t o = off == kOOB ? kOOB : off + 4 * d;
-        if constexpr (ALIGNED) {
+        if constexpr (VEC >= 4) {
             dst[d] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, o, 0, 0);
         } else {
             uint32_t v = 0;
@@ -121,9 +138,12 @@ __device__ __forceinline__ void mx_any_gather(const char *X, int64_t ld_b, int r
 }
 
 // q.g.lda / q.g.ldb in BYTES; q.g.K in elements (a multiple of 32).
-template <int FMT, bool OUT_BF16, bool ALIGNED, bool AMN = false, bool BMN = false>
+// VEC: the widest load (16, 8, 4 or 1 bytes) every K-contiguous operand
+// row allows; fp6 lanes' 24-byte blocks start at multiples of 8 only.
+template <int FMT, bool OUT_BF16, int VEC, bool AMN = false, bool BMN = false>
 __global__ void __launch_bounds__(256) gemm_mx_any_kernel(MxArgs q) {
     constexpr int R = MxAnyFmt<FMT>::kRegs;
+    constexpr int V = (FMT == 2 || FMT == 3) && VEC > 8 ? 8 : VEC;
     const F16Args &p = q.g;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave >> 1, wn = wave & 1;
@@ -149,9 +169,18 @@ __global__ void __launch_bounds__(256) gemm_mx_any_kernel(MxArgs q) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    for (int k0 = 0; k0 < K; k0 += 128) {
-        const int blk = k0 / 32 + fq;                  // the K block whose scale this lane supplies
+    // One K step's operands and scales; the loop is software-pipelined over
+    // two register sets, so step k + 1's loads are in flight while step k's
+    // MFMAs run.
+    struct Step {
         uint32_t fa[2][R], fb[2][R], sa[2], sb[2];
+    };
+    auto load_step = [&](int k0, Step &st) __attribute__((always_inline)) {
+        const int blk = k0 / 32 + fq;                  // the K block whose scale this lane supplies
+        uint32_t(&fa)[2][R] = st.fa;
+        uint32_t(&fb)[2][R] = st.fb;
+        uint32_t(&sa)[2] = st.sa;
+        uint32_t(&sb)[2] = st.sb;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int ra = 32 * wm + 16 * h + fr, rb = 32 * wn + 16 * h + fr;   // rows within the tile
@@ -169,30 +198,41 @@ __global__ void __launch_bounds__(256) gemm_mx_any_kernel(MxArgs q) {
                 const uint32_t ob0 = e0 < K ? (uint32_t)(rb * p.ldb + e0) : kOOB;
                 const uint32_t ob1 = e1 < K ? (uint32_t)(rb * p.ldb + e1) : kOOB;
                 if constexpr (!AMN) {
-                    mx_any_load<4, ALIGNED>(rA, oa0, fa[h]);
-                    mx_any_load<4, ALIGNED>(rA, oa1, fa[h] + 4);
+                    mx_any_load<4, V>(rA, oa0, fa[h]);
+                    mx_any_load<4, V>(rA, oa1, fa[h] + 4);
                 }
                 if constexpr (!BMN) {
-                    mx_any_load<4, ALIGNED>(rB, ob0, fb[h]);
-                    mx_any_load<4, ALIGNED>(rB, ob1, fb[h] + 4);
+                    mx_any_load<4, V>(rB, ob0, fb[h]);
+                    mx_any_load<4, V>(rB, ob1, fb[h] + 4);
                 }
             } else {
                 // block blk: 16 bytes (fp4) or 24 bytes (fp6)
                 const int bb = FMT == 4 ? 16 : 24;
                 const uint32_t oa = blk < nblk ? (uint32_t)(ra * p.lda + blk * bb) : kOOB;
                 const uint32_t ob = blk < nblk ? (uint32_t)(rb * p.ldb + blk * bb) : kOOB;
-                if constexpr (!AMN) mx_any_load<R, ALIGNED>(rA, oa, fa[h]);
-                if constexpr (!BMN) mx_any_load<R, ALIGNED>(rB, ob, fb[h]);
+                if constexpr (!AMN) mx_any_load<R, V>(rA, oa, fa[h]);
+                if constexpr (!BMN) mx_any_load<R, V>(rB, ob, fb[h]);
             }
             const uint32_t osa = blk < nblk ? (uint32_t)(ra * q.ldsfa + blk) : kOOB;
             const uint32_t osb = blk < nblk ? (uint32_t)(rb * q.ldsfb + blk) : kOOB;
             sa[h] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rSA, osa, 0, 0);
             sb[h] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rSB, osb, 0, 0);
         }
+    };
+    auto mfma_step = [&](const Step &st) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j) mx_any_mfma<FMT>(acc[i][j], fa[i], fb[j], sa[i], sb[j]);
+            for (int j = 0; j < 2; ++j) mx_any_mfma<FMT>(acc[i][j], st.fa[i], st.fb[j], st.sa[i], st.sb[j]);
+    };
+    Step s0, s1;
+    if (K > 0) load_step(0, s0);
+    for (int k0 = 0; k0 < K; k0 += 256) {
+        if (k0 + 128 < K) load_step(k0 + 128, s1);
+        mfma_step(s0);
+        if (k0 + 128 >= K) break;
+        if (k0 + 256 < K) load_step(k0 + 256, s0);
+        mfma_step(s1);
     }
     // the MFMA results before any other instruction reads them
     asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 3"
@@ -224,8 +264,9 @@ __global__ void __launch_bounds__(256) gemm_mx_any_kernel(MxArgs q) {
 
 // Launch over ceil(M / 64) x ceil(N / 64) workgroups of 256 threads; fmt as
 // FMT above, aligned: every operand row starts at a multiple of 4 bytes.
-// amn / bmn: A / B stored MN-contiguous (then `aligned` is ignored).
-hipError_t launch_mx_any(int fmt, bool out_bf16, bool aligned, bool amn, bool bmn, unsigned grid, hipStream_t s,
+// vec: the widest load the K-contiguous operand rows allow (16, 8, 4, 1
+// bytes); amn / bmn: A / B stored MN-contiguous (then vec is ignored).
+hipError_t launch_mx_any(int fmt, bool out_bf16, int vec, bool amn, bool bmn, unsigned grid, hipStream_t s,
                          const MxArgs &q);
 
 }  // namespace tg

@@ -95,8 +95,11 @@ def _check(t, a, b, SFA, SFB, C, Dg, integer):
 
 
 ORDERS = [(True, False), (False, True), (True, True)]
-# M and N multiples of 4 (the binding's byte views of fp4 / fp6 storage rows)
-SHAPES = [(64, 64, 128), (100, 36, 96), (132, 68, 544), (4, 4, 32), (256, 192, 1024)]
+# M and N multiples of 4 (the binding's byte views of fp4 / fp6 storage rows);
+# fp8 storage rows that are 16-byte multiples (M, N % 16 == 0) take the
+# staged transposing-read path, the others byte gathers
+SHAPES = [(64, 64, 128), (100, 36, 96), (132, 68, 544), (4, 4, 32), (256, 192, 1024), (96, 80, 160),
+          (48, 112, 2080)]
 
 
 @pytest.mark.parametrize("t", TYPES)

@@ -23,6 +23,16 @@
 // (byte loads at the element's bit offset from a resource over the K
 // step's rows) and packs them into its operand registers; elements past K
 // or past M (N) are zero.
+//
+// STAGE (fp8 with a 16-byte-aligned MN-contiguous operand): instead, each K
+// step's 128 x 64-byte panel of that operand is loaded by the workgroup with
+// 16-byte loads, written to LDS (64-byte rows, one per K row) and read back
+// with ds_read_b64_tr_b8, which (probed) gives output lane i of each
+// 16-lane group byte i % 8 of the 8-byte reads of lanes 2b + i / 8, b = 0..7:
+// when lane s of the group reads K row k + s / 2 at columns 8 (s % 2) .. + 7,
+// lane i receives K values k .. k + 7 of column i, in order.  Four such reads
+// (K rows 16 q, 16 q + 8, 64 + 16 q, 64 + 16 q + 8) make the lane's 32-byte
+// operand in the K-contiguous layout.
 #pragma once
 
 #include "common.hpp"
@@ -137,12 +147,53 @@ __device__ __forceinline__ void mx_any_gather(const char *X, int64_t ld_b, int r
     }
 }
 
+// One K step's 128 x 64-byte panel of an MN-contiguous fp8 operand (storage
+// X: K rows of ld_b bytes; columns col0 .. col0 + 63 of `rows`): two 16-byte
+// chunks per thread, chunk c = t and t + 256 at panel row c / 4, bytes
+// 16 (c % 4) ..  Rows past K read zeros; columns past `rows` feed outputs
+// that are not stored.
+__device__ __forceinline__ void mx_any_panel_load(const char *X, int64_t ld_b, int rows, int K, int k0, int col0,
+                                                  u32x4 (&dst)[2]) {
+    const int nk = K - k0 < 128 ? K - k0 : 128;
+    const int64_t cols = rows - col0 < 64 ? rows - col0 : 64;
+    // through the 16-byte chunk holding the last row's last column (the base
+    // is 16-byte aligned, so the chunk stays in its page)
+    const uint32_t span = (uint32_t)(((int64_t)(nk - 1) * ld_b + cols + 15) & ~(int64_t)15);
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(X + (int64_t)k0 * ld_b + col0, span);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int c = (int)threadIdx.x + 256 * h;
+        const uint32_t off = (uint32_t)((c >> 2) * ld_b) + (c & 3) * 16;
+        dst[h] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    }
+}
+
+// The lane's fp8 operand for block h of its wave from a staged panel (LDS
+// byte address `panel`, 64-byte rows): four transposing reads and their
+// wait in one statement, so no register is used before it has landed.
+__device__ __forceinline__ void mx_any_panel_frag(uint32_t panel, int col, int fr, int fq, uint32_t (&dst)[8]) {
+    const uint32_t a = panel + (uint32_t)((16 * fq + (fr >> 1)) * 64 + col + 8 * (fr & 1));
+    u32x2 x0, x1, x2, x3;
+    asm volatile("ds_read_b64_tr_b8 %0, %4\n\t"
+                 "ds_read_b64_tr_b8 %1, %4 offset:512\n\t"
+                 "ds_read_b64_tr_b8 %2, %4 offset:4096\n\t"
+                 "ds_read_b64_tr_b8 %3, %4 offset:4608\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(x0), "=&v"(x1), "=&v"(x2), "=&v"(x3)
+                 : "v"(a)
+                 : "memory");
+    dst[0] = x0[0], dst[1] = x0[1], dst[2] = x1[0], dst[3] = x1[1];
+    dst[4] = x2[0], dst[5] = x2[1], dst[6] = x3[0], dst[7] = x3[1];
+}
+
 // q.g.lda / q.g.ldb in BYTES; q.g.K in elements (a multiple of 32).
 // VEC: the widest load (16, 8, 4 or 1 bytes) every K-contiguous operand
 // row allows; fp6 lanes' 24-byte blocks start at multiples of 8 only.
-template <int FMT, bool OUT_BF16, int VEC, bool AMN = false, bool BMN = false>
+template <int FMT, bool OUT_BF16, int VEC, bool AMN = false, bool BMN = false, bool STAGE = false>
 __global__ void __launch_bounds__(256) gemm_mx_any_kernel(MxArgs q) {
+    static_assert(!STAGE || (FMT == 0 && (AMN || BMN)), "staged panels: fp8 MN-contiguous operands");
     constexpr int R = MxAnyFmt<FMT>::kRegs;
+    __shared__ __attribute__((aligned(16))) char panel[STAGE ? 2 * 128 * 64 : 16];
     constexpr int V = (FMT == 2 || FMT == 3) && VEC > 8 ? 8 : VEC;
     const F16Args &p = q.g;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -174,6 +225,7 @@ __global__ void __launch_bounds__(256) gemm_mx_any_kernel(MxArgs q) {
     // MFMAs run.
     struct Step {
         uint32_t fa[2][R], fb[2][R], sa[2], sb[2];
+        u32x4 pa[2], pb[2];                            // staged panel chunks (STAGE)
     };
     auto load_step = [&](int k0, Step &st) __attribute__((always_inline)) {
         const int blk = k0 / 32 + fq;                  // the K block whose scale this lane supplies
@@ -184,7 +236,7 @@ __global__ void __launch_bounds__(256) gemm_mx_any_kernel(MxArgs q) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int ra = 32 * wm + 16 * h + fr, rb = 32 * wn + 16 * h + fr;   // rows within the tile
-            if constexpr (AMN || BMN) {
+            if constexpr ((AMN || BMN) && !STAGE) {
                 if constexpr (AMN)
                     mx_any_gather<FMT>((const char *)p.A, p.lda, M, K, m0 + ra, k0, fq, fa[h]);
                 if constexpr (BMN)
@@ -218,8 +270,30 @@ __global__ void __launch_bounds__(256) gemm_mx_any_kernel(MxArgs q) {
             sa[h] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rSA, osa, 0, 0);
             sb[h] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rSB, osb, 0, 0);
         }
+        if constexpr (STAGE && AMN) mx_any_panel_load((const char *)p.A, p.lda, M, K, k0, m0, st.pa);
+        if constexpr (STAGE && BMN) mx_any_panel_load((const char *)p.B, p.ldb, N, K, k0, n0, st.pb);
     };
-    auto mfma_step = [&](const Step &st) __attribute__((always_inline)) {
+    // STAGE: panels to LDS, then each lane's operands by transposing reads
+    auto unstage = [&](Step &st) __attribute__((always_inline)) {
+        if constexpr (STAGE) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int c = (int)threadIdx.x + 256 * h;
+                if constexpr (AMN) *(u32x4 *)(panel + c * 16) = st.pa[h];
+                if constexpr (BMN) *(u32x4 *)(panel + 8192 + c * 16) = st.pb[h];
+            }
+            __syncthreads();
+            const uint32_t base = (uint32_t)(uintptr_t)panel;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                if constexpr (AMN) mx_any_panel_frag(base, 32 * wm + 16 * h, fr, fq, st.fa[h]);
+                if constexpr (BMN) mx_any_panel_frag(base + 8192, 32 * wn + 16 * h, fr, fq, st.fb[h]);
+            }
+            __syncthreads();                           // every read done before the next step's writes
+        }
+    };
+    auto mfma_step = [&](Step &st) __attribute__((always_inline)) {
+        unstage(st);
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -265,8 +339,9 @@ __global__ void __launch_bounds__(256) gemm_mx_any_kernel(MxArgs q) {
 // Launch over ceil(M / 64) x ceil(N / 64) workgroups of 256 threads; fmt as
 // FMT above, aligned: every operand row starts at a multiple of 4 bytes.
 // vec: the widest load the K-contiguous operand rows allow (16, 8, 4, 1
-// bytes); amn / bmn: A / B stored MN-contiguous (then vec is ignored).
-hipError_t launch_mx_any(int fmt, bool out_bf16, int vec, bool amn, bool bmn, unsigned grid, hipStream_t s,
-                         const MxArgs &q);
+// bytes); amn / bmn: A / B stored MN-contiguous (then vec only matters with
+// stage, as 16 or not); stage: fp8 MN-contiguous operands 16-byte aligned.
+hipError_t launch_mx_any(int fmt, bool out_bf16, int vec, bool amn, bool bmn, bool stage, unsigned grid,
+                         hipStream_t s, const MxArgs &q);
 
 }  // namespace tg

@@ -35,9 +35,13 @@ inline gemm_status run_mx_any(const Common &a, int fmt, int64_t lda_b, int64_t l
     const int64_t grid = (int64_t)q.g.tiles_m * q.g.tiles_n;
     if (grid >= kMaxDim) return GEMM_ERR_UNSUPPORTED;
     // the widest load every K-contiguous row start allows
-    const uint64_t bits = (uint64_t)(uintptr_t)q.g.A | (uint64_t)(uintptr_t)q.g.B | (uint64_t)lda_b | (uint64_t)ldb_b;
+    const uint64_t abits = (uint64_t)(uintptr_t)q.g.A | (uint64_t)lda_b;
+    const uint64_t bbits = (uint64_t)(uintptr_t)q.g.B | (uint64_t)ldb_b;
+    const uint64_t bits = (amn ? 0 : abits) | (bmn ? 0 : bbits);
     const int vec = bits % 16 == 0 ? 16 : bits % 8 == 0 ? 8 : bits % 4 == 0 ? 4 : 1;
-    return launched(tg::launch_mx_any(fmt, a.out_type == GEMM_OUT_BF16, vec, amn, bmn, (unsigned)grid, s, q));
+    // fp8 MN-contiguous operands with 16-byte rows: staged panels
+    const bool stage = fmt == 0 && (amn || bmn) && (!amn || abits % 16 == 0) && (!bmn || bbits % 16 == 0);
+    return launched(tg::launch_mx_any(fmt, a.out_type == GEMM_OUT_BF16, vec, amn, bmn, stage, (unsigned)grid, s, q));
 }
 
 }  // namespace tg_api

@@ -315,7 +315,8 @@ gemm_status gemm_mxfp6_ex(int64_t M, int64_t N, int64_t K,
  * writing D (the same result on every call).  Source: as gemm_bf16_splitk.
  *   splits: as gemm_bf16_splitk, with at most one split per 512 K; calls
  *     the tiled kernels do not take (see gemm_mxfp8 / gemm_mxfp4 /
- *     gemm_mxfp6: K % 512 == 0, 16-byte rows and scale rows) run unsplit.
+ *     gemm_mxfp6: K % 512 == 0 -- fp6: K % 128 == 0 --, 16-byte rows and
+ *     scale rows) run unsplit.
  *   workspace: as gemm_bf16_splitk; gemm_splitk_workspace_bytes(M, N, K,
  *     splits) bytes always suffice.
  * Everything else (layouts, scales, validation, out_type, C == D) is as the

@@ -1,6 +1,7 @@
 // Block-scaled fp6 D = A.B + C with four waves and
 // v_mfma_scale_f32_16x16x128_f8f6f4 on e2m3 (FMT 2) or e3m2 (FMT 3)
-// operands, gfx950 (K a multiple of 512):
+// operands, gfx950 (K a multiple of 128; a last scale group short of 512 K
+// has its bytes past K cleared in LDS):
 //     a(m,k) = fp6(A, m, k) * 2^(SFA[m][k/32] - 127)
 //     b(k,n) = fp6(B, n, k) * 2^(SFB[n][k/32] - 127)
 // A and B hold six bits per element: element k of a row at bits 6k .. 6k+5

@@ -108,6 +108,10 @@ def main():
                     help="16-bit workloads: store A K-contiguous (M x K) or MN-contiguous (K x M), same values")
     ap.add_argument("--b-order", choices=("k", "mn"), default="k",
                     help="16-bit workloads: store B K-contiguous (N x K) or MN-contiguous (K x N), same values")
+    ap.add_argument("--cold", action="store_true",
+                    help="write a 512 MiB buffer before every timed step, so no operand is left in L2 or the "
+                         "256 MB Infinity Cache; each step is timed alone (events around the GEMM only) and "
+                         "value comes from those times, the writes excluded")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
@@ -183,20 +187,35 @@ def main():
         step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    # an event before every step and after the last, all on the launch stream
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    t0 = time.perf_counter()
-    evs[0].record(stream)
-    for i in range(args.steps):
-        step()
-        evs[i + 1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ev0, ev1 = evs[0], evs[-1]
-    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
-    # one GEMM launch per step (split-K: the GEMM and the reduction of its partials)
-    kernel_ms = ev0.elapsed_time(ev1) / args.steps
-    ms_per_step = wall * 1e3 / args.steps
+    if args.cold:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda:0")
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        for i in range(args.steps):
+            flush.fill_(i & 255)
+            starts[i].record(stream)
+            step()
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+        times = [starts[i].elapsed_time(ends[i]) for i in range(args.steps)]
+        per_step = sorted(times)
+        kernel_ms = sum(times) / args.steps
+        ms_per_step = kernel_ms                        # the flushes are not part of the step
+    else:
+        # an event before every step and after the last, all on the launch stream
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        t0 = time.perf_counter()
+        evs[0].record(stream)
+        for i in range(args.steps):
+            step()
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ev0, ev1 = evs[0], evs[-1]
+        per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
+        # one GEMM launch per step (split-K: the GEMM and the reduction of its partials)
+        kernel_ms = ev0.elapsed_time(ev1) / args.steps
+        ms_per_step = wall * 1e3 / args.steps
 
     tflops = w.flops / (kernel_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.in_type]
@@ -217,6 +236,7 @@ def main():
                    "C": "fp32 U[-1,1]" if w.dist_c else "none", "layout": "A row-major, B column-major (N x K)",
                    "seed": w.seed, "note": w.note,
                    "splits": None if splits is None else (splits or "auto"),
+                   "caches": "cold (512 MiB written before each step)" if args.cold else "warm",
                    "storage": {"A": "K x M" if args.a_order == "mn" else "M x K",
                                "B": "K x N" if args.b_order == "mn" else "N x K"}},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",

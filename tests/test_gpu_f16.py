@@ -237,10 +237,11 @@ def test_ragged_fp16_every_element():
     assert rep["fail"] == 0
 
 
-def test_llm_projection_bf16_out():
-    w = inputs.WORKLOADS["llm_proj_bf16"]
+@pytest.mark.parametrize("name", ["llm_proj_bf16", "llm_proj_shard8_bf16"])
+def test_llm_projection_bf16_out(name):
+    w = inputs.WORKLOADS[name]
     x = inputs.generate(w)
-    say("llm projection 16384x14336x4096 bf16 out")
+    say("%s %dx%dx%d bf16 out" % (name, w.M, w.N, w.K))
     A, B = dev16(x["A"], "bf16"), dev16(x["B"], "bf16")
     D16 = run16("bf16", A, B, None, out="bf16")
     D32 = run16("bf16", A, B, None, out="f32")

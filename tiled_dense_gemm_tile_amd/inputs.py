@@ -73,6 +73,10 @@ WORKLOADS = {
     "llm_proj_bf16": Workload("llm_proj_bf16", 16384, 14336, 4096, "bf16", "bf16",
                               ("normal", 1.0), ("normal", 0.02), None, 3,
                               note="M=16384 N=14336 K=4096 bf16, C=0, bf16 out"),
+    "llm_proj_shard8_bf16": Workload("llm_proj_shard8_bf16", 16384, 1792, 4096, "bf16", "bf16",
+                                     ("normal", 1.0), ("normal", 0.02), None, 3,
+                                     note="one GPU's share of the projection N-sharded 8 ways: M=16384 N=1792 "
+                                          "K=4096 bf16, C=0, bf16 out"),
     "largek_bf16": Workload("largek_bf16", 1024, 1024, 65536, "bf16", "f32", U11, U11, None, 6,
                             note="M=N=1024 K=65536 bf16, C=0, fp32 out (16 output tiles: split-K)"),
     "mxfp8_8192": Workload("mxfp8_8192", 8192, 8192, 8192, "e4m3", "f32", U11, U11, None, 4,

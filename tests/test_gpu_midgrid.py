@@ -1,0 +1,53 @@
+"""Grids of 128 to 239 output tiles of 256 x 256 (part of one wave), which
+the library sends to the four-wave 256 x 256 kernels: exact on
+integer-valued inputs against the oracle at 4096 seeded samples plus the
+tile edges, and within the tolerance on random inputs."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import check
+import tiled_dense_gemm_tile_amd as tg
+from tiled_dense_gemm_tile_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from gpuutil import DEV, dev8, dev16, say, to_f64
+
+# (in_type, M, N, K): 144 tiles with ragged edges and 16-byte rows; 8-byte
+# rows (K = 516); fp8 at 132 tiles; 16-bit at exactly 128 tiles
+CASES = [("bf16", 2900, 3000, 520), ("fp16", 3000, 3000, 516), ("e4m3", 2600, 3000, 1024), ("bf16", 2048, 4096, 256)]
+
+
+@pytest.mark.parametrize("case", CASES, ids=["%s_%dx%dx%d" % c for c in CASES])
+@pytest.mark.parametrize("integer", [True, False])
+def test_partial_wave_grid(case, integer):
+    t, M, N, K = case
+    rng = np.random.default_rng(M + N + K + integer)
+    A = inputs.random_codes(rng, t, (M, K), integer=integer)
+    B = inputs.random_codes(rng, t, (N, K), integer=integer)
+    C = (rng.integers(-4, 5, size=(M, N)) if integer else rng.uniform(-1, 1, size=(M, N))).astype(np.float32)
+    Cd = torch.from_numpy(C).to(DEV)
+    say("partial-wave grid %s %dx%dx%d integer=%s" % (t, M, N, K, integer))
+    kw = {}
+    if t == "e4m3":
+        lo, hi = (0, 2) if integer else (-4, 5)
+        SFA = (127 + rng.integers(lo, hi, size=(M, K // 32))).astype(np.uint8)
+        SFB = (127 + rng.integers(lo, hi, size=(N, K // 32))).astype(np.uint8)
+        D = tg.gemm_mxfp8(dev8(A), dev8(SFA), dev8(B), dev8(SFB), Cd)
+        kw = {"SFA": SFA, "SFB": SFB}
+    else:
+        fn = tg.gemm_bf16 if t == "bf16" else tg.gemm_fp16
+        D = fn(dev16(A, t), dev16(B, t), Cd)
+    torch.cuda.synchronize()
+    rand, forced = inputs.sample_indices(M, N, M + N)
+    idx = np.concatenate([rand, forced])
+    Dg = to_f64(D).ravel()[idx]
+    Dr, S = oracle.gemm_ref(t, A, B, C=C, idx=idx, **kw)
+    if integer:
+        assert np.array_equal(Dg, Dr)
+    else:
+        rep = check.report(Dg, Dr, S)
+        assert rep["fail"] == 0, rep

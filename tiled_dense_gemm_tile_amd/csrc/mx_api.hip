@@ -34,8 +34,14 @@ gemm_status dispatch_mx(const Common &a, const void *SFA, int64_t ldsfa, const v
     int cfg = forced_mx_cfg();
     if ((cfg == tg::kMxPingPong || cfg == tg::kMxFourWave) && !scales16) cfg = -1;
     if (cfg < 0) {
-        if (tiles_of(a, 256, 256) >= 240)
-            cfg = scales16 ? tg::kMxFourWave : 1;
+        // the four-wave kernel once its 256 x 256 grid is over half a wave
+        // (measured at K = 4096: 160 tiles 46.9 against 71.3 us with
+        // 128 x 128 tiles; at 128 tiles 128 x 128 is 2 % ahead)
+        const int64_t t256 = tiles_of(a, 256, 256);
+        if (scales16 && t256 > 128)
+            cfg = tg::kMxFourWave;
+        else if (t256 >= 240)
+            cfg = 1;
         else
             cfg = tiles_of(a, 128, 128) >= 240 ? 2 : 3;
     }

@@ -38,15 +38,16 @@ int pick_f16_cfg(const Common &a, int lane_bytes, int vec) {
     if (forced >= 0 && (lane_bytes == 16 || tg::f16_any_rows(forced))) {
         if (forced != tg::kF16FourWaveS || vec >= 4) return forced;
     }
-    // 8-byte rows: the shifted-row four-wave kernel once the 256 x 256 grid
-    // fills most of the chip (a 0.75-wave grid of 256 x 256 tiles still
-    // beats three waves of 128 x 128 tiles)
-    if (vec == 4 && tiles_of(a, 256, 256) >= 160) return tg::kF16FourWaveS;
-    if (tiles_of(a, 256, 256) >= 240) {
-        if (lane_bytes != 16) return 3;
-        // four-wave kernel, 64-wide K tiles, two slots per operand, balanced schedule
-        return tg::kF16FourWaveB22;
-    }
+    // Four-wave 256 x 256 kernels once that grid covers half the chip: a
+    // grid of 128 to 255 such tiles (part of one wave) finishes in the time
+    // of a full wave, which beats the 2 to 4 waves of 128 x 128 tiles the
+    // same output takes (measured at K = 4096: 144 tiles 74.9 against
+    // 102.7 us, 224 tiles 92.3 against 139.5 us; equal at 128 tiles and
+    // slower below).
+    const int64_t t256 = tiles_of(a, 256, 256);
+    if (vec == 4 && t256 >= 128) return tg::kF16FourWaveS;         // 8-byte rows: shifted-row variant
+    if (lane_bytes == 16 && t256 >= 128) return tg::kF16FourWaveB22;  // 64-wide K tiles, 2 + 2 slots
+    if (t256 >= 240) return 3;
     if (tiles_of(a, 128, 128) >= 240) return 6;
     return 7;
 }

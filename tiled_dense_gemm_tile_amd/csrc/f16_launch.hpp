@@ -24,6 +24,12 @@ namespace tg {
     X(6, 128, 128, 64, 2, 2, 3, 2)      \
     X(7, 64, 64, 64, 2, 2, 2, 2)
 
+// Deep-ring 128 x 128 configurations (A and B both S = 2 or 3 tiles ahead),
+// numbered after the four-wave kernels below.
+#define TG_F16_DMA_DEEP(X)              \
+    X(17, 128, 128, 64, 2, 2, 3, 3)     \
+    X(18, 128, 128, 64, 2, 2, 4, 4)
+
 // Configurations also built with 4-byte global->LDS lanes (for rows that are
 // only 4-byte aligned).
 constexpr bool f16_has_lane4(int id) { return id == 3 || id == 6 || id == 7; }
@@ -46,7 +52,8 @@ constexpr F16CfgInfo kF16DmaCfgs[] = {TG_F16_DMA_CONFIGS(TG_F16_INFO){256, 256, 
                                       {256, 256, 64, 2, 2, 2, 3},
                                       {256, 256, 64, 2, 2, 2, 2},
                                       {256, 256, 64, 2, 2, 2, 3},
-                                      {256, 256, 64, 2, 2, 2, 2}};
+                                      {256, 256, 64, 2, 2, 2, 2},
+                                      TG_F16_DMA_DEEP(TG_F16_INFO)};
 #undef TG_F16_INFO
 constexpr int kNumF16DmaCfgs = sizeof(kF16DmaCfgs) / sizeof(kF16DmaCfgs[0]);
 #define TG_F16_COUNT(...) +1
@@ -57,7 +64,8 @@ constexpr int kF16FourWaveT22 = kF16PingPong32 + 4, kF16FourWaveT23 = kF16PingPo
 constexpr int kF16FourWaveB22 = kF16PingPong32 + 6, kF16FourWaveB23 = kF16PingPong32 + 7;
 // The balanced four-wave kernel for rows that are only 8-byte aligned.
 constexpr int kF16FourWaveS = kF16PingPong32 + 8;
-static_assert(kF16FourWaveS + 1 == kNumF16DmaCfgs, "configuration table");
+constexpr int kF16Deep2 = kF16FourWaveS + 1, kF16Deep3 = kF16FourWaveS + 2;
+static_assert(kF16Deep3 + 1 == kNumF16DmaCfgs && kF16Deep2 == 17, "configuration table");
 // Configurations that take rows only 4- or 8-byte aligned.
 constexpr bool f16_any_rows(int id) { return f16_has_lane4(id) || id == kF16FourWaveS; }
 
@@ -148,6 +156,7 @@ hipError_t launch_f16_dma<TG_FP16, TG_OUT_BF16>(int cfg, int lane_bytes, unsigne
         }                                                                                                  \
         break;
         TG_F16_DMA_CONFIGS(TG_F16_CASE)
+        TG_F16_DMA_DEEP(TG_F16_CASE)
 #undef TG_F16_CASE
     default:
         return hipErrorInvalidValue;

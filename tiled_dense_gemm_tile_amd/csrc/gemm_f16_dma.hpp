@@ -7,12 +7,15 @@
 //     physical chunk L mod CPR of its LDS row and so fetches logical chunk
 //     (L mod CPR) ^ swz(row).  Out-of-range rows and K chunks read as zero.
 //   * Separate prefetch rings for the A and B tiles in LDS: NA slots for A
-//     (prefetch distance SA = NA - 1) and NB = 2 slots for B (distance 1).
-//     Tile t lives in A slot t mod NA and B slot t mod 2.  Right after the
-//     barrier that opens tile t the fetches of B(t + 1) and then A(t + SA) are
-//     issued, each into the slot tile t - 1 used, whose reads every wave
-//     completed before that barrier.  With SA = 2 only half of a tile (B) must
-//     land within one tile's compute; A gets two.  One barrier per K tile.
+//     (prefetch distance SA = NA - 1) and NB slots for B (distance SB =
+//     NB - 1).  Tile t lives in A slot t mod NA and B slot t mod NB.  Right
+//     after the barrier that opens tile t the fetches of B(t + SB) and then
+//     A(t + SA) are issued, each into the slot tile t - 1 used, whose reads
+//     every wave completed before that barrier.  With SB = 1, SA = 2 only half
+//     of a tile (B) must land within one tile's compute; A gets two.  With
+//     SA = SB = S >= 2 (small tiles, where LDS holds deeper rings) both get S
+//     tiles, and the loads of S - 1 tiles stay in flight across every
+//     barrier.  One barrier per K tile.
 //   * Fragments are software-pipelined: while the MFMAs of K step kk run, the
 //     fragments of step kk + 1 are read from LDS; the last step's MFMAs are
 //     issued after the next tile's barrier so the matrix pipe restarts at once.
@@ -64,14 +67,16 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_f16_dma_kernel(F16Args p, F16Epi
     constexpr int B_INST = B_BYTES / IB / NW;
     constexpr int LPW = A_INST + B_INST;
     constexpr int SA = NA - 1, SB = NB - 1;            // prefetch distances
-    constexpr int WAIT_N = (SA - SB) * A_INST;         // loads still in flight at a tile barrier
+    // loads still in flight at a tile barrier: those issued after the newest
+    // fetch the next tile needs (see the issue order below)
+    constexpr int WAIT_N = SB == 1 ? (SA - SB) * A_INST : (SB - 1) * LPW;
     constexpr int B_BASE = NA * A_BYTES;               // B ring follows the A ring
     constexpr int RING_BYTES = NA * A_BYTES + NB * B_BYTES;
     constexpr int EPI_BYTES = epilogue_lds_bytes(NW, WTN);
     constexpr int LDS_BYTES = RING_BYTES > EPI_BYTES ? RING_BYTES : EPI_BYTES;
     static_assert(LB == 16 || LB == 4, "lane bytes");
     static_assert(A_BYTES % (IB * NW) == 0 && B_BYTES % (IB * NW) == 0 && RPI >= 1, "load tiling");
-    static_assert(SB == 1 && (SA == 1 || SA == 2), "ring depths");
+    static_assert(SB == 1 ? (SA == 1 || SA == 2) : SA == SB, "ring depths");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS capacity");
     static_assert(KK % 2 == 0, "fragment double buffer parity");
 
@@ -217,13 +222,15 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_f16_dma_kernel(F16Args p, F16Epi
     // only writes D: C "part" q (QR accumulator registers of one 32x32 block
     // per lane) is loaded at the transition into tile q + 1, ahead of that
     // transition's B fetch, so the next barrier's wait covers it, and added
-    // right after that wait.  With fewer than NQ + 2 tiles the epilogue adds C.
+    // right after that wait.  With fewer than NQ + 2 tiles, or with deep
+    // rings (the wait no longer covers the previous transition's loads), the
+    // epilogue adds C.
     constexpr int QR = (TM * TN * 16 / 32) > 4 ? (TM * TN * 16 / 32) : 4;
     constexpr int NQ = TM * TN * 16 / QR;
     constexpr int OS = OUT_BF16 ? 2 : 4;
     const int nk = (K + BK - 1) / BK;
     const bool hasC = p.C != nullptr;
-    const bool c_loop = hasC && nk >= NQ + 2;
+    const bool c_loop = SB == 1 && hasC && nk >= NQ + 2;
     const __amdgpu_buffer_rsrc_t rC =
         make_rsrc(hasC ? (const char *)p.C + (int64_t)m0 * p.ldc * OS : (const char *)p.D,
                   hasC ? span_bytes(M - m0, N, p.ldc, OS) : 0u);
@@ -252,13 +259,23 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_f16_dma_kernel(F16Args p, F16Epi
     // The rings always fetch once per tile; fetches of tiles past the end
     // read nothing (every chunk is out of range), write zeros into a slot no
     // later tile uses, and keep the loads in flight at every tile barrier at
-    // exactly WAIT_N: the B fetch of the next tile (with the C part before
-    // it) is the newest load that must have landed, and only the A fetch
-    // issued after it may still run.
+    // exactly WAIT_N.  SB = 1: the B fetch of the next tile (with the C part
+    // before it) is the newest load that must have landed, and only the A
+    // fetch issued after it may still run.  SA = SB = S: fetches go out in
+    // (B, A) pairs, tile after tile (S pairs before the first barrier, one
+    // after each), so the next tile's pair is followed by S - 1 newer pairs.
     if (nk > 0) {
         fetchB(0);
         fetchA(0);
-        if constexpr (SA == 2) fetchA(1);
+        if constexpr (SB == 1) {
+            if constexpr (SA == 2) fetchA(1);
+        } else {
+#pragma unroll
+            for (int u = 1; u < SB; ++u) {
+                fetchB(u);
+                fetchA(u);
+            }
+        }
         wait_vmcnt<WAIT_N>();
         wait_lgkmcnt0();
         barrier();
@@ -271,7 +288,7 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_f16_dma_kernel(F16Args p, F16Epi
             wait_lgkmcnt0();
             add_c_part(t - 1);
             barrier();
-            load_c_part(t);
+            if constexpr (SB == 1) load_c_part(t);
             fetchB(t + 1 + SB);
             fetchA(t + 1 + SA);
             load_frags(0, t + 1, 0);

@@ -48,7 +48,13 @@ int pick_f16_cfg(const Common &a, int lane_bytes, int vec) {
     if (vec == 4 && t256 >= 128) return tg::kF16FourWaveS;         // 8-byte rows: shifted-row variant
     if (lane_bytes == 16 && t256 >= 128) return tg::kF16FourWaveB22;  // 64-wide K tiles, 2 + 2 slots
     if (t256 >= 240) return 3;
-    if (tiles_of(a, 128, 128) >= 240) return 6;
+    // 128 x 128 tiles: about one wave of them (one workgroup per CU) runs
+    // best with both rings two tiles ahead (2048 x 2048 x 4096: 40.0 against
+    // 45.1 us); more, with two workgroups per CU sharing it, on the smaller
+    // three-slot A ring (2304 x 2304 x 4096: 62.1 against 71.7 us).
+    const int64_t t128 = tiles_of(a, 128, 128);
+    if (lane_bytes == 16 && t128 >= 240 && t128 <= 256) return tg::kF16Deep2;
+    if (t128 >= 240) return 6;
     return 7;
 }
 

@@ -265,7 +265,7 @@ def test_llm_projection_bf16_out(name):
 N_DMA_CFGS = 16
 
 
-@pytest.mark.parametrize("cfg", list(range(N_DMA_CFGS)) + [17, 18])
+@pytest.mark.parametrize("cfg", list(range(N_DMA_CFGS)) + [17, 18, 19, 20])
 def test_every_config(cfg, monkeypatch):
     """Each direct-to-LDS configuration, forced through the tuning override:
     bit-exact on integers over ragged shapes, within tolerance on random data."""
@@ -304,7 +304,7 @@ def test_lane4_configs(cfg, pad, monkeypatch):
             _full_check(in_type, x, to_f64(D), integer, C)
 
 
-@pytest.mark.parametrize("cfg", [1, 3, 6, 8, 9, 10, 11, 12, 13, 14, 15, 17, 18])
+@pytest.mark.parametrize("cfg", [1, 3, 6, 8, 9, 10, 11, 12, 13, 14, 15, 17, 18, 19, 20])
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 def test_c_streamed_in_k_loop(cfg, out, monkeypatch):
     """K long enough (>= 34 tiles of 64) that C is added during the K loop

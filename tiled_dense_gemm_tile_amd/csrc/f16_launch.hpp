@@ -24,11 +24,13 @@ namespace tg {
     X(6, 128, 128, 64, 2, 2, 3, 2)      \
     X(7, 64, 64, 64, 2, 2, 2, 2)
 
-// Deep-ring 128 x 128 configurations (A and B both S = 2 or 3 tiles ahead),
-// numbered after the four-wave kernels below.
+// Deep-ring configurations (A and B both S = 2 .. 4 tiles ahead), numbered
+// after the four-wave kernels below.
 #define TG_F16_DMA_DEEP(X)              \
     X(17, 128, 128, 64, 2, 2, 3, 3)     \
-    X(18, 128, 128, 64, 2, 2, 4, 4)
+    X(18, 128, 128, 64, 2, 2, 4, 4)     \
+    X(19, 64, 64, 64, 2, 2, 3, 3)       \
+    X(20, 64, 64, 64, 2, 2, 5, 5)
 
 // Configurations also built with 4-byte global->LDS lanes (for rows that are
 // only 4-byte aligned).
@@ -65,7 +67,8 @@ constexpr int kF16FourWaveB22 = kF16PingPong32 + 6, kF16FourWaveB23 = kF16PingPo
 // The balanced four-wave kernel for rows that are only 8-byte aligned.
 constexpr int kF16FourWaveS = kF16PingPong32 + 8;
 constexpr int kF16Deep2 = kF16FourWaveS + 1, kF16Deep3 = kF16FourWaveS + 2;
-static_assert(kF16Deep3 + 1 == kNumF16DmaCfgs && kF16Deep2 == 17, "configuration table");
+constexpr int kF16Deep64x2 = kF16FourWaveS + 3, kF16Deep64x4 = kF16FourWaveS + 4;
+static_assert(kF16Deep64x4 + 1 == kNumF16DmaCfgs && kF16Deep2 == 17, "configuration table");
 // Configurations that take rows only 4- or 8-byte aligned.
 constexpr bool f16_any_rows(int id) { return f16_has_lane4(id) || id == kF16FourWaveS; }
 

@@ -55,6 +55,10 @@ int pick_f16_cfg(const Common &a, int lane_bytes, int vec) {
     const int64_t t128 = tiles_of(a, 128, 128);
     if (lane_bytes == 16 && t128 >= 240 && t128 <= 256) return tg::kF16Deep2;
     if (t128 >= 240) return 6;
+    // smaller grids: 64 x 64 tiles, both rings two tiles ahead, up to two
+    // workgroups per CU (1024 x 1024 x 4096: 18.9 against 30.0 us with the
+    // two-slot rings; past 512 tiles the two-slot rings are ahead again)
+    if (lane_bytes == 16 && tiles_of(a, 64, 64) <= 512) return tg::kF16Deep64x2;
     return 7;
 }
 

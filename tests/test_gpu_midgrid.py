@@ -1,7 +1,7 @@
 """Grids at the library's kernel-choice boundaries: 128 to 239 output tiles
 of 256 x 256 (part of one wave), which go to the four-wave 256 x 256
-kernels, and 240 to 256 tiles of 128 x 128, which go to the deep-ring
-128 x 128 kernel.  Exact on integer-valued inputs against the oracle at 4096
+kernels, and grids of up to one 128 x 128 (or 64 x 64) tile per CU, which
+go to the deep-ring kernels.  Exact on integer-valued inputs against the oracle at 4096
 seeded samples plus the tile edges, and within the tolerance on random
 inputs."""
 import numpy as np
@@ -22,7 +22,8 @@ if torch.cuda.is_available():
 # rows (K = 516); fp8 at 132 tiles; 16-bit at exactly 128 tiles; 256 and 240
 # tiles of 128 x 128 with ragged edges and K
 CASES = [("bf16", 2900, 3000, 520), ("fp16", 3000, 3000, 516), ("e4m3", 2600, 3000, 1024), ("bf16", 2048, 4096, 256),
-         ("bf16", 2000, 2000, 1000), ("fp16", 1900, 2000, 4104)]
+         ("bf16", 2000, 2000, 1000), ("fp16", 1900, 2000, 4104),
+         ("e4m3", 2000, 1900, 2048), ("e4m3", 1000, 1000, 4096)]
 
 
 @pytest.mark.parametrize("case", CASES, ids=["%s_%dx%dx%d" % c for c in CASES])

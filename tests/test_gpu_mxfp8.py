@@ -76,7 +76,7 @@ def test_scale_structure():
     _full_check(x, to_f64(D), True)
 
 
-@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 5])
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3, 4, 5, 6, 7])
 def test_every_config(cfg, monkeypatch):
     monkeypatch.setenv("TILEGEMM_MX_CONFIG", str(cfg))
     for (M, N, K) in [(300, 520, 256), (777, 513, 1024), (520, 300, 384), (1100, 1030, 2048)]:

@@ -6,8 +6,9 @@
 //
 // Same structure as the 16-bit direct-to-LDS kernel: a K tile is 128 fp8
 // elements (one 128-byte row chunked and XOR-swizzled in 16-byte units),
-// A and B tiles arrive by buffer_load ... lds into two-slot rings, one
-// barrier per K tile, fragments software-pipelined, LDS-staged epilogue.
+// A and B tiles arrive by buffer_load ... lds into rings of NS slots (the
+// tile NS - 1 ahead is fetched), one barrier per K tile, fragments
+// software-pipelined, LDS-staged epilogue.
 //
 // Operand placement (measured on gfx950 with one-hot operands): in a
 // 32 x 32 x 64 MFMA, bytes 0-15 of a lane form half of the first 32-wide K
@@ -37,9 +38,9 @@ struct MxArgs {
     int64_t ldsfa, ldsfb;
 };
 
-template <int BM_, int BN_, int WM_, int WN_>
+template <int BM_, int BN_, int WM_, int WN_, int NS_ = 2>
 struct MxCfg {
-    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, NS = NS_;
     static constexpr int NT = WM * WN * 64;
 };
 
@@ -53,7 +54,7 @@ __device__ __forceinline__ f32x16 mfma_mx(const i32x8 &a, const i32x8 &b, const 
 template <class Cfg, bool OUT_BF16>
 __global__ void __launch_bounds__(Cfg::NT) gemm_mxfp8_kernel(MxArgs q, F16Epi e) {
     const F16Args &p = q.g;
-    constexpr int BM = Cfg::BM, BN = Cfg::BN, WM = Cfg::WM, WN = Cfg::WN, NW = WM * WN;
+    constexpr int BM = Cfg::BM, BN = Cfg::BN, WM = Cfg::WM, WN = Cfg::WN, NW = WM * WN, NS = Cfg::NS;
     constexpr int BK = 128;                            // fp8 elements per K tile = bytes per row
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int TM = WTM / 32, TN = WTN / 32;
@@ -65,20 +66,21 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_mxfp8_kernel(MxArgs q, F16Epi e)
     constexpr int A_INST = A_BYTES / 1024 / NW;
     constexpr int B_INST = B_BYTES / 1024 / NW;
     constexpr int NSI = (BM + BN) / 64;                // scale load instructions per tile (whole group)
-    constexpr int A_BASE = 0, B_BASE = 2 * A_BYTES, S_BASE = B_BASE + 2 * B_BYTES;
+    constexpr int A_BASE = 0, B_BASE = NS * A_BYTES, S_BASE = B_BASE + NS * B_BYTES;
     constexpr int S_SLOT = SA_BYTES + SB_BYTES;
-    constexpr int RING_BYTES = S_BASE + 2 * S_SLOT;
+    constexpr int RING_BYTES = S_BASE + NS * S_SLOT;
     constexpr int EPI_BYTES = epilogue_lds_bytes(NW, WTN);
     constexpr int LDS_BYTES = RING_BYTES > EPI_BYTES ? RING_BYTES : EPI_BYTES;
     static_assert(A_BYTES % (1024 * NW) == 0 && B_BYTES % (1024 * NW) == 0, "load tiling");
     static_assert(BM % 64 == 0 && BN % 64 == 0, "scale load tiling");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS capacity");
     static_assert(KK == 2, "fragment double buffer parity");
+    static_assert(NS >= 2, "ring depth");
 
     __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     int tmi, tni;
     tile_order(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, tmi, tni);
     const int m0 = tmi * BM, n0 = tni * BN;
@@ -112,7 +114,7 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_mxfp8_kernel(MxArgs q, F16Epi e)
     // a tile at or past K is not.
     auto fetchA = [&](int t) {
         const int k0 = t * BK;
-        char *s = smem + A_BASE + (t & 1) * A_BYTES;
+        char *s = smem + A_BASE + (t % NS) * A_BYTES;
 #pragma unroll
         for (int j = 0; j < A_INST; ++j) {
             const uint32_t off = k0 < K ? a_goff[j] + (uint32_t)k0 : kOOB;
@@ -122,7 +124,7 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_mxfp8_kernel(MxArgs q, F16Epi e)
     };
     auto fetchB = [&](int t) {
         const int k0 = t * BK;
-        char *s = smem + B_BASE + (t & 1) * B_BYTES;
+        char *s = smem + B_BASE + (t % NS) * B_BYTES;
 #pragma unroll
         for (int j = 0; j < B_INST; ++j) {
             const uint32_t off = k0 < K ? b_goff[j] + (uint32_t)k0 : kOOB;
@@ -130,7 +132,7 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_mxfp8_kernel(MxArgs q, F16Epi e)
                 rB, (__attribute__((address_space(3))) void *)(s + (j * NW + wave) * 1024), 16, off, 0, 0, 0);
         }
         // scale rows of this tile: 4 bytes (blocks 4t .. 4t+3) per row of A and of B
-        char *ss = smem + S_BASE + (t & 1) * S_SLOT;
+        char *ss = smem + S_BASE + (t % NS) * S_SLOT;
         const bool kin = k0 < K;
 #pragma unroll
         for (int j = wave; j < NSI; j += NW) {
@@ -179,9 +181,9 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_mxfp8_kernel(MxArgs q, F16Epi e)
     // 4kk + 2 + fh of each row, and the row's scale dword (the tile's four
     // blocks) shifted so byte 2kk is block 2kk + fh (op_sel 2kk picks it).
     auto load_step = [&](int kk, int t) {
-        const char *sA = smem + A_BASE + (t & 1) * A_BYTES;
-        const char *sB = smem + B_BASE + (t & 1) * B_BYTES;
-        const char *ss = smem + S_BASE + (t & 1) * S_SLOT;
+        const char *sA = smem + A_BASE + (t % NS) * A_BYTES;
+        const char *sB = smem + B_BASE + (t % NS) * B_BYTES;
+        const char *ss = smem + S_BASE + (t % NS) * S_SLOT;
         const int c0 = ((4 * kk + fh) ^ fswz) << 4, c1 = ((4 * kk + 2 + fh) ^ fswz) << 4;
 #pragma unroll
         for (int i = 0; i < TM; ++i) fa[kk][i] = ld32(sA + a_frag + i * 32 * ROWB, c0, c1);
@@ -223,30 +225,47 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_mxfp8_kernel(MxArgs q, F16Epi e)
         }
     };
 
-    // Rings: A and B two slots each (prefetch distance 1), scales with B.
-    // Every tile barrier waits for all fetches issued so far; the tile the
-    // barrier opens was fetched one tile earlier, and the slot refilled after
-    // it held the tile whose last reads finished before it.  A fetch past the
-    // last tile reads nothing and fills a slot no later tile uses.
+    // Rings: A and B NS slots each (prefetch distance S = NS - 1), scales
+    // with B.  Fetches go out one tile at a time (B with its scales, then A):
+    // S tiles before the first barrier, one after each.  A tile barrier waits
+    // until only the S - 1 newest tiles' fetches may still be in flight, so
+    // the tile it opens has landed; the slot refilled after it held the tile
+    // whose last reads finished before it.  A fetch past the last tile reads
+    // nothing and fills a slot no later tile uses.  A wave's loads per tile
+    // depend on how many of the scale loads fall to it.
+    constexpr int NSI_LO = NSI / NW, NSI_HI = (NSI + NW - 1) / NW;
+    constexpr int WAIT_LO = (NS - 2) * (A_INST + B_INST + NSI_LO);
+    constexpr int WAIT_HI = (NS - 2) * (A_INST + B_INST + NSI_HI);
+    auto wait_ring = [&]() {
+        if (wave < NSI % NW)
+            wait_vmcnt<WAIT_HI>();
+        else
+            wait_vmcnt<WAIT_LO>();
+    };
     const int nk = K / BK;
     if (nk > 0) {
         fetchB(0);
         fetchA(0);
-        wait_vmcnt<0>();
+#pragma unroll
+        for (int u = 1; u < NS - 1; ++u) {
+            fetchB(u);
+            fetchA(u);
+        }
+        wait_ring();
         wait_lgkmcnt0();
         barrier();
-        fetchB(1);
-        fetchA(1);
+        fetchB(NS - 1);
+        fetchA(NS - 1);
         load_step(0, 0);
         for (int t = 0; t + 1 < nk; ++t) {
             load_step(1, t);
             mfmas(0);
             interleave();
-            wait_vmcnt<0>();
+            wait_ring();
             wait_lgkmcnt0();
             barrier();
-            fetchB(t + 2);
-            fetchA(t + 2);
+            fetchB(t + NS);
+            fetchA(t + NS);
             load_step(0, t + 1);
             mfmas(1);
             interleave();

@@ -37,13 +37,18 @@ gemm_status dispatch_mx(const Common &a, const void *SFA, int64_t ldsfa, const v
         // the four-wave kernel once its 256 x 256 grid is over half a wave
         // (measured at K = 4096: 160 tiles 46.9 against 71.3 us with
         // 128 x 128 tiles; at 128 tiles 128 x 128 is 2 % ahead)
-        const int64_t t256 = tiles_of(a, 256, 256);
+        const int64_t t256 = tiles_of(a, 256, 256), t128 = tiles_of(a, 128, 128);
         if (scales16 && t256 > 128)
             cfg = tg::kMxFourWave;
         else if (t256 >= 240)
             cfg = 1;
+        else if (t128 > 256)
+            cfg = 2;                                    // two workgroups per CU share the waves
+        else if (t128 > 128)
+            cfg = tg::kMxDeep128;                       // at most one 128 x 128 tile per CU: three-slot rings
         else
-            cfg = tiles_of(a, 128, 128) >= 240 ? 2 : 3;
+            cfg = tg::kMxDeep64;                        // (2048 x 2048 x 8192: 43.8 against 59.3 us;
+                                                        //  1024 x 1024 x 8192 in 64 x 64 tiles: 23.2 against 37.4)
     }
     tg::MxArgs q;
     q.g.A = a.A;

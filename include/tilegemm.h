@@ -236,7 +236,9 @@ gemm_status gemm_mxfp6(int64_t M, int64_t N, int64_t K,
  * accumulating tiles into one global tile); here the accumulation is a
  * separate pass over fp32 partials rather than a reducing store.
  *   splits: 0 = the library's choice (split only grids of fewer than 128
- *     tiles of 256 x 256, up to 256 workgroups, at least 4096 K per range),
+ *     tiles of 256 x 256, up to 256 workgroups; under 16 tiles at least
+ *     4096 K per range, else at least 1280 K per range and only when that
+ *     gives 200 or more workgroups),
  *     1 = no split, up to 64; fewer are used when K has fewer 64-wide tiles,
  *     and none when rows are not 8-byte aligned.  Else GEMM_ERR_UNSUPPORTED.
  *   workspace: device memory, 256-byte aligned (else GEMM_ERR_MISALIGNED), of

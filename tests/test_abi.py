@@ -168,6 +168,10 @@ def test_splitk_workspace_bytes():
     assert splitk_bytes(1024, 1024, 65536, 0) == 16 * 1024 * 1024 * 4   # 16 tiles, 1024 K tiles: 16 splits
     assert splitk_bytes(4096, 4096, 4096, 0) == 0             # 256 tiles: the library does not split
     assert splitk_bytes(512, 512, 8192, 0) == 2 * 512 * 512 * 4   # 4 tiles, 128 K tiles: 2 splits of 4096
+    assert splitk_bytes(1024, 1024, 8192, 0) == 0             # 16 tiles x 6 ranges < 200 workgroups: unsplit
+    assert splitk_bytes(2304, 2304, 4096, 0) == 3 * 2304 * 2304 * 4   # 81 tiles: 3 ranges of >= 20 K tiles
+    assert splitk_bytes(2048, 2048, 8192, 0) == 4 * 2048 * 2048 * 4   # 64 tiles: 4 ranges
+    assert splitk_bytes(2048, 2048, 4096, 0) == 0             # 64 tiles x 3 ranges < 200: unsplit
     assert splitk_bytes(64, 64, 4096, 65) == 0 and splitk_bytes(-1, 64, 4096, 2) == 0
 
 

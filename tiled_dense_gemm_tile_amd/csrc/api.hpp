@@ -101,13 +101,24 @@ inline int effective_splits(int64_t K, int splits, int64_t unit = 64) {
 // up to one wave of 256 workgroups, keeping at least 4096 K per split so that
 // writing and re-reading a split's fp32 partial tile stays small next to its
 // multiply work.
+// Only grids of fewer than 128 output tiles of 256 x 256 are split, into as
+// many K ranges as fill one wave (256 / tiles).  Under 16 tiles each range
+// keeps at least 64 K tiles of 64.  From 16 tiles each keeps at least 20, and
+// the grid is split only if the ranges then give 200 or more workgroups:
+// below that the unsplit call's small-tile kernels, which cover the chip by
+// themselves, are as fast or faster (bf16, measured: 1024 x 1024 x 8192
+// unsplit 34.2 us, 2 ranges 77.3; 2048 x 2048 x 4096 unsplit 40-44, 3 ranges
+// 46.0; 2304 x 2304 x 4096 unsplit 58.7, 3 ranges 52.7; 2048 x 2048 x 8192
+// unsplit 76.2, 4 ranges 66.8).
 inline int auto_splits(int64_t M, int64_t N, int64_t K) {
     const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
     if (tiles <= 0 || tiles >= 128) return 1;
     int64_t s = 256 / tiles;
-    const int64_t by_k = ((K + 63) / 64) / 64;
+    const int64_t kt = (K + 63) / 64;
+    const int64_t by_k = tiles < 16 ? kt / 64 : kt / 20;
     if (by_k < s) s = by_k;
     if (s > kMaxSplits) s = kMaxSplits;
+    if (tiles >= 16 && tiles * s < 200) return 1;
     return s < 2 ? 1 : (int)s;
 }
 

@@ -49,7 +49,7 @@ def report(D, D_ref, S, extra_rel=0.0):
             "max_abs_err": float(np.nanmax(err)) if D.size else 0.0}
 
 
-def freivalds_blocks(D, a, b, c=None, block=64, seed=12345, integer=False, extra_rel=0.0):
+def freivalds_blocks(D, a, b, c=None, block=64, seed=12345, integer=False):
     """Block-Freivalds check of a whole D (float64 operands from ``operands_f64``).
 
     ``D``: (M, N) result under test; ``a``: (M, K); ``b``: (N, K); ``c``: (M, N)
@@ -75,8 +75,6 @@ def freivalds_blocks(D, a, b, c=None, block=64, seed=12345, integer=False, extra
     absX = np.abs(X)
     Ssum = np.abs(a) @ (np.abs(b).T @ absX)            # sum_n |x_n| S_mn per block
     bound = TOL_REL * Ssum + TOL_ABS * absX.sum(axis=0)[None, :]
-    if extra_rel:
-        bound = bound + extra_rel * (np.abs(rhs) + np.abs(a) @ (np.abs(b).T @ absX))
     # slack for the float64 evaluation of both sides
     mag = np.abs(D) @ absX + Ssum
     if c is not None:

@@ -285,3 +285,52 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(tg, "_lib", None)
     with pytest.raises(tg.LibraryMissing):
         tg.raw.gemm_bf16
+
+
+class _FakeDevice:
+    """A host tensor that reports itself as living on cuda:0, so the
+    binding's argument checks can be driven without a GPU.  The checks under
+    test must raise before any pointer reaches the library."""
+
+    def __init__(self, t):
+        import torch
+        self._t, self.is_cuda, self.device = t, True, torch.device("cuda", 0)
+
+    def __getattr__(self, name):
+        return getattr(self._t, name)
+
+
+@pytest.mark.parametrize("which", ["C", "D"])
+def test_binding_rejects_host_c_and_d(which):
+    import torch
+    A = _FakeDevice(torch.zeros(8, 16, dtype=torch.bfloat16))
+    B = _FakeDevice(torch.zeros(4, 16, dtype=torch.bfloat16))
+    host = torch.zeros(8, 4)
+    dev = _FakeDevice(torch.zeros(8, 4))
+    kw = {"C": host, "D": dev} if which == "C" else {"C": None, "D": host}
+    for fn in (tg.gemm_bf16, tg.gemm_bf16_splitk):
+        with pytest.raises(ValueError, match=which):
+            fn(A, B, **kw)
+    A8 = _FakeDevice(torch.zeros(8, 64, dtype=torch.uint8))
+    B8 = _FakeDevice(torch.zeros(4, 64, dtype=torch.uint8))
+    SFA = _FakeDevice(torch.full((8, 2), 127, dtype=torch.uint8))
+    SFB = _FakeDevice(torch.full((4, 2), 127, dtype=torch.uint8))
+    for order in ("k", "mn"):
+        Ao = A8 if order == "k" else _FakeDevice(torch.zeros(64, 8, dtype=torch.uint8))
+        with pytest.raises(ValueError, match=which):
+            tg.gemm_mxfp8(Ao, SFA, B8, SFB, a_order=order, **kw)
+
+
+def test_binding_rejects_host_workspace_and_scales():
+    import torch
+    A = _FakeDevice(torch.zeros(256, 8192, dtype=torch.bfloat16))
+    B = _FakeDevice(torch.zeros(256, 8192, dtype=torch.bfloat16))
+    D = _FakeDevice(torch.zeros(256, 256))
+    with pytest.raises(ValueError, match="workspace"):
+        tg.gemm_bf16_splitk(A, B, D=D, splits=4, workspace=torch.zeros(1 << 24, dtype=torch.uint8))
+    A8 = _FakeDevice(torch.zeros(8, 64, dtype=torch.uint8))
+    B8 = _FakeDevice(torch.zeros(4, 64, dtype=torch.uint8))
+    D8 = _FakeDevice(torch.zeros(8, 4))
+    with pytest.raises(ValueError):
+        tg.gemm_mxfp8(A8, torch.full((8, 2), 127, dtype=torch.uint8), B8,
+                      _FakeDevice(torch.full((4, 2), 127, dtype=torch.uint8)), D=D8)

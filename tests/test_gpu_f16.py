@@ -237,6 +237,56 @@ def test_ragged_fp16_every_element():
     assert rep["fail"] == 0
 
 
+def test_ragged_fp16_integer_every_element():
+    """The ragged workload's shape and launch with integer inputs in [-4, 4]:
+    every element bit-exact against the float64 product (exact here: every
+    partial sum is an integer below 2^24), the samples against the naive loop."""
+    w = inputs.WORKLOADS["ragged_fp16"]
+    x = inputs.generate(w, integer=True)
+    say("ragged fp16 4000x3000x4100 integer")
+    D = run16("fp16", dev16(x["A"], "fp16"), dev16(x["B"], "fp16"), None)
+    torch.cuda.synchronize()
+    Dg = to_f64(D)
+    Dr, _ = oracle.gemm_ref_full("fp16", x["A"], x["B"])
+    bad = np.argwhere(Dg != Dr)
+    assert bad.size == 0, "first mismatches %s" % bad[:5].tolist()
+    rand, forced = inputs.sample_indices(x["M"], x["N"], w.seed)
+    idx = np.concatenate([rand, forced])
+    Dn, _ = oracle.gemm_ref("fp16", x["A"], x["B"], idx=idx)
+    assert np.array_equal(Dg.ravel()[idx], Dn)
+
+
+@pytest.mark.parametrize("name", ["llm_proj_bf16", "llm_proj_shard8_bf16"])
+def test_llm_projection_integer(name):
+    """The projection shapes with integer inputs in [-4, 4] (|partial sums| <=
+    65536 < 2^24, so the exact result is an fp32 value): the fp32-output call
+    is exact on every element (integer block-Freivalds, exact in float64) and
+    on the samples; the bf16-output call equals the nearest-even rounding of
+    that exact result on every element, and on the samples the rounding of
+    the naive loop's value."""
+    w = inputs.WORKLOADS[name]
+    x = inputs.generate(w, integer=True)
+    say("%s %dx%dx%d integer, bf16 and fp32 out" % (name, w.M, w.N, w.K))
+    A, B = dev16(x["A"], "bf16"), dev16(x["B"], "bf16")
+    D16 = run16("bf16", A, B, None, out="bf16")
+    D32 = run16("bf16", A, B, None, out="f32")
+    torch.cuda.synchronize()
+    d32 = D32.cpu().numpy()
+    del D32
+    d16 = bf16_bits(D16)
+    del D16
+    a, b = oracle.operands_f64("bf16", x["A"], x["B"])
+    ok, worst = check.freivalds_blocks(d32, a, b, None, block=64, integer=True)
+    say("  integer freivalds ok=%s worst %.3g" % (ok, worst))
+    assert ok
+    assert np.array_equal(d16, oracle.rne_bf16_f32(d32))
+    rand, forced = inputs.sample_indices(x["M"], x["N"], w.seed)
+    idx = np.concatenate([rand, forced])
+    Dn, _ = oracle.gemm_ref("bf16", x["A"], x["B"], idx=idx)
+    assert np.array_equal(d32.ravel()[idx].astype(np.float64), Dn)
+    assert np.array_equal(d16.ravel()[idx], oracle.rne_bf16(Dn))
+
+
 @pytest.mark.parametrize("name", ["llm_proj_bf16", "llm_proj_shard8_bf16"])
 def test_llm_projection_bf16_out(name):
     w = inputs.WORKLOADS[name]

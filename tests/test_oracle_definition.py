@@ -338,3 +338,21 @@ def test_full_matches_naive(in_type, scaled):
     idx = np.array([0, 5, M * N - 1, 100])
     Di, Si = oracle.gemm_ref(in_type, A, B, C=C, SFA=SFA, SFB=SFB, idx=idx)
     assert np.array_equal(Di, D.ravel()[idx]) and np.array_equal(Si, S.ravel()[idx])
+
+
+def test_full_bf16_c_matches_naive():
+    """The whole-matrix form with C given as bf16 bits: C decoded as bf16
+    (bits << 16), the same as the naive loop's bf16 C; a one-element case
+    whose C alone decides the result pins the decoding by value."""
+    rng = np.random.default_rng(23)
+    M, N, K = 19, 23, 96
+    A = inputs.random_codes(rng, "bf16", (M, K))
+    B = inputs.random_codes(rng, "bf16", (N, K))
+    C = inputs.random_codes(rng, "bf16", (M, N))
+    D, S = oracle.gemm_ref("bf16", A, B, C=C, c_type="bf16")
+    Df, Sf = oracle.gemm_ref_full("bf16", A, B, C=C, c_type="bf16")
+    cval = (C.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    assert np.all(np.abs(D - Df) <= 4 * K * 2.0 ** -53 * (S + np.abs(cval)))
+    Z = np.zeros((1, 4), np.uint16)
+    Dz, _ = oracle.gemm_ref_full("bf16", Z, Z, C=np.array([[0xC0A0]], np.uint16), c_type="bf16")
+    assert Dz[0, 0] == -5.0

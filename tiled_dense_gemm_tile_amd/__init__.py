@@ -129,6 +129,14 @@ def _ld(t, cols):
     return t.stride(0)
 
 
+def _on_device(ref, **tensors):
+    """Raise unless every given tensor lives on ``ref``'s GPU: a host tensor's
+    data_ptr() handed to a kernel would be an address the GPU cannot map."""
+    for name, t in tensors.items():
+        if t is not None and (not t.is_cuda or t.device != ref.device):
+            raise ValueError("%s must be a device tensor on %s" % (name, ref.device))
+
+
 def _prep(A, B, C, D, out_dtype, in_dtypes):
     import torch
     if A.dtype not in in_dtypes or B.dtype not in in_dtypes:
@@ -147,9 +155,22 @@ def _prep(A, B, C, D, out_dtype, in_dtypes):
         raise ValueError("D must be (M, N) of out_dtype")
     if C is not None and (C.dtype != out_dtype or tuple(C.shape) != (M, N)):
         raise ValueError("C must be (M, N) of out_dtype")
-    stream = torch.cuda.current_stream(A.device).cuda_stream
+    _on_device(A, B=B, C=C, D=D)
     out = OUT_BF16 if out_dtype == torch.bfloat16 else OUT_F32
-    return M, N, K, D, stream, out
+    return M, N, K, D, _Stream(A), out
+
+
+class _Stream:
+    """torch's current stream on A's device, looked up when the call is
+    marshalled (after every argument check), as a ctypes argument."""
+
+    def __init__(self, A):
+        self._dev = A.device
+
+    @property
+    def _as_parameter_(self):
+        import torch
+        return ctypes.c_void_p(torch.cuda.current_stream(self._dev).cuda_stream)
 
 
 K_CONTIGUOUS, MN_CONTIGUOUS = 0, 1
@@ -205,10 +226,12 @@ def splitk_workspace_bytes(M: int, N: int, K: int, splits: int = 0) -> int:
 
 def _call16_split(name, A, B, C, out_dtype, D, dtype, splits, workspace):
     import torch
+    _on_device(A, workspace=workspace)
     M, N, K, D, stream, out = _prep(A, B, C, D, out_dtype, (dtype,))
     need = splitk_workspace_bytes(M, N, K, splits) if M and N and K else 0
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=A.device)
+    _on_device(A, workspace=workspace)
     wp = workspace.data_ptr() if workspace is not None else None
     wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = getattr(_load(), name)(M, N, K, A.data_ptr(), _ld(A, K) if K else 0, B.data_ptr(), _ld(B, K) if K else 0,
@@ -235,11 +258,12 @@ def gemm_fp16_splitk(A, B, C=None, out_dtype=None, D=None, splits=0, workspace=N
                          torch.float16, splits, workspace)
 
 
-def _scales(SFA, SFB, M, N):
+def _scales(SFA, SFB, M, N, A):
     import torch
     for s, rows in ((SFA, M), (SFB, N)):
         if s.dtype not in (torch.uint8, torch.float8_e8m0fnu) or not s.is_cuda or s.shape[0] != rows:
             raise ValueError("scale arrays must be uint8/e8m0 device tensors of shape (rows, K/32)")
+    _on_device(A, SFA=SFA, SFB=SFB)
 
 
 def _split_tail(M, N, K, A, splits, workspace):
@@ -248,6 +272,7 @@ def _split_tail(M, N, K, A, splits, workspace):
     need = splitk_workspace_bytes(M, N, K, splits) if M and N and K else 0
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=A.device)
+    _on_device(A, workspace=workspace)
     wp = workspace.data_ptr() if workspace is not None else None
     wb = workspace.numel() * workspace.element_size() if workspace is not None else 0
     return [splits, wp, wb], workspace
@@ -294,9 +319,10 @@ def _mx_ex(t, A, SFA, B, SFB, C, out_dtype, D, a_order, b_order, fmt=None):
         raise ValueError("D must be (M, N) of out_dtype")
     if C is not None and (C.dtype != out_dtype or tuple(C.shape) != (M, N)):
         raise ValueError("C must be (M, N) of out_dtype")
-    _scales(SFA, SFB, M, N)
+    _on_device(A, B=B, C=C, D=D)
+    _scales(SFA, SFB, M, N, A)
     nkb = K // 32
-    stream = torch.cuda.current_stream(A.device).cuda_stream
+    stream = _Stream(A)
     out = OUT_BF16 if out_dtype == torch.bfloat16 else OUT_F32
     args = [M, N, K, A.data_ptr(), lda if K else 0, _ORDERS[a_order], SFA.data_ptr(), _ld(SFA, nkb) if K else 0,
             B.data_ptr(), ldb if K else 0, _ORDERS[b_order], SFB.data_ptr(), _ld(SFB, nkb) if K else 0,
@@ -310,9 +336,11 @@ def _mx_ex(t, A, SFA, B, SFB, C, out_dtype, D, a_order, b_order, fmt=None):
 
 def _mx8(name, A, SFA, B, SFB, C, out_dtype, D, split):
     import torch
+    if split is not None:
+        _on_device(A, workspace=split[1])
     out_dtype = torch.float32 if out_dtype is None else out_dtype
     M, N, K, D, stream, out = _prep(A, B, C, D, out_dtype, (torch.float8_e4m3fn, torch.uint8))
-    _scales(SFA, SFB, M, N)
+    _scales(SFA, SFB, M, N, A)
     nkb = K // 32
     args = [M, N, K, A.data_ptr(), _ld(A, K) if K else 0, SFA.data_ptr(), _ld(SFA, nkb) if K else 0,
             B.data_ptr(), _ld(B, K) if K else 0, SFB.data_ptr(), _ld(SFB, nkb) if K else 0,
@@ -344,11 +372,13 @@ def gemm_mxfp8_splitk(A, SFA, B, SFB, C=None, out_dtype=None, D=None, splits=0, 
 
 def _mx4(name, A, SFA, B, SFB, C, out_dtype, D, split):
     import torch
+    if split is not None:
+        _on_device(A, workspace=split[1])
     out_dtype = torch.float32 if out_dtype is None else out_dtype
     fp4x2 = getattr(torch, "float4_e2m1fn_x2", torch.uint8)
     M, N, KB, D, stream, out = _prep(A, B, C, D, out_dtype, (torch.uint8, fp4x2))
     K = 2 * KB
-    _scales(SFA, SFB, M, N)
+    _scales(SFA, SFB, M, N, A)
     nkb = K // 32
     args = [M, N, K, A.data_ptr(), 2 * _ld(A, KB) if K else 0, SFA.data_ptr(), _ld(SFA, nkb) if K else 0,
             B.data_ptr(), 2 * _ld(B, KB) if K else 0, SFB.data_ptr(), _ld(SFB, nkb) if K else 0,
@@ -384,6 +414,8 @@ FP6_FORMATS = {"e2m3": 0, "e3m2": 1}
 
 def _mx6(name, A, SFA, B, SFB, C, out_dtype, D, fmt, split):
     import torch
+    if split is not None:
+        _on_device(A, workspace=split[1])
     out_dtype = torch.float32 if out_dtype is None else out_dtype
     if fmt not in FP6_FORMATS:
         raise ValueError("fmt must be 'e2m3' or 'e3m2'")
@@ -391,7 +423,7 @@ def _mx6(name, A, SFA, B, SFB, C, out_dtype, D, fmt, split):
     if KB % 3:
         raise ValueError("the byte width of A and B must be a multiple of 3 (four elements per three bytes)")
     K = KB // 3 * 4
-    _scales(SFA, SFB, M, N)
+    _scales(SFA, SFB, M, N, A)
     lds = []
     for X in (A, B):
         ldb_ = _ld(X, KB) if K else 0

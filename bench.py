@@ -7,7 +7,9 @@ HBM.  W untimed steps, then exactly K timed steps bracketed by device
 synchronisation; the GEMM kernel's average duration is taken with HIP events
 recorded on the stream the kernel is launched on (torch's current stream).
 Prints one JSON line.  The default workload is the 4096^3 bf16 GEMM with fp32
-C and D.
+C and D; the same run then times the 8192^3 block-scaled fp8 GEMM (e4m3 with
+e8m0 scales per 32 K, fp32 D) the same way and reports it under
+"secondary", with its own roofline and CPU baseline.
 """
 from __future__ import annotations
 
@@ -71,22 +73,58 @@ def device_inputs(w, x, torch):
     return A, B, C, extra
 
 
+def cpu_model():
+    """The host CPU's model name (first processor of /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, x, target_rows):
-    """Time the oracle on the first `target_rows` full rows of D (every column)."""
+    """Time the oracle on the first `target_rows` full rows of D (every column),
+    on every host thread OpenMP gives it."""
     import numpy as np
     import oracle
     rows = min(target_rows, w.M)
     idx = np.arange(rows * w.N, dtype=np.int64)
+    cores = oracle.num_threads()
     s1 = (lambda s: s[:1] if s is not None else None)
     oracle.gemm_ref(w.in_type, x["A"][:1], x["B"][:1], C=None, SFA=s1(x["SFA"]), SFB=s1(x["SFB"]),
-                    idx=np.zeros(1, np.int64))  # load, warm
+                    idx=np.zeros(1, np.int64), nthreads=cores)  # load, warm
     t0 = time.perf_counter()
-    oracle.gemm_ref(w.in_type, x["A"], x["B"], C=x["C"], SFA=x["SFA"], SFB=x["SFB"], idx=idx)
+    oracle.gemm_ref(w.in_type, x["A"], x["B"], C=x["C"], SFA=x["SFA"], SFB=x["SFB"], idx=idx, nthreads=cores)
     dt = time.perf_counter() - t0
     flops = 2.0 * rows * w.N * w.K
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": "first %d rows x all %d columns of D (%d elements, each a full K=%d fp64 dot product); "
                       "%.1f s" % (rows, w.N, rows * w.N, w.K, dt)}
+
+
+def cpu_small_full():
+    """The oracle on the whole 256^3 bf16 workload (every element), on all
+    host threads and on one thread: the median of three runs each."""
+    import oracle
+    from tiled_dense_gemm_tile_amd import inputs
+    w = inputs.WORKLOADS["square256_bf16"]
+    x = inputs.generate(w)
+    cores = oracle.num_threads()
+    out = {"workload": w.name, "elements": w.M * w.N, "cpu_model": cpu_model()}
+    for key, nt in (("all_threads", cores), ("one_thread", 1)):
+        ts = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            oracle.gemm_ref("bf16", x["A"], x["B"], C=x["C"], nthreads=nt)
+            ts.append(time.perf_counter() - t0)
+        t = sorted(ts)[1]
+        out[key] = {"threads": nt, "seconds": round(t, 5), "TFLOP/s": w.flops / t / 1e12}
+    oracle.gemm_ref("bf16", x["A"][:1], x["B"][:1], nthreads=cores)    # leave the thread count as found
+    return out
 
 
 def main():
@@ -96,6 +134,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="square4096_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="with the default workload, skip the 8192^3 block-scaled fp8 line (secondary)")
     ap.add_argument("--settle", type=float, default=0.3, metavar="SECONDS",
                     help="untimed run of the same step before the warmup steps, so the timed steps "
                          "see the clocks the GPU holds under sustained load (0 disables)")
@@ -131,22 +171,41 @@ def main():
         sys.exit(2)
 
     import torch
-    import tiled_dense_gemm_tile_amd as tg
     from tiled_dense_gemm_tile_amd import inputs
 
-    w = inputs.WORKLOADS[args.workload]
+    primary = measure(inputs.WORKLOADS[args.workload], args, args.a_order, args.b_order, args.splits)
+    res = {"metric": METRIC}
+    res.update(primary)
+    if args.workload == "square4096_bf16" and not args.no_secondary:
+        # the metric's second configuration, timed in the same process the same way
+        torch.cuda.empty_cache()
+        sec = measure(inputs.WORKLOADS["mxfp8_8192"], args, "k", "k", None)
+        res["secondary"] = {k: sec[k] for k in ("value", "unit", "ms_per_step", "dtype", "config", "roofline")
+                            if k in sec}
+        if "cpu_baseline" in sec:
+            res["secondary"]["cpu_baseline"] = sec["cpu_baseline"]
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"]["small_full"] = cpu_small_full()
+    print(json.dumps(res), flush=True)
+
+
+def measure(w, args, a_order, b_order, splits):
+    """Time one workload's step (settle, warmup, then exactly args.steps
+    timed steps) and return the JSON fields that describe it."""
+    import torch
+    import tiled_dense_gemm_tile_amd as tg
+    from tiled_dense_gemm_tile_amd import inputs
     x = inputs.generate(w)
     A, B, C, extra = device_inputs(w, x, torch)
     if w.in_type in ("bf16", "fp16"):
         # MN-contiguous storage: the transposed copy, viewed back as (rows, K)
-        if args.a_order == "mn":
+        if a_order == "mn":
             A = A.t().contiguous().t()
-        if args.b_order == "mn":
+        if b_order == "mn":
             B = B.t().contiguous().t()
     out_dtype = torch.float32 if w.out_type == "f32" else torch.bfloat16
     D = torch.empty((w.M, w.N), dtype=out_dtype, device="cuda:0")
 
-    splits = args.splits
     if splits is None and ((w.M + 255) // 256) * ((w.N + 255) // 256) < 128:
         splits = 0
     kernels_per_step = 1
@@ -220,7 +279,6 @@ def main():
     tflops = w.flops / (kernel_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.in_type]
     res = {
-        "metric": METRIC,
         "value": round(w.flops / (ms_per_step * 1e-3) / 1e12, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -237,18 +295,19 @@ def main():
                    "seed": w.seed, "note": w.note,
                    "splits": None if splits is None else (splits or "auto"),
                    "caches": "cold (512 MiB written before each step)" if args.cold else "warm",
-                   "storage": {"A": "K x M" if args.a_order == "mn" else "M x K",
-                               "B": "K x N" if args.b_order == "mn" else "N x K"}},
+                   "storage": {"A": "K x M" if a_order == "mn" else "M x K",
+                               "B": "K x N" if b_order == "mn" else "N x K"}},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": peak, "unit": "TFLOP/s",
                      "frac": round(tflops / peak, 4), "traffic": measured_traffic(w),
                      "kernel_ms": round(kernel_ms, 5), "kernel_ms_median": round(per_step[len(per_step) // 2], 5),
                      "kernel_ms_min": round(per_step[0], 5), "kernels_per_step": kernels_per_step,
                      "algorithmic_bytes": algorithmic_bytes(w)},
     }
+    del A, B, C, D, extra, step
     if not args.no_cpu_baseline:
         rows = args.cpu_rows or max(1, int(1.3e10 // (w.N * w.K)))
         res["cpu_baseline"] = cpu_baseline(w, x, rows)
-    print(json.dumps(res), flush=True)
+    return res
 
 
 if __name__ == "__main__":

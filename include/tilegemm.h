@@ -65,7 +65,8 @@ typedef enum {
     GEMM_ERR_MISALIGNED = 4,     /* a pointer is not aligned to its element size */
     GEMM_ERR_UNSUPPORTED = 5,    /* valid but outside this library's limits */
     GEMM_ERR_HIP = 6,            /* the HIP runtime reported an error */
-    GEMM_ERR_WORKSPACE = 7       /* a required workspace is NULL or smaller than needed */
+    GEMM_ERR_WORKSPACE = 7,      /* a required workspace is NULL or smaller than needed */
+    GEMM_ERR_SCRATCH_LIMIT = 8   /* gemm_bf16_splitk_noalloc: partials larger than its scratch area */
 } gemm_status;
 
 typedef enum {
@@ -265,6 +266,37 @@ gemm_status gemm_fp16_splitk(int64_t M, int64_t N, int64_t K,
                              void *D, int64_t ldd,
                              int out_type, int splits,
                              void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * gemm_bf16_splitk_noalloc -- gemm_bf16_splitk for callers that cannot
+ * allocate memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same split choice, kernels and
+ * result, bit for bit, with the fp32 partials in a scratch area the library
+ * holds in static device memory instead of a caller workspace.
+ *   - The call allocates nothing (no hipMalloc / hipFree, no allocating
+ *     library routine); the caller still passes A, B, C and D.
+ *   - The scratch area holds gemm_splitk_scratch_limit() bytes (64 MiB) per
+ *     GPU, kept until the process ends; its address is looked up once per
+ *     GPU, on the first call there (the GPU of `stream`; NULL: the current
+ *     device).  A call whose partials, gemm_splitk_workspace_bytes(M, N, K,
+ *     splits), exceed it returns GEMM_ERR_SCRATCH_LIMIT with nothing
+ *     enqueued.  Calls that use no split touch no scratch.
+ *   - Every call on one GPU shares that GPU's area, which keeps whatever the
+ *     last call left there (the partials need no initialisation): calls
+ *     that may overlap on one GPU (different streams without ordering, or
+ *     several host threads) race and give undefined results.
+ * Everything else (splits, layouts, validation, out_type, C == D) is as
+ * gemm_bf16_splitk.
+ */
+gemm_status gemm_bf16_splitk_noalloc(int64_t M, int64_t N, int64_t K,
+                                     const void *A, int64_t lda,
+                                     const void *B, int64_t ldb,
+                                     const void *C, int64_t ldc,
+                                     void *D, int64_t ldd,
+                                     int out_type, int splits, hipStream_t stream);
+
+/* Bytes of gemm_bf16_splitk_noalloc's scratch area per GPU. */
+size_t gemm_splitk_scratch_limit(void);
 
 /*
  * gemm_mxfp8_ex, gemm_mxfp4_ex, gemm_mxfp6_ex -- as gemm_mxfp8 / gemm_mxfp4 /

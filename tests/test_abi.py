@@ -23,10 +23,11 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["gemm_bf16", "gemm_bf16_ex", "gemm_bf16_splitk", "gemm_fp16", "gemm_fp16_ex",
-                                    "gemm_fp16_splitk", "gemm_last_hip_error", "gemm_mxfp4", "gemm_mxfp4_ex", "gemm_mxfp4_splitk",
+    assert declared_functions() == ["gemm_bf16", "gemm_bf16_ex", "gemm_bf16_splitk", "gemm_bf16_splitk_noalloc",
+                                    "gemm_fp16", "gemm_fp16_ex", "gemm_fp16_splitk", "gemm_last_hip_error",
+                                    "gemm_mxfp4", "gemm_mxfp4_ex", "gemm_mxfp4_splitk",
                                     "gemm_mxfp6", "gemm_mxfp6_ex", "gemm_mxfp6_splitk", "gemm_mxfp8",
-                                    "gemm_mxfp8_ex", "gemm_mxfp8_splitk",
+                                    "gemm_mxfp8_ex", "gemm_mxfp8_splitk", "gemm_splitk_scratch_limit",
                                     "gemm_splitk_workspace_bytes", "gemm_status_string"]
 
 
@@ -41,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for s in range(8):
+    for s in range(9):
         assert tg.raw.status_string(s).startswith(tg.STATUS[s])
     assert "unknown" in tg.raw.status_string(99)
     assert tg.raw.gemm_last_hip_error() == 0
@@ -334,3 +335,25 @@ def test_binding_rejects_host_workspace_and_scales():
     with pytest.raises(ValueError):
         tg.gemm_mxfp8(A8, torch.full((8, 2), 127, dtype=torch.uint8), B8,
                       _FakeDevice(torch.full((4, 2), 127, dtype=torch.uint8)), D=D8)
+
+
+def test_noalloc_splitk_validation_and_limit():
+    """The allocation-free split-K entry point validates like gemm_bf16_splitk
+    and refuses partials beyond its static scratch area before any GPU call."""
+    f = tg.raw.gemm_bf16_splitk_noalloc
+    D = P + (1 << 24)
+    call = lambda M=1024, N=1024, K=65536, lda=65536, ldb=65536, splits=16, out=F32, A=P, B=P: \
+        f(M, N, K, A, lda, B, ldb, None, 0, D, N, out, splits, None)
+    assert tg.raw.gemm_splitk_scratch_limit() == 64 << 20
+    assert call(M=-1) == INVALID_SIZE
+    assert call(lda=100) == BAD_LD
+    assert call(A=None) == NULL_POINTER
+    assert call(A=P + 1) == MISALIGNED
+    assert call(splits=65) == UNSUPPORTED
+    assert call(out=3) == UNSUPPORTED
+    assert call(M=0) == OK
+    # 4096 x 4096 in 64 ranges: 4 GiB of partials
+    assert call(M=4096, N=4096, splits=64) == 8
+    assert tg.raw.status_string(8).startswith("GEMM_ERR_SCRATCH_LIMIT")
+    # 1024 x 1024 in 17 ranges: 68 MiB, one range past the 64 MiB area
+    assert call(splits=17) == 8

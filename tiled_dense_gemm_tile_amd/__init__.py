@@ -27,7 +27,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libtilegemm.so")
 
 STATUS = {0: "GEMM_OK", 1: "GEMM_ERR_INVALID_SIZE", 2: "GEMM_ERR_NULL_POINTER", 3: "GEMM_ERR_BAD_LD",
-          4: "GEMM_ERR_MISALIGNED", 5: "GEMM_ERR_UNSUPPORTED", 6: "GEMM_ERR_HIP", 7: "GEMM_ERR_WORKSPACE"}
+          4: "GEMM_ERR_MISALIGNED", 5: "GEMM_ERR_UNSUPPORTED", 6: "GEMM_ERR_HIP", 7: "GEMM_ERR_WORKSPACE",
+          8: "GEMM_ERR_SCRATCH_LIMIT"}
 OUT_F32, OUT_BF16 = 0, 1
 
 
@@ -69,6 +70,10 @@ def _load():
             for name in ("gemm_bf16_splitk", "gemm_fp16_splitk"):
                 f = getattr(L, name)
                 f.restype, f.argtypes = ci, sig16[:-1] + [ci, vp, sz, vp]
+            L.gemm_bf16_splitk_noalloc.restype = ci
+            L.gemm_bf16_splitk_noalloc.argtypes = sig16[:-1] + [ci, vp]
+            L.gemm_splitk_scratch_limit.restype = sz
+            L.gemm_splitk_scratch_limit.argtypes = []
             L.gemm_splitk_workspace_bytes.restype = sz
             L.gemm_splitk_workspace_bytes.argtypes = [i64, i64, i64, ci]
             for name in ("gemm_mxfp8", "gemm_mxfp4"):
@@ -256,6 +261,29 @@ def gemm_fp16_splitk(A, B, C=None, out_dtype=None, D=None, splits=0, workspace=N
     import torch
     return _call16_split("gemm_fp16_splitk", A, B, C, torch.float32 if out_dtype is None else out_dtype, D,
                          torch.float16, splits, workspace)
+
+
+def gemm_bf16_splitk_noalloc(A, B, C=None, out_dtype=None, D=None, splits=0):
+    """:func:`gemm_bf16_splitk` with the partials in the library's static
+    scratch area instead of a workspace: the C call allocates nothing (give
+    ``D`` to keep the whole call allocation-free).  Raises GemmError
+    (GEMM_ERR_SCRATCH_LIMIT) when the partials exceed
+    :func:`splitk_scratch_limit` bytes.  Calls that may overlap on one GPU
+    race on the shared area."""
+    import torch
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    M, N, K, D, stream, out = _prep(A, B, C, D, out_dtype, (torch.bfloat16,))
+    st = _load().gemm_bf16_splitk_noalloc(M, N, K, A.data_ptr(), _ld(A, K) if K else 0, B.data_ptr(),
+                                          _ld(B, K) if K else 0, C.data_ptr() if C is not None else None,
+                                          _ld(C, N) if C is not None else 0, D.data_ptr(), _ld(D, N), out, splits,
+                                          stream)
+    _check(st)
+    return D
+
+
+def splitk_scratch_limit() -> int:
+    """Bytes of the static scratch area behind :func:`gemm_bf16_splitk_noalloc`."""
+    return int(_load().gemm_splitk_scratch_limit())
 
 
 def _scales(SFA, SFB, M, N, A):

@@ -3,6 +3,8 @@
 // helpers.  The declarations and their contract are in include/tilegemm.h.
 #include <stdlib.h>
 
+#include <mutex>
+
 #include "api.hpp"
 #include "f16_launch.hpp"
 
@@ -210,6 +212,60 @@ gemm_status run_f16_splitk(bool fp16, const Common &a, int splits, void *ws, siz
     return reduce_splits(a, ws, S, s);
 }
 
+// ---- split-K with the library's static scratch area --------------------------
+
+// fp32 split partials of gemm_bf16_splitk_noalloc: one copy of this array per
+// GPU, created when the library's code is loaded there and held until the
+// process ends.  In host code the name is only a host-side stand-in for the
+// device symbol; the device address comes from scratch_address().
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+// Device address of the stream's GPU's copy of `scratch`, looked up once per
+// device (hipGetSymbolAddress with that device current) and kept.
+gemm_status scratch_address(hipStream_t s, void **out) {
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return launched(e);
+    if (dev < 0 || dev >= kMaxDevices) return GEMM_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        int cur = 0;
+        e = hipGetDevice(&cur);
+        if (e != hipSuccess) return launched(e);
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return launched(e);
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return launched(e);
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return GEMM_OK;
+}
+
+gemm_status run_bf16_splitk_noalloc(const Common &a, int splits, hipStream_t s) {
+    bool none = false;
+    gemm_status st = validate(a, &none);
+    if (st != GEMM_OK || none) return st;
+    if (splits < 0 || splits > kMaxSplits) return GEMM_ERR_UNSUPPORTED;
+    // the split count and kernel choice of run_f16_splitk
+    const int S = effective_splits(a.K, splits == 0 ? auto_splits(a.M, a.N, a.K) : splits);
+    if (S == 1 || pick_vec(a) < 4) return run_f16(false, a, s);
+    const size_t need = splitk_bytes(a.M, a.N, S);
+    if (need > kScratchBytes) return GEMM_ERR_SCRATCH_LIMIT;
+    void *ws = nullptr;
+    st = scratch_address(s, &ws);
+    if (st != GEMM_OK) return st;
+    return run_f16_splitk(false, a, splits, ws, kScratchBytes, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -259,6 +315,15 @@ gemm_status gemm_fp16_splitk(int64_t M, int64_t N, int64_t K, const void *A, int
     return run_f16_splitk(true, a, splits, workspace, workspace_bytes, stream);
 }
 
+gemm_status gemm_bf16_splitk_noalloc(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B,
+                                     int64_t ldb, const void *C, int64_t ldc, void *D, int64_t ldd, int out_type,
+                                     int splits, hipStream_t stream) {
+    Common a{M, N, K, A, lda, B, ldb, C, ldc, D, ldd, out_type, 2};
+    return run_bf16_splitk_noalloc(a, splits, stream);
+}
+
+size_t gemm_splitk_scratch_limit(void) { return kScratchBytes; }
+
 const char *gemm_status_string(int s) {
     switch (s) {
     case GEMM_OK: return "GEMM_OK";
@@ -269,6 +334,8 @@ const char *gemm_status_string(int s) {
     case GEMM_ERR_UNSUPPORTED: return "GEMM_ERR_UNSUPPORTED: outside the library's limits";
     case GEMM_ERR_HIP: return "GEMM_ERR_HIP: the HIP runtime reported an error";
     case GEMM_ERR_WORKSPACE: return "GEMM_ERR_WORKSPACE: the workspace is missing or too small";
+    case GEMM_ERR_SCRATCH_LIMIT:
+        return "GEMM_ERR_SCRATCH_LIMIT: the split partials exceed the library's static scratch area";
     default: return "unknown gemm_status";
     }
 }

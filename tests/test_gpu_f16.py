@@ -312,13 +312,19 @@ def test_llm_projection_bf16_out(name):
 
 # ---- every kernel configuration ------------------------------------------------------------
 
-N_DMA_CFGS = 16
+# Kernel configurations (csrc/f16_launch.hpp): 0 takes rows only 4- or
+# 8-byte aligned; 1 .. 4 the direct-to-LDS kernels; 5 the four-wave kernel;
+# 6 its shifted-row variant (which takes 16-byte rows too).
+LANE16_CFGS = [1, 2, 3, 4, 5, 6]
+LANE4_CFGS = [0, 1, 2]
+FOUR_WAVE, FOUR_WAVE_SHIFTED = 5, 6
 
 
-@pytest.mark.parametrize("cfg", list(range(N_DMA_CFGS)) + [17, 18, 19, 20])
+@pytest.mark.parametrize("cfg", LANE16_CFGS)
 def test_every_config(cfg, monkeypatch):
-    """Each direct-to-LDS configuration, forced through the tuning override:
-    bit-exact on integers over ragged shapes, within tolerance on random data."""
+    """Each configuration the kernel choice uses, forced through the test
+    override on 16-byte rows: bit-exact on integers over ragged shapes,
+    within tolerance on random data."""
     monkeypatch.setenv("TILEGEMM_F16_CONFIG", str(cfg))
     for (M, N, K) in [(300, 520, 200), (777, 513, 1000), (64, 64, 64)]:
         for integer in (True, False):
@@ -335,7 +341,7 @@ def test_every_config(cfg, monkeypatch):
     assert np.array_equal(bf16_bits(D16), oracle.rne_bf16_f32(D32.cpu().numpy()))
 
 
-@pytest.mark.parametrize("cfg", [3, 6, 7])
+@pytest.mark.parametrize("cfg", LANE4_CFGS)
 @pytest.mark.parametrize("pad", [2, 4])
 def test_lane4_configs(cfg, pad, monkeypatch):
     """Rows only 4- or 8-byte aligned (leading dimension K + pad) take the
@@ -354,7 +360,7 @@ def test_lane4_configs(cfg, pad, monkeypatch):
             _full_check(in_type, x, to_f64(D), integer, C)
 
 
-@pytest.mark.parametrize("cfg", [1, 3, 6, 8, 9, 10, 11, 12, 13, 14, 15, 17, 18, 19, 20])
+@pytest.mark.parametrize("cfg", LANE16_CFGS)
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 def test_c_streamed_in_k_loop(cfg, out, monkeypatch):
     """K long enough (>= 34 tiles of 64) that C is added during the K loop
@@ -362,10 +368,9 @@ def test_c_streamed_in_k_loop(cfg, out, monkeypatch):
     monkeypatch.setenv("TILEGEMM_F16_CONFIG", str(cfg))
     M = 300
     cases = [(520, 2304)]
-    if cfg in (12, 13, 14, 15):
-        # the stream's threshold (20 K tiles with a two-slot B ring, 21 with
-        # three), a ragged K with the stream, and N % 4 != 0 (C added in the
-        # epilogue)
+    if cfg in (FOUR_WAVE, FOUR_WAVE_SHIFTED):
+        # the stream's threshold (20 K tiles), a ragged K with the stream,
+        # and N % 4 != 0 (C added in the epilogue)
         cases += [(520, 1344), (520, 1280), (520, 1216), (520, 1300), (518, 2304)]
     for N, K, integer in [(n, k, i) for (n, k) in cases for i in (True, False)]:
         x, C = _case("bf16", M, N, K, seed=cfg * 7 + (out == "bf16"), integer=integer)
@@ -390,16 +395,37 @@ def test_c_streamed_in_k_loop(cfg, out, monkeypatch):
             assert torch.equal(D, inplace)
 
 
+@pytest.mark.parametrize("cfg", [None, FOUR_WAVE, FOUR_WAVE_SHIFTED, 1, 3])
+@pytest.mark.parametrize("K,pad", [(100, 4), (200, 8), (72, 16), (4100, 4), (36, 60)])
+def test_nan_past_k_never_reaches_d(cfg, K, pad, monkeypatch):
+    """Rows padded past K with NaN codes: the kernels load whole chunks and
+    clear what lies past K in LDS, so no padding value may reach D (a NaN
+    times a zero would).  Integer inputs, every element exact."""
+    if cfg is not None:
+        monkeypatch.setenv("TILEGEMM_F16_CONFIG", str(cfg))
+    M, N = 300, 520
+    ld = K + pad
+    if cfg in (FOUR_WAVE, 1, 3) and ld % 8:
+        pytest.skip("16-byte rows only")
+    x, C = _case("bf16", M, N, K, seed=K + pad, integer=True)
+    Ab = np.full((M, ld), 0x7FC0, np.uint16); Ab[:, :K] = x["A"]
+    Bb = np.full((N, ld), 0x7FC0, np.uint16); Bb[:, :K] = x["B"]
+    say("NaN past K cfg %s K %d ld %d" % (cfg, K, ld))
+    D = run16("bf16", dev16(Ab, "bf16")[:, :K], dev16(Bb, "bf16")[:, :K], torch.from_numpy(C).to(DEV))
+    torch.cuda.synchronize()
+    _full_check("bf16", x, to_f64(D), True, C)
+
+
 # ---- rows only 8-byte aligned: the shifted-row four-wave kernel ---------------------------
 
-N_SHIFTED_CFG = 16
+N_SHIFTED_CFG = FOUR_WAVE_SHIFTED
 
 
 @pytest.mark.parametrize("case", [
     # M, N, K, pad (lda = ldb = K + pad), element offset of A and B, C, output
-    (520, 300, 4100, 0, 0, True, "f32"),     # packed 8-byte rows, ragged last K tile (fix-up)
+    (520, 300, 4100, 0, 0, True, "f32"),     # packed 8-byte rows, ragged last K tile (past K cleared)
     (300, 520, 4100, 0, 4, True, "f32"),     # operands start 8 bytes past a 16-byte boundary
-    (257, 260, 36, 0, 0, True, "f32"),       # one ragged K tile (fix-up in the prologue)
+    (257, 260, 36, 0, 0, True, "f32"),       # one ragged K tile (cleared in the prologue)
     (257, 260, 100, 4, 0, False, "f32"),     # two K tiles, padded rows
     (256, 256, 320, 4, 4, True, "f32"),      # K a multiple of 64, 8-byte rows
     (300, 520, 2308, 0, 0, True, "f32"),     # C streamed in the K loop

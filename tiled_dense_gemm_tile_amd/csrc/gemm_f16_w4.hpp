@@ -1,25 +1,13 @@
-// Four-wave schedule for D = A.B + C with 16-bit inputs whose rows are
-// 16-byte aligned (K a multiple of 8), gfx950.
+// Four-wave kernel for D = A.B + C with 16-bit inputs, gfx950: the default
+// for grids of at least half a wave of 256 x 256 output tiles.
 //
 // The workgroup computes a 256 x 256 output tile with 4 waves, one per SIMD,
 // each owning a 128 x 128 quadrant as 8 x 8 blocks of 16 x 16 accumulators
 // (v_mfma_f32_16x16x32: 256 accumulator registers per lane).  Large wave
-// tiles keep LDS traffic low: per 32-wide K slab each wave reads 16 KiB of
-// fragments (64 KiB for the workgroup) against 32 KiB of tile data written
-// by the direct global->LDS loads, and the 16x16 MFMA form draws less power
-// per flop than 32x32, so the clock holds higher under load.
-//
-// K advances in slabs of 32 (one MFMA step).  A and B each have a ring of NS
-// LDS slots of 256 rows x 64 bytes.  In iteration s a wave
-//   - issues the 64 MFMAs of slab s from fragments already in registers,
-//   - reads slab s + 1's fragments into the other register buffer,
-//   - issues its quarter of the global->LDS loads of slab s + NS into the
-//     slot slab s used (every wave finished reading it before the barrier
-//     that opened iteration s),
-// then waits until its own loads of slab s + 2 have landed and joins the
-// barrier that opens iteration s + 1.  A slab's loads thus have NS - 1
-// iterations to land.  Loads past K read nothing (out-of-range offsets give
-// zeros) so the wait counts stay fixed to the end.
+// tiles keep LDS traffic low (per 64-wide K tile each wave reads 32 KiB of
+// fragments against 64 KiB of tile data written by the direct global->LDS
+// loads), and the 16x16 MFMA form draws less power per flop than 32x32, so
+// the clock holds higher under load.
 #pragma once
 
 #include <type_traits>
@@ -69,161 +57,19 @@ __device__ __forceinline__ void mfma_result_fence(f32x4 (&acc)[TM][TN]) {
     }
 }
 
-// 64-byte LDS rows (four 16-byte chunks): logical chunk c of row r sits at
-// physical chunk c ^ ((r >> 2) & 3).  A 16x16x32 fragment read has each
-// group of 16 lanes read one chunk of 16 consecutive rows; rows r and r + 4
-// share banks, and the swizzle gives those four rows four different chunks,
-// so every 16-lane (and 8-lane) group hits distinct banks.
-__device__ __forceinline__ int swz64(int r) { return (r >> 2) & 3; }
-
-template <int NS, bool FP16, bool OUT_BF16>
-__global__ void __launch_bounds__(256) gemm_f16_w4_kernel(F16Args p, F16Epi e) {
-    constexpr int BM = 256, BN = 256, KS = 32;         // tile and K slab
-    constexpr int WTM = 128, WTN = 128, TM = 8, TN = 8;
-    constexpr int ROWB = KS * 2;                       // 64-byte LDS rows
-    constexpr int SLOT = 256 * ROWB;                   // 16 KiB per operand slot
-    constexpr int B_BASE = NS * SLOT;
-    constexpr int RING_BYTES = 2 * NS * SLOT;
-    constexpr int EPI_BYTES = 4 * 32 * (WTN + 8) * 4;
-    constexpr int LDS_BYTES = RING_BYTES > EPI_BYTES ? RING_BYTES : EPI_BYTES;
-    constexpr int IB = 1024;                           // one load instruction: 16 rows
-    constexpr int LPS = 4;                             // load instructions per wave per operand per slab
-    constexpr int WAIT_N = (NS - 2) * 2 * LPS;         // loads still in flight at a barrier
-    static_assert(NS >= 3 && LDS_BYTES <= 160 * 1024 && WAIT_N < 64, "ring");
-
-    __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
-    int tmi, tni;
-    tile_order(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, tmi, tni);
-    const int m0 = tmi * BM, n0 = tni * BN;
-    const int M = p.M, N = p.N, K = p.K;
-
-    const __amdgpu_buffer_rsrc_t rA =
-        make_rsrc((const char *)p.A + (int64_t)m0 * p.lda * 2, span_bytes(M - m0, K, p.lda, 2));
-    const __amdgpu_buffer_rsrc_t rB =
-        make_rsrc((const char *)p.B + (int64_t)n0 * p.ldb * 2, span_bytes(N - n0, K, p.ldb, 2));
-
-    // Load instruction j of a wave fills slot rows (4 j + wave) * 16 + lane / 4:
-    // lane L writes physical chunk L % 4 and fetches logical chunk
-    // (L % 4) ^ swz64(row) = (L % 4) ^ ((L / 16) % 4), the same for every j.
-    const int chunk = (lane & 3) ^ ((lane >> 4) & 3);
-    const int kel = chunk * 8;
-    uint32_t a_off[LPS], b_off[LPS];
-#pragma unroll
-    for (int j = 0; j < LPS; ++j) {
-        const int row = (4 * j + wave) * 16 + (lane >> 2);
-        a_off[j] = (uint32_t)(row * p.lda * 2) + chunk * 16;
-        b_off[j] = (uint32_t)(row * p.ldb * 2) + chunk * 16;
-    }
-    // Load k (0..7) of this wave for slab sl: k < 4 is A instruction k, else B.
-    auto dma = [&](int sl, int k) {
-        const int k0 = sl * KS;
-        const uint32_t oob = (uint32_t)(k0 + kel >= K) << 31;   // offsets stay below 2^31
-        char *d = smem + (sl % NS) * SLOT + (k >= LPS ? B_BASE : 0) + ((k % LPS) * 4 + wave) * IB;
-        const uint32_t off = ((k < LPS ? a_off[k % LPS] : b_off[k % LPS]) + (uint32_t)k0 * 2) | oob;
-        dma_load<16>(k < LPS ? rA : rB, d, off);
-    };
-
-    // Fragment reads: lane l reads row l % 16 of each block, chunk l / 16.
-    const int fr = lane & 15, fq = lane >> 4;
-    const int coff = (fq ^ swz64(fr)) << 4;            // the same for every block (16 rows apart)
-    const int a_read = (wm * WTM + fr) * ROWB + coff;
-    const int b_read = B_BASE + (wn * WTN + fr) * ROWB + coff;
-
-    // The accumulators live in AGPRs and every MFMA updates its block in
-    // place (tied asm operand), so the register allocator never moves them.
-    // The asm is volatile and a scheduling barrier follows each MFMA, so
-    // MFMAs, LDS reads, global->LDS loads and their address arithmetic issue
-    // in source order: nothing is hoisted in front of a slab's first MFMA.
-    f32x4 acc[TM][TN];
-    u32x4 fa[2][TM], fb[2][TN];
-    auto read_frag = [&](int buf, int sl, int k) {     // k < 8: A block k, else B block k - 8
-        const char *s0 = smem + (sl % NS) * SLOT;
-        if (k < TM)
-            fa[buf][k] = *(const u32x4 *)(s0 + a_read + k * 16 * ROWB);
-        else
-            fb[buf][k - TM] = *(const u32x4 *)(s0 + b_read + (k - TM) * 16 * ROWB);
-    };
-    auto slab_end = [&]() {
-        wait_vmcnt<WAIT_N>();
-        wait_lgkmcnt0();
-        barrier();
-    };
-    // Slab sl: its 64 MFMAs on fragment buffer buf; after every second of the
-    // first 32 MFMAs one fragment read of slab sl + 1 into buf ^ 1, and after
-    // every fourth of MFMAs 28..56 one load of slab sl + NS.  FIRST: the
-    // accumulators start from zero (the MFMA's C operand is the constant 0).
-    auto iteration = [&](auto first, int buf, int sl) {
-#pragma unroll
-        for (int q = 0; q < TM * TN; ++q) {
-            const int i = q / TN, j = q % TN;
-            if constexpr (decltype(first)::value)
-                mfma16_zero_asm<FP16>(acc[i][j], fa[buf][i], fb[buf][j]);
-            else
-                mfma16_acc_asm<FP16>(acc[i][j], fa[buf][i], fb[buf][j]);
-            __builtin_amdgcn_sched_barrier(0);
-            if (q % 2 == 1 && q / 2 < TM + TN) read_frag(buf ^ 1, sl + 1, q / 2);
-            if (q >= 28 && q % 4 == 0 && (q - 28) / 4 < 2 * LPS) dma(sl + NS, (q - 28) / 4);
-        }
-        slab_end();
-    };
-
-    const int ns = (K + KS - 1) / KS;
-    if (ns > 0) {
-#pragma unroll
-        for (int q = 0; q < NS; ++q)                   // slabs 0 .. NS-1
-#pragma unroll
-            for (int k = 0; k < 2 * LPS; ++k) dma(q, k);
-        wait_vmcnt<(NS - 1) * 2 * LPS>();              // slab 0 landed
-        barrier();
-#pragma unroll
-        for (int k = 0; k < TM + TN; ++k) read_frag(0, 0, k);
-        slab_end();                                    // slab 1 landed, slab 0 fragments in registers
-        iteration(std::true_type(), 0, 0);
-        // Slabs in pairs: with ns even the last pass multiplies the all-zero
-        // slab ns (loaded out of range) and adds nothing.
-        for (int s = 1; s < ns; s += 2) {
-            iteration(std::false_type(), 1, s);
-            iteration(std::false_type(), 0, s + 1);
-        }
-        // The epilogue reads the accumulators with VALU instructions; the
-        // compiler cannot see that they were last written by MFMAs, so wait
-        // out that hazard here, ahead of every accumulator use.
-        mfma_result_fence<TM, TN>(acc);
-    } else {
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    }
-
-    wait_vmcnt<0>();
-    wait_lgkmcnt0();
-    barrier();
-    epilogue_lds16<OUT_BF16, TM, TN, WTM, WTN>(acc, smem, wave, lane, wm, wn, m0, n0, M, N, p.C, p.ldc, p.D, p.ldd, e);
-}
-
-
-// The same four-wave, 128 x 128-per-wave layout with 64-wide K tiles:
-// 128-byte LDS rows, so every global->LDS load instruction moves whole
-// 128-byte lines (8 rows of a tile), and rings of NA slots for A and NB for
-// B (32 KiB a slot).  Per tile a wave issues 128 MFMAs in two K steps of
-// 32.  Half of the second step's MFMAs are issued after the barrier that
-// opens the next tile, while that tile's first fragments are read, so the
-// matrix pipe does not drain at the barrier:
-//   after barrier t:  MFMAs of tile t-1 step 1 (blocks i = 4..7)
-//                     + fragment reads of tile t step 0 + loads of A(t+NA-1)
-//                     MFMAs of tile t step 0
-//                     + fragment reads of tile t step 1 + loads of B(t+NB-1)
-//                     MFMAs of tile t step 1 (blocks i = 0..3)
+// K tiles are 64 wide: 128-byte LDS rows, so every global->LDS load
+// instruction moves whole 128-byte lines (8 rows of a tile); A and B each
+// have two ring slots of 32 KiB.  Per tile a wave issues 128 MFMAs in two K
+// steps of 32, and the second step of tile t-1 runs after the barrier that
+// opens tile t, so the matrix pipe does not drain at the barrier:
+//   after barrier t:  the 64 MFMAs of tile t-1 step 1, with the fragment
+//                     reads of tile t step 0 (one per 4 MFMAs) and the loads
+//                     of A(t+1), B(t+1) (one per 4 MFMAs)
+//                     the 64 MFMAs of tile t step 0, with the fragment reads
+//                     of tile t step 1 (one per 3 MFMAs)
 //                     wait for A(t+1), B(t+1); barrier t+1
-// A tile's slots are read only between its own two barriers, so the loads
-// of A(t+NA-1) and B(t+NB-1) go to slots freed at barrier t; A has one
-// tile of time to land, B (with NB = NA + 1) two.
+// A tile's slots are read only between its own barrier and the next one, so
+// the loads of tile t+1 go to the slots tile t-1 used, freed at barrier t.
 //
 // With C given and at least 18 K tiles, C is streamed into the accumulators
 // during the first 18 tiles and the epilogue only writes D.  Those tiles are
@@ -275,9 +121,10 @@ constexpr int tr_row_wait(int i) {
     return n > 15 ? 15 : n;
 }
 
-template <int NA, int NB, bool FP16, bool OUT_BF16, int SCHED = 0, int DAUX = kStoreStream, bool SH = false,
-          bool SPLIT = false, bool AT = false, bool BT = false>
+template <bool FP16, bool OUT_BF16, bool SH = false, bool SPLIT = false, bool AT = false, bool BT = false>
 __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) {
+    constexpr int NA = 2, NB = 2;                      // ring slots of A and B
+    constexpr int DAUX = kStoreStream;                 // D store policy
     constexpr int BM = 256, BN = 256, KT = 64;         // tile
     constexpr int WTM = 128, WTN = 128, TM = 8, TN = 8;
     // SH: rows only 8-byte aligned (see the row layout below): 144-byte rows
@@ -289,11 +136,9 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
     constexpr int LDS_BYTES = RING_BYTES > EPI_BYTES ? RING_BYTES : EPI_BYTES;
     constexpr int IB = 1024;                           // one load instruction: 8 rows
     constexpr int LPT = SH ? 9 : 8;                    // load instructions per wave per operand per tile
-    constexpr int WAIT_N = (NB - NA) * LPT;            // B loads still in flight at a barrier
-    static_assert(NA == 2 && (NB == 2 || NB == 3) && LDS_BYTES <= 160 * 1024, "ring");
-    static_assert(!SH || (NB == 2 && SCHED == 1), "shifted rows: balanced schedule, two B slots");
+    static_assert(LDS_BYTES <= 160 * 1024, "ring");
     static_assert(!SPLIT || !OUT_BF16, "split-K partial tiles are fp32");
-    static_assert(!(AT || BT) || (!SH && !SPLIT && SCHED == 1 && NB == 2), "MN-contiguous operands: 16-byte rows");
+    static_assert(!(AT || BT) || (!SH && !SPLIT), "MN-contiguous operands: 16-byte rows");
 
     __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
 
@@ -362,28 +207,22 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
     }
     // SH: K element (relative to the tile's K offset) at which chunk c of
     // row r starts: 8 c - (s % 16) / 2, i.e. -4 for the first chunk of a
-    // shifted row.  A chunk reaching past K is read as zeros (a partly
-    // out-of-range load is never issued); if its first half is valid, the
-    // ragged tile's fix-up writes that half afterwards.
+    // shifted row.
     auto sh_kel = [&](int mis0, int64_t ld, int j) __attribute__((always_inline)) {
         const int s_ = mis0 + sh_row(j) * (int)ld * 2;
         return 8 * sh_chk(j) - ((s_ & 15) >> 1);
     };
-    // Loads of K tile t.  SO: the tile is wholly inside K or wholly past it,
-    // so the K offset is uniform and goes in the scalar offset (bit 31 set
-    // past K: every lane reads zeros) and no vector instruction is spent per
-    // load; otherwise (the tile holding a ragged end of K) each lane adds the
-    // K offset and sets bit 31 itself when its chunk lies past K.
-    auto dma = [&](auto so, __amdgpu_buffer_rsrc_t r, char *d, uint32_t voff, int t, int kelj) __attribute__((always_inline)) {
+    // Loads of K tile t: whole 16-byte chunks, the K offset in the scalar
+    // offset (no vector instruction per load).  The last tile reads past K
+    // (into the next row, or zeros past the resource) and clear_past_k then
+    // zeroes those bytes in LDS; tiles past K are read through a resource of
+    // size zero, which returns zeros.
+    const __amdgpu_buffer_rsrc_t rZ = make_rsrc(p.D, 0u);
+    auto dma = [&](__amdgpu_buffer_rsrc_t r, char *d, uint32_t voff, int t) __attribute__((always_inline)) {
         const int k0 = t * KT;
-        if constexpr (decltype(so)::value) {
-            const int sk = __builtin_amdgcn_readfirstlane((k0 * 2) | ((int)(k0 >= K) << 31));
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)d, 16, voff, sk, 0, 0);
-        } else {
-            const uint32_t oob = (uint32_t)(SH ? k0 + kelj + 8 > K : k0 + kelj >= K) << 31;   // offsets stay below 2^31
-            const uint32_t off = (voff + (uint32_t)k0 * 2) | oob;
-            dma_load<16>(r, d, off);
-        }
+        const __amdgpu_buffer_rsrc_t rr = k0 < K ? r : rZ;
+        const int sk = __builtin_amdgcn_readfirstlane(k0 * 2);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rr, (__attribute__((address_space(3))) void *)d, 16, voff, sk, 0, 0);
     };
     // MN-contiguous operand, K tile t: a resource based at row 64 t, column
     // e0 of the K x (M or N) storage, ending with the 16-byte block that
@@ -399,51 +238,43 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
         const __amdgpu_buffer_rsrc_t r = make_rsrc((const char *)base + ((int64_t)k0 * ld + e0) * 2, span);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)d, 16, voff, 0, 0, 0);
     };
-    auto dma_a = [&](auto so, int t, int j) __attribute__((always_inline)) {
+    auto dma_a = [&](int t, int j) __attribute__((always_inline)) {
         char *d = smem + (t % NA) * SLOT + (j * 4 + wave) * IB;
-        if constexpr (AT) {
+        if constexpr (AT)
             dma_mn(p.A, p.lda, m0, M, d, a_off[j], t);
-        } else {
-            const int kelj = SH ? sh_kel(a_mis0, p.lda, j) : kel;
-            dma(so, rA, d, a_off[j], t, kelj);
-        }
+        else
+            dma(rA, d, a_off[j], t);
     };
-    auto dma_b = [&](auto so, int t, int j) __attribute__((always_inline)) {
+    auto dma_b = [&](int t, int j) __attribute__((always_inline)) {
         char *d = smem + B_BASE + (t % NB) * SLOT + (j * 4 + wave) * IB;
-        if constexpr (BT) {
+        if constexpr (BT)
             dma_mn(p.B, p.ldb, n0, N, d, b_off[j], t);
-        } else {
-            const int kelj = SH ? sh_kel(b_mis0, p.ldb, j) : kel;
-            dma(so, rB, d, b_off[j], t, kelj);
-        }
+        else
+            dma(rB, d, b_off[j], t);
     };
-    // SH, last K tile nt - 1 (after its loads landed, before the barrier
-    // that publishes it): each chunk whose first half is inside K and second
-    // half past it was read as zeros; load its valid 8 bytes with an in-range
-    // 8-byte load and write them into the chunk's first half.  Such chunks
-    // exist whether or not K is a multiple of 64 (the ninth chunk of a row
-    // shifted by 8 bytes ends 4 elements past its tile).
-    auto sh_fixup = [&](int t) __attribute__((always_inline)) {
-        const int k0 = t * KT;
-        u32x2 v[2 * LPT];
+    // Last K tile t (after this lane's loads of it landed, before the
+    // barrier that publishes it): the lane zeroes what its own direct-to-LDS
+    // loads brought from past K -- whole chunks past K, and with SH the
+    // second half of a chunk that straddles K (K % 4 == 0, so a chunk holds
+    // 0, 4 or 8 elements inside K).  MN-contiguous operands read zeros past
+    // K already.
+    auto clear_past_k = [&](int t) __attribute__((always_inline)) {
+        const int kr = K - t * KT;                     // elements of the tile inside K
+        if (kr >= KT) return;
+        auto clear = [&](char *d, int inside) __attribute__((always_inline)) {
+            if (inside <= 0)
+                *(u32x4 *)d = u32x4{0u, 0u, 0u, 0u};
+            else if (inside < 8)
+                *(u32x2 *)(d + 8) = u32x2{0u, 0u};
+        };
 #pragma unroll
-        for (int j = 0; j < 2 * LPT; ++j) {
-            const bool isb = j >= LPT;
-            const int jj = isb ? j - LPT : j;
-            const int kelj = isb ? sh_kel(b_mis0, p.ldb, jj) : sh_kel(a_mis0, p.lda, jj);
-            const bool half = kelj >= 0 && k0 + kelj + 4 <= K && k0 + kelj + 8 > K;
-            const uint32_t off = half ? (isb ? b_off[jj] : a_off[jj]) + (uint32_t)k0 * 2 : kOOB;
-            v[j] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(isb ? rB : rA, off, 0, 0));
-        }
-        wait_vmcnt<0>();
-#pragma unroll
-        for (int j = 0; j < 2 * LPT; ++j) {
-            const bool isb = j >= LPT;
-            const int jj = isb ? j - LPT : j;
-            const int kelj = isb ? sh_kel(b_mis0, p.ldb, jj) : sh_kel(a_mis0, p.lda, jj);
-            const bool half = kelj >= 0 && k0 + kelj + 4 <= K && k0 + kelj + 8 > K;
-            char *d = smem + (isb ? B_BASE + (t % NB) * SLOT : (t % NA) * SLOT) + (jj * 4 + wave) * IB + lane * 16;
-            if (half) *(u32x2 *)d = v[j];
+        for (int j = 0; j < LPT; ++j) {
+            if constexpr (!AT)
+                clear(smem + (t % NA) * SLOT + (j * 4 + wave) * IB + lane * 16,
+                      kr - (SH ? sh_kel(a_mis0, p.lda, j) : kel));
+            if constexpr (!BT)
+                clear(smem + B_BASE + (t % NB) * SLOT + (j * 4 + wave) * IB + lane * 16,
+                      kr - (SH ? sh_kel(b_mis0, p.ldb, j) : kel));
         }
         wait_lgkmcnt0();
     };
@@ -576,97 +407,54 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
     // One tile; FIRST: no previous tile (no deferred MFMAs, accumulators
     // start from zero).  LP: the C part this tile loads (-1: none); AP: the
     // C part it adds (-1: none); SO: the K tiles it loads are whole.
-    auto tile = [&](auto first, auto lp, auto ap, auto so, int t) __attribute__((always_inline)) {
+    auto tile = [&](auto first, auto lp, auto ap, int t) __attribute__((always_inline)) {
         constexpr int LP = decltype(lp)::value, AP = decltype(ap)::value;
-        if constexpr (SCHED == 1) {
-            // Balanced: the whole step 1 of tile t-1 runs after barrier t
-            // while step 0 of tile t is read (one read per 4 MFMAs), then
-            // step 0 of tile t while step 1 is read (one per 3).  NB = 2: A
-            // and B of tile t+1 load in the first half (one per 4 MFMAs);
-            // NB = 3: A(t+1) in the first half, B(t+2) and C in the second.
-            // Block b gets its C at slot (b + 32) % 64 of the first half,
-            // 32 MFMAs from its updates on either side.
-#pragma unroll
-            for (int q = 0; q < 64; ++q) {
-                if constexpr (!decltype(first)::value) mfma(std::false_type(), 1, q / TN, q % TN);
-                if (q % 4 == 0) read_frag(t, 0, q / 4);
-                if constexpr (SH) {
-                    if (q % 7 == 1 && q / 7 < LPT) dma_a(so, t + 1, q / 7);
-                    if (q % 7 == 4 && q / 7 < LPT) dma_b(so, t + 1, q / 7);
-                } else if constexpr (NB == 3) {
-                    if (q % 8 == 2) dma_a(so, t + 1, q / 8);
-                } else {
-                    if (q % 8 == 2) dma_a(so, t + 1, q / 8);
-                    if (q % 8 == 6) dma_b(so, t + 1, q / 8);
-                }
-                if constexpr (AP >= 0) {
-                    constexpr int s0 = (4 * AP + 32) % 64;
-                    if (q >= s0 && q < s0 + 4) add_c(AP, q - s0);
-                }
-            }
-#pragma unroll
-            for (int q = 0; q < 64; ++q) {
-                if constexpr (AT || BT) {
-                    constexpr int CA = AT ? 2 : 1, CB = BT ? 2 : 1;
-                    if (q % TN == 0) {
-                        switch (q / TN) {
-#define TG_TR_WAIT(i) \
-    case i: __builtin_amdgcn_s_waitcnt(0xC07F | (tr_row_wait<CA, CB>(i) << 8)); break;
-                            TG_TR_WAIT(0) TG_TR_WAIT(1) TG_TR_WAIT(2) TG_TR_WAIT(3)
-                            TG_TR_WAIT(4) TG_TR_WAIT(5) TG_TR_WAIT(6) TG_TR_WAIT(7)
-#undef TG_TR_WAIT
-                        }
-                    }
-                }
-                mfma(first, 0, q / TN, q % TN);
-                if (q % 3 == 0 && q / 3 < 16) read_frag(t, 1, q / 3);
-                if constexpr (NB == 3) {
-                    if (q % 8 == 2) dma_b(so, t + 2, q / 8);
-                }
-                if constexpr (LP >= 0) {
-                    if (q % 16 == 6) load_c(LP, q / 16);
-                }
-            }
-            wait_vmcnt<WAIT_N + (LP >= 0 ? 4 : 0)>();
-            wait_lgkmcnt0();
-            if constexpr (SH && !decltype(so)::value) {
-                if (t + 1 == nt - 1) sh_fixup(t + 1);
-            }
-            barrier();
-            return;
-        }
-        // step 1 of tile t-1, blocks i = 4..7, with tile t step 0 reads and A loads
-#pragma unroll
-        for (int q = 0; q < 32; ++q) {
-            if constexpr (!decltype(first)::value) mfma(std::false_type(), 1, 4 + q / TN, q % TN);
-            if (q % 2 == 0) read_frag(t, 0, q / 2);
-            if (q % 4 == 1) dma_a(so, t + NA - 1, q / 4);
-            if constexpr (AP >= 0 && AP < CPARTS / 2) {
-                if (q >= 16 && q < 20) add_c(AP, q - 16);       // blocks of rows 0..63
-            }
-        }
-        // step 0 of tile t, with step 1 reads (first half) and B loads (second half)
+        // The whole step 1 of tile t-1 runs after barrier t while step 0 of
+        // tile t is read (one read per 4 MFMAs) and A(t+1), B(t+1) are
+        // loaded, then step 0 of tile t while step 1 is read (one per 3).
+        // Block b gets its C at slot (b + 32) % 64 of the first half, 32
+        // MFMAs from its updates on either side.
 #pragma unroll
         for (int q = 0; q < 64; ++q) {
-            mfma(first, 0, q / TN, q % TN);
-            if (q % 2 == 1 && q < 32) read_frag(t, 1, q / 2);
-            if (q % 4 == 1 && q >= 32) dma_b(so, t + NB - 1, (q - 32) / 4);
-            if constexpr (AP >= CPARTS / 2) {
-                if (q >= 16 && q < 20) add_c(AP, q - 16);       // blocks of rows 64..127
+            if constexpr (!decltype(first)::value) mfma(std::false_type(), 1, q / TN, q % TN);
+            if (q % 4 == 0) read_frag(t, 0, q / 4);
+            if constexpr (SH) {
+                if (q % 7 == 1 && q / 7 < LPT) dma_a(t + 1, q / 7);
+                if (q % 7 == 4 && q / 7 < LPT) dma_b(t + 1, q / 7);
+            } else {
+                if (q % 8 == 2) dma_a(t + 1, q / 8);
+                if (q % 8 == 6) dma_b(t + 1, q / 8);
+            }
+            if constexpr (AP >= 0) {
+                constexpr int s0 = (4 * AP + 32) % 64;
+                if (q >= s0 && q < s0 + 4) add_c(AP, q - s0);
             }
         }
-        // step 1 of tile t, blocks i = 0..3, with the loads of C part LP
 #pragma unroll
-        for (int q = 0; q < 32; ++q) {
-            mfma(std::false_type(), 1, q / TN, q % TN);
+        for (int q = 0; q < 64; ++q) {
+            if constexpr (AT || BT) {
+                constexpr int CA = AT ? 2 : 1, CB = BT ? 2 : 1;
+                if (q % TN == 0) {
+                    switch (q / TN) {
+#define TG_TR_WAIT(i) \
+    case i: __builtin_amdgcn_s_waitcnt(0xC07F | (tr_row_wait<CA, CB>(i) << 8)); break;
+                        TG_TR_WAIT(0) TG_TR_WAIT(1) TG_TR_WAIT(2) TG_TR_WAIT(3)
+                        TG_TR_WAIT(4) TG_TR_WAIT(5) TG_TR_WAIT(6) TG_TR_WAIT(7)
+#undef TG_TR_WAIT
+                    }
+                }
+            }
+            mfma(first, 0, q / TN, q % TN);
+            if (q % 3 == 0 && q / 3 < 16) read_frag(t, 1, q / 3);
             if constexpr (LP >= 0) {
-                if (q % 8 == 1) load_c(LP, q / 8);
+                if (q % 16 == 6) load_c(LP, q / 16);
             }
         }
-        // A(t+1), B(t+1) landed; B(t+NB-1) and this tile's C loads (one per
-        // block of the part) may still run
-        wait_vmcnt<WAIT_N + (LP >= 0 ? 4 : 0)>();
+        // A(t+1), B(t+1) landed; this tile's C loads (one per block of the
+        // part) may still run
+        wait_vmcnt<(LP >= 0 ? 4 : 0)>();
         wait_lgkmcnt0();
+        if (t + 1 == nt - 1) clear_past_k(t + 1);
         barrier();
     };
     // tiles 1 .. CPARTS + 1 of the C stream, unrolled: tile t loads part t
@@ -675,53 +463,35 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
         constexpr int T = decltype(tc)::value;
         if constexpr (T <= CPARTS + 1) {
             tile(std::false_type(), std::integral_constant<int, (T < CPARTS ? T : -1)>(),
-                 std::integral_constant<int, T - 2>(), std::true_type(), T);
+                 std::integral_constant<int, T - 2>(), T);
             self(self, std::integral_constant<int, T + 1>());
         }
     };
 
     if (nt > 0) {
-        // A(0); B(0) .. B(NB-2): the loads the first tiles' iterations do not issue
+        // A(0), B(0): the loads the first tile's iteration does not issue
 #pragma unroll
-        for (int j = 0; j < LPT; ++j) dma_a(std::false_type(), 0, j);
+        for (int j = 0; j < LPT; ++j) dma_a(0, j);
 #pragma unroll
-        for (int b = 0; b < NB - 1; ++b)
-#pragma unroll
-            for (int j = 0; j < LPT; ++j) dma_b(std::false_type(), b, j);
-        wait_vmcnt<(NB - 2) * LPT>();                  // A(0), B(0) landed
-        if constexpr (SH) {
-            if (nt == 1) sh_fixup(0);
-        }
+        for (int j = 0; j < LPT; ++j) dma_b(0, j);
+        wait_vmcnt<0>();                               // A(0), B(0) landed
+        if (nt == 1) clear_past_k(0);
         barrier();
         using none = std::integral_constant<int, -1>;
         using yes = std::true_type;
         using no = std::false_type;
-        // Tile t loads K tiles up to t + NB - 1; only the last K tile can be
-        // ragged, so tiles 0 .. nt - NB - 1 take scalar-offset loads and the
-        // last NB tiles the per-lane form.
-        if (nt > NB) {
-            int t0 = 1;
-            if (c_loop) {
-                tile(yes(), std::integral_constant<int, 0>(), none(), yes(), 0);   // loads C part 0
-                c_tiles(c_tiles, std::integral_constant<int, 1>());               // tiles 1 .. CPARTS + 1
-                t0 = CPARTS + 2;
-            } else {
-                tile(yes(), none(), none(), yes(), 0);
-            }
-            for (int t = t0; t < nt - NB; ++t) tile(no(), none(), none(), yes(), t);
-            for (int t = nt - NB; t < nt; ++t) tile(no(), none(), none(), no(), t);
+        int t0 = 1;
+        if (c_loop) {
+            tile(yes(), std::integral_constant<int, 0>(), none(), 0);   // loads C part 0
+            c_tiles(c_tiles, std::integral_constant<int, 1>());         // tiles 1 .. CPARTS + 1
+            t0 = CPARTS + 2;
         } else {
-            tile(yes(), none(), none(), no(), 0);
-            for (int t = 1; t < nt; ++t) tile(no(), none(), none(), no(), t);
+            tile(yes(), none(), none(), 0);
         }
+        for (int t = t0; t < nt; ++t) tile(no(), none(), none(), t);
         // the deferred part of the last tile's step 1
-        if constexpr (SCHED == 1) {
 #pragma unroll
-            for (int q = 0; q < 64; ++q) mfma(std::false_type(), 1, q / TN, q % TN);
-        } else {
-#pragma unroll
-            for (int q = 0; q < 32; ++q) mfma(std::false_type(), 1, 4 + q / TN, q % TN);
-        }
+        for (int q = 0; q < 64; ++q) mfma(std::false_type(), 1, q / TN, q % TN);
         mfma_result_fence<TM, TN>(acc);
     } else {
 #pragma unroll

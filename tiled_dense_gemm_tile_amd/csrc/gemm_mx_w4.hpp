@@ -44,16 +44,6 @@
 
 namespace tg {
 
-// f(integral_constant<int, I>) for I = B .. E - 1, each call its own
-// instantiation: the indices are constant expressions however large the body.
-template <int B, int E, class F>
-__device__ __forceinline__ void static_for(F &&f) {
-    if constexpr (B < E) {
-        f(std::integral_constant<int, B>());
-        static_for<B + 1, E>(f);
-    }
-}
-
 // Extent of a tile's scale resource: through the 16-byte word (a scale
 // load's unit) holding the last row's last block.  Range checks are per
 // dword and a dword partly past the end reads as zero, so an extent ending

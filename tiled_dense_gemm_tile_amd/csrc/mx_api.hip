@@ -11,6 +11,8 @@ using namespace tg_api;
 
 namespace {
 
+// Test override: TILEGEMM_MX_CONFIG=<id> forces one configuration where
+// the call's alignment allows it (read at every call).
 int forced_mx_cfg() {
     const char *e = getenv("TILEGEMM_MX_CONFIG");
     if (!e || !*e) return -1;
@@ -26,13 +28,12 @@ gemm_status dispatch_mx(const Common &a, const void *SFA, int64_t ldsfa, const v
                       ldsfb % 4 == 0;
     // other K % 32 and alignments: the general kernel
     if (!fast && a.K > 0) return run_mx_any(a, 0, a.lda, a.ldb, SFA, ldsfa, SFB, ldsfb, s);
-    // The four-wave and ping-pong kernels load a row's scales 16 bytes (512
-    // K) at a time, so they need 16-byte-aligned scale rows and whole groups
-    // of 16 blocks.
+    // The four-wave kernel loads a row's scales 16 bytes (512 K) at a time,
+    // so it needs 16-byte-aligned scale rows and whole groups of 16 blocks.
     const bool scales16 = a.K % 512 == 0 && (uintptr_t)SFA % 16 == 0 && (uintptr_t)SFB % 16 == 0 &&
                           ldsfa % 16 == 0 && ldsfb % 16 == 0;
     int cfg = forced_mx_cfg();
-    if ((cfg == tg::kMxPingPong || cfg == tg::kMxFourWave) && !scales16) cfg = -1;
+    if (cfg == tg::kMxFourWave && !scales16) cfg = -1;
     if (cfg < 0) {
         // the four-wave kernel once its 256 x 256 grid is over half a wave
         // (measured at K = 4096: 160 tiles 46.9 against 71.3 us with
@@ -41,9 +42,9 @@ gemm_status dispatch_mx(const Common &a, const void *SFA, int64_t ldsfa, const v
         if (scales16 && t256 > 128)
             cfg = tg::kMxFourWave;
         else if (t256 >= 240)
-            cfg = 1;
+            cfg = tg::kMxWide;
         else if (t128 > 256)
-            cfg = 2;                                    // two workgroups per CU share the waves
+            cfg = tg::kMx128;                           // two workgroups per CU share the waves
         else if (t128 > 128)
             cfg = tg::kMxDeep128;                       // at most one 128 x 128 tile per CU: three-slot rings
         else

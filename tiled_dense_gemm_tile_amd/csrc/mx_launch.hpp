@@ -5,40 +5,30 @@
 #include <hip/hip_runtime.h>
 
 #include "gemm_mxfp8.hpp"
-#include "gemm_mx_pp.hpp"
 #include "gemm_mx_w4.hpp"
 
 namespace tg {
 
-// id, BM, BN, waves along M, waves along N (two-slot rings)
-#define TG_MX_CONFIGS(X)     \
-    X(0, 256, 256, 2, 4)     \
-    X(1, 256, 256, 2, 2)     \
-    X(2, 128, 128, 2, 2)     \
-    X(3, 64, 64, 2, 2)
-
-// Three-slot rings (the tile two ahead fetched), numbered after the
-// ping-pong and four-wave kernels: id, BM, BN, waves along M, waves along N.
-#define TG_MX_DEEP(X)        \
-    X(6, 128, 128, 2, 2)     \
-    X(7, 64, 64, 2, 2)
+// The configurations the kernel choice (mx_api.hip, dispatch_mx) uses:
+// id, BM, BN, waves along M, waves along N, ring slots.
+#define TG_MX_CONFIGS(X)        \
+    X(0, 256, 256, 2, 2, 2)     \
+    X(1, 128, 128, 2, 2, 2)     \
+    X(2, 128, 128, 2, 2, 3)     \
+    X(3, 64, 64, 2, 2, 3)
 
 struct MxCfgInfo {
     int bm, bn, wm, wn;
 };
 
-#define TG_MX_INFO(id, bm, bn, wm, wn) {bm, bn, wm, wn},
-// Then the ping-pong kernel (256 x 256, 8 waves) and the four-wave kernel
-// (256 x 256, 128 x 128 per wave), both 16x16x128 MFMA, K % 512 == 0.
-constexpr MxCfgInfo kMxCfgs[] = {TG_MX_CONFIGS(TG_MX_INFO){256, 256, 2, 4}, {256, 256, 2, 2},
-                                  TG_MX_DEEP(TG_MX_INFO)};
+#define TG_MX_INFO(id, bm, bn, wm, wn, ns) {bm, bn, wm, wn},
+// Then the four-wave kernel (256 x 256, 128 x 128 per wave, 16x16x128
+// MFMA, K % 512 == 0, 16-byte scale rows; gemm_mx_w4.hpp).
+constexpr MxCfgInfo kMxCfgs[] = {TG_MX_CONFIGS(TG_MX_INFO){256, 256, 2, 2}};
 #undef TG_MX_INFO
 constexpr int kNumMxCfgs = sizeof(kMxCfgs) / sizeof(kMxCfgs[0]);
-#define TG_MX_COUNT(...) +1
-constexpr int kMxPingPong = 0 TG_MX_CONFIGS(TG_MX_COUNT), kMxFourWave = kMxPingPong + 1;
-#undef TG_MX_COUNT
-constexpr int kMxDeep128 = kMxFourWave + 1, kMxDeep64 = kMxFourWave + 2;
-static_assert(kMxDeep64 + 1 == kNumMxCfgs && kMxDeep128 == 6, "configuration table");
+constexpr int kMxWide = 0, kMx128 = 1, kMxDeep128 = 2, kMxDeep64 = 3, kMxFourWave = 4;
+static_assert(kMxFourWave + 1 == kNumMxCfgs, "configuration table");
 
 template <bool OUT_BF16>
 hipError_t launch_mx(int cfg, unsigned grid, hipStream_t s, const MxArgs &q, const F16Epi &e);
@@ -54,28 +44,17 @@ namespace tg {
 
 template <>
 hipError_t launch_mx<TG_OUT_BF16>(int cfg, unsigned grid, hipStream_t s, const MxArgs &q, const F16Epi &e) {
-    if (cfg == kMxPingPong) {
-        hipLaunchKernelGGL((gemm_mx_pp_kernel<TG_OUT_BF16>), dim3(grid), dim3(512), 0, s, q, e);
-        return hipGetLastError();
-    }
     if (cfg == kMxFourWave) {
         hipLaunchKernelGGL((gemm_mx_w4_kernel<TG_OUT_BF16>), dim3(grid), dim3(256), 0, s, q, e);
         return hipGetLastError();
     }
     switch (cfg) {
-#define TG_MX_CASE(id, bm, bn, wm, wn)                                                                  \
+#define TG_MX_CASE(id, bm, bn, wm, wn, ns)                                                              \
     case id:                                                                                            \
-        hipLaunchKernelGGL((gemm_mxfp8_kernel<MxCfg<bm, bn, wm, wn>, TG_OUT_BF16>), dim3(grid),         \
+        hipLaunchKernelGGL((gemm_mxfp8_kernel<MxCfg<bm, bn, wm, wn, ns>, TG_OUT_BF16>), dim3(grid),     \
                            dim3(wm * wn * 64), 0, s, q, e);                                              \
         break;
         TG_MX_CONFIGS(TG_MX_CASE)
-#undef TG_MX_CASE
-#define TG_MX_CASE(id, bm, bn, wm, wn)                                                                  \
-    case id:                                                                                            \
-        hipLaunchKernelGGL((gemm_mxfp8_kernel<MxCfg<bm, bn, wm, wn, 3>, TG_OUT_BF16>), dim3(grid),      \
-                           dim3(wm * wn * 64), 0, s, q, e);                                              \
-        break;
-        TG_MX_DEEP(TG_MX_CASE)
 #undef TG_MX_CASE
     default:
         return hipErrorInvalidValue;

@@ -23,8 +23,9 @@ int pick_vec(const Common &a) {
     return 1;
 }
 
-// Tuning override: TILEGEMM_F16_CONFIG=<id> forces one direct-to-LDS
-// configuration (read at every call; ignored when out of range).
+// Test override: TILEGEMM_F16_CONFIG=<id> forces one of the configurations
+// below where its load width allows the call (read at every call; ignored
+// when out of range), so the tests can reach each one on small shapes.
 int forced_f16_cfg() {
     const char *e = getenv("TILEGEMM_F16_CONFIG");
     if (!e || !*e) return -1;
@@ -32,13 +33,15 @@ int forced_f16_cfg() {
     return (id >= 0 && id < tg::kNumF16DmaCfgs) ? id : -1;
 }
 
-// lane_bytes 4 (rows 8- or 4-byte aligned) is only built for the
-// configurations f16_any_rows names.  vec: the widest vector in elements
-// that every row allows (8 or 4 here).
+// lane_bytes 16: rows 16-byte aligned; 4: rows only 8- or 4-byte aligned.
+// vec: the widest vector in elements that every row allows (8, 4 or 2 here).
 int pick_f16_cfg(const Common &a, int lane_bytes, int vec) {
     const int forced = forced_f16_cfg();
-    if (forced >= 0 && (lane_bytes == 16 || tg::f16_any_rows(forced))) {
-        if (forced != tg::kF16FourWaveS || vec >= 4) return forced;
+    if (forced >= 0) {
+        const bool ok = forced == tg::kF16FourWaveS ? vec >= 4
+                        : forced == tg::kF16FourWave ? lane_bytes == 16
+                        : lane_bytes == 16 ? tg::f16_has_lane16(forced) : tg::f16_has_lane4(forced);
+        if (ok) return forced;
     }
     // Four-wave 256 x 256 kernels once that grid covers half the chip: a
     // grid of 128 to 255 such tiles (part of one wave) finishes in the time
@@ -47,21 +50,21 @@ int pick_f16_cfg(const Common &a, int lane_bytes, int vec) {
     // 102.7 us, 224 tiles 92.3 against 139.5 us; equal at 128 tiles and
     // slower below).
     const int64_t t256 = tiles_of(a, 256, 256);
-    if (vec == 4 && t256 >= 128) return tg::kF16FourWaveS;         // 8-byte rows: shifted-row variant
-    if (lane_bytes == 16 && t256 >= 128) return tg::kF16FourWaveB22;  // 64-wide K tiles, 2 + 2 slots
-    if (t256 >= 240) return 3;
+    if (vec == 4 && t256 >= 128) return tg::kF16FourWaveS;        // 8-byte rows: shifted-row variant
+    if (lane_bytes == 16 && t256 >= 128) return tg::kF16FourWave;  // 64-wide K tiles, 2 + 2 slots
+    if (t256 >= 240) return tg::kF16Wide4Lane;                     // (rows 4-byte aligned here)
     // 128 x 128 tiles: about one wave of them (one workgroup per CU) runs
     // best with both rings two tiles ahead (2048 x 2048 x 4096: 40.0 against
     // 45.1 us); more, with two workgroups per CU sharing it, on the smaller
     // three-slot A ring (2304 x 2304 x 4096: 62.1 against 71.7 us).
     const int64_t t128 = tiles_of(a, 128, 128);
-    if (lane_bytes == 16 && t128 >= 240 && t128 <= 256) return tg::kF16Deep2;
-    if (t128 >= 240) return 6;
+    if (lane_bytes == 16 && t128 >= 240 && t128 <= 256) return tg::kF16Deep128;
+    if (t128 >= 240) return tg::kF16Wide128;
     // smaller grids: 64 x 64 tiles, both rings two tiles ahead, up to two
     // workgroups per CU (1024 x 1024 x 4096: 18.9 against 30.0 us with the
     // two-slot rings; past 512 tiles the two-slot rings are ahead again)
-    if (lane_bytes == 16 && tiles_of(a, 64, 64) <= 512) return tg::kF16Deep64x2;
-    return 7;
+    if (lane_bytes == 16 && tiles_of(a, 64, 64) <= 512) return tg::kF16Deep64;
+    return tg::kF16Small64;
 }
 
 template <bool FP16, bool OUT_BF16>
@@ -80,7 +83,8 @@ gemm_status dispatch_f16(const Common &a, hipStream_t s) {
     p.K = (int)a.K;
     p.group_m = 4;
     // 16-byte rows: 16-byte direct-to-LDS lanes; 4- or 8-byte rows: 4-byte
-    // lanes; 2-byte rows (odd K or leading dimension): register staging.
+    // lanes; 2-byte rows (odd K or leading dimension): register staging,
+    // element by element.
     const int vec = pick_vec(a);
     const int lane_bytes = vec == 8 ? 16 : 4;
     int bm = tg::StagedCfg::BM, bn = tg::StagedCfg::BN, cfg = -1;
@@ -101,7 +105,7 @@ gemm_status dispatch_f16(const Common &a, hipStream_t s) {
         e.vec_c = a.C && ((uintptr_t)a.C % vb) == 0 && a.ldc % 4 == 0;
         return launched(tg::launch_f16_dma<FP16, OUT_BF16>(cfg, lane_bytes, (unsigned)tiles, s, p, e));
     }
-    return launched(tg::launch_f16_staged<FP16, OUT_BF16>(vec, (unsigned)tiles, s, p));
+    return launched(tg::launch_f16_staged<FP16, OUT_BF16>((unsigned)tiles, s, p));
 }
 
 gemm_status run_f16(bool fp16, const Common &a, hipStream_t s) {

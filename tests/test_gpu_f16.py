@@ -313,11 +313,13 @@ def test_llm_projection_bf16_out(name):
 # ---- every kernel configuration ------------------------------------------------------------
 
 # Kernel configurations (csrc/f16_launch.hpp): 0 takes rows only 4- or
-# 8-byte aligned; 1 .. 4 the direct-to-LDS kernels; 5 the four-wave kernel;
-# 6 its shifted-row variant (which takes 16-byte rows too).
-LANE16_CFGS = [1, 2, 3, 4, 5, 6]
+# 8-byte aligned; 1 .. 4 the direct-to-LDS kernels; 5 the four-wave kernel
+# (256 x 256 tiles), 6 its shifted-row variant (which takes 16-byte rows
+# too); 7 and 8 the same two with 192 x 256 tiles.
+LANE16_CFGS = [1, 2, 3, 4, 5, 6, 7, 8]
 LANE4_CFGS = [0, 1, 2]
-FOUR_WAVE, FOUR_WAVE_SHIFTED = 5, 6
+FOUR_WAVE, FOUR_WAVE_SHIFTED, FOUR_WAVE_192, FOUR_WAVE_SHIFTED_192 = 5, 6, 7, 8
+FOUR_WAVE_ALL = (FOUR_WAVE, FOUR_WAVE_SHIFTED, FOUR_WAVE_192, FOUR_WAVE_SHIFTED_192)
 
 
 @pytest.mark.parametrize("cfg", LANE16_CFGS)
@@ -368,9 +370,10 @@ def test_c_streamed_in_k_loop(cfg, out, monkeypatch):
     monkeypatch.setenv("TILEGEMM_F16_CONFIG", str(cfg))
     M = 300
     cases = [(520, 2304)]
-    if cfg in (FOUR_WAVE, FOUR_WAVE_SHIFTED):
-        # the stream's threshold (20 K tiles), a ragged K with the stream,
-        # and N % 4 != 0 (C added in the epilogue)
+    if cfg in FOUR_WAVE_ALL:
+        # the stream's threshold (20 K tiles for 256 x 256 tiles, 16 for
+        # 192 x 256), a ragged K with the stream, and N % 4 != 0 (C added in
+        # the epilogue)
         cases += [(520, 1344), (520, 1280), (520, 1216), (520, 1300), (518, 2304)]
     for N, K, integer in [(n, k, i) for (n, k) in cases for i in (True, False)]:
         x, C = _case("bf16", M, N, K, seed=cfg * 7 + (out == "bf16"), integer=integer)
@@ -395,7 +398,7 @@ def test_c_streamed_in_k_loop(cfg, out, monkeypatch):
             assert torch.equal(D, inplace)
 
 
-@pytest.mark.parametrize("cfg", [None, FOUR_WAVE, FOUR_WAVE_SHIFTED, 1, 3])
+@pytest.mark.parametrize("cfg", [None, FOUR_WAVE, FOUR_WAVE_SHIFTED, FOUR_WAVE_192, FOUR_WAVE_SHIFTED_192, 1, 3])
 @pytest.mark.parametrize("K,pad", [(100, 4), (200, 8), (72, 16), (4100, 4), (36, 60)])
 def test_nan_past_k_never_reaches_d(cfg, K, pad, monkeypatch):
     """Rows padded past K with NaN codes: the kernels load whole chunks and
@@ -405,7 +408,7 @@ def test_nan_past_k_never_reaches_d(cfg, K, pad, monkeypatch):
         monkeypatch.setenv("TILEGEMM_F16_CONFIG", str(cfg))
     M, N = 300, 520
     ld = K + pad
-    if cfg in (FOUR_WAVE, 1, 3) and ld % 8:
+    if cfg in (FOUR_WAVE, FOUR_WAVE_192, 1, 3) and ld % 8:
         pytest.skip("16-byte rows only")
     x, C = _case("bf16", M, N, K, seed=K + pad, integer=True)
     Ab = np.full((M, ld), 0x7FC0, np.uint16); Ab[:, :K] = x["A"]
@@ -418,9 +421,7 @@ def test_nan_past_k_never_reaches_d(cfg, K, pad, monkeypatch):
 
 # ---- rows only 8-byte aligned: the shifted-row four-wave kernel ---------------------------
 
-N_SHIFTED_CFG = FOUR_WAVE_SHIFTED
-
-
+@pytest.mark.parametrize("cfg", [FOUR_WAVE_SHIFTED, FOUR_WAVE_SHIFTED_192])
 @pytest.mark.parametrize("case", [
     # M, N, K, pad (lda = ldb = K + pad), element offset of A and B, C, output
     (520, 300, 4100, 0, 0, True, "f32"),     # packed 8-byte rows, ragged last K tile (past K cleared)
@@ -431,8 +432,8 @@ N_SHIFTED_CFG = FOUR_WAVE_SHIFTED
     (300, 520, 2308, 0, 0, True, "f32"),     # C streamed in the K loop
     (300, 520, 2308, 0, 0, True, "bf16"),
 ])
-def test_shifted_rows(case, monkeypatch):
-    monkeypatch.setenv("TILEGEMM_F16_CONFIG", str(N_SHIFTED_CFG))
+def test_shifted_rows(case, cfg, monkeypatch):
+    monkeypatch.setenv("TILEGEMM_F16_CONFIG", str(cfg))
     M, N, K, pad, off, with_c, out = case
     for in_type in ("fp16", "bf16"):
         for integer in (True, False):

@@ -121,24 +121,34 @@ constexpr int tr_row_wait(int i) {
     return n > 15 ? 15 : n;
 }
 
-template <bool FP16, bool OUT_BF16, bool SH = false, bool SPLIT = false, bool AT = false, bool BT = false>
+// TM_: blocks of 16 rows per wave along M -- 8 (256 x 256 tiles) or 6
+// (192 x 256 tiles, for grids whose 256 x 256 tiles fill only part of the
+// last wave: 4000 x 3000 is 192 such tiles but 252 of 192 x 256).
+template <bool FP16, bool OUT_BF16, bool SH = false, bool SPLIT = false, bool AT = false, bool BT = false,
+          int TM_ = 8>
 __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) {
     constexpr int NA = 2, NB = 2;                      // ring slots of A and B
     constexpr int DAUX = kStoreStream;                 // D store policy
-    constexpr int BM = 256, BN = 256, KT = 64;         // tile
-    constexpr int WTM = 128, WTN = 128, TM = 8, TN = 8;
+    constexpr int TM = TM_, TN = 8;
+    constexpr int BM = 32 * TM, BN = 256, KT = 64;     // tile
+    constexpr int WTM = 16 * TM, WTN = 128;
+    constexpr int Q = TM * TN;                         // MFMAs per wave per K step
     // SH: rows only 8-byte aligned (see the row layout below): 144-byte rows
     constexpr int ROWB = SH ? KT * 2 + 16 : KT * 2;    // 128-byte LDS rows
-    constexpr int SLOT = 256 * ROWB;                   // 32 KiB per operand slot (36 KiB with SH)
-    constexpr int B_BASE = NA * SLOT;
-    constexpr int RING_BYTES = (NA + NB) * SLOT;
+    constexpr int IB = 1024;                           // one load instruction: 8 rows (SH: 64 chunks)
+    // load instructions per wave per tile (SH: a row is 9 chunks; the last
+    // instruction of A may reach past row BM, into spare slot space)
+    constexpr int LPTA = SH ? (BM * 9 + 255) / 256 : BM / 32, LPTB = SH ? 9 : 8;
+    constexpr int SLOTA = LPTA * 4 * IB, SLOTB = LPTB * 4 * IB;    // >= rows x ROWB
+    constexpr int B_BASE = NA * SLOTA;
+    constexpr int RING_BYTES = NA * SLOTA + NB * SLOTB;
     constexpr int EPI_BYTES = 4 * 32 * (WTN + 8) * 4;
     constexpr int LDS_BYTES = RING_BYTES > EPI_BYTES ? RING_BYTES : EPI_BYTES;
-    constexpr int IB = 1024;                           // one load instruction: 8 rows
-    constexpr int LPT = SH ? 9 : 8;                    // load instructions per wave per operand per tile
+    static_assert(SLOTA >= BM * ROWB && SLOTB >= BN * ROWB, "slots");
     static_assert(LDS_BYTES <= 160 * 1024, "ring");
+    static_assert(TM == 8 || TM == 6, "wave tile");
     static_assert(!SPLIT || !OUT_BF16, "split-K partial tiles are fp32");
-    static_assert(!(AT || BT) || (!SH && !SPLIT), "MN-contiguous operands: 16-byte rows");
+    static_assert(!(AT || BT) || (!SH && !SPLIT && TM == 8), "MN-contiguous operands: 16-byte rows, 256 x 256");
 
     __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
 
@@ -181,7 +191,7 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
     // spreads the 16 rows of a fragment read over all banks without a swizzle.
     const int chunk = (lane & 7) ^ (lane >> 3);
     const int kel = chunk * 8;
-    uint32_t a_off[LPT], b_off[LPT];
+    uint32_t a_off[LPTA], b_off[LPTB];
     auto sh_row = [&](int j) __attribute__((always_inline)) { return ((4 * j + wave) * 64 + lane) / 9; };
     auto sh_chk = [&](int j) __attribute__((always_inline)) { return ((4 * j + wave) * 64 + lane) % 9; };
     // MN-contiguous operand: load instruction j of a wave fills LDS rows
@@ -194,14 +204,20 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
         return (uint32_t)((row * ld + lchk * 16 + (lane & 1) * 8) * 2);
     };
 #pragma unroll
-    for (int j = 0; j < LPT; ++j) {
+    for (int j = 0; j < LPTA; ++j) {
         if constexpr (SH) {
-            const int row = sh_row(j), c = sh_chk(j);
-            a_off[j] = ((uint32_t)(a_mis0 + row * p.lda * 2) & ~15u) + c * 16;
-            b_off[j] = ((uint32_t)(b_mis0 + row * p.ldb * 2) & ~15u) + c * 16;
+            a_off[j] = ((uint32_t)(a_mis0 + sh_row(j) * p.lda * 2) & ~15u) + sh_chk(j) * 16;
         } else {
             const int row = (4 * j + wave) * 8 + (lane >> 3);
             a_off[j] = AT ? mn_off(p.lda, j) : (uint32_t)(row * p.lda * 2) + chunk * 16;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < LPTB; ++j) {
+        if constexpr (SH) {
+            b_off[j] = ((uint32_t)(b_mis0 + sh_row(j) * p.ldb * 2) & ~15u) + sh_chk(j) * 16;
+        } else {
+            const int row = (4 * j + wave) * 8 + (lane >> 3);
             b_off[j] = BT ? mn_off(p.ldb, j) : (uint32_t)(row * p.ldb * 2) + chunk * 16;
         }
     }
@@ -239,14 +255,14 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)d, 16, voff, 0, 0, 0);
     };
     auto dma_a = [&](int t, int j) __attribute__((always_inline)) {
-        char *d = smem + (t % NA) * SLOT + (j * 4 + wave) * IB;
+        char *d = smem + (t % NA) * SLOTA + (j * 4 + wave) * IB;
         if constexpr (AT)
             dma_mn(p.A, p.lda, m0, M, d, a_off[j], t);
         else
             dma(rA, d, a_off[j], t);
     };
     auto dma_b = [&](int t, int j) __attribute__((always_inline)) {
-        char *d = smem + B_BASE + (t % NB) * SLOT + (j * 4 + wave) * IB;
+        char *d = smem + B_BASE + (t % NB) * SLOTB + (j * 4 + wave) * IB;
         if constexpr (BT)
             dma_mn(p.B, p.ldb, n0, N, d, b_off[j], t);
         else
@@ -268,12 +284,15 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
                 *(u32x2 *)(d + 8) = u32x2{0u, 0u};
         };
 #pragma unroll
-        for (int j = 0; j < LPT; ++j) {
+        for (int j = 0; j < LPTA; ++j) {
             if constexpr (!AT)
-                clear(smem + (t % NA) * SLOT + (j * 4 + wave) * IB + lane * 16,
+                clear(smem + (t % NA) * SLOTA + (j * 4 + wave) * IB + lane * 16,
                       kr - (SH ? sh_kel(a_mis0, p.lda, j) : kel));
+        }
+#pragma unroll
+        for (int j = 0; j < LPTB; ++j) {
             if constexpr (!BT)
-                clear(smem + B_BASE + (t % NB) * SLOT + (j * 4 + wave) * IB + lane * 16,
+                clear(smem + B_BASE + (t % NB) * SLOTB + (j * 4 + wave) * IB + lane * 16,
                       kr - (SH ? sh_kel(b_mis0, p.ldb, j) : kel));
         }
         wait_lgkmcnt0();
@@ -337,7 +356,7 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
 
     // C streamed into the accumulators (see above).
     constexpr int OS = OUT_BF16 ? 2 : 4;
-    constexpr int CPARTS = TM * TN / 4;                // 16 parts of 4 blocks
+    constexpr int CPARTS = TM * TN / 4;                // parts of 4 blocks
     const int nt = (K + KT - 1) / KT;
     // (whole 4-column vectors: every C row segment a lane reads is either in
     // range or past N)
@@ -376,22 +395,22 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
         a = t;
     };
 
-    // Fragment read k of K step st of tile t: k = 0 is A block 0, k = 1..8
-    // B blocks 0..7, k = 9..15 A blocks 1..7 -- the order the MFMAs use them.
+    // Fragment read k of K step st of tile t: k = 0 is A block 0, k = 1..TN
+    // B blocks 0..TN-1, then A blocks 1..TM-1 -- the order the MFMAs use them.
     auto read_frag = [&](int t, int st, int k) __attribute__((always_inline)) {
         const int coff = ((4 * st + fq) ^ fswz) << 4;
-        if (k == 0 || k >= 9) {
-            const int i = k == 0 ? 0 : k - 8;
+        if (k == 0 || k > TN) {
+            const int i = k == 0 ? 0 : k - TN;
             if constexpr (AT)
-                fa[st][i] = ldfrag_tr(a_mn[i] + (t % NA) * SLOT + st * 32 * 512);
+                fa[st][i] = ldfrag_tr(a_mn[i] + (t % NA) * SLOTA + st * 32 * 512);
             else
-                fa[st][i] = ldfrag((t % NA) * SLOT + a_read + i * 16 * ROWB + coff);
+                fa[st][i] = ldfrag((t % NA) * SLOTA + a_read + i * 16 * ROWB + coff);
         } else {
             const int j = k - 1;
             if constexpr (BT)
-                fb[st][j] = ldfrag_tr(b_mn[j] + (t % NB) * SLOT + st * 32 * 512);
+                fb[st][j] = ldfrag_tr(b_mn[j] + (t % NB) * SLOTB + st * 32 * 512);
             else
-                fb[st][j] = ldfrag(B_BASE + (t % NB) * SLOT + b_read + j * 16 * ROWB + coff);
+                fb[st][j] = ldfrag(B_BASE + (t % NB) * SLOTB + b_read + j * 16 * ROWB + coff);
         }
     };
     // B is the MFMA's first operand and A its second, so block (i, j) holds
@@ -410,28 +429,36 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
     auto tile = [&](auto first, auto lp, auto ap, int t) __attribute__((always_inline)) {
         constexpr int LP = decltype(lp)::value, AP = decltype(ap)::value;
         // The whole step 1 of tile t-1 runs after barrier t while step 0 of
-        // tile t is read (one read per 4 MFMAs) and A(t+1), B(t+1) are
-        // loaded, then step 0 of tile t while step 1 is read (one per 3).
-        // Block b gets its C at slot (b + 32) % 64 of the first half, 32
-        // MFMAs from its updates on either side.
+        // tile t is read (TM + TN reads spread evenly) and A(t+1), B(t+1)
+        // are loaded (also spread), then step 0 of tile t while step 1 is
+        // read (one per 3 MFMAs).  Block b gets its C at slot (b + Q/2) % Q
+        // of the first half, Q/2 MFMAs from its updates on either side.
+        // (issue slots: read k at MFMA k Q / (TM + TN); SH: loads j of A and B
+        // at 7 j Q / 64 + 1 and + 4, 16 loads of 9 over 64 MFMAs; else A load
+        // j at j Q / LPTA + 2, B load j at j Q / LPTB + Q / (2 LPTB) + 2)
+        constexpr int RD = TM + TN;
 #pragma unroll
-        for (int q = 0; q < 64; ++q) {
+        for (int q = 0; q < Q; ++q) {
             if constexpr (!decltype(first)::value) mfma(std::false_type(), 1, q / TN, q % TN);
-            if (q % 4 == 0) read_frag(t, 0, q / 4);
+            const int kr = (q * RD + Q - 1) / Q;
+            if (kr < RD && kr * Q / RD == q) read_frag(t, 0, kr);
             if constexpr (SH) {
-                if (q % 7 == 1 && q / 7 < LPT) dma_a(t + 1, q / 7);
-                if (q % 7 == 4 && q / 7 < LPT) dma_b(t + 1, q / 7);
+                const int ja = (64 * (q - 1) + 7 * Q - 1) / (7 * Q), jb = (64 * (q - 4) + 7 * Q - 1) / (7 * Q);
+                if (q >= 1 && ja < LPTA && 7 * ja * Q / 64 + 1 == q) dma_a(t + 1, ja);
+                if (q >= 4 && jb < LPTB && 7 * jb * Q / 64 + 4 == q) dma_b(t + 1, jb);
             } else {
-                if (q % 8 == 2) dma_a(t + 1, q / 8);
-                if (q % 8 == 6) dma_b(t + 1, q / 8);
+                const int ja = ((q - 2) * LPTA + Q - 1) / Q, ob = Q / LPTB / 2 + 2;
+                const int jb = ((q - ob) * LPTB + Q - 1) / Q;
+                if (q >= 2 && ja < LPTA && ja * Q / LPTA + 2 == q) dma_a(t + 1, ja);
+                if (q >= ob && jb < LPTB && jb * Q / LPTB + ob == q) dma_b(t + 1, jb);
             }
             if constexpr (AP >= 0) {
-                constexpr int s0 = (4 * AP + 32) % 64;
+                constexpr int s0 = (4 * AP + Q / 2) % Q;
                 if (q >= s0 && q < s0 + 4) add_c(AP, q - s0);
             }
         }
 #pragma unroll
-        for (int q = 0; q < 64; ++q) {
+        for (int q = 0; q < Q; ++q) {
             if constexpr (AT || BT) {
                 constexpr int CA = AT ? 2 : 1, CB = BT ? 2 : 1;
                 if (q % TN == 0) {
@@ -445,9 +472,10 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
                 }
             }
             mfma(first, 0, q / TN, q % TN);
-            if (q % 3 == 0 && q / 3 < 16) read_frag(t, 1, q / 3);
+            if (q % 3 == 0 && q / 3 < TM + TN) read_frag(t, 1, q / 3);
             if constexpr (LP >= 0) {
-                if (q % 16 == 6) load_c(LP, q / 16);
+                const int u = (q - 6) * 4 / Q;
+                if (q >= 6 && u < 4 && u * Q / 4 + 6 == q) load_c(LP, u);
             }
         }
         // A(t+1), B(t+1) landed; this tile's C loads (one per block of the
@@ -471,9 +499,9 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
     if (nt > 0) {
         // A(0), B(0): the loads the first tile's iteration does not issue
 #pragma unroll
-        for (int j = 0; j < LPT; ++j) dma_a(0, j);
+        for (int j = 0; j < LPTA; ++j) dma_a(0, j);
 #pragma unroll
-        for (int j = 0; j < LPT; ++j) dma_b(0, j);
+        for (int j = 0; j < LPTB; ++j) dma_b(0, j);
         wait_vmcnt<0>();                               // A(0), B(0) landed
         if (nt == 1) clear_past_k(0);
         barrier();
@@ -491,7 +519,7 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
         for (int t = t0; t < nt; ++t) tile(no(), none(), none(), t);
         // the deferred part of the last tile's step 1
 #pragma unroll
-        for (int q = 0; q < 64; ++q) mfma(std::false_type(), 1, q / TN, q % TN);
+        for (int q = 0; q < Q; ++q) mfma(std::false_type(), 1, q / TN, q % TN);
         mfma_result_fence<TM, TN>(acc);
     } else {
 #pragma unroll

@@ -38,8 +38,8 @@ int forced_f16_cfg() {
 int pick_f16_cfg(const Common &a, int lane_bytes, int vec) {
     const int forced = forced_f16_cfg();
     if (forced >= 0) {
-        const bool ok = forced == tg::kF16FourWaveS ? vec >= 4
-                        : forced == tg::kF16FourWave ? lane_bytes == 16
+        const bool ok = (forced == tg::kF16FourWaveS || forced == tg::kF16FourWaveS192) ? vec >= 4
+                        : (forced == tg::kF16FourWave || forced == tg::kF16FourWave192) ? lane_bytes == 16
                         : lane_bytes == 16 ? tg::f16_has_lane16(forced) : tg::f16_has_lane4(forced);
         if (ok) return forced;
     }
@@ -49,9 +49,14 @@ int pick_f16_cfg(const Common &a, int lane_bytes, int vec) {
     // same output takes (measured at K = 4096: 144 tiles 74.9 against
     // 102.7 us, 224 tiles 92.3 against 139.5 us; equal at 128 tiles and
     // slower below).
+    // Of the two four-wave tile heights, 192 x 256 tiles (0.75 of the work
+    // each) when their waves of 256 workgroups cost less than those of
+    // 256 x 256 tiles: 4000 x 3000 is 192 tiles of 256^2 (one wave, 3/4 of
+    // the CUs busy) but 252 of 192 x 256 (one wave at 3/4 of the time).
     const int64_t t256 = tiles_of(a, 256, 256);
-    if (vec == 4 && t256 >= 128) return tg::kF16FourWaveS;        // 8-byte rows: shifted-row variant
-    if (lane_bytes == 16 && t256 >= 128) return tg::kF16FourWave;  // 64-wide K tiles, 2 + 2 slots
+    const bool h192 = 3 * ((tiles_of(a, 192, 256) + 255) / 256) < 4 * ((t256 + 255) / 256);
+    if (vec == 4 && t256 >= 128) return h192 ? tg::kF16FourWaveS192 : tg::kF16FourWaveS;   // 8-byte rows
+    if (lane_bytes == 16 && t256 >= 128) return h192 ? tg::kF16FourWave192 : tg::kF16FourWave;
     if (t256 >= 240) return tg::kF16Wide4Lane;                     // (rows 4-byte aligned here)
     // 128 x 128 tiles: about one wave of them (one workgroup per CU) runs
     // best with both rings two tiles ahead (2048 x 2048 x 4096: 40.0 against

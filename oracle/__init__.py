@@ -77,7 +77,7 @@ def lib():
                                       vp, i64, vp, i64,
                                       vp, i64, vp, i64,
                                       ctypes.c_int, vp, i64,
-                                      i64, vp, dp, dp, ctypes.c_int]
+                                      i64, vp, dp, dp, ctypes.c_int, i64]
             for name, arg in (("orc_dec_bf16", ctypes.c_uint16), ("orc_dec_fp16", ctypes.c_uint16),
                               ("orc_dec_e4m3", ctypes.c_uint8), ("orc_dec_e8m0", ctypes.c_uint8),
                               ("orc_dec_e2m1", ctypes.c_uint8),
@@ -101,7 +101,8 @@ class OracleError(RuntimeError):
     pass
 
 
-_ERRS = {-1: "bad argument", -2: "NaN e8m0 scale code (0xFF)", -3: "scaled form needs K % 32 == 0"}
+_ERRS = {-1: "bad argument", -2: "NaN e8m0 scale code (0xFF)",
+         -3: "scaled form needs K % 32 == 0 and a scale block width that is a multiple of 32"}
 
 
 def _ptr(a):
@@ -109,7 +110,7 @@ def _ptr(a):
 
 
 def gemm_ref(in_type: str, A, B, K: int | None = None, C=None, c_type: str = "f32",
-             SFA=None, SFB=None, idx=None, nthreads: int = 0):
+             SFA=None, SFB=None, idx=None, nthreads: int = 0, kblock: int = 32):
     """D_ref and S = sum_k |a*b| at the requested elements, in float64.
 
     ``A``: (M, lda) raw element bits (uint16 for bf16/fp16, uint8 for e4m3),
@@ -118,7 +119,10 @@ def gemm_ref(in_type: str, A, B, K: int | None = None, C=None, c_type: str = "f3
     column n of the K x N operand; ``K`` (elements) defaults to the row
     length.  ``C``: (M, ldc) float32 array
     (``c_type='f32'``) or uint16 bf16 bits (``c_type='bf16'``), or None.
-    ``SFA``/``SFB``: (M, ldsfa) / (N, ldsfb) uint8 e8m0 codes, both or neither.
+    ``SFA``/``SFB``: (M, ldsfa) / (N, ldsfb) uint8 e8m0 codes, both or neither;
+    ``kblock``: the scale block's width in K elements (a multiple of 32;
+    the standard form is 32), scale j of a row covering K elements
+    [j kblock, (j + 1) kblock).
     ``idx``: flat indices ``m*N + n`` (None: every element, row-major).
 
     Returns ``(D, S)`` float64 arrays of shape ``idx.shape`` (or (M, N)).
@@ -164,7 +168,7 @@ def gemm_ref(in_type: str, A, B, K: int | None = None, C=None, c_type: str = "f3
                        _ptr(A), lda, _ptr(SFA), ldsfa,
                        _ptr(B), ldb, _ptr(SFB), ldsfb,
                        TYPE_CODES[c_type], _ptr(C), ldc,
-                       n_out, _ptr(idx_arr), _ptr(D), _ptr(S), int(nthreads))
+                       n_out, _ptr(idx_arr), _ptr(D), _ptr(S), int(nthreads), int(kblock))
     if rc != 0:
         raise OracleError(_ERRS.get(rc, "error %d" % rc))
     return D.reshape(out_shape), S.reshape(out_shape)
@@ -266,7 +270,7 @@ def num_threads() -> int:
 
 # ---- whole-matrix form with a library matmul as its one step --------------
 
-def operands_f64(in_type: str, A, B, K=None, SFA=None, SFB=None):
+def operands_f64(in_type: str, A, B, K=None, SFA=None, SFB=None, kblock=32):
     """Decoded, scaled operands a(m,k) (M x K) and b(k,n) stored as (N x K), float64."""
     A = np.asarray(A)
     B = np.asarray(B)
@@ -279,7 +283,7 @@ def operands_f64(in_type: str, A, B, K=None, SFA=None, SFB=None):
     a = decode(in_type, A[:, :K])
     b = decode(in_type, B[:, :K])
     if SFA is not None:
-        blk = np.arange(K) // 32
+        blk = np.arange(K) // kblock
         a = a * decode("e8m0", np.asarray(SFA)[:, blk])
         b = b * decode("e8m0", np.asarray(SFB)[:, blk])
     return a, b
@@ -294,14 +298,14 @@ def c_f64(C, c_type="f32"):
 
 
 def gemm_ref_full(in_type: str, A, B, K=None, C=None, c_type="f32", SFA=None, SFB=None,
-                  rows=None):
+                  rows=None, kblock=32):
     """(D_ref, S) for every element (or for the given rows) via numpy float64 matmul.
 
     Same definition as :func:`gemm_ref`; the sum over k is a BLAS float64
     product, whose rounding (at most about K * 2^-53 * S) is far below every
     tolerance used here.
     """
-    a, b = operands_f64(in_type, A, B, K, SFA, SFB)
+    a, b = operands_f64(in_type, A, B, K, SFA, SFB, kblock)
     if rows is not None:
         a = a[rows]
     D = a @ b.T

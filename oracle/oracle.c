@@ -10,13 +10,14 @@
  * What it computes (all in IEEE binary64, one output element at a time,
  * k ascending, no blocking and no reordering):
  *
- *   a(m,k) = dec_A(A[m*lda + k]) * 2^(SFA[m*ldsfa + k/32] - 127)
- *   b(k,n) = dec_B(B[n*ldb + k]) * 2^(SFB[n*ldsfb + k/32] - 127)
+ *   a(m,k) = dec_A(A[m*lda + k]) * 2^(SFA[m*ldsfa + k/kb] - 127)
+ *   b(k,n) = dec_B(B[n*ldb + k]) * 2^(SFB[n*ldsfb + k/kb] - 127)
  *   D[m,n] = c(m,n) + sum_k a(m,k) * b(k,n)
  *   S[m,n] = sum_k |a(m,k) * b(k,n)|          (feeds the error bound)
  *
  * The scale factors are present only for the block-scaled forms (fp8
- * e4m3 and fp4 e2m1 elements).
+ * e4m3, fp4 e2m1 and fp6 e2m3 / e3m2 elements); kb is the scale block's
+ * width in K elements (32 in the standard form).
  *
  * Sources on the pages:
  *  - "Tensor Core 数据布局的演进" (Evolution of Tensor Core data layouts),
@@ -28,8 +29,10 @@
  *  - same page, section Block-Scaled MMA 的 Scale Factors: SFA[m,sfk]
  *    scales the sfk-th K block of row m of A, SFB[n,sfk] scales column n of
  *    B, and one scale is shared by every K element of its block.  The block
- *    is 32 K elements wide and the scale is an e8m0 power of two (the
- *    reading of the block-scaled workload; the pages do not print a width).
+ *    is kb K elements wide, 32 in the standard form, and the scale is an
+ *    e8m0 power of two (the reading of the block-scaled workload; the pages
+ *    do not print a width).  Coarser blocks -- kb a multiple of 32, up to
+ *    one scale per row -- are the same definition with a wider block.
  *
  * Decoders are written from the format definitions (sign, biased exponent,
  * fraction), not from bit casts, so that they are an independent statement
@@ -77,7 +80,7 @@ enum {
     ORC_OK = 0,
     ORC_ERR_ARG = -1,     /* bad size, type or missing pointer */
     ORC_ERR_SCALE = -2,   /* an e8m0 scale code is NaN (0xFF) */
-    ORC_ERR_KBLOCK = -3,  /* scaled form with K % 32 != 0 */
+    ORC_ERR_KBLOCK = -3,  /* scaled form with K % 32 != 0 or a block width not a multiple of 32 */
 };
 
 /* ---- format decoders ------------------------------------------------- */
@@ -270,7 +273,7 @@ static double dec_elem(int type, const void *base, int64_t i)
 /* One output element of D = A.B + C, per the definition in the header. */
 static void one_element(int in_type, int64_t m, int64_t n, int64_t K,
                         const void *A, int64_t lda, const uint8_t *SFA, int64_t ldsfa,
-                        const void *B, int64_t ldb, const uint8_t *SFB, int64_t ldsfb,
+                        const void *B, int64_t ldb, const uint8_t *SFB, int64_t ldsfb, int64_t kb,
                         int c_type, const void *C, int64_t ldc,
                         double *d_out, double *s_out)
 {
@@ -279,9 +282,9 @@ static void one_element(int in_type, int64_t m, int64_t n, int64_t K,
         double a = dec_elem(in_type, A, m * lda + k);
         double b = dec_elem(in_type, B, n * ldb + k);
         if (SFA)
-            a *= orc_dec_e8m0(SFA[m * ldsfa + k / 32]);
+            a *= orc_dec_e8m0(SFA[m * ldsfa + k / kb]);
         if (SFB)
-            b *= orc_dec_e8m0(SFB[n * ldsfb + k / 32]);
+            b *= orc_dec_e8m0(SFB[n * ldsfb + k / kb]);
         double p = a * b;
         acc += p;
         sabs += fabs(p);
@@ -301,9 +304,11 @@ static void one_element(int in_type, int64_t m, int64_t n, int64_t K,
  *             ORC_E2M1 even, two elements per byte; for the fp6 types a
  *             multiple of 4, four elements per three bytes)
  *   B       : column-major K x N stored as N rows of K, leading dim ldb
- *   SFA/SFB : e8m0 codes, M x ceil(K/32) and N x ceil(K/32), row-major
+ *   SFA/SFB : e8m0 codes, M x ceil(K/kb) and N x ceil(K/kb), row-major
  *             with leading dims ldsfa/ldsfb; both NULL for the unscaled
  *             forms, both non-NULL for the block-scaled form
+ *   kb      : scale block width in K elements, a positive multiple of 32
+ *             (ignored for the unscaled forms)
  *   C       : M x N row-major of c_type (ORC_F32 or ORC_BF16), or NULL
  *   idx     : n_out flat indices m*N + n; NULL means every element in
  *             row-major order (then n_out must equal M*N)
@@ -317,7 +322,7 @@ int oracle_gemm(int in_type, int64_t M, int64_t N, int64_t K,
                 const void *B, int64_t ldb, const uint8_t *SFB, int64_t ldsfb,
                 int c_type, const void *C, int64_t ldc,
                 int64_t n_out, const int64_t *idx,
-                double *D_out, double *S_out, int nthreads)
+                double *D_out, double *S_out, int nthreads, int64_t kb)
 {
     if (M < 0 || N < 0 || K < 0 || n_out < 0)
         return ORC_ERR_ARG;
@@ -339,14 +344,15 @@ int oracle_gemm(int in_type, int64_t M, int64_t N, int64_t K,
     if ((SFA == NULL) != (SFB == NULL))
         return ORC_ERR_ARG;
     if (SFA) {
-        if (K % 32 != 0)
+        if (K % 32 != 0 || kb <= 0 || kb % 32 != 0)
             return ORC_ERR_KBLOCK;
+        const int64_t nsc = (K + kb - 1) / kb;         /* scales per row */
         for (int64_t m = 0; m < M; ++m)
-            for (int64_t j = 0; j < K / 32; ++j)
+            for (int64_t j = 0; j < nsc; ++j)
                 if (SFA[m * ldsfa + j] == 0xFF)
                     return ORC_ERR_SCALE;
         for (int64_t n = 0; n < N; ++n)
-            for (int64_t j = 0; j < K / 32; ++j)
+            for (int64_t j = 0; j < nsc; ++j)
                 if (SFB[n * ldsfb + j] == 0xFF)
                     return ORC_ERR_SCALE;
     }
@@ -365,7 +371,7 @@ int oracle_gemm(int in_type, int64_t M, int64_t N, int64_t K,
     for (int64_t t = 0; t < n_out; ++t) {
         int64_t flat = idx ? idx[t] : t;
         int64_t m = flat / N, n = flat % N;
-        one_element(in_type, m, n, K, A, lda, SFA, ldsfa, B, ldb, SFB, ldsfb,
+        one_element(in_type, m, n, K, A, lda, SFA, ldsfa, B, ldb, SFB, ldsfb, kb,
                     c_type, C, ldc, &D_out[t], &S_out[t]);
     }
     return ORC_OK;

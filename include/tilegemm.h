@@ -84,6 +84,13 @@ typedef enum {
     GEMM_FP6_E3M2 = 1            /* OCP FP6 E3M2: 1 sign, 3 exponent (bias 3), 2 mantissa bits; max 28 */
 } gemm_fp6_format;
 
+typedef enum {                   /* element formats of gemm_mx_kblock */
+    GEMM_MX_E4M3 = 0,            /* as gemm_mxfp8 */
+    GEMM_MX_E2M1 = 1,            /* as gemm_mxfp4 */
+    GEMM_MX_E2M3 = 2,            /* as gemm_mxfp6 with GEMM_FP6_E2M3 */
+    GEMM_MX_E3M2 = 3             /* as gemm_mxfp6 with GEMM_FP6_E3M2 */
+} gemm_mx_format;
+
 /*
  * gemm_bf16 -- D = A.B + C with bf16 A and B, fp32 accumulation.
  * Source: "Tensor Core 数据布局的演进", section 一个具体的 fragment 映射
@@ -339,6 +346,34 @@ gemm_status gemm_mxfp6_ex(int64_t M, int64_t N, int64_t K,
                           const void *C, int64_t ldc,
                           void *D, int64_t ldd,
                           int format, int out_type, hipStream_t stream);
+
+/*
+ * gemm_mx_kblock -- the block-scaled forms (gemm_mxfp8, gemm_mxfp4,
+ * gemm_mxfp6, chosen by `format`, a gemm_mx_format) with scale blocks
+ * `kblock` K elements wide instead of 32: scale j of row m of A (column n
+ * of B) applies to K elements [j kblock, (j + 1) kblock).  Source:
+ * "Tensor Core 数据布局的演进", section Block-Scaled MMA 的 Scale Factors
+ * (one scale factor per row or column and K block, shared by the block's
+ * elements; the page fixes no block width).
+ *   kblock: 32, 64, 128, ... (32 times a power of two), or any multiple
+ *     of 32 that is at least K: one scale per row of A and column of B;
+ *     other values give GEMM_ERR_UNSUPPORTED.
+ *   SFA: e8m0 codes, M x ceil(K / kblock), row-major, leading dimension
+ *     ldsfa >= ceil(K / kblock) (else GEMM_ERR_BAD_LD); SFB: N x
+ *     ceil(K / kblock), ldsfb likewise.
+ *   kblock == 32 is the standard call (its tiled kernels); wider blocks run
+ *   the general block-scaled kernel (each lane reads the one scale byte its
+ *   32-element block shares), K-contiguous operands only.
+ * Everything else (element formats and packing, leading dimensions in
+ * elements, K % 32 == 0, validation, out_type, C == D) is as the
+ * format's standard call.
+ */
+gemm_status gemm_mx_kblock(int format, int64_t M, int64_t N, int64_t K, int64_t kblock,
+                           const void *A, int64_t lda, const void *SFA, int64_t ldsfa,
+                           const void *B, int64_t ldb, const void *SFB, int64_t ldsfb,
+                           const void *C, int64_t ldc,
+                           void *D, int64_t ldd,
+                           int out_type, hipStream_t stream);
 
 /*
  * gemm_mxfp8_splitk, gemm_mxfp4_splitk, gemm_mxfp6_splitk -- as gemm_mxfp8 /

@@ -25,7 +25,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["gemm_bf16", "gemm_bf16_ex", "gemm_bf16_splitk", "gemm_bf16_splitk_noalloc",
                                     "gemm_fp16", "gemm_fp16_ex", "gemm_fp16_splitk", "gemm_last_hip_error",
-                                    "gemm_mxfp4", "gemm_mxfp4_ex", "gemm_mxfp4_splitk",
+                                    "gemm_mx_kblock", "gemm_mxfp4", "gemm_mxfp4_ex", "gemm_mxfp4_splitk",
                                     "gemm_mxfp6", "gemm_mxfp6_ex", "gemm_mxfp6_splitk", "gemm_mxfp8",
                                     "gemm_mxfp8_ex", "gemm_mxfp8_splitk", "gemm_splitk_scratch_limit",
                                     "gemm_splitk_workspace_bytes", "gemm_status_string"]
@@ -357,3 +357,26 @@ def test_noalloc_splitk_validation_and_limit():
     assert tg.raw.status_string(8).startswith("GEMM_ERR_SCRATCH_LIMIT")
     # 1024 x 1024 in 17 ranges: 68 MiB, one range past the 64 MiB area
     assert call(splits=17) == 8
+
+
+def test_validation_mx_kblock():
+    """Wide scale blocks: block width, scale leading dimensions and element
+    packing are checked before any GPU call."""
+    f = tg.raw.gemm_mx_kblock
+    D = P + (1 << 24)
+
+    def call(fmt=0, M=64, N=64, K=256, kb=64, lda=256, ldsfa=4, ldb=256, ldsfb=4, SFA=P + 4096, out=F32):
+        return f(fmt, M, N, K, kb, P, lda, SFA, ldsfa, P, ldb, P + 8192, ldsfb, None, 0, D, N, out, None)
+    for bad_kb in (0, 16, 48, -32):
+        assert call(kb=bad_kb) == UNSUPPORTED
+    assert call(fmt=4) == UNSUPPORTED
+    assert call(ldsfa=3) == BAD_LD                     # ceil(256 / 64) = 4 scales per row
+    assert call(kb=96, ldsfa=3, ldsfb=3) == UNSUPPORTED  # not 32 times a power of two, below K
+    assert call(kb=288, ldsfa=0, ldsfb=1) == BAD_LD   # >= K: one scale per row
+    assert call(kb=512, ldsfa=1, ldsfb=1, SFA=None) == NULL_POINTER
+    assert call(K=48) == UNSUPPORTED                   # K % 32
+    assert call(fmt=1, lda=255) == UNSUPPORTED         # fp4 rows of whole bytes
+    assert call(fmt=2, lda=254) == UNSUPPORTED         # fp6 rows of whole byte groups
+    assert call(lda=100) == BAD_LD
+    assert call(M=0) == OK
+    assert call(M=-1) == INVALID_SIZE

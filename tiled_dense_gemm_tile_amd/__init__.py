@@ -94,6 +94,8 @@ def _load():
                 f.restype, f.argtypes = ci, sex + [ci, vp]
             L.gemm_mxfp6_ex.restype = ci
             L.gemm_mxfp6_ex.argtypes = sex + [ci, ci, vp]
+            L.gemm_mx_kblock.restype = ci
+            L.gemm_mx_kblock.argtypes = [ci, i64, i64, i64, i64] + smx[3:] + [ci, vp]
             L.gemm_status_string.restype = ctypes.c_char_p
             L.gemm_status_string.argtypes = [ci]
             L.gemm_last_hip_error.restype = ci
@@ -483,6 +485,46 @@ def gemm_mxfp6(A, SFA, B, SFB, C=None, out_dtype=None, D=None, fmt="e2m3", a_ord
             raise ValueError("fmt must be 'e2m3' or 'e3m2'")
         return _mx_ex(fmt, A, SFA, B, SFB, C, out_dtype, D, a_order, b_order, fmt)
     return _mx6("gemm_mxfp6", A, SFA, B, SFB, C, out_dtype, D, fmt, None)
+
+
+MX_FORMATS = {"e4m3": 0, "e2m1": 1, "e2m3": 2, "e3m2": 3}
+
+
+def gemm_mx_kblock(fmt, A, SFA, B, SFB, kblock, C=None, out_dtype=None, D=None):
+    """Block-scaled D = A @ B.T + C with scale blocks ``kblock`` K elements
+    wide (a multiple of 32; >= K: one scale per row).  ``fmt``: "e4m3",
+    "e2m1", "e2m3" or "e3m2"; A (M, K bytes-of-format) and B (N, ...) as the
+    format's standard call takes them; SFA (M, ceil(K / kblock)), SFB (N,
+    ceil(K / kblock)) e8m0 codes."""
+    import torch
+    if fmt not in MX_FORMATS:
+        raise ValueError("fmt must be one of %s" % sorted(MX_FORMATS))
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    ok = (torch.uint8, torch.float8_e4m3fn) if fmt == "e4m3" else (torch.uint8,)
+    if A.dtype not in ok or B.dtype not in ok or not (A.is_cuda and B.is_cuda):
+        raise TypeError("A and B must be device byte tensors")
+    M, K, lda = _mx_operand(fmt, A, "k")
+    N, KB, ldb = _mx_operand(fmt, B, "k")
+    if K != KB:
+        raise ValueError("A and B disagree on K")
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out_dtype must be float32 or bfloat16")
+    if D is None:
+        D = torch.empty((M, N), dtype=out_dtype, device=A.device)
+    if D.dtype != out_dtype or tuple(D.shape) != (M, N):
+        raise ValueError("D must be (M, N) of out_dtype")
+    if C is not None and (C.dtype != out_dtype or tuple(C.shape) != (M, N)):
+        raise ValueError("C must be (M, N) of out_dtype")
+    _on_device(A, B=B, C=C, D=D)
+    _scales(SFA, SFB, M, N, A)
+    nsc = -(-K // kblock) if kblock > 0 else 0
+    out = OUT_BF16 if out_dtype == torch.bfloat16 else OUT_F32
+    _check(_load().gemm_mx_kblock(MX_FORMATS[fmt], M, N, K, int(kblock), A.data_ptr(), lda if K else 0,
+                                  SFA.data_ptr(), _ld(SFA, nsc) if K else 0, B.data_ptr(), ldb if K else 0,
+                                  SFB.data_ptr(), _ld(SFB, nsc) if K else 0,
+                                  C.data_ptr() if C is not None else None, _ld(C, N) if C is not None else 0,
+                                  D.data_ptr(), _ld(D, N), out, _Stream(A)))
+    return D
 
 
 def gemm_mxfp6_splitk(A, SFA, B, SFB, C=None, out_dtype=None, D=None, fmt="e2m3", splits=0, workspace=None):

@@ -202,6 +202,8 @@ __global__ void __launch_bounds__(256) gemm_mx_any_kernel(MxArgs q) {
     const int m0 = tm * 64, n0 = tn * 64;
     const int M = p.M, N = p.N, K = p.K;
     const int nblk = K / 32;
+    // scales per row: one per 2^kb_shift blocks of 32 (the scale block width)
+    const int kb_shift = q.kb_shift, nsc = ((nblk - 1) >> kb_shift) + 1;
     // bytes of a row's K elements
     const int64_t kbytes = FMT == 0 ? K : FMT == 4 ? K / 2 : K / 4 * 3;
     const __amdgpu_buffer_rsrc_t rA =
@@ -209,9 +211,9 @@ __global__ void __launch_bounds__(256) gemm_mx_any_kernel(MxArgs q) {
     const __amdgpu_buffer_rsrc_t rB =
         make_rsrc((const char *)p.B + (int64_t)n0 * p.ldb, span_bytes(N - n0, (int)kbytes, p.ldb, 1));
     const __amdgpu_buffer_rsrc_t rSA =
-        make_rsrc((const char *)q.SFA + (int64_t)m0 * q.ldsfa, span_bytes(M - m0, nblk, q.ldsfa, 1));
+        make_rsrc((const char *)q.SFA + (int64_t)m0 * q.ldsfa, span_bytes(M - m0, nsc, q.ldsfa, 1));
     const __amdgpu_buffer_rsrc_t rSB =
-        make_rsrc((const char *)q.SFB + (int64_t)n0 * q.ldsfb, span_bytes(N - n0, nblk, q.ldsfb, 1));
+        make_rsrc((const char *)q.SFB + (int64_t)n0 * q.ldsfb, span_bytes(N - n0, nsc, q.ldsfb, 1));
 
     const int fr = lane & 15, fq = lane >> 4;
     f32x4 acc[2][2];
@@ -265,8 +267,9 @@ __global__ void __launch_bounds__(256) gemm_mx_any_kernel(MxArgs q) {
                 if constexpr (!AMN) mx_any_load<R, V>(rA, oa, fa[h]);
                 if constexpr (!BMN) mx_any_load<R, V>(rB, ob, fb[h]);
             }
-            const uint32_t osa = blk < nblk ? (uint32_t)(ra * q.ldsfa + blk) : kOOB;
-            const uint32_t osb = blk < nblk ? (uint32_t)(rb * q.ldsfb + blk) : kOOB;
+            const int sc = blk >> kb_shift;            // the block's scale (wider blocks share one)
+            const uint32_t osa = blk < nblk ? (uint32_t)(ra * q.ldsfa + sc) : kOOB;
+            const uint32_t osb = blk < nblk ? (uint32_t)(rb * q.ldsfb + sc) : kOOB;
             sa[h] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rSA, osa, 0, 0);
             sb[h] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rSB, osb, 0, 0);
         }

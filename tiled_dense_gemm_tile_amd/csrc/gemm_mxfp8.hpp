@@ -36,6 +36,7 @@ struct MxArgs {
     const void *SFA;
     const void *SFB;
     int64_t ldsfa, ldsfb;
+    int kb_shift = 0;    // scale block width = 32 << kb_shift (general kernel only; the tiled kernels take 0)
 };
 
 template <int BM_, int BN_, int WM_, int WN_, int NS_ = 2>

@@ -10,9 +10,10 @@ namespace tg_api {
 // fmt: 0 e4m3, 2 e2m3, 3 e3m2, 4 e2m1; lda_b / ldb_b: leading dimensions in
 // bytes; amn / bmn: A / B stored MN-contiguous.  The call has been validated
 // (K % 32 == 0, whole-byte rows).
+// kb_shift: the scale block width is 32 << kb_shift (0: the standard form).
 inline gemm_status run_mx_any(const Common &a, int fmt, int64_t lda_b, int64_t ldb_b, const void *SFA,
                               int64_t ldsfa, const void *SFB, int64_t ldsfb, hipStream_t s, bool amn = false,
-                              bool bmn = false) {
+                              bool bmn = false, int kb_shift = 0) {
     tg::MxArgs q;
     q.g.A = a.A ? a.A : a.D;                            // K == 0 reads nothing
     q.g.B = a.B ? a.B : a.D;
@@ -32,6 +33,7 @@ inline gemm_status run_mx_any(const Common &a, int fmt, int64_t lda_b, int64_t l
     q.SFB = SFB ? SFB : a.D;
     q.ldsfa = ldsfa;
     q.ldsfb = ldsfb;
+    q.kb_shift = kb_shift;
     const int64_t grid = (int64_t)q.g.tiles_m * q.g.tiles_n;
     if (grid >= kMaxDim) return GEMM_ERR_UNSUPPORTED;
     // the widest load every K-contiguous row start allows

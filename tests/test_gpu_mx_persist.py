@@ -1,0 +1,98 @@
+"""Block-scaled fp8 grids of more 256 x 256 tiles than the GPU has compute
+units, without C: the persistent four-wave kernel (one workgroup per CU
+walking the tiles, its next tile's first loads in flight while the finished
+tile's D is stored).
+
+Bar: exact on integer-valued inputs against the oracle at 4096 seeded
+samples plus the tile edges, within the tolerance on random inputs, and bit
+for bit equal to the one-workgroup-per-tile kernel (same MFMAs in the same
+order) over the whole of D, for fp32 and bf16 output.  Padding of a D with
+ldd > N stays untouched.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import check
+import tiled_dense_gemm_tile_amd as tg
+from tiled_dense_gemm_tile_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from gpuutil import DEV, bf16_bits, dev8, say, to_f64
+
+# (M, N, K): ragged rows and columns (17 x 17 tiles); 32 x 32 tiles (four
+# per CU); 17 x 16 tiles, one K group; 2 tiles past one per CU, long K
+CASES = [(4200, 4300, 1024), (8192, 8192, 512), (4352, 4096, 512), (4100, 4104, 2048)]
+
+
+def _inputs(M, N, K, seed, integer):
+    rng = np.random.default_rng(seed)
+    A = inputs.random_codes(rng, "e4m3", (M, K), integer=integer)
+    B = inputs.random_codes(rng, "e4m3", (N, K), integer=integer)
+    lo, hi = (0, 2) if integer else (-4, 5)
+    SFA = (127 + rng.integers(lo, hi, size=(M, K // 32))).astype(np.uint8)
+    SFB = (127 + rng.integers(lo, hi, size=(N, K // 32))).astype(np.uint8)
+    return A, B, SFA, SFB
+
+
+def _sampled_check(A, B, SFA, SFB, Dg, integer, seed):
+    M, N = Dg.shape
+    rand, forced = inputs.sample_indices(M, N, seed)
+    idx = np.concatenate([rand, forced])
+    Dr, S = oracle.gemm_ref("e4m3", A, B, idx=idx, SFA=SFA, SFB=SFB)
+    got = Dg.ravel()[idx]
+    if integer:
+        assert np.array_equal(got, Dr)
+    else:
+        rep = check.report(got, Dr, S)
+        assert rep["fail"] == 0, rep
+
+
+@pytest.mark.parametrize("case", CASES, ids=["%dx%dx%d" % c for c in CASES])
+@pytest.mark.parametrize("out", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
+@pytest.mark.parametrize("integer", [True, False])
+def test_persistent_grid(case, out, integer, monkeypatch):
+    M, N, K = case
+    A, B, SFA, SFB = _inputs(M, N, K, M + N + K + integer, integer)
+    dA, dB, dSA, dSB = dev8(A), dev8(B), dev8(SFA), dev8(SFB)
+    say("mx persistent %dx%dx%d %s integer=%s" % (M, N, K, out, integer))
+    D = tg.gemm_mxfp8(dA, dSA, dB, dSB, out_dtype=out)
+    monkeypatch.setenv("TILEGEMM_MX_CONFIG", "4")          # one workgroup per tile
+    D1 = tg.gemm_mxfp8(dA, dSA, dB, dSB, out_dtype=out)
+    torch.cuda.synchronize()
+    assert torch.equal(D, D1)
+    if out == torch.float32:
+        _sampled_check(A, B, SFA, SFB, to_f64(D), integer, M + N)
+    else:
+        # bf16 D: the round-to-nearest-even of the fp32 result (itself
+        # checked against the oracle by the float32 cases)
+        monkeypatch.delenv("TILEGEMM_MX_CONFIG")
+        D32 = tg.gemm_mxfp8(dA, dSA, dB, dSB)
+        torch.cuda.synchronize()
+        assert np.array_equal(bf16_bits(D), oracle.rne_bf16_f32(D32.cpu().numpy()))
+
+
+def test_padded_d_rows_untouched():
+    M, N, K, pad = 4200, 4300, 512, 68
+    A, B, SFA, SFB = _inputs(M, N, K, 11, True)
+    Dbig = torch.full((M, N + pad), float("nan"), dtype=torch.float32, device=DEV)
+    D = Dbig[:, :N]
+    say("mx persistent padded D")
+    tg.gemm_mxfp8(dev8(A), dev8(SFA), dev8(B), dev8(SFB), D=D)
+    torch.cuda.synchronize()
+    assert bool(torch.isnan(Dbig[:, N:]).all())
+    _sampled_check(A, B, SFA, SFB, to_f64(D), True, 5)
+
+
+def test_calls_in_a_row_of_different_grids():
+    """Consecutive calls of the persistent kernel with different tile counts
+    and a smaller second grid (each workgroup's walk ends with its grid)."""
+    for (M, N, K) in [(8192, 4352, 512), (4200, 4300, 512), (4608, 4096, 1024)]:
+        A, B, SFA, SFB = _inputs(M, N, K, M + 2 * N, True)
+        say("mx persistent in a row %dx%dx%d" % (M, N, K))
+        D = tg.gemm_mxfp8(dev8(A), dev8(SFA), dev8(B), dev8(SFB))
+        torch.cuda.synchronize()
+        _sampled_check(A, B, SFA, SFB, to_f64(D), True, M)

@@ -8,6 +8,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "splitk.hpp"
 
 namespace tg_api {
@@ -81,6 +83,18 @@ inline gemm_status launched(hipError_t e) {
 }
 
 inline int64_t tiles_of(const Common &a, int bm, int bn) { return ((a.M + bm - 1) / bm) * ((a.N + bn - 1) / bn); }
+
+// Compute units of the stream's GPU (NULL stream: the current device),
+// looked up once per device; 0 when the runtime cannot tell.
+inline int cu_count(hipStream_t s) {
+    static std::atomic<int> counts[64];
+    int dev = 0;
+    if ((s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev)) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int n = counts[dev].load(std::memory_order_relaxed);
+    if (n == 0 && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+        counts[dev].store(n, std::memory_order_relaxed);
+    return n > 0 ? n : 0;
+}
 
 // ---- split-K (every input family) ------------------------------------------
 

@@ -122,8 +122,29 @@ __device__ __forceinline__ void mfma_mx16_acc(f32x4 &acc, const i32x8 &a, const 
 #undef TG_STR2
 }
 
-template <bool OUT_BF16, int DAUX = kStoreStream, bool SPLIT = false>
+// The kernel's arguments read again from the kernarg segment (where the
+// first argument, an MxArgs, starts at offset 0) through a pointer the
+// compiler cannot see through: a persistent kernel reads what it needs for
+// its next tile this way, so those values are not held in scalar registers
+// through the main loop.
+__device__ __forceinline__ MxArgs mx_args_reloaded() {
+    using KPtr = const __attribute__((address_space(4))) MxArgs *;
+    KPtr k = (KPtr)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(k));
+    return *(const MxArgs *)k;                         // (the loads stay scalar constant-memory loads)
+}
+
+// PERSIST: one workgroup per CU walks the tiles w, w + grid, w + 2 grid, ...
+// (virtual workgroup ids, so the XCD-aware tile order is the one a full
+// grid would have).  After a tile's last K step it issues the next tile's
+// first loads (K tile 0 and its scales, into the slots K tile 0 always
+// uses) and only then stages and stores the finished tile's D, from the
+// other slots, so those loads run while D drains; the next tile then waits
+// for its loads only, not for the stores issued after them.  Taken for
+// calls without C whose D rows allow whole 16-byte row segments.
+template <bool OUT_BF16, int DAUX = kStoreStream, bool SPLIT = false, bool PERSIST = false>
 __global__ void __launch_bounds__(256) gemm_mx_w4_kernel(MxArgs q, F16Epi e) {
+    static_assert(!(PERSIST && SPLIT), "persistent: whole tiles");
     const F16Args &p = q.g;
     constexpr int BK = 128, ROWB = 128;                // fp8: one byte per element
     constexpr int TM = 8, TN = 8, WTM = 128, WTN = 128;
@@ -144,18 +165,25 @@ __global__ void __launch_bounds__(256) gemm_mx_w4_kernel(MxArgs q, F16Epi e) {
     const int wm = wave >> 1, wn = wave & 1;
     int m0, n0, split, k_lo, K;
     mx_work_item<SPLIT>(p, m0, n0, split, k_lo, K);
-    const int M = p.M, N = p.N;
     const int nblk = K / 32;
     const int nk = K / BK, nep = K / 512;
+    int vt = blockIdx.x;                               // PERSIST: the virtual workgroup id
+    if constexpr (PERSIST) {
+        int tmi, tni;
+        tile_order(vt, p.tiles_m * p.tiles_n, p.tiles_m, p.tiles_n, p.group_m, tmi, tni);
+        m0 = tmi * 256;
+        n0 = tni * 256;
+    }
 
-    const __amdgpu_buffer_rsrc_t rA =
-        make_rsrc((const char *)p.A + (int64_t)m0 * p.lda + k_lo, span_bytes(M - m0, K, p.lda, 1));
-    const __amdgpu_buffer_rsrc_t rB =
-        make_rsrc((const char *)p.B + (int64_t)n0 * p.ldb + k_lo, span_bytes(N - n0, K, p.ldb, 1));
-    const __amdgpu_buffer_rsrc_t rSA =
-        make_rsrc((const char *)q.SFA + (int64_t)m0 * q.ldsfa + k_lo / 32, span_bytes(M - m0, nblk, q.ldsfa, 1));
-    const __amdgpu_buffer_rsrc_t rSB =
-        make_rsrc((const char *)q.SFB + (int64_t)n0 * q.ldsfb + k_lo / 32, span_bytes(N - n0, nblk, q.ldsfb, 1));
+    __amdgpu_buffer_rsrc_t rA, rB, rSA, rSB;
+    auto tile_resources = [&](const MxArgs &a) __attribute__((always_inline)) {
+        const F16Args &g = a.g;
+        rA = make_rsrc((const char *)g.A + (int64_t)m0 * g.lda + k_lo, span_bytes(g.M - m0, K, g.lda, 1));
+        rB = make_rsrc((const char *)g.B + (int64_t)n0 * g.ldb + k_lo, span_bytes(g.N - n0, K, g.ldb, 1));
+        rSA = make_rsrc((const char *)a.SFA + (int64_t)m0 * a.ldsfa + k_lo / 32, span_bytes(g.M - m0, nblk, a.ldsfa, 1));
+        rSB = make_rsrc((const char *)a.SFB + (int64_t)n0 * a.ldsfb + k_lo / 32, span_bytes(g.N - n0, nblk, a.ldsfb, 1));
+    };
+    tile_resources(q);
     const __amdgpu_buffer_rsrc_t rZ = make_rsrc(p.A, 0u);
 
     // Operand loads: instruction j of wave w fills slot rows (4 j + w) * 8 +
@@ -201,8 +229,13 @@ __global__ void __launch_bounds__(256) gemm_mx_w4_kernel(MxArgs q, F16Epi e) {
     // period, so the chunk offsets are the same for every block.
     const int fr = lane & 15, fq = lane >> 4;
     const int c0 = (fq ^ swz16(fr)) << 4;              // chunk q; chunk 4 + q is c0 ^ 64
-    const int la0 = A_BASE + (wm * WTM + fr) * ROWB + c0, la1 = la0 ^ 64;
-    const int lb0 = B_BASE + (wn * WTN + fr) * ROWB + c0, lb1 = lb0 ^ 64;
+    // (the four base addresses pass through an empty asm: otherwise the
+    // compiler rewrites base + constant as a bitwise or, which LDS reads
+    // cannot take as an immediate offset, and holds one address register per
+    // block and slot)
+    int la0 = A_BASE + (wm * WTM + fr) * ROWB + c0, la1 = la0 ^ 64;
+    int lb0 = B_BASE + (wn * WTN + fr) * ROWB + c0, lb1 = lb0 ^ 64;
+    asm volatile("" : "+v"(la0), "+v"(la1), "+v"(lb0), "+v"(lb1));
     auto ld32 = [&](int a0, int a1) __attribute__((always_inline)) {
         const u32x4 lo = *(const u32x4 *)(smem + a0), hi = *(const u32x4 *)(smem + a1);
         return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -212,11 +245,6 @@ __global__ void __launch_bounds__(256) gemm_mx_w4_kernel(MxArgs q, F16Epi e) {
     i32x8 fa[TM], fx;                                  // A fragments; fx: row 7 of odd tiles
     i32x8 fb[2][TN];                                   // B fragments by tile parity
     uint32_t sa[2][2], sb[2][2];                       // scale bytes by tile parity, 4 blocks each
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    mfma_result_fence<TM, TN>(acc);                    // the zeroing before the first MFMA reads them
 
     // Reads of tile t, whose position in its epoch U = t % 4 is a
     // compile-time constant at every call site (the loop advances by whole
@@ -311,29 +339,86 @@ __global__ void __launch_bounds__(256) gemm_mx_w4_kernel(MxArgs q, F16Epi e) {
         barrier();
     };
 
+    // The first K tile of the current output tile and its scales (nk > 0).
+    // wv, as, bs: the wave index and row steps; a persistent kernel passes
+    // them through an empty asm so that the 32 LDS destinations and scalar
+    // offsets of these loads are computed here, not held through the main
+    // loop.
+    auto prologue_loads = [&](int wv, uint32_t as, uint32_t bs) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dma(rA, A_BASE + (j * 4 + wv) * IB, a_base, (int)(j * as));
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dma(rB, B_BASE + (j * 4 + wv) * IB, b_base, (int)(j * bs));
+        const int l = lane_id();
+        dma(rSA, SA_BASE + wv * IB, (uint32_t)((64 * wv + l) * q.ldsfa), 0);
+        dma(rSB, SB_BASE + wv * IB, (uint32_t)((64 * wv + l) * q.ldsfb), 0);
+    };
+    // PERSIST: stores per wave of the finished tile's D (epilogue_rows16_vec:
+    // WTM / 16 passes of 16 / RPS stores, RPS = 64 / (WTN / 4))
+    constexpr int D_STORES = (WTM / 16) * (16 * WTN / 4 / 64);
+    // PERSIST: this wave's D staging area, in the slots K tile 0 does not use
+    float *stage = (float *)(smem + (wave < 2 ? A_BASE + SLOT : B_BASE + SLOT) + (wave & 1) * 16 * (WTN + 4) * 4);
+    static_assert(2 * 16 * (WTN + 4) * 4 <= SLOT, "staging areas");
+
     if (nk > 0) {
-        // prologue: tile 0 and the first epoch's scales
-#pragma unroll
-        for (int j = 0; j < 8; ++j) fetch_a(0, j);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) fetch_b(0, j);
-        fetch_scales(0);
+        prologue_loads(wave, a_step, b_step);
         wait_vmcnt<0>();
         barrier();
-        window(std::true_type(), std::integral_constant<int, 0>(), 0);
-        // windows 1 .. nk (nk a multiple of 4): tiles 0 .. nk - 1 computed
-        for (int t = 1; t <= nk; t += 4) {
-            window(std::false_type(), std::integral_constant<int, 1>(), t);
-            window(std::false_type(), std::integral_constant<int, 2>(), t + 1);
-            window(std::false_type(), std::integral_constant<int, 3>(), t + 2);
-            window(std::false_type(), std::integral_constant<int, 0>(), t + 3);
+    }
+    while (true) {
+        float z = 0.0f;                                // (made here, not a register held through the loop)
+        asm volatile("" : "+v"(z));
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{z, z, z, z};
+        mfma_result_fence<TM, TN>(acc);                // the zeroing before the first MFMA reads them
+        if (nk > 0) {
+            window(std::true_type(), std::integral_constant<int, 0>(), 0);
+            // windows 1 .. nk (nk a multiple of 4): tiles 0 .. nk - 1 computed
+            for (int t = 1; t <= nk; t += 4) {
+                window(std::false_type(), std::integral_constant<int, 1>(), t);
+                window(std::false_type(), std::integral_constant<int, 2>(), t + 1);
+                window(std::false_type(), std::integral_constant<int, 3>(), t + 2);
+                window(std::false_type(), std::integral_constant<int, 0>(), t + 3);
+            }
+        }
+        mfma_result_fence<TM, TN>(acc);
+        wait_vmcnt<0>();
+        wait_lgkmcnt0();
+        barrier();
+        if constexpr (!PERSIST) {
+            mx_epilogue<OUT_BF16, DAUX, SPLIT>(acc, smem, wave, lane, wm, wn, m0, n0, p, split, e);
+            break;
+        } else {
+            const MxArgs r = mx_args_reloaded();
+            const int dm0 = m0, dn0 = n0;              // the finished tile
+            const int nt = r.g.tiles_m * r.g.tiles_n;
+            vt += gridDim.x;
+            const bool more = vt < nt;
+            if (more) {
+                int tmi, tni;
+                tile_order(vt, nt, r.g.tiles_m, r.g.tiles_n, r.g.group_m, tmi, tni);
+                m0 = tmi * 256;
+                n0 = tni * 256;
+                tile_resources(r);
+                if (nk > 0) {
+                    int wv = wave;
+                    uint32_t as = a_step, bs = b_step;
+                    asm volatile("" : "+s"(wv), "+s"(as), "+s"(bs));
+                    prologue_loads(wv, as, bs);
+                }
+            }
+            epilogue_rows16_vec<OUT_BF16, TM, TN, DAUX>(acc, stage, lane, wm, wn, dm0, dn0, r.g.M, r.g.N, r.g.D,
+                                                        r.g.ldd);
+            if (!more) break;
+            // the next tile's first loads landed; up to 63 of the D stores issued after them may still run
+            static_assert(D_STORES >= 63, "vmcnt");
+            wait_vmcnt<63>();
+            wait_lgkmcnt0();
+            barrier();                                 // staging reads done before window 0 refills those slots
         }
     }
-    mfma_result_fence<TM, TN>(acc);
-    wait_vmcnt<0>();
-    wait_lgkmcnt0();
-    barrier();
-    mx_epilogue<OUT_BF16, DAUX, SPLIT>(acc, smem, wave, lane, wm, wn, m0, n0, p, split, e);
 }
 
 }  // namespace tg

@@ -33,14 +33,14 @@ gemm_status dispatch_mx(const Common &a, const void *SFA, int64_t ldsfa, const v
     const bool scales16 = a.K % 512 == 0 && (uintptr_t)SFA % 16 == 0 && (uintptr_t)SFB % 16 == 0 &&
                           ldsfa % 16 == 0 && ldsfb % 16 == 0;
     int cfg = forced_mx_cfg();
-    if (cfg == tg::kMxFourWave && !scales16) cfg = -1;
+    if ((cfg == tg::kMxFourWave || cfg == tg::kMxFourWavePersist) && !scales16) cfg = -1;
     if (cfg < 0) {
         // the four-wave kernel once its 256 x 256 grid is over half a wave
         // (measured at K = 4096: 160 tiles 46.9 against 71.3 us with
         // 128 x 128 tiles; at 128 tiles 128 x 128 is 2 % ahead)
         const int64_t t256 = tiles_of(a, 256, 256), t128 = tiles_of(a, 128, 128);
         if (scales16 && t256 > 128)
-            cfg = tg::kMxFourWave;
+            cfg = tg::kMxFourWavePersist;             // (persistent when the grid is over one wave, below)
         else if (t256 >= 240)
             cfg = tg::kMxWide;
         else if (t128 > 256)
@@ -79,6 +79,15 @@ gemm_status dispatch_mx(const Common &a, const void *SFA, int64_t ldsfa, const v
     tg::F16Epi e;
     e.vec_d = ((uintptr_t)a.D % vb) == 0 && a.ldd % 4 == 0;
     e.vec_c = a.C && ((uintptr_t)a.C % vb) == 0 && a.ldc % 4 == 0;
+    if (cfg == tg::kMxFourWavePersist) {
+        // persistent over grids of more than one workgroup per CU, without C
+        // and with D rows of whole 16-byte segments (its epilogue's stores)
+        const int cus = cu_count(s);
+        if (!a.C && e.vec_d && a.N % 4 == 0 && cus > 0 && tiles > cus)
+            return launched(bf16 ? tg::launch_mx_persist<true>((unsigned)cus, s, q, e)
+                                 : tg::launch_mx_persist<false>((unsigned)cus, s, q, e));
+        cfg = tg::kMxFourWave;
+    }
     return launched(bf16 ? tg::launch_mx<true>(cfg, (unsigned)tiles, s, q, e)
                          : tg::launch_mx<false>(cfg, (unsigned)tiles, s, q, e));
 }

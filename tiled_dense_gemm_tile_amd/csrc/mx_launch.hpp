@@ -23,15 +23,20 @@ struct MxCfgInfo {
 
 #define TG_MX_INFO(id, bm, bn, wm, wn, ns) {bm, bn, wm, wn},
 // Then the four-wave kernel (256 x 256, 128 x 128 per wave, 16x16x128
-// MFMA, K % 512 == 0, 16-byte scale rows; gemm_mx_w4.hpp).
-constexpr MxCfgInfo kMxCfgs[] = {TG_MX_CONFIGS(TG_MX_INFO){256, 256, 2, 2}};
+// MFMA, K % 512 == 0, 16-byte scale rows; gemm_mx_w4.hpp), one workgroup
+// per tile or persistent (one per CU walking the tiles).
+constexpr MxCfgInfo kMxCfgs[] = {TG_MX_CONFIGS(TG_MX_INFO){256, 256, 2, 2}, {256, 256, 2, 2}};
 #undef TG_MX_INFO
 constexpr int kNumMxCfgs = sizeof(kMxCfgs) / sizeof(kMxCfgs[0]);
-constexpr int kMxWide = 0, kMx128 = 1, kMxDeep128 = 2, kMxDeep64 = 3, kMxFourWave = 4;
-static_assert(kMxFourWave + 1 == kNumMxCfgs, "configuration table");
+constexpr int kMxWide = 0, kMx128 = 1, kMxDeep128 = 2, kMxDeep64 = 3, kMxFourWave = 4, kMxFourWavePersist = 5;
+static_assert(kMxFourWavePersist + 1 == kNumMxCfgs, "configuration table");
 
 template <bool OUT_BF16>
 hipError_t launch_mx(int cfg, unsigned grid, hipStream_t s, const MxArgs &q, const F16Epi &e);
+
+// The persistent four-wave kernel: `grid` workgroups walk all tiles.
+template <bool OUT_BF16>
+hipError_t launch_mx_persist(unsigned grid, hipStream_t s, const MxArgs &q, const F16Epi &e);
 
 // Split-K partial tiles (fp32, into q.g.ws): the four-wave kernel with SPLIT;
 // defined in the fp32-output translation unit.
@@ -59,6 +64,12 @@ hipError_t launch_mx<TG_OUT_BF16>(int cfg, unsigned grid, hipStream_t s, const M
     default:
         return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+
+template <>
+hipError_t launch_mx_persist<TG_OUT_BF16>(unsigned grid, hipStream_t s, const MxArgs &q, const F16Epi &e) {
+    hipLaunchKernelGGL((gemm_mx_w4_kernel<TG_OUT_BF16, kStoreStream, false, true>), dim3(grid), dim3(256), 0, s, q, e);
     return hipGetLastError();
 }
 

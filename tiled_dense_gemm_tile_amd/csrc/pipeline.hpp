@@ -180,6 +180,67 @@ __device__ __forceinline__ void epilogue_lds16(const f32x4 (&acc)[TM][TN], char 
     epilogue_lds_passes<OUT_BF16, WTM, WTN, 4, DAUX>(stage, smem, wave, lane, wm, wn, m0, n0, M, N, C, ldc, D, ldd, e);
 }
 
+// D = acc (no C) for one wave's (16 TM) x (16 TN) block of 16x16 MFMA
+// accumulators acc[i][j] (lane l, register r: row 4 (l / 16) + r, column
+// l % 16 of block (i, j)), for the persistent kernels: passes of one block
+// row (16 rows) staged through `stage`, this wave's own 16 x (16 TN + 4)
+// floats, and every lane stores whole 16-byte (bf16: 8-byte) row segments
+// -- the caller guarantees N % 4 == 0, 16-byte-aligned D rows, and segments
+// past M or N get an offset beyond the resource, which drops them.  So a
+// pass issues exactly 16 / RPS stores per lane whatever the tile's edges
+// (the caller counts them to wait for loads issued before the stores).
+template <bool OUT_BF16, int TM, int TN, int DAUX>
+__device__ __forceinline__ void epilogue_rows16_vec(const f32x4 (&acc)[TM][TN], float *stage, int lane, int wm,
+                                                    int wn, int m0, int n0, int M, int N, void *D, int64_t ldd) {
+    constexpr int OS = OUT_BF16 ? 2 : 4;
+    constexpr int WTM = TM * 16, WTN = TN * 16;
+    constexpr int EP = WTN + 4;                        // lane quarters 4 rows apart: 16 banks apart
+    constexpr int LPR = WTN / 4;                       // lanes per staged row (4 floats each)
+    constexpr int RPS = 64 / LPR;                      // rows per store instruction
+    const __amdgpu_buffer_rsrc_t rD =
+        make_rsrc((char *)D + (int64_t)m0 * ldd * OS, span_bytes(M - m0, N, ldd, OS));
+    // (the lane index passes through an empty asm: in a persistent kernel's
+    // tile loop, offsets derived from it would otherwise be hoisted out of
+    // the loop and held in registers through the whole main loop)
+    asm volatile("" : "+v"(lane));
+    const int fc = lane & 15, fq = lane >> 4;
+    const int erow = lane / LPR, ecol = (lane % LPR) * 4;
+    const int gcol = n0 + wn * WTN + ecol;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        // (one block row's accumulators in flight at a time: the scheduler
+        // would otherwise read them all out of the AGPRs at once)
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                // (read out of the AGPR here, at its store: left to the
+                // compiler, all of acc is copied to VGPRs at the epilogue's start)
+                float v;
+                asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(acc[i][j][r]));
+                stage[(4 * fq + r) * EP + j * 16 + fc] = v;
+            }
+        wait_lgkmcnt0();
+#pragma unroll
+        for (int q = 0; q < 16 / RPS; ++q) {
+            const int lr = q * RPS + erow;
+            const f32x4 v = *(const f32x4 *)(stage + lr * EP + ecol);
+            const int row = wm * WTM + i * 16 + lr;
+            const uint32_t doff = (m0 + row < M && gcol < N) ? (uint32_t)(row * ldd + gcol) * OS : kOOB;
+            if constexpr (OUT_BF16) {
+                u32x2 pk;
+                pk[0] = pack_bf16x2(v[0], v[1]);
+                pk[1] = pack_bf16x2(v[2], v[3]);
+                __builtin_amdgcn_raw_buffer_store_b64(pk, rD, doff, 0, DAUX);
+            } else {
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rD, doff, 0, DAUX);
+            }
+        }
+        wait_lgkmcnt0();   // reads of this pass done before the next pass overwrites the stage
+    }
+}
+
 // Epilogue for transposed 16x16 MFMA blocks acc[i][j] (lane l, register r
 // holds row l % 16 and column 4 (l / 16) + r of block (i, j)); a pass stages
 // two block rows, one 16-byte LDS write per block.

@@ -1,7 +1,7 @@
-"""Block-scaled fp8 grids of more 256 x 256 tiles than the GPU has compute
-units, without C: the persistent four-wave kernel (one workgroup per CU
-walking the tiles, its next tile's first loads in flight while the finished
-tile's D is stored).
+"""Block-scaled fp8 and fp4 grids of more 256 x 256 tiles than the GPU has
+compute units, without C: the persistent four-wave kernels (one workgroup
+per CU walking the tiles, its next tile's first loads in flight while the
+finished tile's D is stored).
 
 Bar: exact on integer-valued inputs against the oracle at 4096 seeded
 samples plus the tile edges, within the tolerance on random inputs, and bit
@@ -28,21 +28,28 @@ if torch.cuda.is_available():
 CASES = [(4200, 4300, 1024), (8192, 8192, 512), (4352, 4096, 512), (4100, 4104, 2048)]
 
 
-def _inputs(M, N, K, seed, integer):
+# fp8: integer codes in [-4, 4] with scale exponents 0, 1; fp4: any code
+# with exponents 1, 2 (every product an integer)
+def _inputs(M, N, K, seed, integer, fmt="e4m3"):
     rng = np.random.default_rng(seed)
-    A = inputs.random_codes(rng, "e4m3", (M, K), integer=integer)
-    B = inputs.random_codes(rng, "e4m3", (N, K), integer=integer)
-    lo, hi = (0, 2) if integer else (-4, 5)
+    A = inputs.random_codes(rng, fmt, (M, K), integer=integer)
+    B = inputs.random_codes(rng, fmt, (N, K), integer=integer)
+    lo, hi = ((0, 2) if fmt == "e4m3" else (1, 3)) if integer else (-4, 5)
     SFA = (127 + rng.integers(lo, hi, size=(M, K // 32))).astype(np.uint8)
     SFB = (127 + rng.integers(lo, hi, size=(N, K // 32))).astype(np.uint8)
     return A, B, SFA, SFB
 
 
-def _sampled_check(A, B, SFA, SFB, Dg, integer, seed):
+def _call(fmt, A, SFA, B, SFB, **kw):
+    fn = tg.gemm_mxfp8 if fmt == "e4m3" else tg.gemm_mxfp4
+    return fn(A, SFA, B, SFB, **kw)
+
+
+def _sampled_check(A, B, SFA, SFB, Dg, integer, seed, fmt="e4m3"):
     M, N = Dg.shape
     rand, forced = inputs.sample_indices(M, N, seed)
     idx = np.concatenate([rand, forced])
-    Dr, S = oracle.gemm_ref("e4m3", A, B, idx=idx, SFA=SFA, SFB=SFB)
+    Dr, S = oracle.gemm_ref(fmt, A, B, idx=idx, SFA=SFA, SFB=SFB)
     got = Dg.ravel()[idx]
     if integer:
         assert np.array_equal(got, Dr)
@@ -51,48 +58,55 @@ def _sampled_check(A, B, SFA, SFB, Dg, integer, seed):
         assert rep["fail"] == 0, rep
 
 
+# the switch that sends a call to the one-workgroup-per-tile kernel instead
+PER_TILE = {"e4m3": ("TILEGEMM_MX_CONFIG", "4"), "e2m1": ("TILEGEMM_MX4_PERSIST", "0")}
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
 @pytest.mark.parametrize("case", CASES, ids=["%dx%dx%d" % c for c in CASES])
 @pytest.mark.parametrize("out", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
 @pytest.mark.parametrize("integer", [True, False])
-def test_persistent_grid(case, out, integer, monkeypatch):
+def test_persistent_grid(fmt, case, out, integer, monkeypatch):
     M, N, K = case
-    A, B, SFA, SFB = _inputs(M, N, K, M + N + K + integer, integer)
+    A, B, SFA, SFB = _inputs(M, N, K, M + N + K + integer, integer, fmt)
     dA, dB, dSA, dSB = dev8(A), dev8(B), dev8(SFA), dev8(SFB)
-    say("mx persistent %dx%dx%d %s integer=%s" % (M, N, K, out, integer))
-    D = tg.gemm_mxfp8(dA, dSA, dB, dSB, out_dtype=out)
-    monkeypatch.setenv("TILEGEMM_MX_CONFIG", "4")          # one workgroup per tile
-    D1 = tg.gemm_mxfp8(dA, dSA, dB, dSB, out_dtype=out)
+    say("mx persistent %s %dx%dx%d %s integer=%s" % (fmt, M, N, K, out, integer))
+    D = _call(fmt, dA, dSA, dB, dSB, out_dtype=out)
+    monkeypatch.setenv(*PER_TILE[fmt])
+    D1 = _call(fmt, dA, dSA, dB, dSB, out_dtype=out)
     torch.cuda.synchronize()
     assert torch.equal(D, D1)
     if out == torch.float32:
-        _sampled_check(A, B, SFA, SFB, to_f64(D), integer, M + N)
+        _sampled_check(A, B, SFA, SFB, to_f64(D), integer, M + N, fmt)
     else:
         # bf16 D: the round-to-nearest-even of the fp32 result (itself
         # checked against the oracle by the float32 cases)
-        monkeypatch.delenv("TILEGEMM_MX_CONFIG")
-        D32 = tg.gemm_mxfp8(dA, dSA, dB, dSB)
+        monkeypatch.delenv(PER_TILE[fmt][0])
+        D32 = _call(fmt, dA, dSA, dB, dSB)
         torch.cuda.synchronize()
         assert np.array_equal(bf16_bits(D), oracle.rne_bf16_f32(D32.cpu().numpy()))
 
 
-def test_padded_d_rows_untouched():
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
+def test_padded_d_rows_untouched(fmt):
     M, N, K, pad = 4200, 4300, 512, 68
-    A, B, SFA, SFB = _inputs(M, N, K, 11, True)
+    A, B, SFA, SFB = _inputs(M, N, K, 11, True, fmt)
     Dbig = torch.full((M, N + pad), float("nan"), dtype=torch.float32, device=DEV)
     D = Dbig[:, :N]
-    say("mx persistent padded D")
-    tg.gemm_mxfp8(dev8(A), dev8(SFA), dev8(B), dev8(SFB), D=D)
+    say("mx persistent %s padded D" % fmt)
+    _call(fmt, dev8(A), dev8(SFA), dev8(B), dev8(SFB), D=D)
     torch.cuda.synchronize()
     assert bool(torch.isnan(Dbig[:, N:]).all())
-    _sampled_check(A, B, SFA, SFB, to_f64(D), True, 5)
+    _sampled_check(A, B, SFA, SFB, to_f64(D), True, 5, fmt)
 
 
-def test_calls_in_a_row_of_different_grids():
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
+def test_calls_in_a_row_of_different_grids(fmt):
     """Consecutive calls of the persistent kernel with different tile counts
     and a smaller second grid (each workgroup's walk ends with its grid)."""
     for (M, N, K) in [(8192, 4352, 512), (4200, 4300, 512), (4608, 4096, 1024)]:
-        A, B, SFA, SFB = _inputs(M, N, K, M + 2 * N, True)
-        say("mx persistent in a row %dx%dx%d" % (M, N, K))
-        D = tg.gemm_mxfp8(dev8(A), dev8(SFA), dev8(B), dev8(SFB))
+        A, B, SFA, SFB = _inputs(M, N, K, M + 2 * N, True, fmt)
+        say("mx persistent %s in a row %dx%dx%d" % (fmt, M, N, K))
+        D = _call(fmt, dev8(A), dev8(SFA), dev8(B), dev8(SFB))
         torch.cuda.synchronize()
-        _sampled_check(A, B, SFA, SFB, to_f64(D), True, M)
+        _sampled_check(A, B, SFA, SFB, to_f64(D), True, M, fmt)

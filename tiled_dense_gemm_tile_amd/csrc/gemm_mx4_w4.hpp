@@ -56,9 +56,12 @@ __device__ __forceinline__ void mfma_mx4_acc(f32x4 &acc, const u32x4 &a, const u
 }
 
 // q.g.lda and q.g.ldb are in BYTES here (half the leading dimension in
-// elements); q.g.K is in elements.
-template <bool OUT_BF16, int DAUX = kStoreStream, bool SPLIT = false>
+// elements); q.g.K is in elements.  PERSIST: one workgroup per CU walking
+// the tiles, as the persistent fp8 kernel (no C, D rows of whole 16-byte
+// segments).
+template <bool OUT_BF16, int DAUX = kStoreStream, bool SPLIT = false, bool PERSIST = false>
 __global__ void __launch_bounds__(256) gemm_mx4_w4_kernel(MxArgs q, F16Epi e) {
+    static_assert(!(PERSIST && SPLIT), "persistent: whole tiles");
     const F16Args &p = q.g;
     constexpr int ROWB = 128, BKB = 128;               // bytes per LDS row = bytes per K tile (256 elements)
     constexpr int TM = 8, TN = 8, WTM = 128, WTN = 128;
@@ -79,18 +82,25 @@ __global__ void __launch_bounds__(256) gemm_mx4_w4_kernel(MxArgs q, F16Epi e) {
     const int wm = wave >> 1, wn = wave & 1;
     int m0, n0, split, k_lo, K;
     mx_work_item<SPLIT>(p, m0, n0, split, k_lo, K);
-    const int M = p.M, N = p.N;
     const int kb = K / 2, nblk = K / 32;
     const int nk = K / 256, nep = K / 512;
+    int vt = blockIdx.x;                               // PERSIST: the virtual workgroup id
+    if constexpr (PERSIST) {
+        int tmi, tni;
+        tile_order(vt, p.tiles_m * p.tiles_n, p.tiles_m, p.tiles_n, p.group_m, tmi, tni);
+        m0 = tmi * 256;
+        n0 = tni * 256;
+    }
 
-    const __amdgpu_buffer_rsrc_t rA =
-        make_rsrc((const char *)p.A + (int64_t)m0 * p.lda + k_lo / 2, span_bytes(M - m0, kb, p.lda, 1));
-    const __amdgpu_buffer_rsrc_t rB =
-        make_rsrc((const char *)p.B + (int64_t)n0 * p.ldb + k_lo / 2, span_bytes(N - n0, kb, p.ldb, 1));
-    const __amdgpu_buffer_rsrc_t rSA =
-        make_rsrc((const char *)q.SFA + (int64_t)m0 * q.ldsfa + k_lo / 32, span_bytes(M - m0, nblk, q.ldsfa, 1));
-    const __amdgpu_buffer_rsrc_t rSB =
-        make_rsrc((const char *)q.SFB + (int64_t)n0 * q.ldsfb + k_lo / 32, span_bytes(N - n0, nblk, q.ldsfb, 1));
+    __amdgpu_buffer_rsrc_t rA, rB, rSA, rSB;
+    auto tile_resources = [&](const MxArgs &a) __attribute__((always_inline)) {
+        const F16Args &g = a.g;
+        rA = make_rsrc((const char *)g.A + (int64_t)m0 * g.lda + k_lo / 2, span_bytes(g.M - m0, kb, g.lda, 1));
+        rB = make_rsrc((const char *)g.B + (int64_t)n0 * g.ldb + k_lo / 2, span_bytes(g.N - n0, kb, g.ldb, 1));
+        rSA = make_rsrc((const char *)a.SFA + (int64_t)m0 * a.ldsfa + k_lo / 32, span_bytes(g.M - m0, nblk, a.ldsfa, 1));
+        rSB = make_rsrc((const char *)a.SFB + (int64_t)n0 * a.ldsfb + k_lo / 32, span_bytes(g.N - n0, nblk, a.ldsfb, 1));
+    };
+    tile_resources(q);
     const __amdgpu_buffer_rsrc_t rZ = make_rsrc(p.A, 0u);
 
     // Operand loads: instruction j of wave w fills slot rows (4 j + w) * 8 +
@@ -136,25 +146,26 @@ __global__ void __launch_bounds__(256) gemm_mx4_w4_kernel(MxArgs q, F16Epi e) {
     // period, so the offsets are the same for every block.
     const int fr = lane & 15, fq = lane >> 4;
     const int c0 = (fq ^ swz16(fr)) << 4;              // step 0: chunk q; step 1: chunk 4 + q at c0 ^ 64
-    const int la = A_BASE + (wm * WTM + fr) * ROWB + c0;
-    const int lb = B_BASE + (wn * WTN + fr) * ROWB + c0;
+    // (one base per operand and step, through an empty asm so that block and
+    // slot offsets fold into the LDS reads' immediate offsets)
+    int la[2], lb[2];
+    la[0] = A_BASE + (wm * WTM + fr) * ROWB + c0;
+    lb[0] = B_BASE + (wn * WTN + fr) * ROWB + c0;
+    la[1] = la[0] ^ 64;
+    lb[1] = lb[0] ^ 64;
+    asm volatile("" : "+v"(la[0]), "+v"(la[1]), "+v"(lb[0]), "+v"(lb[1]));
     auto ld16 = [&](int a) __attribute__((always_inline)) { return *(const u32x4 *)(smem + a); };
 
     f32x4 acc[TM][TN];
     u32x4 fa[2][TM], fx[2];                            // A fragments by step; fx: row 7 of odd tiles
     u32x4 fb[2][2][TN];                                // B fragments by tile parity and step
     uint32_t sa[2][4], sb[2][4];                       // scale bytes by tile parity and block-row pair
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    mfma_result_fence<TM, TN>(acc);                    // the zeroing before the first MFMA reads them
 
     // Reads of tile t (parity P = U, its place in the epoch, a compile-time
     // constant at every call site).  A fragment of block row I, step S:
     auto read_a = [&](auto uc, auto ic, auto sc) __attribute__((always_inline)) {
         constexpr int P = decltype(uc)::value, I = decltype(ic)::value, S = decltype(sc)::value;
-        const u32x4 v = ld16((la ^ (S * 64)) + P * SLOT + I * 16 * ROWB);
+        const u32x4 v = ld16(la[S] + P * SLOT + I * 16 * ROWB);
         if constexpr (I < TM - 1 || !P)
             fa[S][I] = v;
         else
@@ -162,7 +173,7 @@ __global__ void __launch_bounds__(256) gemm_mx4_w4_kernel(MxArgs q, F16Epi e) {
     };
     auto read_b = [&](auto uc, auto jc, auto sc) __attribute__((always_inline)) {
         constexpr int P = decltype(uc)::value, J = decltype(jc)::value, S = decltype(sc)::value;
-        fb[P][S][J] = ld16((lb ^ (S * 64)) + P * SLOT + J * 16 * ROWB);
+        fb[P][S][J] = ld16(lb[S] + P * SLOT + J * 16 * ROWB);
     };
     // Scale registers of a tile: register h of A (of B) holds, for the
     // lane's row r of the quadrant and its K block q of each step, the
@@ -176,7 +187,11 @@ __global__ void __launch_bounds__(256) gemm_mx4_w4_kernel(MxArgs q, F16Epi e) {
     // LDS reads still in flight.
     const uint32_t sel_lo = (uint32_t)fq | ((uint32_t)(fq + 4) << 8) | 0x0c0c0000u;   // 0x0c: a zero byte
     const uint32_t sel_hi = 0x00000c0cu | ((uint32_t)fq << 16) | ((uint32_t)(fq + 4) << 24);
-    const int srow_a = SA_BASE + (wm * WTM + fr) * 16, srow_b = SB_BASE + (wn * WTN + fr) * 16;
+    // (row bases through an empty asm: every scale read then takes its
+    // block-row and epoch offset as an immediate, instead of the compiler
+    // holding a hoisted address per read)
+    int srow_a = SA_BASE + (wm * WTM + fr) * 16, srow_b = SB_BASE + (wn * WTN + fr) * 16;
+    asm volatile("" : "+v"(srow_a), "+v"(srow_b));
     u32x2 sraw[2][2];
     // register c of tile t: A pair c (c < 4) or B pair c - 4
     auto scale_issue = [&](auto uc, auto cc, auto gc, int t) __attribute__((always_inline)) {
@@ -245,27 +260,79 @@ __global__ void __launch_bounds__(256) gemm_mx4_w4_kernel(MxArgs q, F16Epi e) {
         barrier();
     };
 
+    // Tile 0 of the current output tile and the first epoch's scales (nk >
+    // 0); wv, as, bs as in the persistent fp8 kernel.
+    auto prologue_loads = [&](int wv, uint32_t as, uint32_t bs) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dma(rA, A_BASE + (j * 4 + wv) * IB, a_base, (int)(j * as));
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dma(rB, B_BASE + (j * 4 + wv) * IB, b_base, (int)(j * bs));
+        const int l = lane_id();
+        dma(rSA, SA_BASE + wv * IB, (uint32_t)((64 * wv + l) * q.ldsfa), 0);
+        dma(rSB, SB_BASE + wv * IB, (uint32_t)((64 * wv + l) * q.ldsfb), 0);
+    };
+    // PERSIST: this wave's D staging area, in the slots tile 0 does not use
+    float *stage = (float *)(smem + (wave < 2 ? A_BASE + SLOT : B_BASE + SLOT) + (wave & 1) * 16 * (WTN + 4) * 4);
+    static_assert(2 * 16 * (WTN + 4) * 4 <= SLOT, "staging areas");
+    constexpr int D_STORES = (WTM / 16) * (16 * WTN / 4 / 64);
+
     if (nk > 0) {
-        // prologue: tile 0 and the first epoch's scales
-#pragma unroll
-        for (int j = 0; j < 8; ++j) fetch_a(0, j);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) fetch_b(0, j);
-        fetch_scales(0);
+        prologue_loads(wave, a_step, b_step);
         wait_vmcnt<0>();
         barrier();
-        window(std::true_type(), std::integral_constant<int, 0>(), 0);
-        // windows 1 .. nk (nk even): tiles 0 .. nk - 1 computed
-        for (int t = 1; t <= nk; t += 2) {
-            window(std::false_type(), std::integral_constant<int, 1>(), t);
-            window(std::false_type(), std::integral_constant<int, 0>(), t + 1);
+    }
+    while (true) {
+        float z = 0.0f;                                // (made here, not a register held through the loop)
+        asm volatile("" : "+v"(z));
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{z, z, z, z};
+        mfma_result_fence<TM, TN>(acc);                // the zeroing before the first MFMA reads them
+        if (nk > 0) {
+            window(std::true_type(), std::integral_constant<int, 0>(), 0);
+            // windows 1 .. nk (nk even): tiles 0 .. nk - 1 computed
+            for (int t = 1; t <= nk; t += 2) {
+                window(std::false_type(), std::integral_constant<int, 1>(), t);
+                window(std::false_type(), std::integral_constant<int, 0>(), t + 1);
+            }
+        }
+        mfma_result_fence<TM, TN>(acc);
+        wait_vmcnt<0>();
+        wait_lgkmcnt0();
+        barrier();
+        if constexpr (!PERSIST) {
+            mx_epilogue<OUT_BF16, DAUX, SPLIT>(acc, smem, wave, lane, wm, wn, m0, n0, p, split, e);
+            break;
+        } else {
+            const MxArgs r = mx_args_reloaded();
+            const int dm0 = m0, dn0 = n0;              // the finished tile
+            const int nt = r.g.tiles_m * r.g.tiles_n;
+            vt += gridDim.x;
+            const bool more = vt < nt;
+            if (more) {
+                int tmi, tni;
+                tile_order(vt, nt, r.g.tiles_m, r.g.tiles_n, r.g.group_m, tmi, tni);
+                m0 = tmi * 256;
+                n0 = tni * 256;
+                tile_resources(r);
+                if (nk > 0) {
+                    int wv = wave;
+                    uint32_t as = a_step, bs = b_step;
+                    asm volatile("" : "+s"(wv), "+s"(as), "+s"(bs));
+                    prologue_loads(wv, as, bs);
+                }
+            }
+            epilogue_rows16_vec<OUT_BF16, TM, TN, DAUX>(acc, stage, lane, wm, wn, dm0, dn0, r.g.M, r.g.N, r.g.D,
+                                                        r.g.ldd);
+            if (!more) break;
+            // the next tile's first loads landed; up to 63 of the D stores issued after them may still run
+            static_assert(D_STORES >= 63, "vmcnt");
+            wait_vmcnt<63>();
+            wait_lgkmcnt0();
+            barrier();                                 // staging reads done before window 0 refills those slots
         }
     }
-    mfma_result_fence<TM, TN>(acc);
-    wait_vmcnt<0>();
-    wait_lgkmcnt0();
-    barrier();
-    mx_epilogue<OUT_BF16, DAUX, SPLIT>(acc, smem, wave, lane, wm, wn, m0, n0, p, split, e);
 }
 
 }  // namespace tg

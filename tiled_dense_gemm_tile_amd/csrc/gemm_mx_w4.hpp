@@ -277,10 +277,13 @@ __global__ void __launch_bounds__(256) gemm_mx_w4_kernel(MxArgs q, F16Epi e) {
     const uint32_t sel_lo = (uint32_t)fq | ((uint32_t)(fq + 4) << 8) | 0x0c0c0000u;   // 0x0c: a zero byte
     const uint32_t sel_hi = 0x00000c0cu | ((uint32_t)fq << 16) | ((uint32_t)(fq + 4) << 24);
     uint32_t sraw[2][4];
+    // (row bases through an empty asm: every scale read then takes its
+    // block-row and epoch offset as an immediate)
+    int srow_a = SA_BASE + (wm * WTM + fr) * 16, srow_b = SB_BASE + (wn * WTN + fr) * 16;
+    asm volatile("" : "+v"(srow_a), "+v"(srow_b));
     auto scale_issue = [&](auto uc, auto hc, auto gc, int t) __attribute__((always_inline)) {
         constexpr int U = decltype(uc)::value, H = decltype(hc)::value, G = decltype(gc)::value;
-        const int row = (H < 2 ? wm * WTM : wn * WTN) + fr;
-        const int base = (H < 2 ? SA_BASE : SB_BASE) + row * 16 + ((t >> 2) & 1) * SS + U * 4 + (H & 1) * 4 * 256;
+        const int base = (H < 2 ? srow_a : srow_b) + ((t >> 2) & 1) * SS + U * 4 + (H & 1) * 4 * 256;
 #pragma unroll
         for (int u = 0; u < 4; ++u) sraw[G][u] = *(const uint32_t *)(smem + base + u * 256);
     };

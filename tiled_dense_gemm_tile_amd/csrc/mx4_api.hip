@@ -11,6 +11,13 @@ using namespace tg_api;
 
 namespace {
 
+// Test override: TILEGEMM_MX4_PERSIST=0 launches one workgroup per tile
+// where the persistent kernel would run.
+bool persist_allowed() {
+    const char *e = getenv("TILEGEMM_MX4_PERSIST");
+    return !(e && e[0] == '0');
+}
+
 // 16-byte A/B chunks (32 elements), 16-byte scale words (512 K) per row
 bool fast_mx4(const Common &a, const void *SFA, int64_t ldsfa, const void *SFB, int64_t ldsfb) {
     return a.K % 512 == 0 && (uintptr_t)a.A % 16 == 0 && (uintptr_t)a.B % 16 == 0 && a.lda % 32 == 0 &&
@@ -60,6 +67,12 @@ gemm_status dispatch_mx4(const Common &a, const void *SFA, int64_t ldsfa, const 
     tg::F16Epi e;
     e.vec_d = ((uintptr_t)a.D % vb) == 0 && a.ldd % 4 == 0;
     e.vec_c = a.C && ((uintptr_t)a.C % vb) == 0 && a.ldc % 4 == 0;
+    // more tiles than CUs, no C, D rows of whole 16-byte segments: the
+    // persistent kernel (TILEGEMM_MX4_PERSIST=0 turns it off)
+    const int cus = cu_count(s);
+    if (!a.C && e.vec_d && a.N % 4 == 0 && cus > 0 && tiles > cus && persist_allowed())
+        return launched(bf16 ? tg::launch_mx4_persist<true>((unsigned)cus, s, q, e)
+                             : tg::launch_mx4_persist<false>((unsigned)cus, s, q, e));
     return launched(bf16 ? tg::launch_mx4<true>((unsigned)tiles, s, q, e)
                          : tg::launch_mx4<false>((unsigned)tiles, s, q, e));
 }

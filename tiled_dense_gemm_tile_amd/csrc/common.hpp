@@ -111,6 +111,19 @@ __device__ __forceinline__ void tile_order(int wg, int nwg, int tiles_m, int til
 }
 
 // Split-K work item of workgroup wg out of nwg = tiles * splits: the same
+// The kernel's first argument, a T at offset 0 of the kernarg segment, read
+// again through a pointer the compiler cannot see through: a persistent
+// kernel reads what it needs for its next tile this way, so those values are
+// not held in scalar registers through its main loop.  (The cast back to a
+// generic pointer keeps the loads scalar constant-memory loads.)
+template <class T>
+__device__ __forceinline__ T kernel_arg0_reloaded() {
+    using KPtr = const __attribute__((address_space(4))) T *;
+    KPtr k = (KPtr)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(k));
+    return *(const T *)k;
+}
+
 // XCD renumbering as tile_order, then split = id / tiles and the tile from
 // id % tiles in groups of `group_m` tile-rows, so the workgroups running
 // together on an XCD share the K range of their A and B panels.

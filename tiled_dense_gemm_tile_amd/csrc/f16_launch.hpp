@@ -31,17 +31,20 @@ struct F16CfgInfo {
 
 #define TG_F16_INFO(id, bm, bn, bk, wm, wn, na, nb) {bm, bn, bk, wm, wn, na, nb},
 // Then the four-wave kernels (gemm_f16_w4.hpp): 256 x 256 tiles with
-// 16-byte rows and with rows only 8-byte aligned (shifted rows), and the
-// same two with 192 x 256 tiles.
+// 16-byte rows and with rows only 8-byte aligned (shifted rows), the same
+// two with 192 x 256 tiles, and the persistent one (16-byte rows, 256 x 256,
+// no C; launched with one workgroup per CU).
 constexpr F16CfgInfo kF16DmaCfgs[] = {TG_F16_DMA_CONFIGS(TG_F16_INFO){256, 256, 64, 2, 2, 2, 2},
                                       {256, 256, 64, 2, 2, 2, 2},
                                       {192, 256, 64, 2, 2, 2, 2},
-                                      {192, 256, 64, 2, 2, 2, 2}};
+                                      {192, 256, 64, 2, 2, 2, 2},
+                                      {256, 256, 64, 2, 2, 2, 2}};
 #undef TG_F16_INFO
 constexpr int kNumF16DmaCfgs = sizeof(kF16DmaCfgs) / sizeof(kF16DmaCfgs[0]);
 constexpr int kF16Wide4Lane = 0, kF16Wide128 = 1, kF16Small64 = 2, kF16Deep128 = 3, kF16Deep64 = 4;
 constexpr int kF16FourWave = 5, kF16FourWaveS = 6, kF16FourWave192 = 7, kF16FourWaveS192 = 8;
-static_assert(kF16FourWaveS192 + 1 == kNumF16DmaCfgs, "configuration table");
+constexpr int kF16FourWavePersist = 9;
+static_assert(kF16FourWavePersist + 1 == kNumF16DmaCfgs, "configuration table");
 // Configurations that take rows only 4- or 8-byte aligned.
 constexpr bool f16_any_rows(int id) {
     return f16_has_lane4(id) || id == kF16FourWaveS || id == kF16FourWaveS192;
@@ -90,12 +93,15 @@ hipError_t launch_f16_dma<TG_FP16, TG_OUT_BF16>(int cfg, int lane_bytes, unsigne
                            dim3(256), 0, s, p, e);
         return hipGetLastError();
     }
-    if (cfg == kF16FourWave || cfg == kF16FourWave192) {
+    if (cfg == kF16FourWave || cfg == kF16FourWave192 || cfg == kF16FourWavePersist) {
         if (lane_bytes != 16) return hipErrorInvalidValue;
         if (cfg == kF16FourWave)
             hipLaunchKernelGGL((gemm_f16_w4t_kernel<TG_FP16, TG_OUT_BF16>), dim3(grid), dim3(256), 0, s, p, e);
-        else
+        else if (cfg == kF16FourWave192)
             hipLaunchKernelGGL((gemm_f16_w4t_kernel<TG_FP16, TG_OUT_BF16, false, false, false, false, 6>),
+                               dim3(grid), dim3(256), 0, s, p, e);
+        else    // (grid: one workgroup per CU, fewer than the tiles; p.C null)
+            hipLaunchKernelGGL((gemm_f16_w4t_kernel<TG_FP16, TG_OUT_BF16, false, false, false, false, 8, true>),
                                dim3(grid), dim3(256), 0, s, p, e);
         return hipGetLastError();
     }

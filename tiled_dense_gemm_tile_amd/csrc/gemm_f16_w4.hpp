@@ -124,8 +124,16 @@ constexpr int tr_row_wait(int i) {
 // TM_: blocks of 16 rows per wave along M -- 8 (256 x 256 tiles) or 6
 // (192 x 256 tiles, for grids whose 256 x 256 tiles fill only part of the
 // last wave: 4000 x 3000 is 192 such tiles but 252 of 192 x 256).
+//
+// PERSIST: one workgroup per CU walks the tiles w, w + grid, w + 2 grid, ...
+// (virtual workgroup ids, so the XCD-aware order is that of a full grid).
+// After a tile's last K step it issues the next tile's K tile 0 loads (into
+// the slots K tile 0 always uses) and only then stages and stores the
+// finished tile's D, from the other slots, so those loads run while D
+// drains.  Taken for calls without C, with 16-byte rows and D rows of whole
+// 16-byte segments.
 template <bool FP16, bool OUT_BF16, bool SH = false, bool SPLIT = false, bool AT = false, bool BT = false,
-          int TM_ = 8>
+          int TM_ = 8, bool PERSIST = false>
 __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) {
     constexpr int NA = 2, NB = 2;                      // ring slots of A and B
     constexpr int DAUX = kStoreStream;                 // D store policy
@@ -149,6 +157,7 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
     static_assert(TM == 8 || TM == 6, "wave tile");
     static_assert(!SPLIT || !OUT_BF16, "split-K partial tiles are fp32");
     static_assert(!(AT || BT) || (!SH && !SPLIT && TM == 8), "MN-contiguous operands: 16-byte rows, 256 x 256");
+    static_assert(!PERSIST || (!SH && !SPLIT && !AT && !BT && TM == 8), "persistent: 16-byte rows, 256 x 256");
 
     __shared__ __attribute__((aligned(1024))) char smem[LDS_BYTES];
 
@@ -157,11 +166,12 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     int tmi, tni, split = 0;
+    int vt = blockIdx.x;                               // PERSIST: the virtual workgroup id
     if constexpr (SPLIT)
         tile_order_split(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, tmi, tni, split);
     else
-        tile_order(blockIdx.x, gridDim.x, p.tiles_m, p.tiles_n, p.group_m, tmi, tni);
-    const int m0 = tmi * BM, n0 = tni * BN;
+        tile_order(vt, PERSIST ? p.tiles_m * p.tiles_n : (int)gridDim.x, p.tiles_m, p.tiles_n, p.group_m, tmi, tni);
+    int m0 = tmi * BM, n0 = tni * BN;
     const int k_lo = SPLIT ? split * p.kt_split * KT : 0;          // first K element of this range
     const int M = p.M, N = p.N;
     const int K = SPLIT ? (p.K - k_lo < p.kt_split * KT ? p.K - k_lo : p.kt_split * KT) : p.K;
@@ -175,8 +185,8 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
     const char *b_tile = (const char *)p.B + (int64_t)n0 * p.ldb * 2 + (int64_t)k_lo * 2;
     const int a_mis0 = SH ? (int)((uintptr_t)a_tile & 15) : 0;
     const int b_mis0 = SH ? (int)((uintptr_t)b_tile & 15) : 0;
-    const __amdgpu_buffer_rsrc_t rA = make_rsrc(a_tile - a_mis0, span_bytes(M - m0, K, p.lda, 2) + a_mis0);
-    const __amdgpu_buffer_rsrc_t rB = make_rsrc(b_tile - b_mis0, span_bytes(N - n0, K, p.ldb, 2) + b_mis0);
+    __amdgpu_buffer_rsrc_t rA = make_rsrc(a_tile - a_mis0, span_bytes(M - m0, K, p.lda, 2) + a_mis0);
+    __amdgpu_buffer_rsrc_t rB = make_rsrc(b_tile - b_mis0, span_bytes(N - n0, K, p.ldb, 2) + b_mis0);
 
     // 16-byte rows (no SH): load instruction j of a wave fills slot rows
     // (4 j + wave) * 8 + lane / 8: lane L writes physical chunk L % 8 and
@@ -361,7 +371,8 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
     // (whole 4-column vectors: every C row segment a lane reads is either in
     // range or past N)
     // (and the stream's tiles load only whole K tiles: see the loop below)
-    const bool c_loop = !SPLIT && p.C != nullptr && nt >= CPARTS + 2 + NB && e.vec_c && N % 4 == 0;
+    constexpr bool CSTREAM = !SPLIT && !PERSIST;       // (persistent calls have no C)
+    const bool c_loop = CSTREAM && p.C != nullptr && nt >= CPARTS + 2 + NB && e.vec_c && N % 4 == 0;
     const __amdgpu_buffer_rsrc_t rC =
         make_rsrc(c_loop ? (const char *)p.C + (int64_t)m0 * p.ldc * OS : (const char *)p.D,
                   c_loop ? span_bytes(M - m0, N, p.ldc, OS) : 0u);
@@ -496,6 +507,22 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
         }
     };
 
+    // PERSIST: the next tile's A(0), B(0), with the wave index passed
+    // through an empty asm so that these loads' LDS destinations are
+    // computed here, not held through the main loop
+    auto next_tile_loads = [&]() __attribute__((always_inline)) {
+        int wv = wave;
+        asm volatile("" : "+s"(wv));
+#pragma unroll
+        for (int j = 0; j < LPTA; ++j) dma(rA, smem + (j * 4 + wv) * IB, a_off[j], 0);
+#pragma unroll
+        for (int j = 0; j < LPTB; ++j) dma(rB, smem + B_BASE + (j * 4 + wv) * IB, b_off[j], 0);
+    };
+    // PERSIST: this wave's D staging area, in the slots K tile 0 does not use
+    float *stage = (float *)(smem + (wave < 2 ? SLOTA : B_BASE + SLOTB) + (wave & 1) * 16 * (WTN + 4) * 4);
+    static_assert(!PERSIST || 2 * 16 * (WTN + 4) * 4 <= SLOTA, "staging areas");
+    constexpr int D_STORES = (WTM / 16) * (16 * WTN / 4 / 64);
+
     if (nt > 0) {
         // A(0), B(0): the loads the first tile's iteration does not issue
 #pragma unroll
@@ -505,40 +532,73 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
         wait_vmcnt<0>();                               // A(0), B(0) landed
         if (nt == 1) clear_past_k(0);
         barrier();
-        using none = std::integral_constant<int, -1>;
-        using yes = std::true_type;
-        using no = std::false_type;
-        int t0 = 1;
-        if (c_loop) {
-            tile(yes(), std::integral_constant<int, 0>(), none(), 0);   // loads C part 0
-            c_tiles(c_tiles, std::integral_constant<int, 1>());         // tiles 1 .. CPARTS + 1
-            t0 = CPARTS + 2;
-        } else {
-            tile(yes(), none(), none(), 0);
-        }
-        for (int t = t0; t < nt; ++t) tile(no(), none(), none(), t);
-        // the deferred part of the last tile's step 1
-#pragma unroll
-        for (int q = 0; q < Q; ++q) mfma(std::false_type(), 1, q / TN, q % TN);
-        mfma_result_fence<TM, TN>(acc);
-    } else {
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     }
+    while (true) {
+        if (nt > 0) {
+            using none = std::integral_constant<int, -1>;
+            using yes = std::true_type;
+            using no = std::false_type;
+            int t0 = 1;
+            if constexpr (CSTREAM) {
+                if (c_loop) {
+                    tile(yes(), std::integral_constant<int, 0>(), none(), 0);   // loads C part 0
+                    c_tiles(c_tiles, std::integral_constant<int, 1>());         // tiles 1 .. CPARTS + 1
+                    t0 = CPARTS + 2;
+                } else {
+                    tile(yes(), none(), none(), 0);
+                }
+            } else {
+                tile(yes(), none(), none(), 0);
+            }
+            for (int t = t0; t < nt; ++t) tile(no(), none(), none(), t);
+            // the deferred part of the last tile's step 1
+#pragma unroll
+            for (int q = 0; q < Q; ++q) mfma(std::false_type(), 1, q / TN, q % TN);
+            mfma_result_fence<TM, TN>(acc);
+        } else {
+#pragma unroll
+            for (int i = 0; i < TM; ++i)
+#pragma unroll
+                for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        }
 
-    wait_vmcnt<0>();
-    wait_lgkmcnt0();
-    barrier();
-    if constexpr (SPLIT) {
-        // partial tiles stay cacheable: the reduction reads them right after
-        float *part = p.ws + (int64_t)split * M * p.ldw;
-        epilogue_lds16t<false, TM, TN, WTM, WTN, 0>(acc, smem, wave, lane, wm, wn, m0, n0, M, N, nullptr, 0, part,
-                                                    p.ldw, e);
-    } else {
-        epilogue_lds16t<OUT_BF16, TM, TN, WTM, WTN, DAUX>(acc, smem, wave, lane, wm, wn, m0, n0, M, N,
-                                                          c_loop ? nullptr : p.C, p.ldc, p.D, p.ldd, e);
+        wait_vmcnt<0>();
+        wait_lgkmcnt0();
+        barrier();
+        if constexpr (SPLIT) {
+            // partial tiles stay cacheable: the reduction reads them right after
+            float *part = p.ws + (int64_t)split * M * p.ldw;
+            epilogue_lds16t<false, TM, TN, WTM, WTN, 0>(acc, smem, wave, lane, wm, wn, m0, n0, M, N, nullptr, 0, part,
+                                                        p.ldw, e);
+            break;
+        } else if constexpr (!PERSIST) {
+            epilogue_lds16t<OUT_BF16, TM, TN, WTM, WTN, DAUX>(acc, smem, wave, lane, wm, wn, m0, n0, M, N,
+                                                              c_loop ? nullptr : p.C, p.ldc, p.D, p.ldd, e);
+            break;
+        } else {
+            const F16Args r = kernel_arg0_reloaded<F16Args>();
+            const int dm0 = m0, dn0 = n0;              // the finished tile
+            const int ntl = r.tiles_m * r.tiles_n;
+            vt += gridDim.x;
+            const bool more = vt < ntl;
+            if (more) {
+                tile_order(vt, ntl, r.tiles_m, r.tiles_n, r.group_m, tmi, tni);
+                m0 = tmi * BM;
+                n0 = tni * BN;
+                rA = make_rsrc((const char *)r.A + (int64_t)m0 * r.lda * 2, span_bytes(r.M - m0, K, r.lda, 2));
+                rB = make_rsrc((const char *)r.B + (int64_t)n0 * r.ldb * 2, span_bytes(r.N - n0, K, r.ldb, 2));
+                if (nt > 0) next_tile_loads();
+            }
+            epilogue_rows16_vec<OUT_BF16, TM, TN, DAUX, true>(acc, stage, lane, wm, wn, dm0, dn0, r.M, r.N, r.D,
+                                                              r.ldd);
+            if (!more) break;
+            // the next tile's first loads landed; up to 63 of the D stores issued after them may still run
+            static_assert(D_STORES >= 63, "vmcnt");
+            wait_vmcnt<63>();
+            wait_lgkmcnt0();
+            if (nt == 1) clear_past_k(0);
+            barrier();                                 // staging reads done before tile 0 refills those slots
+        }
     }
 }
 

@@ -305,7 +305,7 @@ __global__ void __launch_bounds__(256) gemm_mx4_w4_kernel(MxArgs q, F16Epi e) {
             mx_epilogue<OUT_BF16, DAUX, SPLIT>(acc, smem, wave, lane, wm, wn, m0, n0, p, split, e);
             break;
         } else {
-            const MxArgs r = mx_args_reloaded();
+            const MxArgs r = kernel_arg0_reloaded<MxArgs>();
             const int dm0 = m0, dn0 = n0;              // the finished tile
             const int nt = r.g.tiles_m * r.g.tiles_n;
             vt += gridDim.x;

@@ -122,18 +122,6 @@ __device__ __forceinline__ void mfma_mx16_acc(f32x4 &acc, const i32x8 &a, const 
 #undef TG_STR2
 }
 
-// The kernel's arguments read again from the kernarg segment (where the
-// first argument, an MxArgs, starts at offset 0) through a pointer the
-// compiler cannot see through: a persistent kernel reads what it needs for
-// its next tile this way, so those values are not held in scalar registers
-// through the main loop.
-__device__ __forceinline__ MxArgs mx_args_reloaded() {
-    using KPtr = const __attribute__((address_space(4))) MxArgs *;
-    KPtr k = (KPtr)__builtin_amdgcn_kernarg_segment_ptr();
-    asm volatile("" : "+s"(k));
-    return *(const MxArgs *)k;                         // (the loads stay scalar constant-memory loads)
-}
-
 // PERSIST: one workgroup per CU walks the tiles w, w + grid, w + 2 grid, ...
 // (virtual workgroup ids, so the XCD-aware tile order is the one a full
 // grid would have).  After a tile's last K step it issues the next tile's
@@ -394,7 +382,7 @@ __global__ void __launch_bounds__(256) gemm_mx_w4_kernel(MxArgs q, F16Epi e) {
             mx_epilogue<OUT_BF16, DAUX, SPLIT>(acc, smem, wave, lane, wm, wn, m0, n0, p, split, e);
             break;
         } else {
-            const MxArgs r = mx_args_reloaded();
+            const MxArgs r = kernel_arg0_reloaded<MxArgs>();
             const int dm0 = m0, dn0 = n0;              // the finished tile
             const int nt = r.g.tiles_m * r.g.tiles_n;
             vt += gridDim.x;

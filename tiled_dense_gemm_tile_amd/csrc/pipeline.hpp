@@ -181,15 +181,16 @@ __device__ __forceinline__ void epilogue_lds16(const f32x4 (&acc)[TM][TN], char 
 }
 
 // D = acc (no C) for one wave's (16 TM) x (16 TN) block of 16x16 MFMA
-// accumulators acc[i][j] (lane l, register r: row 4 (l / 16) + r, column
-// l % 16 of block (i, j)), for the persistent kernels: passes of one block
-// row (16 rows) staged through `stage`, this wave's own 16 x (16 TN + 4)
-// floats, and every lane stores whole 16-byte (bf16: 8-byte) row segments
-// -- the caller guarantees N % 4 == 0, 16-byte-aligned D rows, and segments
-// past M or N get an offset beyond the resource, which drops them.  So a
-// pass issues exactly 16 / RPS stores per lane whatever the tile's edges
-// (the caller counts them to wait for loads issued before the stores).
-template <bool OUT_BF16, int TM, int TN, int DAUX>
+// accumulators acc[i][j] -- lane l, register r: row 4 (l / 16) + r, column
+// l % 16 of block (i, j); with TRANS row l % 16, column 4 (l / 16) + r --
+// for the persistent kernels: passes of one block row (16 rows) staged
+// through `stage`, this wave's own 16 x (16 TN + 4) floats, and every lane
+// stores whole 16-byte (bf16: 8-byte) row segments -- the caller guarantees
+// N % 4 == 0, 16-byte-aligned D rows, and segments past M or N get an
+// offset beyond the resource, which drops them.  So a pass issues exactly
+// 16 / RPS stores per lane whatever the tile's edges (the caller counts them
+// to wait for loads issued before the stores).
+template <bool OUT_BF16, int TM, int TN, int DAUX, bool TRANS = false>
 __device__ __forceinline__ void epilogue_rows16_vec(const f32x4 (&acc)[TM][TN], float *stage, int lane, int wm,
                                                     int wn, int m0, int n0, int M, int N, void *D, int64_t ldd) {
     constexpr int OS = OUT_BF16 ? 2 : 4;
@@ -212,15 +213,19 @@ __device__ __forceinline__ void epilogue_rows16_vec(const f32x4 (&acc)[TM][TN], 
         // would otherwise read them all out of the AGPRs at once)
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int j = 0; j < TN; ++j)
+        for (int j = 0; j < TN; ++j) {
+            // (read out of the AGPRs here, at their store: left to the
+            // compiler, all of acc is copied to VGPRs at the epilogue's start)
+            f32x4 v;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                // (read out of the AGPR here, at its store: left to the
-                // compiler, all of acc is copied to VGPRs at the epilogue's start)
-                float v;
-                asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(acc[i][j][r]));
-                stage[(4 * fq + r) * EP + j * 16 + fc] = v;
+            for (int r = 0; r < 4; ++r) asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v[r]) : "a"(acc[i][j][r]));
+            if constexpr (TRANS) {
+                *(f32x4 *)(stage + fc * EP + j * 16 + 4 * fq) = v;      // rows EP apart: 4 banks apart
+            } else {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) stage[(4 * fq + r) * EP + j * 16 + fc] = v[r];
             }
+        }
         wait_lgkmcnt0();
 #pragma unroll
         for (int q = 0; q < 16 / RPS; ++q) {

@@ -39,7 +39,9 @@ int pick_f16_cfg(const Common &a, int lane_bytes, int vec) {
     const int forced = forced_f16_cfg();
     if (forced >= 0) {
         const bool ok = (forced == tg::kF16FourWaveS || forced == tg::kF16FourWaveS192) ? vec >= 4
-                        : (forced == tg::kF16FourWave || forced == tg::kF16FourWave192) ? lane_bytes == 16
+                        : (forced == tg::kF16FourWave || forced == tg::kF16FourWave192 ||
+                           forced == tg::kF16FourWavePersist)
+                            ? lane_bytes == 16
                         : lane_bytes == 16 ? tg::f16_has_lane16(forced) : tg::f16_has_lane4(forced);
         if (ok) return forced;
     }
@@ -56,7 +58,9 @@ int pick_f16_cfg(const Common &a, int lane_bytes, int vec) {
     const int64_t t256 = tiles_of(a, 256, 256);
     const bool h192 = 3 * ((tiles_of(a, 192, 256) + 255) / 256) < 4 * ((t256 + 255) / 256);
     if (vec == 4 && t256 >= 128) return h192 ? tg::kF16FourWaveS192 : tg::kF16FourWaveS;   // 8-byte rows
-    if (lane_bytes == 16 && t256 >= 128) return h192 ? tg::kF16FourWave192 : tg::kF16FourWave;
+    // (persistent where the grid is over one wave and the call allows it:
+    // dispatch_f16)
+    if (lane_bytes == 16 && t256 >= 128) return h192 ? tg::kF16FourWave192 : tg::kF16FourWavePersist;
     if (t256 >= 240) return tg::kF16Wide4Lane;                     // (rows 4-byte aligned here)
     // 128 x 128 tiles: about one wave of them (one workgroup per CU) runs
     // best with both rings two tiles ahead (2048 x 2048 x 4096: 40.0 against
@@ -108,6 +112,15 @@ gemm_status dispatch_f16(const Common &a, hipStream_t s) {
         tg::F16Epi e;
         e.vec_d = ((uintptr_t)a.D % vb) == 0 && a.ldd % 4 == 0;
         e.vec_c = a.C && ((uintptr_t)a.C % vb) == 0 && a.ldc % 4 == 0;
+        if (cfg == tg::kF16FourWavePersist) {
+            // one workgroup per CU over grids of more tiles than CUs, without
+            // C and with D rows of whole 16-byte segments (its epilogue's
+            // stores); otherwise one workgroup per tile
+            const int cus = cu_count(s);
+            if (!a.C && e.vec_d && a.N % 4 == 0 && cus > 0 && tiles > cus)
+                return launched(tg::launch_f16_dma<FP16, OUT_BF16>(cfg, lane_bytes, (unsigned)cus, s, p, e));
+            cfg = tg::kF16FourWave;
+        }
         return launched(tg::launch_f16_dma<FP16, OUT_BF16>(cfg, lane_bytes, (unsigned)tiles, s, p, e));
     }
     return launched(tg::launch_f16_staged<FP16, OUT_BF16>((unsigned)tiles, s, p));

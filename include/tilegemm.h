@@ -376,6 +376,32 @@ gemm_status gemm_mx_kblock(int format, int64_t M, int64_t N, int64_t K, int64_t 
                            int out_type, hipStream_t stream);
 
 /*
+ * gemm_mx_kblock_ws -- gemm_mx_kblock on the format's tiled kernels, by
+ * scale replication: a first kernel on `stream` writes each scale once per
+ * 32-element K block it covers (a scale of a kblock-wide block shared by
+ * its kblock / 32 blocks of 32) into the caller's workspace, and the
+ * standard call (gemm_mxfp8 / gemm_mxfp4 / gemm_mxfp6) then runs on the
+ * replicated scales -- the same products and sums, so the same D as
+ * gemm_mx_kblock up to summation order.  Source: as gemm_mx_kblock.
+ *   workspace: device memory, 256-byte aligned (else GEMM_ERR_MISALIGNED),
+ *     at least gemm_mx_kblock_workspace_bytes(M, N, K) bytes (else
+ *     GEMM_ERR_WORKSPACE), not overlapping any other argument; its
+ *     contents are undefined after the call.  NULL: exactly gemm_mx_kblock.
+ *   kblock == 32 needs no workspace (the standard call).
+ * Everything else is as gemm_mx_kblock.
+ */
+gemm_status gemm_mx_kblock_ws(int format, int64_t M, int64_t N, int64_t K, int64_t kblock,
+                              const void *A, int64_t lda, const void *SFA, int64_t ldsfa,
+                              const void *B, int64_t ldb, const void *SFB, int64_t ldsfb,
+                              const void *C, int64_t ldc,
+                              void *D, int64_t ldd,
+                              int out_type, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes of gemm_mx_kblock_ws: (M + N) rows of ceil(K / 32)
+ * scale bytes, each row rounded up to 16 bytes; 0 for negative sizes. */
+size_t gemm_mx_kblock_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
  * gemm_mxfp8_splitk, gemm_mxfp4_splitk, gemm_mxfp6_splitk -- as gemm_mxfp8 /
  * gemm_mxfp4 / gemm_mxfp6, with K cut into `splits` ranges of whole groups
  * of 512 K (16 scale blocks) computed by separate workgroups, each range's

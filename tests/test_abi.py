@@ -25,7 +25,8 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["gemm_bf16", "gemm_bf16_ex", "gemm_bf16_splitk", "gemm_bf16_splitk_noalloc",
                                     "gemm_fp16", "gemm_fp16_ex", "gemm_fp16_splitk", "gemm_last_hip_error",
-                                    "gemm_mx_kblock", "gemm_mxfp4", "gemm_mxfp4_ex", "gemm_mxfp4_splitk",
+                                    "gemm_mx_kblock", "gemm_mx_kblock_workspace_bytes", "gemm_mx_kblock_ws",
+                                    "gemm_mxfp4", "gemm_mxfp4_ex", "gemm_mxfp4_splitk",
                                     "gemm_mxfp6", "gemm_mxfp6_ex", "gemm_mxfp6_splitk", "gemm_mxfp8",
                                     "gemm_mxfp8_ex", "gemm_mxfp8_splitk", "gemm_splitk_scratch_limit",
                                     "gemm_splitk_workspace_bytes", "gemm_status_string"]
@@ -379,4 +380,32 @@ def test_validation_mx_kblock():
     assert call(fmt=2, lda=254) == UNSUPPORTED         # fp6 rows of whole byte groups
     assert call(lda=100) == BAD_LD
     assert call(M=0) == OK
+    assert call(M=-1) == INVALID_SIZE
+
+
+def test_validation_mx_kblock_ws():
+    """The replicated-scale path checks everything, its workspace included,
+    before launching anything (no GPU call: every case below fails a check
+    or has nothing to do)."""
+    f = tg.raw.gemm_mx_kblock_ws
+    D = P + (1 << 24)
+    WS = P + (1 << 26)
+
+    def call(fmt=0, M=64, N=64, K=256, kb=64, lda=256, ldsfa=4, ldb=256, ldsfb=4, out=F32, ws=WS, wsb=1 << 20,
+             ldd=64):
+        return f(fmt, M, N, K, kb, P, lda, P + 4096, ldsfa, P, ldb, P + 8192, ldsfb, None, 0, D, ldd, out, ws, wsb,
+                 None)
+    need = tg.raw.gemm_mx_kblock_workspace_bytes(64, 64, 256)
+    assert need == 128 * 16                            # 8 scale bytes per row rounded up to 16
+    assert tg.raw.gemm_mx_kblock_workspace_bytes(3, 5, 1024) == 8 * 32
+    assert tg.raw.gemm_mx_kblock_workspace_bytes(-1, 5, 1024) == 0
+    assert call(wsb=need - 1) == WORKSPACE
+    assert call(ws=WS + 64) == MISALIGNED
+    # the operand and scale checks come first, as in gemm_mx_kblock
+    assert call(kb=96, ldsfa=3, ldsfb=3) == UNSUPPORTED
+    assert call(ldsfa=3) == BAD_LD
+    assert call(lda=100) == BAD_LD
+    assert call(ldd=32) == BAD_LD
+    assert call(fmt=1, lda=255) == UNSUPPORTED
+    assert call(M=0, wsb=0) == OK
     assert call(M=-1) == INVALID_SIZE

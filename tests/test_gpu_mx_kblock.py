@@ -4,7 +4,10 @@
 a(m,k) = x(A, m, k) * 2^(SFA[m, k / kb] - 127), b(k,n) likewise with SFB, for
 e4m3, e2m1, e2m3 and e3m2 elements.  Bar: bit-exact on integer-valued inputs;
 otherwise |D - D_ref| <= 2^-12 * sum|a*b| + 1e-6; and the 32-wide call on
-the replicated scales equals the wide call (exact on integers).
+the replicated scales equals the wide call (exact on integers).  The
+workspace path (scales replicated on the GPU, then the format's tiled
+kernels) is held to the same bar and, on integer inputs, equals the general
+kernel's D.
 """
 import numpy as np
 import pytest
@@ -115,3 +118,65 @@ def test_unsupported_widths_raise():
     x, _ = _case("e4m3", 64, 64, 256, 32, seed=5, integer=True, with_c=False)
     with pytest.raises(tg.GemmError):
         _run("e4m3", dict(x, SFA=x["SFA"][:, :3], SFB=x["SFB"][:, :3]), 96)
+
+
+# The workspace path (gemm_mx_kblock_ws): scales replicated to 32-wide blocks,
+# then the format's tiled kernels.  K % 512 == 0 (the four-wave kernels),
+# K % 128 only (fp8's smaller kernels, fp6's tiled path, fp4's general
+# kernel), a short last block, one scale per row.
+WS_CASES = [(300, 260, 512, 64), (600, 520, 1024, 128), (129, 70, 1024, 1024), (200, 100, 512, 4096),
+            (257, 300, 384, 128), (300, 300, 2048, 512), (64, 96, 96, 64)]
+
+
+def _run_ws(fmt, x, kb, C=None, out=torch.float32):
+    M, N = x["A"].shape[0], x["B"].shape[0]
+    ws = torch.empty(tg.mx_kblock_workspace_bytes(M, N, _k_of(fmt, x)) + 256, dtype=torch.uint8, device=DEV)
+    ws = ws[(-ws.data_ptr()) % 256:]
+    Cd = torch.from_numpy(C).to(DEV) if C is not None else None
+    return tg.gemm_mx_kblock(fmt, dev8(x["A"]), dev8(x["SFA"]), dev8(x["B"]), dev8(x["SFB"]), kb, Cd, out_dtype=out,
+                             workspace=ws)
+
+
+def _k_of(fmt, x):
+    cols = x["A"].shape[1]
+    return {"e4m3": cols, "e2m1": 2 * cols}.get(fmt, cols // 3 * 4)
+
+
+@pytest.mark.parametrize("fmt", FORMATS)
+@pytest.mark.parametrize("case", WS_CASES, ids=["%dx%dx%d_kb%d" % c for c in WS_CASES])
+def test_workspace_path(fmt, case):
+    M, N, K, kb = case
+    for integer in (True, False):
+        x, C = _case(fmt, M, N, K, kb, seed=3 * M + N + K + kb, integer=integer)
+        say("mx kblock ws %s %dx%dx%d kb %d integer=%s" % (fmt, M, N, K, kb, integer))
+        Dw = _run_ws(fmt, x, kb, C)
+        Dg = _run(fmt, x, kb, C)
+        torch.cuda.synchronize()
+        _full_check(fmt, x, kb, to_f64(Dw), integer, C)
+        if integer:
+            assert torch.equal(Dw, Dg)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
+def test_workspace_path_persistent_grid(fmt):
+    """More 256 x 256 tiles than CUs, no C, kb = 128: the persistent
+    four-wave kernel on replicated scales; exact on integer inputs at the
+    sampled elements, bf16 out the RNE of fp32 out."""
+    M, N, K, kb = 4200, 4300, 1024, 128
+    x, _ = _case(fmt, M, N, K, kb, seed=17, integer=True, with_c=False)
+    say("mx kblock ws %s persistent grid" % fmt)
+    D = _run_ws(fmt, x, kb)
+    D16 = _run_ws(fmt, x, kb, out=torch.bfloat16)
+    torch.cuda.synchronize()
+    rand, forced = inputs.sample_indices(M, N, 23)
+    idx = np.concatenate([rand, forced])
+    Dr, _ = oracle.gemm_ref(fmt, x["A"], x["B"], idx=idx, SFA=x["SFA"], SFB=x["SFB"], kblock=kb)
+    assert np.array_equal(to_f64(D).ravel()[idx], Dr)
+    assert np.array_equal(bf16_bits(D16), oracle.rne_bf16_f32(D.cpu().numpy()))
+
+
+def test_workspace_too_small_raises():
+    x, _ = _case("e4m3", 64, 64, 512, 64, seed=5, integer=True, with_c=False)
+    ws = torch.empty(tg.mx_kblock_workspace_bytes(64, 64, 512) - 16, dtype=torch.uint8, device=DEV)
+    with pytest.raises(tg.GemmError):
+        tg.gemm_mx_kblock("e4m3", dev8(x["A"]), dev8(x["SFA"]), dev8(x["B"]), dev8(x["SFB"]), 64, workspace=ws)

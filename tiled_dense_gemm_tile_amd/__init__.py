@@ -96,6 +96,10 @@ def _load():
             L.gemm_mxfp6_ex.argtypes = sex + [ci, ci, vp]
             L.gemm_mx_kblock.restype = ci
             L.gemm_mx_kblock.argtypes = [ci, i64, i64, i64, i64] + smx[3:] + [ci, vp]
+            L.gemm_mx_kblock_ws.restype = ci
+            L.gemm_mx_kblock_ws.argtypes = [ci, i64, i64, i64, i64] + smx[3:] + [ci, vp, sz, vp]
+            L.gemm_mx_kblock_workspace_bytes.restype = sz
+            L.gemm_mx_kblock_workspace_bytes.argtypes = [i64, i64, i64]
             L.gemm_status_string.restype = ctypes.c_char_p
             L.gemm_status_string.argtypes = [ci]
             L.gemm_last_hip_error.restype = ci
@@ -490,12 +494,20 @@ def gemm_mxfp6(A, SFA, B, SFB, C=None, out_dtype=None, D=None, fmt="e2m3", a_ord
 MX_FORMATS = {"e4m3": 0, "e2m1": 1, "e2m3": 2, "e3m2": 3}
 
 
-def gemm_mx_kblock(fmt, A, SFA, B, SFB, kblock, C=None, out_dtype=None, D=None):
+def mx_kblock_workspace_bytes(M: int, N: int, K: int) -> int:
+    """Workspace bytes :func:`gemm_mx_kblock` needs with ``workspace``."""
+    return int(_load().gemm_mx_kblock_workspace_bytes(M, N, K))
+
+
+def gemm_mx_kblock(fmt, A, SFA, B, SFB, kblock, C=None, out_dtype=None, D=None, workspace=None):
     """Block-scaled D = A @ B.T + C with scale blocks ``kblock`` K elements
     wide (a multiple of 32; >= K: one scale per row).  ``fmt``: "e4m3",
     "e2m1", "e2m3" or "e3m2"; A (M, K bytes-of-format) and B (N, ...) as the
     format's standard call takes them; SFA (M, ceil(K / kblock)), SFB (N,
-    ceil(K / kblock)) e8m0 codes."""
+    ceil(K / kblock)) e8m0 codes.  ``workspace``: a device byte tensor of at
+    least :func:`mx_kblock_workspace_bytes` bytes, 256-byte aligned: the
+    scales are replicated to 32-wide blocks there and the call runs on the
+    format's tiled kernels (gemm_mx_kblock_ws); None: the general kernel."""
     import torch
     if fmt not in MX_FORMATS:
         raise ValueError("fmt must be one of %s" % sorted(MX_FORMATS))
@@ -515,15 +527,20 @@ def gemm_mx_kblock(fmt, A, SFA, B, SFB, kblock, C=None, out_dtype=None, D=None):
         raise ValueError("D must be (M, N) of out_dtype")
     if C is not None and (C.dtype != out_dtype or tuple(C.shape) != (M, N)):
         raise ValueError("C must be (M, N) of out_dtype")
-    _on_device(A, B=B, C=C, D=D)
+    _on_device(A, B=B, C=C, D=D, workspace=workspace)
     _scales(SFA, SFB, M, N, A)
     nsc = -(-K // kblock) if kblock > 0 else 0
     out = OUT_BF16 if out_dtype == torch.bfloat16 else OUT_F32
-    _check(_load().gemm_mx_kblock(MX_FORMATS[fmt], M, N, K, int(kblock), A.data_ptr(), lda if K else 0,
-                                  SFA.data_ptr(), _ld(SFA, nsc) if K else 0, B.data_ptr(), ldb if K else 0,
-                                  SFB.data_ptr(), _ld(SFB, nsc) if K else 0,
-                                  C.data_ptr() if C is not None else None, _ld(C, N) if C is not None else 0,
-                                  D.data_ptr(), _ld(D, N), out, _Stream(A)))
+    args = [MX_FORMATS[fmt], M, N, K, int(kblock), A.data_ptr(), lda if K else 0,
+            SFA.data_ptr(), _ld(SFA, nsc) if K else 0, B.data_ptr(), ldb if K else 0,
+            SFB.data_ptr(), _ld(SFB, nsc) if K else 0,
+            C.data_ptr() if C is not None else None, _ld(C, N) if C is not None else 0,
+            D.data_ptr(), _ld(D, N), out]
+    if workspace is None:
+        _check(_load().gemm_mx_kblock(*args, _Stream(A)))
+    else:
+        nbytes = workspace.numel() * workspace.element_size()
+        _check(_load().gemm_mx_kblock_ws(*args, workspace.data_ptr(), nbytes, _Stream(A)))
     return D
 
 

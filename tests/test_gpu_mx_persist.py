@@ -1,5 +1,5 @@
-"""Block-scaled fp8 and fp4 grids of more 256 x 256 tiles than the GPU has
-compute units, without C: the persistent four-wave kernels (one workgroup
+"""Block-scaled fp8, fp4 and fp6 grids of more 256 x 256 tiles than the GPU
+has compute units, without C: the persistent four-wave kernels (one workgroup
 per CU walking the tiles, its next tile's first loads in flight while the
 finished tile's D is stored).
 
@@ -29,18 +29,30 @@ CASES = [(4200, 4300, 1024), (8192, 8192, 512), (4352, 4096, 512), (4100, 4104, 
 
 
 # fp8: integer codes in [-4, 4] with scale exponents 0, 1; fp4: any code
-# with exponents 1, 2 (every product an integer)
+# with exponents 1, 2; fp6: codes of magnitude at most 1 with the format's
+# integer exponent (every product an integer)
+def _int_exponents(fmt):
+    if fmt == "e4m3":
+        return 0, 2
+    if fmt == "e2m1":
+        return 1, 3
+    e = inputs.fp6_integer_scale(fmt)
+    return e, e + 1
+
+
 def _inputs(M, N, K, seed, integer, fmt="e4m3"):
     rng = np.random.default_rng(seed)
     A = inputs.random_codes(rng, fmt, (M, K), integer=integer)
     B = inputs.random_codes(rng, fmt, (N, K), integer=integer)
-    lo, hi = ((0, 2) if fmt == "e4m3" else (1, 3)) if integer else (-4, 5)
+    lo, hi = _int_exponents(fmt) if integer else (-4, 5)
     SFA = (127 + rng.integers(lo, hi, size=(M, K // 32))).astype(np.uint8)
     SFB = (127 + rng.integers(lo, hi, size=(N, K // 32))).astype(np.uint8)
     return A, B, SFA, SFB
 
 
 def _call(fmt, A, SFA, B, SFB, **kw):
+    if fmt in ("e2m3", "e3m2"):
+        return tg.gemm_mxfp6(A, SFA, B, SFB, fmt=fmt, **kw)
     fn = tg.gemm_mxfp8 if fmt == "e4m3" else tg.gemm_mxfp4
     return fn(A, SFA, B, SFB, **kw)
 
@@ -59,10 +71,12 @@ def _sampled_check(A, B, SFA, SFB, Dg, integer, seed, fmt="e4m3"):
 
 
 # the switch that sends a call to the one-workgroup-per-tile kernel instead
-PER_TILE = {"e4m3": ("TILEGEMM_MX_CONFIG", "4"), "e2m1": ("TILEGEMM_MX4_PERSIST", "0")}
+PER_TILE = {"e4m3": ("TILEGEMM_MX_CONFIG", "4"), "e2m1": ("TILEGEMM_MX4_PERSIST", "0"),
+            "e2m3": ("TILEGEMM_MX6_PERSIST", "0"), "e3m2": ("TILEGEMM_MX6_PERSIST", "0")}
+FORMATS = ["e4m3", "e2m1", "e2m3", "e3m2"]
 
 
-@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
+@pytest.mark.parametrize("fmt", FORMATS)
 @pytest.mark.parametrize("case", CASES, ids=["%dx%dx%d" % c for c in CASES])
 @pytest.mark.parametrize("out", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
 @pytest.mark.parametrize("integer", [True, False])
@@ -87,7 +101,7 @@ def test_persistent_grid(fmt, case, out, integer, monkeypatch):
         assert np.array_equal(bf16_bits(D), oracle.rne_bf16_f32(D32.cpu().numpy()))
 
 
-@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
+@pytest.mark.parametrize("fmt", FORMATS)
 def test_padded_d_rows_untouched(fmt):
     M, N, K, pad = 4200, 4300, 512, 68
     A, B, SFA, SFB = _inputs(M, N, K, 11, True, fmt)
@@ -100,7 +114,7 @@ def test_padded_d_rows_untouched(fmt):
     _sampled_check(A, B, SFA, SFB, to_f64(D), True, 5, fmt)
 
 
-@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
+@pytest.mark.parametrize("fmt", FORMATS)
 def test_calls_in_a_row_of_different_grids(fmt):
     """Consecutive calls of the persistent kernel with different tile counts
     and a smaller second grid (each workgroup's walk ends with its grid)."""
@@ -109,4 +123,21 @@ def test_calls_in_a_row_of_different_grids(fmt):
         say("mx persistent %s in a row %dx%dx%d" % (fmt, M, N, K))
         D = _call(fmt, dev8(A), dev8(SFA), dev8(B), dev8(SFB))
         torch.cuda.synchronize()
+        _sampled_check(A, B, SFA, SFB, to_f64(D), True, M, fmt)
+
+
+@pytest.mark.parametrize("fmt", ["e2m3", "e3m2"])
+def test_fp6_persistent_k_tail(fmt, monkeypatch):
+    """fp6 with K % 512 != 0 (a last scale group short of 512 K, its bytes
+    past K cleared after every tile change) and K of one tile (128)."""
+    for (M, N, K) in [(4200, 4300, 640), (4608, 4100, 128)]:
+        A, B, SFA, SFB = _inputs(M, N, K, M + K, True, fmt)
+        dA, dB, dSA, dSB = dev8(A), dev8(B), dev8(SFA), dev8(SFB)
+        say("mx persistent %s K tail %dx%dx%d" % (fmt, M, N, K))
+        D = _call(fmt, dA, dSA, dB, dSB)
+        monkeypatch.setenv(*PER_TILE[fmt])
+        D1 = _call(fmt, dA, dSA, dB, dSB)
+        monkeypatch.delenv(PER_TILE[fmt][0])
+        torch.cuda.synchronize()
+        assert torch.equal(D, D1)
         _sampled_check(A, B, SFA, SFB, to_f64(D), True, M, fmt)

@@ -63,10 +63,14 @@ __device__ __forceinline__ void mfma_mx6_acc(f32x4 &acc, const u32x6 &a, const u
 }
 
 // q.g.lda and q.g.ldb are in BYTES here (three quarters of the leading
-// dimension in elements); q.g.K is in elements.
-template <bool OUT_BF16, int FMT, int DAUX = kStoreStream, bool SPLIT = false>
+// dimension in elements); q.g.K is in elements.  PERSIST: one workgroup per
+// CU walking the tiles, as the persistent fp8 kernel; the finished tile's D
+// is staged in ring slot 2 while the next tile's tiles 0 and 1 load into
+// slots 0 and 1.
+template <bool OUT_BF16, int FMT, int DAUX = kStoreStream, bool SPLIT = false, bool PERSIST = false>
 __global__ void __launch_bounds__(256) gemm_mx6_w4_kernel(MxArgs q, F16Epi e) {
     static_assert(FMT == 2 || FMT == 3, "fp6 formats");
+    static_assert(!(PERSIST && SPLIT), "persistent: whole tiles");
     const F16Args &p = q.g;
     constexpr int ROWB = 96;                           // bytes per K tile (128 elements) and LDS row
     constexpr int TM = 8, TN = 8, WTM = 128, WTN = 128;
@@ -90,20 +94,27 @@ __global__ void __launch_bounds__(256) gemm_mx6_w4_kernel(MxArgs q, F16Epi e) {
     const int wm = wave >> 1, wn = wave & 1;
     int m0, n0, split, k_lo, K;
     mx_work_item<SPLIT>(p, m0, n0, split, k_lo, K);
-    const int M = p.M, N = p.N;
     // K % 128 == 0: whole K tiles; the loop runs whole groups of four, reading
     // zeros past nk
     const int kb = K / 4 * 3, nblk = K / 32, rem = nblk % 16;
     const int nk = K / 128, nep = (K + 511) / 512;
+    int vt = blockIdx.x;                               // PERSIST: the virtual workgroup id
+    if constexpr (PERSIST) {
+        int tmi, tni;
+        tile_order(vt, p.tiles_m * p.tiles_n, p.tiles_m, p.tiles_n, p.group_m, tmi, tni);
+        m0 = tmi * 256;
+        n0 = tni * 256;
+    }
 
-    const __amdgpu_buffer_rsrc_t rA =
-        make_rsrc((const char *)p.A + (int64_t)m0 * p.lda + k_lo / 4 * 3, span_bytes(M - m0, kb, p.lda, 1));
-    const __amdgpu_buffer_rsrc_t rB =
-        make_rsrc((const char *)p.B + (int64_t)n0 * p.ldb + k_lo / 4 * 3, span_bytes(N - n0, kb, p.ldb, 1));
-    const __amdgpu_buffer_rsrc_t rSA =
-        make_rsrc((const char *)q.SFA + (int64_t)m0 * q.ldsfa + k_lo / 32, scale_span(M - m0, nblk, q.ldsfa));
-    const __amdgpu_buffer_rsrc_t rSB =
-        make_rsrc((const char *)q.SFB + (int64_t)n0 * q.ldsfb + k_lo / 32, scale_span(N - n0, nblk, q.ldsfb));
+    __amdgpu_buffer_rsrc_t rA, rB, rSA, rSB;
+    auto tile_resources = [&](const MxArgs &a) __attribute__((always_inline)) {
+        const F16Args &g = a.g;
+        rA = make_rsrc((const char *)g.A + (int64_t)m0 * g.lda + k_lo / 4 * 3, span_bytes(g.M - m0, kb, g.lda, 1));
+        rB = make_rsrc((const char *)g.B + (int64_t)n0 * g.ldb + k_lo / 4 * 3, span_bytes(g.N - n0, kb, g.ldb, 1));
+        rSA = make_rsrc((const char *)a.SFA + (int64_t)m0 * a.ldsfa + k_lo / 32, scale_span(g.M - m0, nblk, a.ldsfa));
+        rSB = make_rsrc((const char *)a.SFB + (int64_t)n0 * a.ldsfb + k_lo / 32, scale_span(g.N - n0, nblk, a.ldsfb));
+    };
+    tile_resources(q);
     const __amdgpu_buffer_rsrc_t rZ = make_rsrc(p.A, 0u);
 
     // Operand loads: chunk position c = (4 j + wave) * 64 + lane of a slot
@@ -151,10 +162,13 @@ __global__ void __launch_bounds__(256) gemm_mx6_w4_kernel(MxArgs q, F16Epi e) {
     // is half u % 2 of logical chunk u / 2.
     const int fr = lane & 15, fq = lane >> 4;
     auto unit = [&](int u) { return fr * ROWB + (((u >> 1) ^ (fr >> 3)) << 4) + (u & 1) * 8; };
-    const int la0 = A_BASE + wm * WTM * ROWB + unit(3 * fq), la1 = A_BASE + wm * WTM * ROWB + unit(3 * fq + 1),
-              la2 = A_BASE + wm * WTM * ROWB + unit(3 * fq + 2);
-    const int lb0 = B_BASE + wn * WTN * ROWB + unit(3 * fq), lb1 = B_BASE + wn * WTN * ROWB + unit(3 * fq + 1),
-              lb2 = B_BASE + wn * WTN * ROWB + unit(3 * fq + 2);
+    // (through an empty asm: block and slot offsets then fold into the LDS
+    // reads' immediate offsets)
+    int la0 = A_BASE + wm * WTM * ROWB + unit(3 * fq), la1 = A_BASE + wm * WTM * ROWB + unit(3 * fq + 1),
+        la2 = A_BASE + wm * WTM * ROWB + unit(3 * fq + 2);
+    int lb0 = B_BASE + wn * WTN * ROWB + unit(3 * fq), lb1 = B_BASE + wn * WTN * ROWB + unit(3 * fq + 1),
+        lb2 = B_BASE + wn * WTN * ROWB + unit(3 * fq + 2);
+    asm volatile("" : "+v"(la0), "+v"(la1), "+v"(la2), "+v"(lb0), "+v"(lb1), "+v"(lb2));
     constexpr int GB = 16 * ROWB;                      // bytes of a block's 16 rows
     auto ld24 = [&](int a0, int a1, int a2) __attribute__((always_inline)) {
         const u32x2 x = *(const u32x2 *)(smem + a0), y = *(const u32x2 *)(smem + a1),
@@ -166,11 +180,6 @@ __global__ void __launch_bounds__(256) gemm_mx6_w4_kernel(MxArgs q, F16Epi e) {
     u32x6 fa[TM], fx;                                  // A fragments; fx: row 7 of odd tiles
     u32x6 fb[2][TN];                                   // B fragments by tile parity
     uint32_t sa[2][2], sb[2][2];                       // scale registers by tile parity
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    mfma_result_fence<TM, TN>(acc);                    // the zeroing before the first MFMA reads them
 
     // Reads of tile t from ring slot rs; its place in its epoch U = t % 4 is
     // a compile-time constant at every call site (the loop advances by whole
@@ -195,10 +204,11 @@ __global__ void __launch_bounds__(256) gemm_mx6_w4_kernel(MxArgs q, F16Epi e) {
     const uint32_t sel_lo = (uint32_t)fq | ((uint32_t)(fq + 4) << 8) | 0x0c0c0000u;   // 0x0c: a zero byte
     const uint32_t sel_hi = 0x00000c0cu | ((uint32_t)fq << 16) | ((uint32_t)(fq + 4) << 24);
     uint32_t sraw[2][4];
+    int srow_a = SA_BASE + (wm * WTM + fr) * 16, srow_b = SB_BASE + (wn * WTN + fr) * 16;
+    asm volatile("" : "+v"(srow_a), "+v"(srow_b));
     auto scale_issue = [&](auto uc, auto hc, auto gc, int t) __attribute__((always_inline)) {
         constexpr int U = decltype(uc)::value, H = decltype(hc)::value, G = decltype(gc)::value;
-        const int row = (H < 2 ? wm * WTM : wn * WTN) + fr;
-        const int base = (H < 2 ? SA_BASE : SB_BASE) + row * 16 + ((t >> 2) & 1) * SS + U * 4 + (H & 1) * 4 * 256;
+        const int base = (H < 2 ? srow_a : srow_b) + ((t >> 2) & 1) * SS + U * 4 + (H & 1) * 4 * 256;
 #pragma unroll
         for (int u = 0; u < 4; ++u) sraw[G][u] = *(const uint32_t *)(smem + base + u * 256);
     };
@@ -259,38 +269,107 @@ __global__ void __launch_bounds__(256) gemm_mx6_w4_kernel(MxArgs q, F16Epi e) {
         barrier();
     };
 
+    // tile 0 (slot 0), the first epoch's scales, tile 1 (slot 1), for the
+    // current output tile (nk > 0); wv: the wave index (a persistent kernel
+    // passes it through an empty asm, so these loads' LDS destinations are
+    // computed here)
+    // (operands computed into locals first: see the build notes on
+    // conditional expressions as arguments of the direct-to-LDS load)
+    auto prologue_loads = [&](int wv) __attribute__((always_inline)) {
+        const int l = lane_id();
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+#pragma unroll
+            for (int k = 0; k < 2 * LPW; ++k) {
+                const bool isa = k < LPW;
+                const int j = isa ? k : k - LPW;
+                const __amdgpu_buffer_rsrc_t r = t < nk ? (isa ? rA : rB) : rZ;
+                const uint32_t voff = isa ? a_off[j] : b_off[j];
+                const int lds = (isa ? A_BASE : B_BASE) + t * SLOT + (j * 4 + wv) * IB;
+                dma(r, lds, voff, t * ROWB);
+            }
+            if (t == 0) {
+                const uint32_t va = (uint32_t)((64 * wv + l) * q.ldsfa), vb = (uint32_t)((64 * wv + l) * q.ldsfb);
+                dma(rSA, SA_BASE + wv * IB, va, 0);
+                dma(rSB, SB_BASE + wv * IB, vb, 0);
+            }
+        }
+    };
+    // PERSIST: this wave's D staging area, in ring slot 2 (the next tile's
+    // first loads use slots 0 and 1)
+    float *stage = (float *)(smem + (wave < 2 ? A_BASE : B_BASE) + 2 * SLOT + (wave & 1) * 16 * (WTN + 4) * 4);
+    static_assert(2 * 16 * (WTN + 4) * 4 <= SLOT, "staging areas");
+    constexpr int D_STORES = (WTM / 16) * (16 * WTN / 4 / 64);
+
     if (nk > 0) {
-        // prologue: tile 0 (slot 0), the first epoch's scales, tile 1 (slot
-        // 1); wait for all but tile 1's loads
-#pragma unroll
-        for (int k = 0; k < 2 * LPW; ++k) fetch(0, k, 0);
-        fetch_scales(0);
-#pragma unroll
-        for (int k = 0; k < 2 * LPW; ++k) fetch(1, k, 1);
-        wait_vmcnt<2 * LPW>();
+        prologue_loads(wave);
+        wait_vmcnt<2 * LPW>();                         // all but tile 1's loads
         if (rem != 0 && nep == 1) mx_scale_tail_fixup(smem, SA_BASE + wave * IB, SB_BASE + wave * IB, lane_id(), rem);
         barrier();
-        window(std::true_type(), std::integral_constant<int, 0>(), 0, 0);
-        // windows 1 .. (nk rounded up to a multiple of 4): tiles 0 .. nk - 1
-        // computed, then zero tiles
-        int rs = 1;
-        auto next = [](int r) { return r == NS - 1 ? 0 : r + 1; };
-        for (int t = 1; t <= nk; t += 4) {
-            window(std::false_type(), std::integral_constant<int, 1>(), t, rs);
-            rs = next(rs);
-            window(std::false_type(), std::integral_constant<int, 2>(), t + 1, rs);
-            rs = next(rs);
-            window(std::false_type(), std::integral_constant<int, 3>(), t + 2, rs);
-            rs = next(rs);
-            window(std::false_type(), std::integral_constant<int, 0>(), t + 3, rs);
-            rs = next(rs);
+    }
+    while (true) {
+        float z = 0.0f;                                // (made here, not a register held through the loop)
+        asm volatile("" : "+v"(z));
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{z, z, z, z};
+        mfma_result_fence<TM, TN>(acc);                // the zeroing before the first MFMA reads them
+        if (nk > 0) {
+            window(std::true_type(), std::integral_constant<int, 0>(), 0, 0);
+            // windows 1 .. (nk rounded up to a multiple of 4): tiles 0 .. nk - 1
+            // computed, then zero tiles
+            int rs = 1;
+            auto next = [](int r) { return r == NS - 1 ? 0 : r + 1; };
+            for (int t = 1; t <= nk; t += 4) {
+                window(std::false_type(), std::integral_constant<int, 1>(), t, rs);
+                rs = next(rs);
+                window(std::false_type(), std::integral_constant<int, 2>(), t + 1, rs);
+                rs = next(rs);
+                window(std::false_type(), std::integral_constant<int, 3>(), t + 2, rs);
+                rs = next(rs);
+                window(std::false_type(), std::integral_constant<int, 0>(), t + 3, rs);
+                rs = next(rs);
+            }
+        }
+        mfma_result_fence<TM, TN>(acc);
+        wait_vmcnt<0>();
+        wait_lgkmcnt0();
+        barrier();
+        if constexpr (!PERSIST) {
+            mx_epilogue<OUT_BF16, DAUX, SPLIT>(acc, smem, wave, lane, wm, wn, m0, n0, p, split, e);
+            break;
+        } else {
+            const MxArgs r = kernel_arg0_reloaded<MxArgs>();
+            const int dm0 = m0, dn0 = n0;              // the finished tile
+            const int nt = r.g.tiles_m * r.g.tiles_n;
+            vt += gridDim.x;
+            const bool more = vt < nt;
+            if (more) {
+                int tmi, tni;
+                tile_order(vt, nt, r.g.tiles_m, r.g.tiles_n, r.g.group_m, tmi, tni);
+                m0 = tmi * 256;
+                n0 = tni * 256;
+                tile_resources(r);
+                if (nk > 0) {
+                    int wv = wave;
+                    asm volatile("" : "+s"(wv));
+                    prologue_loads(wv);
+                }
+            }
+            epilogue_rows16_vec<OUT_BF16, TM, TN, DAUX>(acc, stage, lane, wm, wn, dm0, dn0, r.g.M, r.g.N, r.g.D,
+                                                        r.g.ldd);
+            if (!more) break;
+            // the next tile's loads (26 per lane) then 64 D stores were issued:
+            // at most 63 in flight means every load has landed
+            static_assert(D_STORES >= 63, "vmcnt");
+            wait_vmcnt<63>();
+            wait_lgkmcnt0();
+            if (rem != 0 && nep == 1)
+                mx_scale_tail_fixup(smem, SA_BASE + wave * IB, SB_BASE + wave * IB, lane_id(), rem);
+            barrier();                                 // staging reads done before the ring refills slot 2
         }
     }
-    mfma_result_fence<TM, TN>(acc);
-    wait_vmcnt<0>();
-    wait_lgkmcnt0();
-    barrier();
-    mx_epilogue<OUT_BF16, DAUX, SPLIT>(acc, smem, wave, lane, wm, wn, m0, n0, p, split, e);
 }
 
 }  // namespace tg

@@ -47,6 +47,13 @@ tg::MxArgs mx6_args(const Common &a, const void *SFA, int64_t ldsfa, const void 
     return q;
 }
 
+// Test override: TILEGEMM_MX6_PERSIST=0 launches one workgroup per tile
+// where the persistent kernel would run.
+bool persist_allowed() {
+    const char *e = getenv("TILEGEMM_MX6_PERSIST");
+    return !(e && e[0] == '0');
+}
+
 gemm_status dispatch_mx6(const Common &a, bool e3m2, const void *SFA, int64_t ldsfa, const void *SFB, int64_t ldsfb,
                          hipStream_t s) {
     // other K % 32 and alignments: the general kernel
@@ -61,6 +68,12 @@ gemm_status dispatch_mx6(const Common &a, bool e3m2, const void *SFA, int64_t ld
     tg::F16Epi e;
     e.vec_d = ((uintptr_t)a.D % vb) == 0 && a.ldd % 4 == 0;
     e.vec_c = a.C && ((uintptr_t)a.C % vb) == 0 && a.ldc % 4 == 0;
+    // more tiles than CUs, no C, D rows of whole 16-byte segments: the
+    // persistent kernel (TILEGEMM_MX6_PERSIST=0 turns it off)
+    const int cus = cu_count(s);
+    if (!a.C && e.vec_d && a.N % 4 == 0 && cus > 0 && tiles > cus && persist_allowed())
+        return launched(bf16 ? tg::launch_mx6_persist<true>(e3m2, (unsigned)cus, s, q, e)
+                             : tg::launch_mx6_persist<false>(e3m2, (unsigned)cus, s, q, e));
     return launched(bf16 ? tg::launch_mx6<true>(e3m2, (unsigned)tiles, s, q, e)
                          : tg::launch_mx6<false>(e3m2, (unsigned)tiles, s, q, e));
 }

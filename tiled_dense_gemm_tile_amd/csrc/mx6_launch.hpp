@@ -17,6 +17,11 @@ hipError_t launch_mx6(bool e3m2, unsigned grid, hipStream_t s, const MxArgs &q, 
 // translation unit.
 hipError_t launch_mx6_split(bool e3m2, unsigned grid, hipStream_t s, const MxArgs &q, const F16Epi &e);
 
+// Persistent: `grid` workgroups (one per CU) walk all tiles; no C, D rows of
+// whole 16-byte segments (q.g.N % 4 == 0, e.vec_d).
+template <bool OUT_BF16>
+hipError_t launch_mx6_persist(bool e3m2, unsigned grid, hipStream_t s, const MxArgs &q, const F16Epi &e);
+
 }  // namespace tg
 
 #ifdef TG_MX6_INSTANCE
@@ -28,6 +33,18 @@ hipError_t launch_mx6<TG_OUT_BF16>(bool e3m2, unsigned grid, hipStream_t s, cons
         hipLaunchKernelGGL((gemm_mx6_w4_kernel<TG_OUT_BF16, 3>), dim3(grid), dim3(256), 0, s, q, e);
     else
         hipLaunchKernelGGL((gemm_mx6_w4_kernel<TG_OUT_BF16, 2>), dim3(grid), dim3(256), 0, s, q, e);
+    return hipGetLastError();
+}
+
+template <>
+hipError_t launch_mx6_persist<TG_OUT_BF16>(bool e3m2, unsigned grid, hipStream_t s, const MxArgs &q,
+                                           const F16Epi &e) {
+    if (e3m2)
+        hipLaunchKernelGGL((gemm_mx6_w4_kernel<TG_OUT_BF16, 3, kStoreStream, false, true>), dim3(grid), dim3(256), 0,
+                           s, q, e);
+    else
+        hipLaunchKernelGGL((gemm_mx6_w4_kernel<TG_OUT_BF16, 2, kStoreStream, false, true>), dim3(grid), dim3(256), 0,
+                           s, q, e);
     return hipGetLastError();
 }
 

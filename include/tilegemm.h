@@ -348,6 +348,68 @@ gemm_status gemm_mxfp6_ex(int64_t M, int64_t N, int64_t K,
                           int format, int out_type, hipStream_t stream);
 
 /*
+ * gemm_bf16_ex_ws, gemm_fp16_ex_ws, gemm_mxfp8_ex_ws, gemm_mxfp4_ex_ws,
+ * gemm_mxfp6_ex_ws -- the *_ex calls with a workspace: each MN-contiguous
+ * operand is first copied, by a kernel on `stream`, into the workspace as
+ * its K-contiguous form (rows of K rounded up to T elements, T = 1024 / e,
+ * or 192 for fp6, element i at bits e*i .. e*i + e - 1 of a row, e the
+ * element's bits), and the plain
+ * call then runs on the copies and its tiled kernels -- the same products
+ * and sums as the *_ex call.  Source: as the *_ex calls (the descriptors'
+ * K-major and MN-major modes: here an MN-major operand becomes K-major once
+ * per call instead of per fragment).
+ *   workspace: device memory, 256-byte aligned (else GEMM_ERR_MISALIGNED),
+ *     at least gemm_ex_workspace_bytes(e, M, N, K, a_order, b_order) bytes
+ *     (else GEMM_ERR_WORKSPACE), not overlapping any other argument; its
+ *     contents are undefined after the call.  NULL, or both operands
+ *     K-contiguous: exactly the *_ex call.
+ * Everything else (orders, leading dimensions, scales, validation,
+ * out_type, C == D) is as the *_ex call; every check comes before any
+ * kernel is enqueued.
+ */
+gemm_status gemm_bf16_ex_ws(int64_t M, int64_t N, int64_t K,
+                            const void *A, int64_t lda, int a_order,
+                            const void *B, int64_t ldb, int b_order,
+                            const void *C, int64_t ldc,
+                            void *D, int64_t ldd,
+                            int out_type, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+gemm_status gemm_fp16_ex_ws(int64_t M, int64_t N, int64_t K,
+                            const void *A, int64_t lda, int a_order,
+                            const void *B, int64_t ldb, int b_order,
+                            const void *C, int64_t ldc,
+                            void *D, int64_t ldd,
+                            int out_type, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+gemm_status gemm_mxfp8_ex_ws(int64_t M, int64_t N, int64_t K,
+                             const void *A, int64_t lda, int a_order, const void *SFA, int64_t ldsfa,
+                             const void *B, int64_t ldb, int b_order, const void *SFB, int64_t ldsfb,
+                             const void *C, int64_t ldc,
+                             void *D, int64_t ldd,
+                             int out_type, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+gemm_status gemm_mxfp4_ex_ws(int64_t M, int64_t N, int64_t K,
+                             const void *A, int64_t lda, int a_order, const void *SFA, int64_t ldsfa,
+                             const void *B, int64_t ldb, int b_order, const void *SFB, int64_t ldsfb,
+                             const void *C, int64_t ldc,
+                             void *D, int64_t ldd,
+                             int out_type, void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+gemm_status gemm_mxfp6_ex_ws(int64_t M, int64_t N, int64_t K,
+                             const void *A, int64_t lda, int a_order, const void *SFA, int64_t ldsfa,
+                             const void *B, int64_t ldb, int b_order, const void *SFB, int64_t ldsfb,
+                             const void *C, int64_t ldc,
+                             void *D, int64_t ldd,
+                             int format, int out_type, void *workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
+/* Workspace bytes of the *_ex_ws calls: element_bits 16 (bf16, fp16), 8
+ * (fp8), 6 (fp6) or 4 (fp4); for each MN-contiguous operand, its M (N) rows
+ * of K rounded up to 1024 / element_bits elements (fp6: 192), rounded up to
+ * 256 bytes; 0 for other element sizes or negative sizes. */
+size_t gemm_ex_workspace_bytes(int element_bits, int64_t M, int64_t N, int64_t K, int a_order, int b_order);
+
+/*
  * gemm_mx_kblock -- the block-scaled forms (gemm_mxfp8, gemm_mxfp4,
  * gemm_mxfp6, chosen by `format`, a gemm_mx_format) with scale blocks
  * `kblock` K elements wide instead of 32: scale j of row m of A (column n

@@ -23,13 +23,16 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["gemm_bf16", "gemm_bf16_ex", "gemm_bf16_splitk", "gemm_bf16_splitk_noalloc",
-                                    "gemm_fp16", "gemm_fp16_ex", "gemm_fp16_splitk", "gemm_last_hip_error",
+    assert declared_functions() == ["gemm_bf16", "gemm_bf16_ex", "gemm_bf16_ex_ws", "gemm_bf16_splitk",
+                                    "gemm_bf16_splitk_noalloc", "gemm_ex_workspace_bytes",
+                                    "gemm_fp16", "gemm_fp16_ex", "gemm_fp16_ex_ws", "gemm_fp16_splitk",
+                                    "gemm_last_hip_error",
                                     "gemm_mx_kblock", "gemm_mx_kblock_workspace_bytes", "gemm_mx_kblock_ws",
-                                    "gemm_mxfp4", "gemm_mxfp4_ex", "gemm_mxfp4_splitk",
-                                    "gemm_mxfp6", "gemm_mxfp6_ex", "gemm_mxfp6_splitk", "gemm_mxfp8",
-                                    "gemm_mxfp8_ex", "gemm_mxfp8_splitk", "gemm_splitk_scratch_limit",
-                                    "gemm_splitk_workspace_bytes", "gemm_status_string"]
+                                    "gemm_mxfp4", "gemm_mxfp4_ex", "gemm_mxfp4_ex_ws", "gemm_mxfp4_splitk",
+                                    "gemm_mxfp6", "gemm_mxfp6_ex", "gemm_mxfp6_ex_ws", "gemm_mxfp6_splitk",
+                                    "gemm_mxfp8", "gemm_mxfp8_ex", "gemm_mxfp8_ex_ws", "gemm_mxfp8_splitk",
+                                    "gemm_splitk_scratch_limit", "gemm_splitk_workspace_bytes",
+                                    "gemm_status_string"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -409,3 +412,40 @@ def test_validation_mx_kblock_ws():
     assert call(fmt=1, lda=255) == UNSUPPORTED
     assert call(M=0, wsb=0) == OK
     assert call(M=-1) == INVALID_SIZE
+
+
+def test_validation_ex_ws():
+    """*_ex_ws: the _ex call's checks, then the workspace's, before any GPU
+    call (every case below fails a check or has nothing to do)."""
+    D = P + (1 << 24)
+    WS = P + (1 << 26)
+    MN, KC = 1, 0
+    f16 = tg.raw.gemm_bf16_ex_ws
+    mx8 = tg.raw.gemm_mxfp8_ex_ws
+
+    def c16(M=300, N=200, K=130, lda=300, ao=MN, ldb=130, bo=KC, ws=WS, wsb=1 << 24, ldd=200):
+        return f16(M, N, K, P, lda, ao, P, ldb, bo, None, 0, D, ldd, F32, ws, wsb, None)
+
+    def c8(M=300, N=200, K=256, lda=300, ao=MN, ldb=256, bo=KC, ws=WS, wsb=1 << 24, ldsfa=8):
+        return mx8(M, N, K, P, lda, ao, P + 4096, ldsfa, P, ldb, bo, P + 8192, 8, None, 0, D, N, F32, ws, wsb, None)
+    # sizes: rows of K rounded up to 1024 / bits elements (fp6 192), each
+    # copy rounded to 256 bytes
+    assert tg.raw.gemm_ex_workspace_bytes(16, 300, 200, 130, MN, KC) == (300 * 192 * 2 + 255) // 256 * 256
+    assert tg.raw.gemm_ex_workspace_bytes(8, 300, 200, 256, MN, MN) == 300 * 256 + 200 * 256
+    assert tg.raw.gemm_ex_workspace_bytes(6, 64, 64, 128, KC, MN) == 64 * 144
+    assert tg.raw.gemm_ex_workspace_bytes(4, 64, 64, 128, MN, KC) == 64 * 128
+    assert tg.raw.gemm_ex_workspace_bytes(4, 64, 64, 128, KC, KC) == 0
+    assert tg.raw.gemm_ex_workspace_bytes(5, 64, 64, 128, MN, MN) == 0
+    need16 = tg.raw.gemm_ex_workspace_bytes(16, 300, 200, 130, MN, KC)
+    assert c16(wsb=need16 - 1) == WORKSPACE
+    assert c16(ws=WS + 16) == MISALIGNED
+    assert c16(lda=299) == BAD_LD                      # MN-contiguous A: lda >= M
+    assert c16(ldd=100) == BAD_LD
+    assert c16(ao=2) == UNSUPPORTED
+    assert c16(M=0, wsb=0) == OK
+    need8 = tg.raw.gemm_ex_workspace_bytes(8, 300, 200, 256, MN, KC)
+    assert c8(wsb=need8 - 1) == WORKSPACE
+    assert c8(ws=WS + 128) == MISALIGNED
+    assert c8(ldsfa=7) == BAD_LD                       # scale rows as the plain call
+    assert c8(K=48) == UNSUPPORTED
+    assert c8(M=-1) == INVALID_SIZE

@@ -94,6 +94,16 @@ def _load():
                 f.restype, f.argtypes = ci, sex + [ci, vp]
             L.gemm_mxfp6_ex.restype = ci
             L.gemm_mxfp6_ex.argtypes = sex + [ci, ci, vp]
+            for name in ("gemm_bf16_ex_ws", "gemm_fp16_ex_ws"):
+                f = getattr(L, name)
+                f.restype, f.argtypes = ci, [i64, i64, i64, vp, i64, ci, vp, i64, ci, vp, i64, vp, i64, ci, vp, sz, vp]
+            for name in ("gemm_mxfp8_ex_ws", "gemm_mxfp4_ex_ws"):
+                f = getattr(L, name)
+                f.restype, f.argtypes = ci, sex + [ci, vp, sz, vp]
+            L.gemm_mxfp6_ex_ws.restype = ci
+            L.gemm_mxfp6_ex_ws.argtypes = sex + [ci, ci, vp, sz, vp]
+            L.gemm_ex_workspace_bytes.restype = sz
+            L.gemm_ex_workspace_bytes.argtypes = [ci, i64, i64, i64, ci, ci]
             L.gemm_mx_kblock.restype = ci
             L.gemm_mx_kblock.argtypes = [ci, i64, i64, i64, i64] + smx[3:] + [ci, vp]
             L.gemm_mx_kblock_ws.restype = ci
@@ -197,7 +207,8 @@ def _order(t):
     raise ValueError("each operand needs a unit stride along K or along M/N")
 
 
-def _call16(name, A, B, C, out_dtype, D, dtype):
+def _call16(name, A, B, C, out_dtype, D, dtype, workspace=None):
+    _on_device(A, workspace=workspace)
     M, N, K, D, stream, out = _prep(A, B, C, D, out_dtype, (dtype,))
     (ao, lda), (bo, ldb) = _order(A), _order(B)
     if not K:
@@ -207,27 +218,41 @@ def _call16(name, A, B, C, out_dtype, D, dtype):
     if ao == K_CONTIGUOUS and bo == K_CONTIGUOUS:
         st = getattr(L, name)(M, N, K, A.data_ptr(), lda, B.data_ptr(), ldb, cptr, ldc, D.data_ptr(), _ld(D, N),
                               out, stream)
-    else:
+    elif workspace is None:
         st = getattr(L, name + "_ex")(M, N, K, A.data_ptr(), lda, ao, B.data_ptr(), ldb, bo, cptr, ldc,
                                       D.data_ptr(), _ld(D, N), out, stream)
+    else:
+        st = getattr(L, name + "_ex_ws")(M, N, K, A.data_ptr(), lda, ao, B.data_ptr(), ldb, bo, cptr, ldc,
+                                         D.data_ptr(), _ld(D, N), out, workspace.data_ptr(),
+                                         workspace.numel() * workspace.element_size(), stream)
     _check(st)
     return D
 
 
-def gemm_bf16(A, B, C=None, out_dtype=None, D=None):
+def gemm_bf16(A, B, C=None, out_dtype=None, D=None, workspace=None):
     """D = A @ B.T + C for bf16 A (M, K) and B (N, K); fp32 accumulation.
 
     ``out_dtype`` float32 (default) or bfloat16; C (optional) has out_dtype;
     D is allocated unless given.  Enqueued on torch's current stream.
+    ``workspace``: for operands given MN-contiguous (a transposed view), a
+    device byte tensor of :func:`ex_workspace_bytes` bytes, 256-byte aligned:
+    they are copied there K-contiguous first (gemm_bf16_ex_ws).
     """
     import torch
-    return _call16("gemm_bf16", A, B, C, torch.float32 if out_dtype is None else out_dtype, D, torch.bfloat16)
+    return _call16("gemm_bf16", A, B, C, torch.float32 if out_dtype is None else out_dtype, D, torch.bfloat16,
+                   workspace)
 
 
-def gemm_fp16(A, B, C=None, out_dtype=None, D=None):
+def gemm_fp16(A, B, C=None, out_dtype=None, D=None, workspace=None):
     """As :func:`gemm_bf16` with float16 A and B."""
     import torch
-    return _call16("gemm_fp16", A, B, C, torch.float32 if out_dtype is None else out_dtype, D, torch.float16)
+    return _call16("gemm_fp16", A, B, C, torch.float32 if out_dtype is None else out_dtype, D, torch.float16,
+                   workspace)
+
+
+def ex_workspace_bytes(element_bits: int, M: int, N: int, K: int, a_order: str = "k", b_order: str = "k") -> int:
+    """Workspace bytes of the *_ex_ws calls (element_bits 16, 8, 6 or 4)."""
+    return int(_load().gemm_ex_workspace_bytes(element_bits, M, N, K, _ORDERS[a_order], _ORDERS[b_order]))
 
 
 def splitk_workspace_bytes(M: int, N: int, K: int, splits: int = 0) -> int:
@@ -332,9 +357,11 @@ def _mx_operand(t, X, order):
     return (r, elems, ld) if order == "k" else (elems, r, ld)
 
 
-def _mx_ex(t, A, SFA, B, SFB, C, out_dtype, D, a_order, b_order, fmt=None):
-    """A block-scaled call with explicit storage orders (the *_ex entry points)."""
+def _mx_ex(t, A, SFA, B, SFB, C, out_dtype, D, a_order, b_order, fmt=None, workspace=None):
+    """A block-scaled call with explicit storage orders (the *_ex entry
+    points; *_ex_ws with a workspace)."""
     import torch
+    _on_device(A, workspace=workspace)
     out_dtype = torch.float32 if out_dtype is None else out_dtype
     if a_order not in _ORDERS or b_order not in _ORDERS:
         raise ValueError("orders are 'k' or 'mn'")
@@ -364,7 +391,11 @@ def _mx_ex(t, A, SFA, B, SFB, C, out_dtype, D, a_order, b_order, fmt=None):
     name = {"e4m3": "gemm_mxfp8_ex", "e2m1": "gemm_mxfp4_ex"}.get(t, "gemm_mxfp6_ex")
     if fmt is not None:
         args.append(FP6_FORMATS[fmt])
-    _check(getattr(_load(), name)(*args, out, stream))
+    if workspace is None:
+        _check(getattr(_load(), name)(*args, out, stream))
+    else:
+        _check(getattr(_load(), name + "_ws")(*args, out, workspace.data_ptr(),
+                                               workspace.numel() * workspace.element_size(), stream))
     return D
 
 
@@ -387,13 +418,14 @@ def _mx8(name, A, SFA, B, SFB, C, out_dtype, D, split):
     return D
 
 
-def gemm_mxfp8(A, SFA, B, SFB, C=None, out_dtype=None, D=None, a_order="k", b_order="k"):
+def gemm_mxfp8(A, SFA, B, SFB, C=None, out_dtype=None, D=None, a_order="k", b_order="k", workspace=None):
     """Block-scaled fp8: A (M, K), B (N, K) e4m3 (float8_e4m3fn or uint8 codes);
     SFA (M, K/32), SFB (N, K/32) e8m0 codes (uint8 or float8_e8m0fnu).
     ``a_order="mn"``: A given as its K x M storage (element (m, k) at [k, m]);
-    ``b_order="mn"``: B as K x N (gemm_mxfp8_ex)."""
+    ``b_order="mn"``: B as K x N (gemm_mxfp8_ex; with ``workspace``, of
+    :func:`ex_workspace_bytes` bytes, gemm_mxfp8_ex_ws)."""
     if a_order != "k" or b_order != "k":
-        return _mx_ex("e4m3", A, SFA, B, SFB, C, out_dtype, D, a_order, b_order)
+        return _mx_ex("e4m3", A, SFA, B, SFB, C, out_dtype, D, a_order, b_order, workspace=workspace)
     return _mx8("gemm_mxfp8", A, SFA, B, SFB, C, out_dtype, D, None)
 
 
@@ -425,14 +457,15 @@ def _mx4(name, A, SFA, B, SFB, C, out_dtype, D, split):
     return D
 
 
-def gemm_mxfp4(A, SFA, B, SFB, C=None, out_dtype=None, D=None, a_order="k", b_order="k"):
+def gemm_mxfp4(A, SFA, B, SFB, C=None, out_dtype=None, D=None, a_order="k", b_order="k", workspace=None):
     """Block-scaled fp4: A (M, K/2), B (N, K/2) uint8 bytes each holding two
     e2m1 codes (element 2i in the low nibble of byte i; float4_e2m1fn_x2 is
     accepted too); SFA (M, K/32), SFB (N, K/32) e8m0 codes.  K is twice the
     byte width of A.  ``a_order="mn"``: A given as its K x M storage, (K,
-    M/2) bytes packed along M; ``b_order="mn"`` likewise (gemm_mxfp4_ex)."""
+    M/2) bytes packed along M; ``b_order="mn"`` likewise (gemm_mxfp4_ex;
+    with ``workspace`` gemm_mxfp4_ex_ws)."""
     if a_order != "k" or b_order != "k":
-        return _mx_ex("e2m1", A, SFA, B, SFB, C, out_dtype, D, a_order, b_order)
+        return _mx_ex("e2m1", A, SFA, B, SFB, C, out_dtype, D, a_order, b_order, workspace=workspace)
     return _mx4("gemm_mxfp4", A, SFA, B, SFB, C, out_dtype, D, None)
 
 
@@ -477,17 +510,19 @@ def _mx6(name, A, SFA, B, SFB, C, out_dtype, D, fmt, split):
     return D
 
 
-def gemm_mxfp6(A, SFA, B, SFB, C=None, out_dtype=None, D=None, fmt="e2m3", a_order="k", b_order="k"):
+def gemm_mxfp6(A, SFA, B, SFB, C=None, out_dtype=None, D=None, fmt="e2m3", a_order="k", b_order="k",
+               workspace=None):
     """Block-scaled fp6: A (M, 3K/4), B (N, 3K/4) uint8 bytes holding six-bit
     codes (element k at bits 6k .. 6k+5 of a row read as a little-endian bit
     string) in format ``fmt`` ("e2m3" or "e3m2"); SFA (M, K/32), SFB (N, K/32)
     e8m0 codes.  K is four thirds of the byte width of A.  ``a_order="mn"``:
     A given as its K x M storage, (K, 3M/4) bytes packed along M;
-    ``b_order="mn"`` likewise (gemm_mxfp6_ex)."""
+    ``b_order="mn"`` likewise (gemm_mxfp6_ex; with ``workspace``
+    gemm_mxfp6_ex_ws)."""
     if a_order != "k" or b_order != "k":
         if fmt not in FP6_FORMATS:
             raise ValueError("fmt must be 'e2m3' or 'e3m2'")
-        return _mx_ex(fmt, A, SFA, B, SFB, C, out_dtype, D, a_order, b_order, fmt)
+        return _mx_ex(fmt, A, SFA, B, SFB, C, out_dtype, D, a_order, b_order, fmt, workspace=workspace)
     return _mx6("gemm_mxfp6", A, SFA, B, SFB, C, out_dtype, D, fmt, None)
 
 

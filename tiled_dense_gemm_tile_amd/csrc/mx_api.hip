@@ -4,6 +4,7 @@
 #include <stdlib.h>
 
 #include "api.hpp"
+#include "transpose.hpp"
 #include "mx_any_api.hpp"
 #include "mx_launch.hpp"
 
@@ -185,6 +186,27 @@ gemm_status gemm_mxfp8_ex(int64_t M, int64_t N, int64_t K, const void *A, int64_
     if (st != GEMM_OK || none) return st;
     if (K == 0) return dispatch_mx(a, SFA, ldsfa, SFB, ldsfb, stream);
     return run_mx_any(a, 0, lda, ldb, SFA, ldsfa, SFB, ldsfb, stream, amn, bmn);
+}
+
+gemm_status gemm_mxfp8_ex_ws(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int a_order,
+                             const void *SFA, int64_t ldsfa, const void *B, int64_t ldb, int b_order,
+                             const void *SFB, int64_t ldsfb, const void *C, int64_t ldc, void *D, int64_t ldd,
+                             int out_type, void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    if ((a_order != GEMM_K_CONTIGUOUS && a_order != GEMM_MN_CONTIGUOUS) ||
+        (b_order != GEMM_K_CONTIGUOUS && b_order != GEMM_MN_CONTIGUOUS))
+        return GEMM_ERR_UNSUPPORTED;
+    const bool amn = a_order == GEMM_MN_CONTIGUOUS, bmn = b_order == GEMM_MN_CONTIGUOUS;
+    if (!workspace || (!amn && !bmn) || K == 0)
+        return gemm_mxfp8_ex(M, N, K, A, lda, a_order, SFA, ldsfa, B, ldb, b_order, SFB, ldsfb, C, ldc, D, ldd,
+                             out_type, stream);
+    Common a{M, N, K, A, lda, B, ldb, C, ldc, D, ldd, out_type, 1};
+    bool none = false;
+    gemm_status st = validate_mx8(a, SFA, ldsfa, SFB, ldsfb, &none, amn ? M : -1, bmn ? N : -1);
+    if (st != GEMM_OK || none) return st;
+    Common k = a;
+    st = k_contiguous_operands(8, a, amn, bmn, workspace, workspace_bytes, stream, &k.A, &k.lda, &k.B, &k.ldb);
+    if (st != GEMM_OK) return st;
+    return gemm_mxfp8(M, N, K, k.A, k.lda, SFA, ldsfa, k.B, k.ldb, SFB, ldsfb, C, ldc, D, ldd, out_type, stream);
 }
 
 gemm_status gemm_mxfp8_splitk(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *SFA,

@@ -6,6 +6,7 @@
 #include <mutex>
 
 #include "api.hpp"
+#include "transpose.hpp"
 #include "f16_launch.hpp"
 
 using namespace tg_api;
@@ -290,6 +291,31 @@ gemm_status run_bf16_splitk_noalloc(const Common &a, int splits, hipStream_t s) 
 
 }  // namespace
 
+// *_ex_ws, 16-bit inputs: the _ex call's checks, then K-contiguous copies
+// of the MN-contiguous operands in the workspace and the plain call.
+gemm_status run_f16_ex_ws(bool fp16, const Common &a, int a_order, int b_order, void *ws, size_t ws_bytes,
+                          hipStream_t s) {
+    if ((a_order != GEMM_K_CONTIGUOUS && a_order != GEMM_MN_CONTIGUOUS) ||
+        (b_order != GEMM_K_CONTIGUOUS && b_order != GEMM_MN_CONTIGUOUS))
+        return GEMM_ERR_UNSUPPORTED;
+    const bool at = a_order == GEMM_MN_CONTIGUOUS, bt = b_order == GEMM_MN_CONTIGUOUS;
+    if (!ws || (!at && !bt)) return run_f16_ex(fp16, a, a_order, b_order, s);
+    if (a.M < 0 || a.N < 0 || a.K < 0) return GEMM_ERR_INVALID_SIZE;
+    if (a.M > 0 && a.N > 0 && ((at && a.lda < a.M) || (bt && a.ldb < a.N))) return GEMM_ERR_BAD_LD;
+    Common v = a;
+    if (at) v.lda = a.K;
+    if (bt) v.ldb = a.K;
+    bool none = false;
+    gemm_status st = validate(v, &none);
+    if (st != GEMM_OK || none) return st;
+    if ((at && a.lda * 2 >= kMaxLdBytes) || (bt && a.ldb * 2 >= kMaxLdBytes)) return GEMM_ERR_UNSUPPORTED;
+    if (a.K == 0) return run_f16_ex(fp16, a, a_order, b_order, s);
+    Common k = a;
+    st = k_contiguous_operands(16, a, at, bt, ws, ws_bytes, s, &k.A, &k.lda, &k.B, &k.ldb);
+    if (st != GEMM_OK) return st;
+    return run_f16(fp16, k, s);
+}
+
 extern "C" {
 
 gemm_status gemm_bf16(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *B, int64_t ldb,
@@ -316,6 +342,22 @@ gemm_status gemm_fp16_ex(int64_t M, int64_t N, int64_t K, const void *A, int64_t
                          hipStream_t stream) {
     Common a{M, N, K, A, lda, B, ldb, C, ldc, D, ldd, out_type, 2};
     return run_f16_ex(true, a, a_order, b_order, stream);
+}
+
+gemm_status gemm_bf16_ex_ws(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int a_order,
+                            const void *B, int64_t ldb, int b_order, const void *C, int64_t ldc, void *D,
+                            int64_t ldd, int out_type, void *workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+    Common a{M, N, K, A, lda, B, ldb, C, ldc, D, ldd, out_type, 2};
+    return run_f16_ex_ws(false, a, a_order, b_order, workspace, workspace_bytes, stream);
+}
+
+gemm_status gemm_fp16_ex_ws(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, int a_order,
+                            const void *B, int64_t ldb, int b_order, const void *C, int64_t ldc, void *D,
+                            int64_t ldd, int out_type, void *workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+    Common a{M, N, K, A, lda, B, ldb, C, ldc, D, ldd, out_type, 2};
+    return run_f16_ex_ws(true, a, a_order, b_order, workspace, workspace_bytes, stream);
 }
 
 size_t gemm_splitk_workspace_bytes(int64_t M, int64_t N, int64_t K, int splits) {

@@ -88,8 +88,50 @@ def _mx_case(t, M, N, K, seed, with_c, out, splits=None, b_order="k"):
     return call, Dr
 
 
+def _ws(n):
+    w = torch.empty(n + 256, dtype=torch.uint8, device=DEV)
+    return w[(-w.data_ptr()) % 256:]
+
+
+def _bf16_ex_ws_case():
+    """A stored K x M with rows of M + 1 elements: its copy kernel, then the
+    plain call, both captured."""
+    M, N, K = 300, 260, 200
+    rng = np.random.default_rng(8)
+    A = inputs.random_codes(rng, "bf16", (M, K), integer=True)
+    B = inputs.random_codes(rng, "bf16", (N, K), integer=True)
+    st = np.zeros((K, M + 1), np.uint16)
+    st[:, :M] = A.T
+    Ad = dev16(st, "bf16")[:, :M].t()
+    Bd = dev16(B, "bf16")
+    ws = _ws(tg.ex_workspace_bytes(16, M, N, K, "mn", "k"))
+
+    def call(D):
+        return tg.gemm_bf16(Ad, Bd, D=D, workspace=ws)
+    return call, oracle.gemm_ref_full("bf16", A, B)[0]
+
+
+def _kblock_ws_case():
+    """fp8 with 128-wide scale blocks: the scale replication kernel, then the
+    tiled call, both captured."""
+    M, N, K, kb = 520, 300, 1024, 128
+    rng = np.random.default_rng(9)
+    A = inputs.random_codes(rng, "e4m3", (M, K), integer=True)
+    B = inputs.random_codes(rng, "e4m3", (N, K), integer=True)
+    SFA = (127 + rng.integers(0, 2, size=(M, K // kb))).astype(np.uint8)
+    SFB = (127 + rng.integers(0, 2, size=(N, K // kb))).astype(np.uint8)
+    Ad, Bd, Sa, Sb = dev8(A), dev8(B), dev8(SFA), dev8(SFB)
+    ws = _ws(tg.mx_kblock_workspace_bytes(M, N, K))
+
+    def call(D):
+        return tg.gemm_mx_kblock("e4m3", Ad, Sa, Bd, Sb, kb, D=D, workspace=ws)
+    return call, oracle.gemm_ref_full("e4m3", A, B, SFA=SFA, SFB=SFB, kblock=kb)[0]
+
+
 # (label, builder): whole and ragged tiles, both output types, C present and
-# absent, split-K with its reduction kernel, the general scaled kernel
+# absent, split-K with its reduction kernel, the general scaled kernel, the
+# persistent kernels, the workspace paths (a copy or replication kernel
+# before the GEMM)
 CASES = {
     "bf16_c_ragged": lambda: _f16_case("bf16", 1000, 700, 1100, 1, True, torch.float32),
     "fp16_bf16out_oddk": lambda: _f16_case("fp16", 384, 520, 4100, 2, False, torch.bfloat16),
@@ -98,6 +140,10 @@ CASES = {
     "mxfp8_general_mn": lambda: _mx_case("e4m3", 200, 136, 1056, 5, True, torch.bfloat16, b_order="mn"),
     "mxfp4_splitk4": lambda: _mx_case("e2m1", 256, 256, 4096, 6, False, torch.float32, splits=4),
     "mxfp6_e3m2": lambda: _mx_case("e3m2", 300, 200, 640, 7, True, torch.float32),
+    "bf16_persistent": lambda: _f16_case("bf16", 4200, 4300, 256, 10, False, torch.bfloat16),
+    "mxfp8_persistent": lambda: _mx_case("e4m3", 4200, 4300, 512, 11, False, torch.float32),
+    "bf16_ex_ws": _bf16_ex_ws_case,
+    "mxfp8_kblock_ws": _kblock_ws_case,
 }
 
 

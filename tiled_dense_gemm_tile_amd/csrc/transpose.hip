@@ -64,22 +64,32 @@ __global__ void __launch_bounds__(256) k_contiguous_copy_kernel(const uint8_t *s
         shift[pos(i)] = k0 + i < K ? (int)(first & 3) : 0;
     }
     __syncthreads();
-    for (int idx = tid; idx < TE * OW; idx += 256) {
-        const int rr = idx / OW, j = idx % OW;
+    // each thread assembles four consecutive destination words (16 bytes)
+    // and stores them at once
+    static_assert(OW % 4 == 0, "whole 16-byte pieces");
+    for (int idx = tid; idx < TE * OW / 4; idx += 256) {
+        const int rr = idx / (OW / 4), j0 = (idx % (OW / 4)) * 4;
         if (r0 + rr >= rows) continue;
-        uint64_t acc = 0;
-        const int e_lo = 32 * j / W, e_hi = (32 * j + 31) / W;
+        uint32_t out[4];
 #pragma unroll
-        for (int n = 0; n < 32 / W + 2; ++n) {
-            const int e = e_lo + n;
-            if (e > e_hi) break;
-            const int pe = pos(e);
-            const int bit = 8 * shift[pe] + W * rr;
-            const int wi = bit >> 5, b = bit & 31;
-            const uint64_t two = (uint64_t)stage[pe][wi] | ((uint64_t)stage[pe][wi + 1] << 32);
-            acc |= ((two >> b) & MASK) << (W * e - 32 * j + 32);
+        for (int q = 0; q < 4; ++q) {
+            const int j = j0 + q;
+            uint64_t acc = 0;
+            const int e_lo = 32 * j / W, e_hi = (32 * j + 31) / W;
+#pragma unroll
+            for (int n = 0; n < 32 / W + 2; ++n) {
+                const int e = e_lo + n;
+                if (e > e_hi) break;
+                const int pe = pos(e);
+                const int bit = 8 * shift[pe] + W * rr;
+                const int wi = bit >> 5, b = bit & 31;
+                const uint64_t two = (uint64_t)stage[pe][wi] | ((uint64_t)stage[pe][wi + 1] << 32);
+                acc |= ((two >> b) & MASK) << (W * e - 32 * j + 32);
+            }
+            out[q] = (uint32_t)(acc >> 32);
         }
-        *(uint32_t *)(dst + (int64_t)(r0 + rr) * ldd + (int64_t)k0 * W / 8 + 4 * j) = (uint32_t)(acc >> 32);
+        *(uint4 *)(dst + (int64_t)(r0 + rr) * ldd + (int64_t)k0 * W / 8 + 4 * j0) =
+            make_uint4(out[0], out[1], out[2], out[3]);
     }
 }
 

@@ -1,6 +1,6 @@
 """Profile the benchmark with rocprofv3 and write short text summaries to profiles/.
 
-    python rocprof_summary.py [--workload square4096_bf16] [--out-dir gpurun_out/rocprof]
+    python rocprof_summary.py [--workload square4096_bf16] [--out-dir rocprof_out]
                               [--skip-trace] [--skip-traffic] [--skip-counters]
 
 Runs, each as its own child process with the program directly after ``--``:
@@ -123,7 +123,7 @@ def main():
     ap.add_argument("--workload", default="square4096_bf16")
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--out-dir", default=os.path.join(ROOT, "gpurun_out", "rocprof"))
+    ap.add_argument("--out-dir", default=os.path.join(ROOT, "rocprof_out"))
     ap.add_argument("--skip-trace", action="store_true")
     ap.add_argument("--skip-traffic", action="store_true")
     ap.add_argument("--skip-counters", action="store_true")

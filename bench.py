@@ -166,7 +166,7 @@ def main():
         print(json.dumps({"calibrate_copy_bytes": n * 4, "copies": 3}))
         return
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (got --gpus %d)" % args.gpus,
+        print("bench.py measures one GPU: the library has no multi-GPU path (got --gpus %d)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
 

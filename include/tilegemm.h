@@ -234,6 +234,58 @@ gemm_status gemm_mxfp6(int64_t M, int64_t N, int64_t K,
                        int format, int out_type, hipStream_t stream);
 
 /*
+ * gemm_mxfp6_pack, gemm_mxfp6_packed_bytes, gemm_mxfp6_packed -- fp6
+ * operands rewritten once as the tile images the fp6 kernel loads, for
+ * operands used by many calls (weights).  The tiled kernel stages a
+ * 256-row, 128-element K tile of each operand in LDS as 256 rows of 96
+ * bytes; from row-major storage each load instruction then fetches 96-byte
+ * row pieces, from the images 1 KiB of consecutive bytes.  Source: "Tensor
+ * Core 数据布局的演进", section 写回结果与对 shared memory 做 swizzle (the
+ * operand staged in a swizzled shared-memory layout; here the global copy
+ * is laid out the same way so the copy into it is a straight stream).
+ *
+ * Image layout of an operand X of `rows` rows and K elements (K % 128 ==
+ * 0): ceil(rows / 256) * (K / 128) images of 24576 bytes; image (b, t)
+ * (rows 256 b .. 256 b + 255, elements 128 t .. 128 t + 127) starts at byte
+ * (b * (K / 128) + t) * 24576, and its 16-byte chunk c (0 .. 1535) holds
+ * bytes 96 t + 16 h .. 96 t + 16 h + 15 of row 256 b + c / 6 of X's
+ * storage, h = (c % 6) ^ ((c / 6 >> 3) & 1); rows past `rows` are zeros.
+ *
+ * gemm_mxfp6_packed_bytes(rows, K): the image bytes of such an operand; 0
+ *   for rows or K negative, K % 128 != 0, rows >= 2^31 or K >= 2^23.
+ * gemm_mxfp6_pack(rows, K, X, ldx, P, p_bytes, stream): enqueue the rewrite
+ *   of X (rows x K fp6 elements, row-major, ldx ELEMENTS per row, a
+ *   multiple of 4, >= K; any byte alignment) into P (device memory of
+ *   p_bytes >= gemm_mxfp6_packed_bytes(rows, K), 16-byte aligned, not
+ *   overlapping X; the caller owns both).  The codes are copied as they
+ *   are: the format is the GEMM's.  rows or K == 0: nothing is enqueued.
+ *   Errors: rows or K negative GEMM_ERR_INVALID_SIZE; K % 128 != 0,
+ *   K >= 2^23, rows >= 2^31 or ldx % 4 != 0 GEMM_ERR_UNSUPPORTED; ldx < K
+ *   GEMM_ERR_BAD_LD; X or P NULL GEMM_ERR_NULL_POINTER; P not 16-byte
+ *   aligned GEMM_ERR_MISALIGNED; p_bytes too small GEMM_ERR_WORKSPACE.
+ * gemm_mxfp6_packed(M, N, K, AP, SFA, ldsfa, BP, SFB, ldsfb, C, ldc, D, ldd,
+ *   format, out_type, stream): gemm_mxfp6 with A and B given as images --
+ *   AP of A (M rows), BP of B (N rows), both with this K, 16-byte aligned
+ *   (GEMM_ERR_MISALIGNED) -- and the same result bit for bit (the same
+ *   kernel and MFMA order).  Requires K % 128 == 0 and K < 2^23, SFA and
+ *   SFB 16-byte aligned with ldsfa and ldsfb multiples of 16
+ *   (GEMM_ERR_UNSUPPORTED otherwise; there is no general fallback for
+ *   images).  SFA, SFB, C, D, format, out_type and the other checks as
+ *   gemm_mxfp6.
+ */
+size_t gemm_mxfp6_packed_bytes(int64_t rows, int64_t K);
+
+gemm_status gemm_mxfp6_pack(int64_t rows, int64_t K, const void *X, int64_t ldx,
+                            void *P, size_t p_bytes, hipStream_t stream);
+
+gemm_status gemm_mxfp6_packed(int64_t M, int64_t N, int64_t K,
+                              const void *AP, const void *SFA, int64_t ldsfa,
+                              const void *BP, const void *SFB, int64_t ldsfb,
+                              const void *C, int64_t ldc,
+                              void *D, int64_t ldd,
+                              int format, int out_type, hipStream_t stream);
+
+/*
  * gemm_bf16_splitk, gemm_fp16_splitk -- as gemm_bf16 / gemm_fp16, with K cut
  * into `splits` ranges computed by separate workgroups (more workgroups for
  * grids too small to fill the GPU: few output tiles, long K).  Each range's

@@ -29,7 +29,8 @@ def test_header_declares_the_entry_points():
                                     "gemm_last_hip_error",
                                     "gemm_mx_kblock", "gemm_mx_kblock_workspace_bytes", "gemm_mx_kblock_ws",
                                     "gemm_mxfp4", "gemm_mxfp4_ex", "gemm_mxfp4_ex_ws", "gemm_mxfp4_splitk",
-                                    "gemm_mxfp6", "gemm_mxfp6_ex", "gemm_mxfp6_ex_ws", "gemm_mxfp6_splitk",
+                                    "gemm_mxfp6", "gemm_mxfp6_ex", "gemm_mxfp6_ex_ws", "gemm_mxfp6_pack",
+                                    "gemm_mxfp6_packed", "gemm_mxfp6_packed_bytes", "gemm_mxfp6_splitk",
                                     "gemm_mxfp8", "gemm_mxfp8_ex", "gemm_mxfp8_ex_ws", "gemm_mxfp8_splitk",
                                     "gemm_splitk_scratch_limit", "gemm_splitk_workspace_bytes",
                                     "gemm_status_string"]
@@ -449,3 +450,53 @@ def test_validation_ex_ws():
     assert c8(ldsfa=7) == BAD_LD                       # scale rows as the plain call
     assert c8(K=48) == UNSUPPORTED
     assert c8(M=-1) == INVALID_SIZE
+
+
+def test_validation_mxfp6_packed():
+    """fp6 tile images: the size rule, and every refused pack or GEMM case
+    checked before anything is launched (no GPU call: each case below fails
+    a check or has nothing to do)."""
+    nbytes = tg.raw.gemm_mxfp6_packed_bytes
+    # ceil(rows / 256) row blocks x K / 128 tiles x 24576 bytes
+    assert nbytes(256, 128) == 24576
+    assert nbytes(257, 512) == 2 * 4 * 24576
+    assert nbytes(1, 8192) == 64 * 24576
+    assert nbytes(0, 128) == 0 and nbytes(300, 0) == 0
+    assert nbytes(300, 96) == 0 and nbytes(-1, 128) == 0 and nbytes(4, 1 << 23) == 0
+
+    def pack(rows=300, K=256, X=P, ldx=256, dst=P + (1 << 26), nb=None):
+        if nb is None:
+            nb = nbytes(rows, K)
+        return tg.raw.gemm_mxfp6_pack(rows, K, X, ldx, dst, nb, None)
+    assert pack(rows=-1) == INVALID_SIZE
+    assert pack(K=-128) == INVALID_SIZE
+    assert pack(K=96, ldx=96) == UNSUPPORTED               # K % 128 != 0
+    assert pack(K=1 << 23, ldx=1 << 23, nb=1 << 40) == UNSUPPORTED
+    assert pack(ldx=258) == UNSUPPORTED                    # rows must start on a byte
+    assert pack(ldx=252) == BAD_LD
+    assert pack(X=None) == NULL_POINTER
+    assert pack(dst=None) == NULL_POINTER
+    assert pack(dst=P + 8) == MISALIGNED
+    assert pack(nb=nbytes(300, 256) - 1) == WORKSPACE
+    assert pack(rows=0) == OK and pack(K=0, ldx=0) == OK
+
+    D = P + (1 << 24)
+
+    def gemm(M=300, N=200, K=256, AP=P, BP=P + (1 << 22), SFA=P + 4096, ldsfa=16, SFB=P + 8192, ldsfb=16,
+             ldd=200, fmt=0, out=F32, C=None, ldc=0):
+        return tg.raw.gemm_mxfp6_packed(M, N, K, AP, SFA, ldsfa, BP, SFB, ldsfb, C, ldc, D, ldd, fmt, out, None)
+    assert gemm(M=-1) == INVALID_SIZE
+    assert gemm(M=0) == OK
+    assert gemm(fmt=2) == UNSUPPORTED
+    assert gemm(out=3) == UNSUPPORTED
+    assert gemm(K=96) == UNSUPPORTED                       # K % 128 != 0
+    assert gemm(K=1 << 23, ldsfa=1 << 18, ldsfb=1 << 18) == UNSUPPORTED
+    assert gemm(AP=P + 4) == MISALIGNED
+    assert gemm(BP=P + 8) == MISALIGNED
+    assert gemm(ldsfa=4) == BAD_LD                         # K / 32 = 8 scales per row
+    assert gemm(SFB=None) == NULL_POINTER
+    assert gemm(AP=None) == NULL_POINTER
+    assert gemm(ldsfa=24) == UNSUPPORTED                   # scale rows of whole 16-byte words
+    assert gemm(SFA=P + 4100) == UNSUPPORTED
+    assert gemm(ldd=100) == BAD_LD
+    assert gemm(C=D, ldc=100) == BAD_LD

@@ -110,6 +110,12 @@ def _load():
             L.gemm_mx_kblock_ws.argtypes = [ci, i64, i64, i64, i64] + smx[3:] + [ci, vp, sz, vp]
             L.gemm_mx_kblock_workspace_bytes.restype = sz
             L.gemm_mx_kblock_workspace_bytes.argtypes = [i64, i64, i64]
+            L.gemm_mxfp6_packed_bytes.restype = sz
+            L.gemm_mxfp6_packed_bytes.argtypes = [i64, i64]
+            L.gemm_mxfp6_pack.restype = ci
+            L.gemm_mxfp6_pack.argtypes = [i64, i64, vp, i64, vp, sz, vp]
+            L.gemm_mxfp6_packed.restype = ci
+            L.gemm_mxfp6_packed.argtypes = [i64, i64, i64, vp, vp, i64, vp, vp, i64, vp, i64, vp, i64, ci, ci, vp]
             L.gemm_status_string.restype = ctypes.c_char_p
             L.gemm_status_string.argtypes = [ci]
             L.gemm_last_hip_error.restype = ci
@@ -576,6 +582,69 @@ def gemm_mx_kblock(fmt, A, SFA, B, SFB, kblock, C=None, out_dtype=None, D=None, 
     else:
         nbytes = workspace.numel() * workspace.element_size()
         _check(_load().gemm_mx_kblock_ws(*args, workspace.data_ptr(), nbytes, _Stream(A)))
+    return D
+
+
+def mxfp6_packed_bytes(rows: int, K: int) -> int:
+    """Bytes of the tile images of an fp6 operand of ``rows`` rows and K
+    elements (gemm_mxfp6_packed_bytes; 0 when K % 128 != 0)."""
+    return int(_load().gemm_mxfp6_packed_bytes(rows, K))
+
+
+def mxfp6_pack(X, out=None):
+    """Tile images of the fp6 operand X -- (rows, 3K/4) uint8 bytes, as
+    :func:`gemm_mxfp6` takes A or B -- for :func:`gemm_mxfp6_packed`
+    (gemm_mxfp6_pack).  ``out``: a device uint8 tensor of at least
+    :func:`mxfp6_packed_bytes` bytes, 16-byte aligned (None: allocated).
+    Returns the images as a flat uint8 tensor."""
+    import torch
+    if X.dtype != torch.uint8 or X.dim() != 2 or not X.is_cuda:
+        raise TypeError("X must be a 2-D uint8 device tensor")
+    rows, KB = X.shape
+    if KB % 3:
+        raise ValueError("the byte width of X must be a multiple of 3 (four elements per three bytes)")
+    K = KB // 3 * 4
+    ldb_ = _ld(X, KB) if K else 0
+    if ldb_ % 3:
+        raise ValueError("the row stride of X must be a multiple of 3 bytes")
+    need = mxfp6_packed_bytes(rows, K)
+    if out is None:
+        out = torch.empty(need, dtype=torch.uint8, device=X.device)
+    _on_device(X, out=out)
+    nb = out.numel() * out.element_size()
+    _check(_load().gemm_mxfp6_pack(rows, K, X.data_ptr(), ldb_ // 3 * 4, out.data_ptr(), nb, _Stream(X)))
+    return out
+
+
+def gemm_mxfp6_packed(AP, SFA, BP, SFB, M, N, K, C=None, out_dtype=None, D=None, fmt="e2m3"):
+    """:func:`gemm_mxfp6` with A and B given as their tile images
+    (:func:`mxfp6_pack` of the (M, 3K/4) and (N, 3K/4) operands; flat
+    device uint8 tensors); the same D bit for bit (gemm_mxfp6_packed)."""
+    import torch
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    if fmt not in FP6_FORMATS:
+        raise ValueError("fmt must be 'e2m3' or 'e3m2'")
+    if out_dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out_dtype must be float32 or bfloat16")
+    for name, X, rows in (("AP", AP, M), ("BP", BP, N)):
+        if X.dtype != torch.uint8 or not X.is_cuda or not X.is_contiguous():
+            raise TypeError("%s must be a contiguous uint8 device tensor" % name)
+        if X.numel() < mxfp6_packed_bytes(rows, K):
+            raise ValueError("%s holds fewer bytes than the images of %d rows" % (name, rows))
+    if D is None:
+        D = torch.empty((M, N), dtype=out_dtype, device=AP.device)
+    if D.dtype != out_dtype or tuple(D.shape) != (M, N):
+        raise ValueError("D must be (M, N) of out_dtype")
+    if C is not None and (C.dtype != out_dtype or tuple(C.shape) != (M, N)):
+        raise ValueError("C must be (M, N) of out_dtype")
+    _on_device(AP, BP=BP, C=C, D=D)
+    _scales(SFA, SFB, M, N, AP)
+    nkb = K // 32
+    out = OUT_BF16 if out_dtype == torch.bfloat16 else OUT_F32
+    _check(_load().gemm_mxfp6_packed(M, N, K, AP.data_ptr(), SFA.data_ptr(), _ld(SFA, nkb) if K else 0,
+                                     BP.data_ptr(), SFB.data_ptr(), _ld(SFB, nkb) if K else 0,
+                                     C.data_ptr() if C is not None else None, _ld(C, N) if C is not None else 0,
+                                     D.data_ptr(), _ld(D, N), FP6_FORMATS[fmt], out, _Stream(AP)))
     return D
 
 

@@ -67,10 +67,18 @@ __device__ __forceinline__ void mfma_mx6_acc(f32x4 &acc, const u32x6 &a, const u
 // CU walking the tiles, as the persistent fp8 kernel; the finished tile's D
 // is staged in ring slot 2 while the next tile's tiles 0 and 1 load into
 // slots 0 and 1.
-template <bool OUT_BF16, int FMT, int DAUX = kStoreStream, bool SPLIT = false, bool PERSIST = false>
+//
+// PACKED: A and B come as their LDS images (mx6_pack.hip): K tile
+// t of row block b (256 rows) is the 24 KiB at ((b * nk) + t) * 24576, laid
+// out exactly as the ring slot holds it, so every load instruction reads
+// 1 KiB of consecutive bytes (the row-major operands' 96-byte row pieces
+// cost two memory requests each); q.g.lda and q.g.ldb are unused.
+template <bool OUT_BF16, int FMT, int DAUX = kStoreStream, bool SPLIT = false, bool PERSIST = false,
+          bool PACKED = false>
 __global__ void __launch_bounds__(256) gemm_mx6_w4_kernel(MxArgs q, F16Epi e) {
     static_assert(FMT == 2 || FMT == 3, "fp6 formats");
     static_assert(!(PERSIST && SPLIT), "persistent: whole tiles");
+    static_assert(!(PACKED && SPLIT), "packed operands: whole K");
     const F16Args &p = q.g;
     constexpr int ROWB = 96;                           // bytes per K tile (128 elements) and LDS row
     constexpr int TM = 8, TN = 8, WTM = 128, WTN = 128;
@@ -109,8 +117,15 @@ __global__ void __launch_bounds__(256) gemm_mx6_w4_kernel(MxArgs q, F16Epi e) {
     __amdgpu_buffer_rsrc_t rA, rB, rSA, rSB;
     auto tile_resources = [&](const MxArgs &a) __attribute__((always_inline)) {
         const F16Args &g = a.g;
-        rA = make_rsrc((const char *)g.A + (int64_t)m0 * g.lda + k_lo / 4 * 3, span_bytes(g.M - m0, kb, g.lda, 1));
-        rB = make_rsrc((const char *)g.B + (int64_t)n0 * g.ldb + k_lo / 4 * 3, span_bytes(g.N - n0, kb, g.ldb, 1));
+        if constexpr (PACKED) {
+            rA = make_rsrc((const char *)g.A + (int64_t)(m0 / 256) * nk * SLOT, (uint32_t)nk * SLOT);
+            rB = make_rsrc((const char *)g.B + (int64_t)(n0 / 256) * nk * SLOT, (uint32_t)nk * SLOT);
+        } else {
+            rA = make_rsrc((const char *)g.A + (int64_t)m0 * g.lda + k_lo / 4 * 3,
+                           span_bytes(g.M - m0, kb, g.lda, 1));
+            rB = make_rsrc((const char *)g.B + (int64_t)n0 * g.ldb + k_lo / 4 * 3,
+                           span_bytes(g.N - n0, kb, g.ldb, 1));
+        }
         rSA = make_rsrc((const char *)a.SFA + (int64_t)m0 * a.ldsfa + k_lo / 32, scale_span(g.M - m0, nblk, a.ldsfa));
         rSB = make_rsrc((const char *)a.SFB + (int64_t)n0 * a.ldsfb + k_lo / 32, scale_span(g.N - n0, nblk, a.ldsfb));
     };
@@ -119,15 +134,17 @@ __global__ void __launch_bounds__(256) gemm_mx6_w4_kernel(MxArgs q, F16Epi e) {
 
     // Operand loads: chunk position c = (4 j + wave) * 64 + lane of a slot
     // is row c / 6, logical chunk (c % 6) ^ (row bit 3); the K offset goes
-    // in the scalar offset.  Scale loads: lane L of wave w brings row
-    // 64 w + L's 16 bytes.
+    // in the scalar offset (PACKED: the chunk is at c * 16 of the tile's
+    // image, the image offset in the scalar offset).  Scale loads: lane L of
+    // wave w brings row 64 w + L's 16 bytes.
+    constexpr int TSTEP = PACKED ? SLOT : ROWB;        // bytes from one K tile to the next
     uint32_t a_off[LPW], b_off[LPW];
 #pragma unroll
     for (int j = 0; j < LPW; ++j) {
         const int c = (4 * j + wave) * 64 + lane;
         const int row = c / 6, chunk = (c % 6) ^ ((row >> 3) & 1);
-        a_off[j] = (uint32_t)(row * p.lda) + chunk * 16;
-        b_off[j] = (uint32_t)(row * p.ldb) + chunk * 16;
+        a_off[j] = PACKED ? (uint32_t)c * 16 : (uint32_t)(row * p.lda) + chunk * 16;
+        b_off[j] = PACKED ? (uint32_t)c * 16 : (uint32_t)(row * p.ldb) + chunk * 16;
     }
     auto dma = [&](__amdgpu_buffer_rsrc_t r, int lds, uint32_t voff, int soff) __attribute__((always_inline)) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)(smem + lds), 16, voff,
@@ -141,7 +158,7 @@ __global__ void __launch_bounds__(256) gemm_mx6_w4_kernel(MxArgs q, F16Epi e) {
         const __amdgpu_buffer_rsrc_t r = t < nk ? (isa ? rA : rB) : rZ;
         const uint32_t voff = isa ? a_off[j] : b_off[j];
         const int lds = (isa ? A_BASE : B_BASE) + slot * SLOT + (j * 4 + wave) * IB;
-        dma(r, lds, voff, t * ROWB);
+        dma(r, lds, voff, t * TSTEP);
     };
     auto lane_id = [&]() __attribute__((always_inline)) {
         int l = lane;
@@ -286,7 +303,7 @@ __global__ void __launch_bounds__(256) gemm_mx6_w4_kernel(MxArgs q, F16Epi e) {
                 const __amdgpu_buffer_rsrc_t r = t < nk ? (isa ? rA : rB) : rZ;
                 const uint32_t voff = isa ? a_off[j] : b_off[j];
                 const int lds = (isa ? A_BASE : B_BASE) + t * SLOT + (j * 4 + wv) * IB;
-                dma(r, lds, voff, t * ROWB);
+                dma(r, lds, voff, t * TSTEP);
             }
             if (t == 0) {
                 const uint32_t va = (uint32_t)((64 * wv + l) * q.ldsfa), vb = (uint32_t)((64 * wv + l) * q.ldsfb);

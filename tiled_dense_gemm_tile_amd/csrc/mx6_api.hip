@@ -136,6 +136,47 @@ gemm_status run_mx6_splitk(const Common &a, int format, const void *SFA, int64_t
     return reduce_splits(a, ws, S, s);
 }
 
+// Operands given as tile images (gemm_mxfp6_pack): the tiled kernel's
+// PACKED form, one workgroup per tile or persistent as dispatch_mx6.
+gemm_status run_mx6_packed(const Common &a, int format, const void *SFA, int64_t ldsfa, const void *SFB,
+                           int64_t ldsfb, hipStream_t s) {
+    if (format != GEMM_FP6_E2M3 && format != GEMM_FP6_E3M2) return GEMM_ERR_UNSUPPORTED;
+    // (the shared checks on a byte view; the images' extents are implied by
+    // M, N and K)
+    Common bytes = a;
+    bytes.K = a.K / 4 * 3;
+    bytes.lda = bytes.K;
+    bytes.ldb = bytes.K;
+    bool none = false;
+    gemm_status st = validate(bytes, &none);
+    if (st != GEMM_OK || none) return st;
+    if (a.K % 128 != 0 || a.K >= ((int64_t)1 << 23)) return GEMM_ERR_UNSUPPORTED;
+    if (a.K > 0) {
+        if (misaligned(a.A, 16) || misaligned(a.B, 16)) return GEMM_ERR_MISALIGNED;
+        if (ldsfa < a.K / 32 || ldsfb < a.K / 32) return GEMM_ERR_BAD_LD;
+        if (!SFA || !SFB) return GEMM_ERR_NULL_POINTER;
+        if (misaligned(SFA, 16) || misaligned(SFB, 16) || ldsfa % 16 != 0 || ldsfb % 16 != 0 ||
+            ldsfa >= kMaxLdBytes || ldsfb >= kMaxLdBytes)
+            return GEMM_ERR_UNSUPPORTED;
+    }
+    Common k = a;
+    k.lda = 0;
+    k.ldb = 0;
+    const tg::MxArgs q = mx6_args(k, SFA, ldsfa, SFB, ldsfb);
+    const int64_t tiles = (int64_t)q.g.tiles_m * q.g.tiles_n;
+    if (tiles >= kMaxDim) return GEMM_ERR_UNSUPPORTED;
+    const bool bf16 = a.out_type == GEMM_OUT_BF16, e3m2 = format == GEMM_FP6_E3M2;
+    const uintptr_t vb = (uintptr_t)(bf16 ? 2 : 4) * 4;
+    tg::F16Epi e;
+    e.vec_d = ((uintptr_t)a.D % vb) == 0 && a.ldd % 4 == 0;
+    e.vec_c = a.C && ((uintptr_t)a.C % vb) == 0 && a.ldc % 4 == 0;
+    const int cus = cu_count(s);
+    const bool persist = !a.C && e.vec_d && a.N % 4 == 0 && cus > 0 && tiles > cus && persist_allowed();
+    const unsigned grid = persist ? (unsigned)cus : (unsigned)tiles;
+    return launched(bf16 ? tg::launch_mx6_packed<true>(e3m2, persist, grid, s, q, e)
+                         : tg::launch_mx6_packed<false>(e3m2, persist, grid, s, q, e));
+}
+
 }  // namespace
 
 extern "C" {
@@ -191,6 +232,13 @@ gemm_status gemm_mxfp6_ex_ws(int64_t M, int64_t N, int64_t K, const void *A, int
     if (st != GEMM_OK) return st;
     return gemm_mxfp6(M, N, K, k.A, k.lda, SFA, ldsfa, k.B, k.ldb, SFB, ldsfb, C, ldc, D, ldd, format, out_type,
                       stream);
+}
+
+gemm_status gemm_mxfp6_packed(int64_t M, int64_t N, int64_t K, const void *AP, const void *SFA, int64_t ldsfa,
+                              const void *BP, const void *SFB, int64_t ldsfb, const void *C, int64_t ldc, void *D,
+                              int64_t ldd, int format, int out_type, hipStream_t stream) {
+    Common a{M, N, K, AP, K, BP, K, C, ldc, D, ldd, out_type, 1};
+    return run_mx6_packed(a, format, SFA, ldsfa, SFB, ldsfb, stream);
 }
 
 gemm_status gemm_mxfp6_splitk(int64_t M, int64_t N, int64_t K, const void *A, int64_t lda, const void *SFA,

@@ -22,6 +22,13 @@ hipError_t launch_mx6_split(bool e3m2, unsigned grid, hipStream_t s, const MxArg
 template <bool OUT_BF16>
 hipError_t launch_mx6_persist(bool e3m2, unsigned grid, hipStream_t s, const MxArgs &q, const F16Epi &e);
 
+// A and B given as their tile images (gemm_mxfp6_pack): one workgroup per
+// tile, or with `persist` (conditions as launch_mx6_persist) `grid`
+// workgroups walking all tiles.
+template <bool OUT_BF16>
+hipError_t launch_mx6_packed(bool e3m2, bool persist, unsigned grid, hipStream_t s, const MxArgs &q,
+                             const F16Epi &e);
+
 }  // namespace tg
 
 #ifdef TG_MX6_INSTANCE
@@ -45,6 +52,24 @@ hipError_t launch_mx6_persist<TG_OUT_BF16>(bool e3m2, unsigned grid, hipStream_t
     else
         hipLaunchKernelGGL((gemm_mx6_w4_kernel<TG_OUT_BF16, 2, kStoreStream, false, true>), dim3(grid), dim3(256), 0,
                            s, q, e);
+    return hipGetLastError();
+}
+
+template <>
+hipError_t launch_mx6_packed<TG_OUT_BF16>(bool e3m2, bool persist, unsigned grid, hipStream_t s, const MxArgs &q,
+                                          const F16Epi &e) {
+    if (e3m2 && persist)
+        hipLaunchKernelGGL((gemm_mx6_w4_kernel<TG_OUT_BF16, 3, kStoreStream, false, true, true>), dim3(grid),
+                           dim3(256), 0, s, q, e);
+    else if (e3m2)
+        hipLaunchKernelGGL((gemm_mx6_w4_kernel<TG_OUT_BF16, 3, kStoreStream, false, false, true>), dim3(grid),
+                           dim3(256), 0, s, q, e);
+    else if (persist)
+        hipLaunchKernelGGL((gemm_mx6_w4_kernel<TG_OUT_BF16, 2, kStoreStream, false, true, true>), dim3(grid),
+                           dim3(256), 0, s, q, e);
+    else
+        hipLaunchKernelGGL((gemm_mx6_w4_kernel<TG_OUT_BF16, 2, kStoreStream, false, false, true>), dim3(grid),
+                           dim3(256), 0, s, q, e);
     return hipGetLastError();
 }
 

@@ -170,3 +170,32 @@ def test_packed_k_zero_gives_c():
     D = tg.gemm_mxfp6_packed(e, s, e, t, M, N, 0, C)
     torch.cuda.synchronize()
     assert torch.equal(D, C)
+
+
+@pytest.mark.parametrize("integer", [False, True])
+def test_packed_workload_8192(integer):
+    """The timed packed workload (8192^3, operands packed once, the
+    persistent kernel): sampled outputs against the oracle, exact on integer
+    inputs, and the block-Freivalds check over all of D."""
+    w = inputs.WORKLOADS["mxfp6_8192_packed"]
+    x = inputs.generate(w, integer=integer)
+    say("mxfp6 packed 8192^3 integer=%s" % integer)
+    SA, SB = dev8(x["SFA"]), dev8(x["SFB"])
+    AP, BP = tg.mxfp6_pack(dev8(x["A"])), tg.mxfp6_pack(dev8(x["B"]))
+    D = tg.gemm_mxfp6_packed(AP, SA, BP, SB, w.M, w.N, w.K, fmt=w.in_type)
+    torch.cuda.synchronize()
+    Dg = D.cpu().numpy()
+    del D, AP, BP
+    rand, forced = inputs.sample_indices(w.M, w.N, w.seed)
+    a, b = oracle.operands_f64(w.in_type, x["A"], x["B"], SFA=x["SFA"], SFB=x["SFB"])
+    for name, idx in (("random", rand), ("forced", forced)):
+        Dr, S = oracle.gemm_ref(w.in_type, x["A"], x["B"], SFA=x["SFA"], SFB=x["SFB"], idx=idx)
+        got = Dg.ravel()[idx].astype(np.float64)
+        if integer:
+            assert np.array_equal(got, Dr), name
+        else:
+            rep = check.report(got, Dr, S)
+            assert rep["fail"] == 0, (name, rep)
+    ok, ratio = check.freivalds_blocks(Dg, a, b, None, block=64, integer=integer)
+    say("  freivalds ok=%s worst %.3g" % (ok, ratio))
+    assert ok

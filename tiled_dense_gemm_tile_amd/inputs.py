@@ -53,6 +53,7 @@ class Workload:
     seed: int
     scaled: bool = False    # block-scaled e4m3 / e2m1 with e8m0 scales per 32 K
     note: str = ""
+    packed: bool = False    # fp6: A and B given as tile images (gemm_mxfp6_packed)
 
     @property
     def flops(self) -> int:
@@ -85,6 +86,10 @@ WORKLOADS = {
                              note="M=N=1024 K=65536 e4m3 + e8m0 per 32 K, C=0, fp32 out (16 output tiles: split-K)"),
     "mxfp6_8192": Workload("mxfp6_8192", 8192, 8192, 8192, "e2m3", "f32", CODES, CODES, None, 7,
                            scaled=True, note="M=N=K=8192 fp6 e2m3 + e8m0 per 32 K, C=0, fp32 out"),
+    "mxfp6_8192_packed": Workload("mxfp6_8192_packed", 8192, 8192, 8192, "e2m3", "f32", CODES, CODES, None, 7,
+                                  scaled=True, packed=True,
+                                  note="mxfp6_8192 with A and B as tile images, packed once before the timed "
+                                       "steps (operands reused across calls, e.g. weights)"),
     "mxfp4_8192": Workload("mxfp4_8192", 8192, 8192, 8192, "e2m1", "f32", CODES, CODES, None, 5,
                            scaled=True, note="M=N=K=8192 e2m1 + e8m0 per 32 K, C=0, fp32 out"),
 }

@@ -251,10 +251,11 @@ __global__ void __launch_bounds__(256) gemm_mx6_w4_kernel(MxArgs q, F16Epi e) {
     // Window t (U = t % 4, tile t in slot rs): MFMAs of tile t - 1 (unless
     // FIRST), reads of tile t -- B block j at MFMA 4 j, A row 7 at MFMA 3 and
     // row i - 1 during row i, scales read at MFMAs 34 .. 46 and assembled 8
-    // MFMAs later -- loads of tile t + 2 during the first 12 MFMAs into the
-    // slot tile t - 1 held (its fragments were read in window t - 1), the
-    // next epoch's scales when U == 2; then a wait for the loads of tile
-    // t + 1 (everything but the 12 just issued).
+    // MFMAs later -- loads of tile t + 2 at every fifth MFMA from MFMA 2 on
+    // (issued back to back, a wave's 12 loads held up its MFMAs: 5-6 %
+    // slower at 8192^3) into the slot tile t - 1 held (its fragments were
+    // read in window t - 1), the next epoch's scales when U == 2; then a
+    // wait for the loads of tile t + 1 (everything but the 12 just issued).
     auto window = [&](auto first, auto uc, int t, int rs) __attribute__((always_inline)) {
         constexpr bool F = decltype(first)::value;
         constexpr int U = decltype(uc)::value;
@@ -263,7 +264,7 @@ __global__ void __launch_bounds__(256) gemm_mx6_w4_kernel(MxArgs q, F16Epi e) {
         static_for<0, 64>([&](auto qc) __attribute__((always_inline)) {
             constexpr int Q = decltype(qc)::value;
             if constexpr (!F) mfma(std::integral_constant<int, (U + 1) & 1>(), qc);
-            if constexpr (Q < 2 * LPW) fetch(t + 2, Q, ws);
+            if constexpr (Q >= 2 && (Q - 2) % 5 == 0 && (Q - 2) / 5 < 2 * LPW) fetch(t + 2, (Q - 2) / 5, ws);
             if constexpr (Q < 32 && Q % 4 == 0) read_b(uc, std::integral_constant<int, Q / 4>(), rs);
             if constexpr (Q == 3) read_a(uc, std::integral_constant<int, TM - 1>(), rs);
             if constexpr (Q >= 8 && Q % 8 == 3) read_a(uc, std::integral_constant<int, Q / 8 - 1>(), rs);

@@ -128,10 +128,36 @@ def _kblock_ws_case():
     return call, oracle.gemm_ref_full("e4m3", A, B, SFA=SFA, SFB=SFB, kblock=kb)[0]
 
 
+def _mxfp6_packed_case():
+    """fp6 operands packed into tile images, then the packed GEMM, both
+    captured (the images are rewritten on every replay)."""
+    M, N, K = 300, 520, 640
+    rng = np.random.default_rng(12)
+    A = inputs.random_codes(rng, "e2m3", (M, K), integer=True)
+    B = inputs.random_codes(rng, "e2m3", (N, K), integer=True)
+    e = inputs.fp6_integer_scale("e2m3")
+    SFA = np.full((M, K // 32), 127 + e, np.uint8)
+    SFB = np.full((N, K // 32), 127 + e, np.uint8)
+    sa = np.zeros((M, 32), np.uint8)
+    sa[:, :K // 32] = SFA
+    sb = np.zeros((N, 32), np.uint8)
+    sb[:, :K // 32] = SFB
+    Ad, Bd = dev8(A), dev8(B)
+    Sa, Sb = dev8(sa)[:, :K // 32], dev8(sb)[:, :K // 32]
+    AP = torch.empty(tg.mxfp6_packed_bytes(M, K), dtype=torch.uint8, device=DEV)
+    BP = torch.empty(tg.mxfp6_packed_bytes(N, K), dtype=torch.uint8, device=DEV)
+
+    def call(D):
+        tg.mxfp6_pack(Ad, out=AP)
+        tg.mxfp6_pack(Bd, out=BP)
+        return tg.gemm_mxfp6_packed(AP, Sa, BP, Sb, M, N, K, D=D)
+    return call, oracle.gemm_ref_full("e2m3", A, B, SFA=SFA, SFB=SFB)[0]
+
+
 # (label, builder): whole and ragged tiles, both output types, C present and
 # absent, split-K with its reduction kernel, the general scaled kernel, the
 # persistent kernels, the workspace paths (a copy or replication kernel
-# before the GEMM)
+# before the GEMM), fp6 tile images (two packing kernels before the GEMM)
 CASES = {
     "bf16_c_ragged": lambda: _f16_case("bf16", 1000, 700, 1100, 1, True, torch.float32),
     "fp16_bf16out_oddk": lambda: _f16_case("fp16", 384, 520, 4100, 2, False, torch.bfloat16),
@@ -144,6 +170,7 @@ CASES = {
     "mxfp8_persistent": lambda: _mx_case("e4m3", 4200, 4300, 512, 11, False, torch.float32),
     "bf16_ex_ws": _bf16_ex_ws_case,
     "mxfp8_kblock_ws": _kblock_ws_case,
+    "mxfp6_packed": _mxfp6_packed_case,
 }
 
 

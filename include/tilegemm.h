@@ -414,7 +414,15 @@ gemm_status gemm_mxfp6_ex(int64_t M, int64_t N, int64_t K,
  *     at least gemm_ex_workspace_bytes(e, M, N, K, a_order, b_order) bytes
  *     (else GEMM_ERR_WORKSPACE), not overlapping any other argument; its
  *     contents are undefined after the call.  NULL, or both operands
- *     K-contiguous: exactly the *_ex call.
+ *     K-contiguous: exactly the *_ex call -- except gemm_mxfp6_ex_ws with
+ *     both operands K-contiguous, K % 128 == 0, SFA and SFB 16-byte aligned
+ *     with ldsfa, ldsfb multiples of 16 and a workspace of at least
+ *     gemm_ex_workspace_bytes(6, M, N, K, GEMM_K_CONTIGUOUS,
+ *     GEMM_K_CONTIGUOUS) bytes (the tile images of A then of B, each
+ *     rounded up to 256 bytes; 0 when K % 128 != 0), 256-byte aligned: the
+ *     operands are rewritten there (gemm_mxfp6_pack) and gemm_mxfp6_packed
+ *     runs, the same D bit for bit (a smaller or misaligned workspace then
+ *     gives the plain call).
  * Everything else (orders, leading dimensions, scales, validation,
  * out_type, C == D) is as the *_ex call; every check comes before any
  * kernel is enqueued.

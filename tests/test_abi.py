@@ -436,6 +436,10 @@ def test_validation_ex_ws():
     assert tg.raw.gemm_ex_workspace_bytes(6, 64, 64, 128, KC, MN) == 64 * 144
     assert tg.raw.gemm_ex_workspace_bytes(4, 64, 64, 128, MN, KC) == 64 * 128
     assert tg.raw.gemm_ex_workspace_bytes(4, 64, 64, 128, KC, KC) == 0
+    # fp6, both K-contiguous: the tile images of A and of B (2 x 2 and 1 x 2
+    # images of 24576 bytes), none when K % 128 != 0
+    assert tg.raw.gemm_ex_workspace_bytes(6, 300, 200, 256, KC, KC) == (4 + 2) * 24576
+    assert tg.raw.gemm_ex_workspace_bytes(6, 300, 200, 96, KC, KC) == 0
     assert tg.raw.gemm_ex_workspace_bytes(5, 64, 64, 128, MN, MN) == 0
     need16 = tg.raw.gemm_ex_workspace_bytes(16, 300, 200, 130, MN, KC)
     assert c16(wsb=need16 - 1) == WORKSPACE
@@ -500,3 +504,21 @@ def test_validation_mxfp6_packed():
     assert gemm(SFA=P + 4100) == UNSUPPORTED
     assert gemm(ldd=100) == BAD_LD
     assert gemm(C=D, ldc=100) == BAD_LD
+
+
+def test_validation_mxfp6_ex_ws_images():
+    """gemm_mxfp6_ex_ws with K-contiguous operands and a workspace for their
+    tile images: the plain call's checks come first (nothing launched)."""
+    D = P + (1 << 24)
+    WS = P + (1 << 26)
+    KC = 0
+
+    def call(M=300, N=200, K=256, lda=256, ldb=256, ldsfa=16, ldsfb=16, ldd=200, fmt=0):
+        return tg.raw.gemm_mxfp6_ex_ws(M, N, K, P, lda, KC, P + 4096, ldsfa, P, ldb, KC, P + 8192, ldsfb, None, 0,
+                                       D, ldd, fmt, F32, WS, 1 << 24, None)
+    assert call(ldsfa=4) == BAD_LD
+    assert call(lda=252) == BAD_LD
+    assert call(ldd=100) == BAD_LD
+    assert call(fmt=2) == UNSUPPORTED
+    assert call(M=-1) == INVALID_SIZE
+    assert call(M=0) == OK

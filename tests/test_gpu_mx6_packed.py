@@ -199,3 +199,34 @@ def test_packed_workload_8192(integer):
     ok, ratio = check.freivalds_blocks(Dg, a, b, None, block=64, integer=integer)
     say("  freivalds ok=%s worst %.3g" % (ok, ratio))
     assert ok
+
+
+@pytest.mark.parametrize("fmt", ["e2m3", "e3m2"])
+@pytest.mark.parametrize("case", [(300, 200, 640, True), (4200, 4300, 512, False)], ids=["300x200x640+C", "4200x4300x512"])
+def test_ex_ws_k_contiguous_uses_images(fmt, case):
+    """gemm_mxfp6 with a workspace and K-contiguous operands (gemm_mxfp6_ex_ws):
+    the operands' tile images in the workspace, then the packed kernel --
+    equal bit for bit to the plain call; a workspace one byte short gives
+    the plain call."""
+    M, N, K, with_c = case
+    A, B, SFA, SFB, C = _case(fmt, M, N, K, M + N + K + len(fmt), True, with_c)
+    dA, dB, dSA, dSB = dev8(A), dev8(B), dev_scales(SFA), dev_scales(SFB)
+    need = tg.ex_workspace_bytes(6, M, N, K)
+    assert need == -(-tg.mxfp6_packed_bytes(M, K) // 256) * 256 + -(-tg.mxfp6_packed_bytes(N, K) // 256) * 256
+    for out in (torch.float32, torch.bfloat16):
+        Cd = torch.from_numpy(C).to(DEV).to(out) if C is not None else None
+        say("mxfp6 ex_ws images %s %dx%dx%d C=%s out=%s" % (fmt, M, N, K, with_c, out))
+        ws = torch.empty(need + 256, dtype=torch.uint8, device=DEV)
+        ws = ws[(-ws.data_ptr()) % 256:]
+        D = tg.gemm_mxfp6(dA, dSA, dB, dSB, Cd, out_dtype=out, fmt=fmt, workspace=ws[:need])
+        Dshort = tg.gemm_mxfp6(dA, dSA, dB, dSB, Cd, out_dtype=out, fmt=fmt, workspace=ws[:need - 1])
+        Ds = tg.gemm_mxfp6(dA, dSA, dB, dSB, Cd, out_dtype=out, fmt=fmt)
+        torch.cuda.synchronize()
+        assert torch.equal(D, Ds)
+        assert torch.equal(Dshort, Ds)
+    if not (M * N > 4 * 10 ** 6):
+        Dr, _ = oracle.gemm_ref_full(fmt, A, B, C=C, SFA=SFA, SFB=SFB)
+        D = tg.gemm_mxfp6(dA, dSA, dB, dSB, torch.from_numpy(C).to(DEV) if C is not None else None, fmt=fmt,
+                          workspace=ws[:need])
+        torch.cuda.synchronize()
+        assert np.array_equal(to_f64(D), Dr)

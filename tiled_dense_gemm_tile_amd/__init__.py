@@ -524,8 +524,10 @@ def gemm_mxfp6(A, SFA, B, SFB, C=None, out_dtype=None, D=None, fmt="e2m3", a_ord
     e8m0 codes.  K is four thirds of the byte width of A.  ``a_order="mn"``:
     A given as its K x M storage, (K, 3M/4) bytes packed along M;
     ``b_order="mn"`` likewise (gemm_mxfp6_ex; with ``workspace``
-    gemm_mxfp6_ex_ws)."""
-    if a_order != "k" or b_order != "k":
+    gemm_mxfp6_ex_ws, which for K-contiguous operands and a workspace of
+    :func:`ex_workspace_bytes` (6, M, N, K) bytes runs on their tile
+    images)."""
+    if a_order != "k" or b_order != "k" or workspace is not None:
         if fmt not in FP6_FORMATS:
             raise ValueError("fmt must be 'e2m3' or 'e3m2'")
         return _mx_ex(fmt, A, SFA, B, SFB, C, out_dtype, D, a_order, b_order, fmt, workspace=workspace)

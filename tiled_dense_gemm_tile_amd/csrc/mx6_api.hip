@@ -220,6 +220,25 @@ gemm_status gemm_mxfp6_ex_ws(int64_t M, int64_t N, int64_t K, const void *A, int
         (b_order != GEMM_K_CONTIGUOUS && b_order != GEMM_MN_CONTIGUOUS))
         return GEMM_ERR_UNSUPPORTED;
     const bool amn = a_order == GEMM_MN_CONTIGUOUS, bmn = b_order == GEMM_MN_CONTIGUOUS;
+    if (workspace && !amn && !bmn && K > 0) {
+        // both K-contiguous: their tile images in the workspace, then the
+        // packed kernel (the same D bit for bit), where the call allows it
+        Common a{M, N, K, A, lda, B, ldb, C, ldc, D, ldd, out_type, 1};
+        bool none = false;
+        gemm_status st = validate_mx6(a, format, SFA, ldsfa, SFB, ldsfb, &none);
+        if (st != GEMM_OK || none) return st;
+        const size_t need = mx6_images_bytes(M, N, K);
+        if (need > 0 && workspace_bytes >= need && (uintptr_t)workspace % 256 == 0 && (uintptr_t)SFA % 16 == 0 &&
+            (uintptr_t)SFB % 16 == 0 && ldsfa % 16 == 0 && ldsfb % 16 == 0) {
+            char *AP = (char *)workspace, *BP = AP + (gemm_mxfp6_packed_bytes(M, K) + 255) / 256 * 256;
+            st = gemm_mxfp6_pack(M, K, A, lda, AP, gemm_mxfp6_packed_bytes(M, K), stream);
+            if (st != GEMM_OK) return st;
+            st = gemm_mxfp6_pack(N, K, B, ldb, BP, gemm_mxfp6_packed_bytes(N, K), stream);
+            if (st != GEMM_OK) return st;
+            return gemm_mxfp6_packed(M, N, K, AP, SFA, ldsfa, BP, SFB, ldsfb, C, ldc, D, ldd, format, out_type,
+                                     stream);
+        }
+    }
     if (!workspace || (!amn && !bmn) || K == 0)
         return gemm_mxfp6_ex(M, N, K, A, lda, a_order, SFA, ldsfa, B, ldb, b_order, SFB, ldsfb, C, ldc, D, ldd,
                              format, out_type, stream);

@@ -138,6 +138,8 @@ extern "C" size_t gemm_ex_workspace_bytes(int element_bits, int64_t M, int64_t N
     if ((element_bits != 16 && element_bits != 8 && element_bits != 6 && element_bits != 4) || M < 0 || N < 0 ||
         K < 0 || M >= kMaxDim || N >= kMaxDim || K >= kMaxDim)
         return 0;
+    if (element_bits == 6 && a_order == GEMM_K_CONTIGUOUS && b_order == GEMM_K_CONTIGUOUS)
+        return mx6_images_bytes(M, N, K);              // (0 unless K % 128 == 0)
     return (a_order == GEMM_MN_CONTIGUOUS ? kc_copy_bytes(element_bits, M, K) : 0) +
            (b_order == GEMM_MN_CONTIGUOUS ? kc_copy_bytes(element_bits, N, K) : 0);
 }

@@ -36,6 +36,15 @@ hipError_t launch_k_contiguous_copy(int bits, const void *src, int64_t lds, int6
 // copies of the MN-contiguous operands and sets the K-contiguous operands
 // (element pointers and leading dimensions in elements) the plain call then
 // takes.  Returns an error before enqueuing anything.
+// fp6 operands both K-contiguous, through a workspace: the tile images of A
+// then of B (gemm_mxfp6_pack), each rounded up to 256 bytes; 0 when K is
+// not a multiple of 128 (no images).
+inline size_t mx6_images_bytes(int64_t M, int64_t N, int64_t K) {
+    const size_t a = gemm_mxfp6_packed_bytes(M, K), b = gemm_mxfp6_packed_bytes(N, K);
+    if (a == 0 || b == 0) return 0;
+    return (a + 255) / 256 * 256 + (b + 255) / 256 * 256;
+}
+
 inline gemm_status k_contiguous_operands(int bits, const Common &a, bool amn, bool bmn, void *ws, size_t ws_bytes,
                                          hipStream_t s, const void **A, int64_t *lda, const void **B,
                                          int64_t *ldb) {

@@ -216,7 +216,11 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
 #pragma unroll
     for (int j = 0; j < LPTA; ++j) {
         if constexpr (SH) {
-            a_off[j] = ((uint32_t)(a_mis0 + sh_row(j) * p.lda * 2) & ~15u) + sh_chk(j) * 16;
+            // (a row that starts on a 16-byte boundary has its 64 elements in
+            // chunks 0 .. 7: its ninth chunk, never read, is not fetched --
+            // an offset past the resource makes no memory request)
+            const uint32_t s_ = (uint32_t)(a_mis0 + sh_row(j) * p.lda * 2);
+            a_off[j] = (sh_chk(j) == 8 && (s_ & 15u) == 0) ? kOOB : (s_ & ~15u) + sh_chk(j) * 16;
         } else {
             const int row = (4 * j + wave) * 8 + (lane >> 3);
             a_off[j] = AT ? mn_off(p.lda, j) : (uint32_t)(row * p.lda * 2) + chunk * 16;
@@ -225,7 +229,8 @@ __global__ void __launch_bounds__(256) gemm_f16_w4t_kernel(F16Args p, F16Epi e) 
 #pragma unroll
     for (int j = 0; j < LPTB; ++j) {
         if constexpr (SH) {
-            b_off[j] = ((uint32_t)(b_mis0 + sh_row(j) * p.ldb * 2) & ~15u) + sh_chk(j) * 16;
+            const uint32_t s_ = (uint32_t)(b_mis0 + sh_row(j) * p.ldb * 2);
+            b_off[j] = (sh_chk(j) == 8 && (s_ & 15u) == 0) ? kOOB : (s_ & ~15u) + sh_chk(j) * 16;
         } else {
             const int row = (4 * j + wave) * 8 + (lane >> 3);
             b_off[j] = BT ? mn_off(p.ldb, j) : (uint32_t)(row * p.ldb * 2) + chunk * 16;

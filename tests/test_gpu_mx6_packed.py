@@ -230,3 +230,37 @@ def test_ex_ws_k_contiguous_uses_images(fmt, case):
                           workspace=ws[:need])
         torch.cuda.synchronize()
         assert np.array_equal(to_f64(D), Dr)
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 128), (1, 300, 256), (257, 1, 384), (16, 16, 8192)],
+                         ids=["1x1x128", "1x300x256", "257x1x384", "16x16x8192"])
+def test_packed_edge_shapes(shape):
+    """Single rows and columns (image blocks almost all padding), one K tile,
+    a long K with a short grid: exact on integer inputs, equal to the plain
+    call."""
+    M, N, K = shape
+    A, B, SFA, SFB, C = _case("e3m2", M, N, K, M * 7 + N * 3 + K, True, True)
+    dSA, dSB = dev_scales(SFA), dev_scales(SFB)
+    AP, BP = tg.mxfp6_pack(dev8(A)), tg.mxfp6_pack(dev8(B))
+    Cd = torch.from_numpy(C).to(DEV)
+    say("mxfp6 packed edge %dx%dx%d" % (M, N, K))
+    D = tg.gemm_mxfp6_packed(AP, dSA, BP, dSB, M, N, K, Cd, fmt="e3m2")
+    Ds = tg.gemm_mxfp6(dev8(A), dSA, dev8(B), dSB, Cd, fmt="e3m2")
+    torch.cuda.synchronize()
+    assert torch.equal(D, Ds)
+    Dr, _ = oracle.gemm_ref_full("e3m2", A, B, C=C, SFA=SFA, SFB=SFB)
+    assert np.array_equal(to_f64(D), Dr)
+
+
+def test_packed_in_place_c_equals_d():
+    """C == D (ldc == ldd): each element read before it is written."""
+    M, N, K = 300, 260, 512
+    A, B, SFA, SFB, C = _case("e2m3", M, N, K, 21, True, True)
+    dSA, dSB = dev_scales(SFA), dev_scales(SFB)
+    AP, BP = tg.mxfp6_pack(dev8(A)), tg.mxfp6_pack(dev8(B))
+    CD = torch.from_numpy(C).to(DEV)
+    say("mxfp6 packed C == D")
+    tg.gemm_mxfp6_packed(AP, dSA, BP, dSB, M, N, K, CD, D=CD)
+    torch.cuda.synchronize()
+    Dr, _ = oracle.gemm_ref_full("e2m3", A, B, C=C, SFA=SFA, SFB=SFB)
+    assert np.array_equal(to_f64(CD), Dr)

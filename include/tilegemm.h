@@ -24,7 +24,10 @@
  *   - Calls are asynchronous: the work is enqueued on `stream` (NULL = the
  *     default stream) and the call returns without synchronising.
  *   - Arguments are validated before anything is enqueued.  On any status
- *     other than GEMM_OK nothing was enqueued and D is untouched.
+ *     other than GEMM_OK and GEMM_ERR_HIP nothing was enqueued and D is
+ *     untouched; GEMM_ERR_HIP (a failed launch) can follow kernels of the
+ *     same call already enqueued (the calls that run a copy, packing or
+ *     reduction kernel beside the GEMM).
  *   - M == 0 or N == 0: GEMM_OK, nothing is launched.  K == 0: D = C (or 0).
  *   - Leading dimensions: lda >= K, ldb >= K, ldc >= N, ldd >= N, else
  *     GEMM_ERR_BAD_LD.  Any such ld is accepted; the load width follows the
